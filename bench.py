@@ -1,0 +1,212 @@
+"""Benchmark: one decode step of query-aware sparse attention over a paged KV
+cache on one MI355X, at 32K context and batch 32 (Llama-3.1-8B-shaped layer:
+32 q / 8 KV heads, head_dim 128, pages of 16 tokens; budget 1 sink + 8 local
++ top-119 pages).
+
+A step = append of the current token (K/V write + page-summary update),
+score_pages, select_topk, sparse_paged_decode (attention + split merge), all
+HIP kernels behind the C ABI, on inputs resident in HBM.  Steps rotate over
+independent layer caches so that no step finds the previous step's data in
+the 256 MB Infinity Cache.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(w, msel_counts):
+    """Algorithmic bytes of one step, split by kernel."""
+    s = w.spec
+    G = s.num_q_heads // s.num_kv_heads
+    lens = w.seq_lens.cpu().tolist()
+    summ_b = 2 * s.head_dim_k * 2
+    kv_b = s.page_size * (s.head_dim_k + (0 if s.v_from_k else s.head_dim_v)) * 2
+    score = decode = 0
+    for b, L in enumerate(lens):
+        P = (L + s.page_size - 1) // s.page_size
+        for g in range(s.num_kv_heads):
+            static = bool(s.static_heads and s.static_heads[g])
+            if not static:
+                C = max(0, P - s.n_sink_pages - s.n_local_pages)
+                score += C * (summ_b + 4 + 8) + G * s.head_dim_k * 2
+            n = int(msel_counts[b][g])
+            decode += n * (kv_b + 4 + 4) + G * s.head_dim_k * 2 + G * s.head_dim_v * 4
+    return score, decode
+
+
+def cpu_baseline(w, msel, n_seqs, threads):
+    """The CPU oracle (test infrastructure) timed on a bounded sample of the
+    workload: the first n_seqs sequences, all KV heads, over precomputed
+    summaries (scores + selection + attention)."""
+    import numpy as np
+    import oracle
+    from query_aware_sparse_paged_amd import workloads
+
+    s = w.spec
+    seqs = list(range(min(n_seqs, s.batch)))
+    pt_full = w.page_table[seqs]
+    valid = pt_full >= 0
+    phys = pt_full[valid].long()
+    k = workloads.bits(w.k_pool[phys])
+    v = None if w.v_pool is None else workloads.bits(w.v_pool[phys])
+    pt = np.full(tuple(pt_full.shape), -1, np.int32)
+    pt[valid.cpu().numpy()] = np.arange(phys.numel(), dtype=np.int32)
+    sl = w.seq_lens[seqs].cpu().numpy()
+    q = workloads.bits(w.q[seqs])
+    lay = oracle.Layout(int(phys.numel()), s.page_size, s.num_kv_heads, s.head_dim_k, s.head_dim_v, s.v_from_k)
+    pol = oracle.Policy(s.n_sink_pages, s.n_local_pages, s.top_k, s.sink_tokens, s.window_tokens, s.static_heads)
+    summ = oracle.summaries(lay, pt, sl, s.num_q_heads, k)
+    t0 = time.perf_counter()
+    oracle.decode(lay, pt, sl, q, k, v, summ, pol, w.scale, num_threads=threads, max_sel_n=msel)
+    dt = time.perf_counter() - t0
+    return {"value": len(seqs) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences (all %d KV heads), one decode step over precomputed summaries, "
+                      "%.2f s wall" % (len(seqs), s.batch, s.num_kv_heads, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_b32_32k")
+    ap.add_argument("--layers", type=int, default=3, help="independent layer caches rotated over")
+    ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-(sequence, KV head) work would shard by batch or KV head with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from query_aware_sparse_paged_amd import api, workloads
+
+    dev = torch.device("cuda:0")
+    layers = []
+    for i in range(args.layers):
+        base = workloads.SPECS[args.workload].seed
+        w = workloads.make(args.workload, seed=base + 100 * i, device=dev)
+        lay, pol = api.layout_of(w), api.policy_of(w)
+        bat = api.Batch(w.page_table, w.seq_lens, w.spec.num_q_heads)
+        bat_before = api.Batch(w.page_table, (w.seq_lens - 1).contiguous(), w.spec.num_q_heads)
+        msel = api.max_sel(lay, pol, bat.max_pages)
+        summ = torch.zeros((w.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16,
+                           device=dev)
+        api.build_summaries(lay, bat, w.k_pool, summ)
+        ws = api.new_workspace(lay, bat, pol, msel, dev)
+        B = w.spec.batch
+        layers.append(dict(w=w, lay=lay, pol=pol, bat=bat, bat_before=bat_before, msel=msel, summ=summ, ws=ws,
+                           scores=torch.empty((B, lay.num_kv_heads, bat.max_pages, 2), dtype=torch.float32,
+                                              device=dev),
+                           sel=torch.empty((B, lay.num_kv_heads, msel), dtype=torch.int32, device=dev),
+                           cnt=torch.empty((B, lay.num_kv_heads), dtype=torch.int32, device=dev),
+                           out=torch.empty((B, w.spec.num_q_heads, lay.head_dim_v), dtype=torch.float32,
+                                           device=dev)))
+        log("layer %d ready: pool %.2f GB" % (i, (w.k_pool.numel() + (0 if w.v_pool is None else w.v_pool.numel()))
+                                               * 2 / 1e9))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    w0 = layers[0]["w"]
+    spec = w0.spec
+
+    def step(L, ev=None):
+        w = L["w"]
+        api.append_kv(L["lay"], L["bat_before"], L["pol"], w.k_new, w.v_new, w.k_pool, w.v_pool, L["summ"])
+        if ev: ev[0].record(stream)
+        api.score_pages(L["lay"], L["bat"], L["pol"], w.q, L["summ"], L["scores"])
+        if ev: ev[1].record(stream)
+        sel, cnt = L["sel"], L["cnt"]
+        api.select_topk(L["lay"], L["bat"], L["pol"], w.q, L["summ"], L["scores"], sel=sel, sel_count=cnt)
+        if ev: ev[2].record(stream)
+        api.sparse_paged_decode(L["lay"], L["bat"], L["pol"], w.q, w.k_pool, w.v_pool, sel, cnt, w.scale,
+                                L["ws"], out=L["out"])
+        if ev: ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(layers[i % len(layers)])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = evs[i]
+        e[4].record(stream)
+        step(layers[i % len(layers)], ev=e)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    score_ms = [e[4].elapsed_time(e[1]) - e[4].elapsed_time(e[0]) for e in evs]
+    select_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    decode_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [e[4].elapsed_time(e[3]) for e in evs]
+    med = statistics.median
+    counts = layers[0]["cnt"].cpu().tolist()
+    b_score, b_decode = step_bytes(w0, counts)
+    total_bytes = b_score + b_decode
+    kern = {"score_pages": (med(score_ms), b_score), "sparse_paged_decode": (med(decode_ms), b_decode)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_ms, dom_bytes = kern[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    tokens_per_s = spec.batch / (ms_per_step * 1e-3)
+    gbps = total_bytes / (ms_per_step * 1e-3) / 1e9
+    log("step events: median %.1f us (p10 %.1f, p90 %.1f); score %.1f us, select %.1f us, decode %.1f us"
+        % (med(step_ms) * 1e3, sorted(step_ms)[len(step_ms) // 10] * 1e3,
+           sorted(step_ms)[(9 * len(step_ms)) // 10] * 1e3, med(score_ms) * 1e3, med(select_ms) * 1e3,
+           med(decode_ms) * 1e3))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(w0, layers[0]["msel"], args.cpu_seqs, threads)
+        log("cpu oracle: %s" % cpu["sample"])
+
+    line = {
+        "metric": "decode tokens/s and achieved KV GB/s (% of MI355X HBM peak), 32K ctx, batch 32",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.batch, "seq_len": spec.seq_len,
+                   "q_heads": spec.num_q_heads, "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim_k,
+                   "page_size": spec.page_size,
+                   "pages_read": "%d sink + %d local + top-%d" % (spec.n_sink_pages, spec.n_local_pages, spec.top_k),
+                   "layer_caches_rotated": args.layers},
+        "kv_gbps": round(gbps, 1),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "step_bytes": total_bytes,
+        "kernel_us": {"score_pages": round(med(score_ms) * 1e3, 2), "select_topk": round(med(select_ms) * 1e3, 2),
+                      "sparse_paged_decode": round(med(decode_ms) * 1e3, 2)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

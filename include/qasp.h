@@ -1,0 +1,209 @@
+/*
+ * qasp: one decode step of query-aware sparse attention over a paged KV cache,
+ * as HIP kernels for AMD CDNA4 (gfx950), behind a C ABI.
+ *
+ * The method (as the pages describe it):
+ *   - the KV cache lives in fixed-size pages scattered through a pool and
+ *     reached through a page table (Vortex explainer, gist.science paper
+ *     2606.06453, section 1: the "paged" library whose boxes are not
+ *     contiguous, and the map that finds the boxes one asks for);
+ *   - at decode time the pages to read are chosen from the current query
+ *     (SparseEngine article, blog.ontle.kr/blog/332, the decode-hook paragraph
+ *     naming Quest; the "dynamic sparse attention" family that keeps every
+ *     token and reads only what the query needs);
+ *   - choosing is logical: nothing is evicted, only the read set shrinks
+ *     (same article, the paragraph separating "not looking" from "discarding");
+ *   - static heads use the A-shape pattern, sink tokens plus a local window,
+ *     with no scoring (SCBench notes, notes.yuuk.io, "Tri-shape" paragraph);
+ *   - attention is computed exactly on the chosen positions (SubQ/SSA
+ *     article, news.neo-ai.one/ja/article/2719, section "How SSA works").
+ * Page summaries are the elementwise min and max of a page's keys; a page's
+ * score is the group maximum of sum_d max(q_d lo_d, q_d hi_d), an upper bound
+ * on q.k for every key in the page.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns and
+ *     allocates every buffer; the library never allocates device memory.
+ *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting for it.
+ *   - Return value: QASP_OK (0) or a negative qasp_status.  Argument checks run
+ *     on the host before anything is enqueued, so an error return means no
+ *     work was queued.  QASP_ERR_LAUNCH reports hipGetLastError after a launch.
+ *   - Device-side data (page table entries, sequence lengths) is trusted:
+ *     page ids outside [0, num_pool_pages) or lengths above
+ *     max_pages * page_size are undefined behaviour.  Inputs must be finite.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef QASP_H
+#define QASP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QASP_OK = 0,
+    QASP_ERR_NULL_ARG = -1,        /* a required pointer is NULL              */
+    QASP_ERR_BAD_SHAPE = -2,       /* negative size, inconsistent dimensions  */
+    QASP_ERR_UNSUPPORTED = -3,     /* a shape the kernels are not built for   */
+    QASP_ERR_WORKSPACE = -4,       /* workspace smaller than qasp_workspace_bytes */
+    QASP_ERR_MAX_SEL = -5,         /* max_sel below qasp_max_sel             */
+    QASP_ERR_LAUNCH = -6           /* a HIP launch failed                     */
+} qasp_status;
+
+/* Pool layout (row-major, bf16):
+ *   k_pool   [num_pool_pages][num_kv_heads][page_size][head_dim_k]
+ *   v_pool   [num_pool_pages][num_kv_heads][head_dim_v][page_size]
+ *            (token index fastest inside a page-head), or NULL when
+ *            v_from_k = 1: the value of a token is then the first head_dim_v
+ *            channels of its key (one latent vector per token, as in MLA).
+ *   summ     [num_pool_pages][num_kv_heads][2][head_dim_k]
+ *            row 0 = elementwise minimum, row 1 = elementwise maximum of the
+ *            keys of the page's valid tokens, with -0 ordered below +0.
+ * Supported shapes:
+ *   grouped-query: page_size 16, head_dim_k = head_dim_v = 128,
+ *                  1 <= num_q_heads / num_kv_heads <= 16, num_kv_heads <= 64;
+ *   latent (MLA):  page_size 64, head_dim_k 576, head_dim_v 512, v_from_k = 1,
+ *                  num_q_heads / num_kv_heads = 128.                         */
+typedef struct {
+    int32_t num_pool_pages;
+    int32_t page_size;
+    int32_t num_kv_heads;
+    int32_t head_dim_k;
+    int32_t head_dim_v;
+    int32_t v_from_k;
+} qasp_layout;
+
+/* A batch of decoding sequences.
+ *   page_table [batch][pt_stride] int32: logical page j of sequence b is
+ *              physical page page_table[b * pt_stride + j];
+ *   seq_lens   [batch] int32: tokens in the cache, the current token included
+ *              (an append with seq_lens = L writes position L);
+ *   max_pages  host-side bound: every ceil(seq_lens[b] / page_size) is
+ *              <= max_pages <= pt_stride.  It sizes scores and grids.
+ * Query q is [batch][num_q_heads][head_dim_k] bf16; q head h reads KV head
+ * h / (num_q_heads / num_kv_heads). */
+typedef struct {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t pt_stride;
+    int32_t max_pages;
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+} qasp_batch;
+
+/* Which pages each KV head reads (logical page ids, per sequence):
+ *   query-aware heads: sink pages [0, n_sink_pages), the local pages
+ *       [P - n_local_pages, P) (the last one may be partial), and the top_k
+ *       remaining pages by score; equal scores go to the lower page id.
+ *   static heads (bit g of static_head_mask set): the tokens t < sink_tokens
+ *       and t >= L - window_tokens; every page holding one is read, the other
+ *       tokens of those pages are masked.  Static heads need no summaries. */
+typedef struct {
+    int32_t n_sink_pages;
+    int32_t n_local_pages;
+    int32_t top_k;
+    int32_t sink_tokens;
+    int32_t window_tokens;
+    uint64_t static_head_mask;
+} qasp_policy;
+
+/* Scores as produced by qasp_score_pages: an fp32 approximation of the exact
+ * group score and a bound on its error, |value - exact| <= err.  Pages that
+ * are not candidates hold value = -inf, err = 0. */
+typedef struct {
+    float value;
+    float err;
+} qasp_score;
+
+/* Library version, "major.minor.patch". */
+const char *qasp_version(void);
+
+/* Human-readable text for a status code (static storage). */
+const char *qasp_status_string(int32_t status);
+
+/* Largest number of pages any KV head can select under `pol`
+ * (n_sink + n_local + top_k for query-aware heads; for static heads the pages
+ * that sink_tokens and window_tokens can touch), capped at max_pages.
+ * Returns a negative status for invalid arguments. */
+int32_t qasp_max_sel(const qasp_layout *lay, const qasp_policy *pol, int32_t max_pages);
+
+/* Bytes of device workspace qasp_decode_step and qasp_sparse_paged_decode need.
+ * The workspace must be zero-filled once after it is allocated (every call
+ * leaves its counters at zero again).  Returns 0 on invalid arguments. */
+size_t qasp_workspace_bytes(const qasp_layout *lay, const qasp_batch *bat,
+                            const qasp_policy *pol, int32_t max_sel);
+
+/* Summaries of every page of every sequence (logical pages
+ * [0, ceil(seq_lens[b] / page_size))), computed from k_pool and written into
+ * summ at the physical pages.  Use after a prefill or to rebuild.  Only the
+ * valid tokens of a partial last page enter its summary. */
+int32_t qasp_build_summaries(const qasp_layout *lay, const qasp_batch *bat,
+                             const uint16_t *k_pool, uint16_t *summ, void *stream);
+
+/* Appends one token per sequence at position seq_lens[b] (the length BEFORE
+ * the append; the caller increments it afterwards) and updates that page's
+ * summary: a token in slot 0 starts the summary, later tokens widen it.
+ *   k_new [batch][num_kv_heads][head_dim_k], v_new [batch][num_kv_heads]
+ *   [head_dim_v] (ignored and may be NULL when v_from_k).
+ * The caller has already mapped page_table[b][seq_lens[b] / page_size].
+ * summ may be NULL only if every KV head is static (then no summary is kept).
+ * A page being appended to must not be shared by two sequences. */
+int32_t qasp_append_kv(const qasp_layout *lay, const qasp_batch *bat_before,
+                       const qasp_policy *pol, const uint16_t *k_new,
+                       const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool,
+                       uint16_t *summ, void *stream);
+
+/* Scores every candidate page of every query-aware head:
+ * scores [batch][num_kv_heads][max_pages] qasp_score. */
+int32_t qasp_score_pages(const qasp_layout *lay, const qasp_batch *bat,
+                         const qasp_policy *pol, const uint16_t *q,
+                         const uint16_t *summ, qasp_score *scores, void *stream);
+
+/* Selects the pages to read, from the scores of qasp_score_pages.  Where the
+ * fp32 scores cannot decide the top_k boundary within their error bounds, the
+ * pages in doubt are re-scored exactly (the correctly rounded fp64 value of
+ * the exact sum) from q and summ, so the selection equals the one the exact
+ * scores give.  Output: sel [batch][num_kv_heads][max_sel] logical page ids in
+ * ascending order, sel_count [batch][num_kv_heads]; entries past the count
+ * are -1.  q and summ may be NULL only if every KV head is static. */
+int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat,
+                         const qasp_policy *pol, const uint16_t *q,
+                         const uint16_t *summ, const qasp_score *scores,
+                         int32_t *sel, int32_t *sel_count, int32_t max_sel,
+                         void *stream);
+
+/* Softmax attention of every query head over the valid tokens of its KV
+ * head's selected pages (static heads: only the sink and window tokens),
+ * split across pages and merged: out [batch][num_q_heads][head_dim_v] fp32.
+ * scale multiplies q.k before the softmax.  A head with no token gets 0.
+ * workspace: >= qasp_workspace_bytes, zero-filled once at allocation. */
+int32_t qasp_sparse_paged_decode(const qasp_layout *lay, const qasp_batch *bat,
+                                 const qasp_policy *pol, const uint16_t *q,
+                                 const uint16_t *k_pool, const uint16_t *v_pool,
+                                 const int32_t *sel, const int32_t *sel_count,
+                                 int32_t max_sel, float scale, float *out,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* One whole decode step on one stream: optional append (when k_new is not
+ * NULL; bat->seq_lens is then the length AFTER the append, the token goes to
+ * position seq_lens[b] - 1), scoring, selection, sparse attention and merge.
+ * Scores and selections live in the workspace; sel / sel_count, when not
+ * NULL, receive a copy of the selection ([batch][num_kv_heads][max_sel]). */
+int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat,
+                         const qasp_policy *pol, const uint16_t *q,
+                         const uint16_t *k_new, const uint16_t *v_new,
+                         uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ,
+                         float scale, float *out, int32_t *sel, int32_t *sel_count,
+                         int32_t max_sel, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

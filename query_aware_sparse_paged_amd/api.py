@@ -1,0 +1,301 @@
+"""Thin ctypes binding of ``include/qasp.h`` (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks
+their dtype/shape/contiguity, and passes raw device pointers plus the current
+HIP stream to ``libqasp.so``.  All computation happens in the HIP kernels;
+there is no CPU path, and a missing library raises ``RuntimeError``.
+bf16 tensors are passed as their 16-bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqasp.so")
+
+OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MAX_SEL, ERR_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+
+
+class QaspError(RuntimeError):
+    def __init__(self, what, status):
+        super().__init__("%s failed: %s (%d)" % (what, status_string(status), status))
+        self.status = status
+
+
+class CLayout(ctypes.Structure):
+    _fields_ = [("num_pool_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32), ("v_from_k", ctypes.c_int32)]
+
+
+class CBatch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("pt_stride", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+class CPolicy(ctypes.Structure):
+    _fields_ = [("n_sink_pages", ctypes.c_int32), ("n_local_pages", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
+                ("window_tokens", ctypes.c_int32), ("static_head_mask", ctypes.c_uint64)]
+
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "qasp_version": (ctypes.c_char_p, []),
+    "qasp_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "qasp_max_sel": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
+    "qasp_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p] * 3 + [ctypes.c_int32]),
+    "qasp_build_summaries": (ctypes.c_int32, [ctypes.c_void_p] * 5),
+    "qasp_append_kv": (ctypes.c_int32, [ctypes.c_void_p] * 9),
+    "qasp_score_pages": (ctypes.c_int32, [ctypes.c_void_p] * 7),
+    "qasp_select_topk": (ctypes.c_int32, [ctypes.c_void_p] * 8 + [ctypes.c_int32, ctypes.c_void_p]),
+    "qasp_sparse_paged_decode": (ctypes.c_int32, [ctypes.c_void_p] * 8 + [ctypes.c_int32, ctypes.c_float,
+                                                                           ctypes.c_void_p, ctypes.c_void_p,
+                                                                           ctypes.c_size_t, ctypes.c_void_p]),
+    "qasp_decode_step": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 3 +
+                         [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+_lib = None
+
+
+def lib():
+    """Loads libqasp.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqasp.so is not built (run __graft_entry__.build() or "
+                               "python query_aware_sparse_paged_amd/build.py); there is no fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qasp_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().qasp_version().decode()
+
+
+@dataclass
+class Layout:
+    num_pool_pages: int
+    page_size: int
+    num_kv_heads: int
+    head_dim_k: int
+    head_dim_v: int
+    v_from_k: bool = False
+
+    def c(self) -> CLayout:
+        return CLayout(self.num_pool_pages, self.page_size, self.num_kv_heads, self.head_dim_k,
+                       self.head_dim_v, int(self.v_from_k))
+
+
+@dataclass
+class Policy:
+    n_sink_pages: int = 1
+    n_local_pages: int = 1
+    top_k: int = 1
+    sink_tokens: int = 0
+    window_tokens: int = 0
+    static_heads: Optional[Sequence[int]] = None
+
+    def mask(self) -> int:
+        m = 0
+        for g, s in enumerate(self.static_heads or []):
+            if s:
+                m |= 1 << g
+        return m
+
+    def c(self) -> CPolicy:
+        return CPolicy(self.n_sink_pages, self.n_local_pages, self.top_k, self.sink_tokens,
+                       self.window_tokens, self.mask())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name, ndim=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims" % (name, ndim))
+    return t
+
+
+def _check(status, what):
+    if status != OK:
+        raise QaspError(what, status)
+
+
+class Batch:
+    """Page table + sequence lengths (device int32) and the host bound max_pages."""
+
+    def __init__(self, page_table: torch.Tensor, seq_lens: torch.Tensor, num_q_heads: int,
+                 max_pages: Optional[int] = None):
+        self.page_table = _dev(page_table, torch.int32, "page_table", 2)
+        self.seq_lens = _dev(seq_lens, torch.int32, "seq_lens", 1)
+        if page_table.shape[0] != seq_lens.shape[0]:
+            raise ValueError("page_table and seq_lens disagree on the batch size")
+        self.num_q_heads = int(num_q_heads)
+        self.max_pages = int(page_table.shape[1] if max_pages is None else max_pages)
+
+    def c(self) -> CBatch:
+        return CBatch(int(self.seq_lens.shape[0]), self.num_q_heads, int(self.page_table.shape[1]),
+                      self.max_pages, self.page_table.data_ptr(), self.seq_lens.data_ptr())
+
+
+def max_sel(layout: Layout, policy: Policy, max_pages: int) -> int:
+    r = lib().qasp_max_sel(ctypes.byref(layout.c()), ctypes.byref(policy.c()), int(max_pages))
+    _check(0 if r >= 0 else r, "qasp_max_sel")
+    return r
+
+
+def workspace_bytes(layout: Layout, batch: Batch, policy: Policy, max_sel_n: int) -> int:
+    return int(lib().qasp_workspace_bytes(ctypes.byref(layout.c()), ctypes.byref(batch.c()),
+                                          ctypes.byref(policy.c()), int(max_sel_n)))
+
+
+def new_workspace(layout: Layout, batch: Batch, policy: Policy, max_sel_n: int, device) -> torch.Tensor:
+    """Zero-filled workspace (the counters in it must start at zero)."""
+    n = workspace_bytes(layout, batch, policy, max_sel_n)
+    if n == 0:
+        raise ValueError("invalid arguments for the workspace size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _u16(t):
+    return t.view(torch.int16) if t is not None else None
+
+
+def build_summaries(layout: Layout, batch: Batch, k_pool: torch.Tensor, summ: torch.Tensor):
+    _dev(k_pool, torch.bfloat16, "k_pool", 4)
+    _dev(summ, torch.bfloat16, "summ", 4)
+    _check(lib().qasp_build_summaries(ctypes.byref(layout.c()), ctypes.byref(batch.c()), _ptr(k_pool),
+                                      _ptr(summ), _stream()), "qasp_build_summaries")
+
+
+def append_kv(layout: Layout, batch_before: Batch, policy: Policy, k_new, v_new, k_pool, v_pool, summ):
+    _dev(k_new, torch.bfloat16, "k_new", 3)
+    _dev(v_new, torch.bfloat16, "v_new", 3)
+    _dev(k_pool, torch.bfloat16, "k_pool", 4)
+    _dev(v_pool, torch.bfloat16, "v_pool", 4)
+    _dev(summ, torch.bfloat16, "summ", 4)
+    _check(lib().qasp_append_kv(ctypes.byref(layout.c()), ctypes.byref(batch_before.c()),
+                                ctypes.byref(policy.c()), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                _ptr(v_pool), _ptr(summ), _stream()), "qasp_append_kv")
+
+
+def score_pages(layout: Layout, batch: Batch, policy: Policy, q, summ, scores=None) -> torch.Tensor:
+    """Returns float32 [B][Hkv][max_pages][2]: (fp32 score, error bound)."""
+    _dev(q, torch.bfloat16, "q", 3)
+    _dev(summ, torch.bfloat16, "summ", 4)
+    B = batch.seq_lens.shape[0]
+    if scores is None:
+        scores = torch.empty((B, layout.num_kv_heads, batch.max_pages, 2), dtype=torch.float32,
+                             device=batch.seq_lens.device)
+    _dev(scores, torch.float32, "scores", 4)
+    _check(lib().qasp_score_pages(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
+                                  _ptr(q), _ptr(summ), _ptr(scores), _stream()), "qasp_score_pages")
+    return scores
+
+
+def select_topk(layout: Layout, batch: Batch, policy: Policy, q, summ, scores, max_sel_n=None, sel=None,
+                sel_count=None):
+    """Returns (sel int32 [B][Hkv][max_sel], sel_count int32 [B][Hkv])."""
+    B = batch.seq_lens.shape[0]
+    dev = batch.seq_lens.device
+    if sel is not None:
+        max_sel_n = int(sel.shape[2])
+    if max_sel_n is None:
+        max_sel_n = max_sel(layout, policy, batch.max_pages)
+    if sel is None:
+        sel = torch.empty((B, layout.num_kv_heads, max_sel_n), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((B, layout.num_kv_heads), dtype=torch.int32, device=dev)
+    cnt = sel_count
+    _dev(sel, torch.int32, "sel", 3)
+    _dev(cnt, torch.int32, "sel_count", 2)
+    _dev(q, torch.bfloat16, "q", 3)
+    _dev(summ, torch.bfloat16, "summ", 4)
+    _dev(scores, torch.float32, "scores", 4)
+    _check(lib().qasp_select_topk(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
+                                  _ptr(q), _ptr(summ), _ptr(scores), _ptr(sel), _ptr(cnt), int(max_sel_n),
+                                  _stream()), "qasp_select_topk")
+    return sel, cnt
+
+
+def sparse_paged_decode(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, sel, sel_count,
+                        scale: float, workspace: torch.Tensor, out=None) -> torch.Tensor:
+    """Returns float32 [B][Hq][Dv]."""
+    _dev(q, torch.bfloat16, "q", 3)
+    _dev(k_pool, torch.bfloat16, "k_pool", 4)
+    _dev(v_pool, torch.bfloat16, "v_pool", 4)
+    _dev(sel, torch.int32, "sel", 3)
+    _dev(sel_count, torch.int32, "sel_count", 2)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    B = batch.seq_lens.shape[0]
+    if out is None:
+        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out", 3)
+    _check(lib().qasp_sparse_paged_decode(ctypes.byref(layout.c()), ctypes.byref(batch.c()),
+                                          ctypes.byref(policy.c()), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(sel), _ptr(sel_count), int(sel.shape[2]), float(scale),
+                                          _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+           "qasp_sparse_paged_decode")
+    return out
+
+
+def decode_step(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, summ, scale: float,
+                workspace: torch.Tensor, max_sel_n: int, k_new=None, v_new=None, out=None, sel=None,
+                sel_count=None) -> torch.Tensor:
+    """Append (if k_new is given; batch.seq_lens then counts the new token),
+    score, select, attend and merge in one call.  Returns out fp32 [B][Hq][Dv]."""
+    for t, name, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
+                        (k_new, "k_new", 3), (v_new, "v_new", 3)):
+        _dev(t, torch.bfloat16, name, nd)
+    _dev(sel, torch.int32, "sel", 3)
+    _dev(sel_count, torch.int32, "sel_count", 2)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    B = batch.seq_lens.shape[0]
+    if out is None:
+        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out", 3)
+    _check(lib().qasp_decode_step(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
+                                  _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(summ),
+                                  float(scale), _ptr(out), _ptr(sel), _ptr(sel_count), int(max_sel_n),
+                                  _ptr(workspace), workspace.numel(), _stream()), "qasp_decode_step")
+    return out
+
+
+def layout_of(w) -> Layout:
+    """Layout of a generated workload (query_aware_sparse_paged_amd.workloads)."""
+    s = w.spec
+    return Layout(w.num_pool_pages, s.page_size, s.num_kv_heads, s.head_dim_k, s.head_dim_v, s.v_from_k)
+
+
+def policy_of(w) -> Policy:
+    s = w.spec
+    return Policy(s.n_sink_pages, s.n_local_pages, s.top_k, s.sink_tokens, s.window_tokens, s.static_heads)

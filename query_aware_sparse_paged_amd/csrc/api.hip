@@ -1,0 +1,287 @@
+// The C ABI of include/qasp.h: host-side argument checks (before any HIP
+// call), workspace layout and launch order.
+#include <string.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace qasp {
+
+hipError_t launch_decode_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                             const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                             const int32_t *sel, const int32_t *sel_count, int max_sel, float scale,
+                             float *out, const Workspace &ws, hipStream_t stream);
+hipError_t launch_decode_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                             const uint16_t *q, const uint16_t *k_pool, const int32_t *sel,
+                             const int32_t *sel_count, int max_sel, float scale, float *out,
+                             const Workspace &ws, hipStream_t stream);
+
+constexpr int kMaxPagesLimit = 16384;  // select keeps 8 bytes per page in LDS
+
+enum Family { kFamilyNone, kFamilyGqa, kFamilyMla };
+
+static Family family_of(const qasp_layout &lay) {
+  if (lay.page_size == 16 && lay.head_dim_k == 128 && lay.head_dim_v == 128 && !lay.v_from_k)
+    return kFamilyGqa;
+  if (lay.page_size == 64 && lay.head_dim_k == 576 && lay.head_dim_v == 512 && lay.v_from_k)
+    return kFamilyMla;
+  return kFamilyNone;
+}
+
+static int32_t check_layout(const qasp_layout *lay) {
+  if (!lay) return QASP_ERR_NULL_ARG;
+  if (lay->num_pool_pages <= 0 || lay->page_size <= 0 || lay->num_kv_heads <= 0 ||
+      lay->head_dim_k <= 0 || lay->head_dim_v <= 0)
+    return QASP_ERR_BAD_SHAPE;
+  if (lay->v_from_k && lay->head_dim_v > lay->head_dim_k) return QASP_ERR_BAD_SHAPE;
+  if (lay->num_kv_heads > 64) return QASP_ERR_UNSUPPORTED;
+  if (family_of(*lay) == kFamilyNone) return QASP_ERR_UNSUPPORTED;
+  return QASP_OK;
+}
+
+static int32_t check_batch(const qasp_layout &lay, const qasp_batch *bat) {
+  if (!bat) return QASP_ERR_NULL_ARG;
+  if (bat->batch < 0 || bat->max_pages < 0 || bat->pt_stride < bat->max_pages || bat->num_q_heads <= 0)
+    return QASP_ERR_BAD_SHAPE;
+  if (bat->num_q_heads % lay.num_kv_heads != 0) return QASP_ERR_BAD_SHAPE;
+  const int G = bat->num_q_heads / lay.num_kv_heads;
+  const Family f = family_of(lay);
+  if (f == kFamilyGqa && G > 16) return QASP_ERR_UNSUPPORTED;
+  if (f == kFamilyMla && G != 128) return QASP_ERR_UNSUPPORTED;
+  if (bat->max_pages > kMaxPagesLimit) return QASP_ERR_UNSUPPORTED;
+  if (bat->batch > 65535) return QASP_ERR_UNSUPPORTED;
+  if (bat->batch > 0 && (!bat->page_table || !bat->seq_lens)) return QASP_ERR_NULL_ARG;
+  return QASP_OK;
+}
+
+static int32_t check_policy(const qasp_layout &lay, const qasp_policy *pol) {
+  if (!pol) return QASP_ERR_NULL_ARG;
+  if (pol->n_sink_pages < 0 || pol->n_local_pages < 0 || pol->top_k < 0 || pol->sink_tokens < 0 ||
+      pol->window_tokens < 0)
+    return QASP_ERR_BAD_SHAPE;
+  if (lay.num_kv_heads < 64 && (pol->static_head_mask >> lay.num_kv_heads) != 0) return QASP_ERR_BAD_SHAPE;
+  return QASP_OK;
+}
+
+static bool all_static(const qasp_layout &lay, const qasp_policy &pol) {
+  const uint64_t all = lay.num_kv_heads == 64 ? ~0ull : ((1ull << lay.num_kv_heads) - 1);
+  return (pol.static_head_mask & all) == all;
+}
+
+static int32_t max_sel_of(const qasp_layout &lay, const qasp_policy &pol, int32_t max_pages) {
+  const int64_t ps = lay.page_size;
+  const int64_t qa = (int64_t)pol.n_sink_pages + pol.n_local_pages + pol.top_k;
+  const int64_t st = ((int64_t)pol.sink_tokens + ps - 1) / ps + ((int64_t)pol.window_tokens + ps - 1) / ps + 1;
+  int64_t m = qa > st ? qa : st;
+  if (m > max_pages) m = max_pages;
+  return (int32_t)m;
+}
+
+int decode_splits(const qasp_layout &lay, int max_sel) {
+  const int per = family_of(lay) == kFamilyMla ? kMlaPagesPerSplit : kGqaPagesPerSplit;
+  const int s = (max_sel + per - 1) / per;
+  return s < 1 ? 1 : s;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
+  const size_t units = (size_t)bat.batch * lay.num_kv_heads;
+  const size_t splits = (size_t)decode_splits(lay, max_sel);
+  size_t n = 0;
+  n += align256(units * (size_t)bat.max_pages * sizeof(qasp_score));
+  n += align256(units * (size_t)max_sel * sizeof(int32_t));
+  n += align256(units * sizeof(int32_t));
+  n += align256(units * sizeof(uint32_t));
+  n += align256((size_t)bat.batch * bat.num_q_heads * splits * lay.head_dim_v * sizeof(float));
+  n += align256((size_t)bat.batch * bat.num_q_heads * splits * sizeof(float2));
+  return n;
+}
+
+Workspace carve_workspace(const qasp_layout &lay, const qasp_batch &bat, int max_sel, void *base) {
+  Workspace w;
+  const size_t units = (size_t)bat.batch * lay.num_kv_heads;
+  w.splits = decode_splits(lay, max_sel);
+  char *p = (char *)base;
+  w.scores = (qasp_score *)p;
+  p += align256(units * (size_t)bat.max_pages * sizeof(qasp_score));
+  w.sel = (int32_t *)p;
+  p += align256(units * (size_t)max_sel * sizeof(int32_t));
+  w.sel_count = (int32_t *)p;
+  p += align256(units * sizeof(int32_t));
+  w.counters = (uint32_t *)p;
+  p += align256(units * sizeof(uint32_t));
+  w.partial = (float *)p;
+  p += align256((size_t)bat.batch * bat.num_q_heads * w.splits * lay.head_dim_v * sizeof(float));
+  w.partial_ml = (float2 *)p;
+  return w;
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t value, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_decode(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                const int32_t *sel, const int32_t *sel_count, int max_sel, float scale,
+                                float *out, const Workspace &ws, hipStream_t stream) {
+  if (bat.batch == 0) return hipSuccess;
+  if (family_of(lay) == kFamilyGqa)
+    return launch_decode_gqa(lay, bat, pol, q, k_pool, v_pool, sel, sel_count, max_sel, scale, out, ws,
+                             stream);
+  return launch_decode_mla(lay, bat, pol, q, k_pool, sel, sel_count, max_sel, scale, out, ws, stream);
+}
+
+static int32_t status_of(hipError_t e) { return e == hipSuccess ? QASP_OK : QASP_ERR_LAUNCH; }
+
+}  // namespace qasp
+
+using namespace qasp;
+
+extern "C" {
+
+const char *qasp_version(void) { return "0.1.0"; }
+
+const char *qasp_status_string(int32_t status) {
+  switch (status) {
+    case QASP_OK: return "ok";
+    case QASP_ERR_NULL_ARG: return "a required pointer is NULL";
+    case QASP_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
+    case QASP_ERR_UNSUPPORTED: return "shape not supported by the kernels";
+    case QASP_ERR_WORKSPACE: return "workspace too small";
+    case QASP_ERR_MAX_SEL: return "max_sel smaller than the largest possible selection";
+    case QASP_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t qasp_max_sel(const qasp_layout *lay, const qasp_policy *pol, int32_t max_pages) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (max_pages < 0) return QASP_ERR_BAD_SHAPE;
+  return max_sel_of(*lay, *pol, max_pages);
+}
+
+size_t qasp_workspace_bytes(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                            int32_t max_sel) {
+  if (check_layout(lay) != QASP_OK || check_batch(*lay, bat) != QASP_OK || check_policy(*lay, pol) != QASP_OK)
+    return 0;
+  if (max_sel < 0) return 0;
+  return workspace_bytes(*lay, *bat, max_sel);
+}
+
+int32_t qasp_build_summaries(const qasp_layout *lay, const qasp_batch *bat, const uint16_t *k_pool,
+                             uint16_t *summ, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if (bat->batch == 0) return QASP_OK;
+  if (!k_pool || !summ) return QASP_ERR_NULL_ARG;
+  return status_of(launch_build_summaries(*lay, *bat, k_pool, summ, (hipStream_t)stream));
+}
+
+int32_t qasp_append_kv(const qasp_layout *lay, const qasp_batch *bat_before, const qasp_policy *pol,
+                       const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool,
+                       uint16_t *summ, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat_before)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (bat_before->batch == 0) return QASP_OK;
+  if (!k_new || !k_pool) return QASP_ERR_NULL_ARG;
+  if (!lay->v_from_k && (!v_new || !v_pool)) return QASP_ERR_NULL_ARG;
+  if (!summ && !all_static(*lay, *pol)) return QASP_ERR_NULL_ARG;
+  return status_of(launch_append_kv(*lay, *bat_before, 0, k_new, v_new, k_pool, v_pool, summ,
+                                    (hipStream_t)stream));
+}
+
+int32_t qasp_score_pages(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                         const uint16_t *q, const uint16_t *summ, qasp_score *scores, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (bat->batch == 0 || bat->max_pages == 0) return QASP_OK;
+  if (!scores) return QASP_ERR_NULL_ARG;
+  if (!all_static(*lay, *pol) && (!q || !summ)) return QASP_ERR_NULL_ARG;
+  return status_of(launch_score_pages(*lay, *bat, *pol, q, summ, scores, (hipStream_t)stream));
+}
+
+int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                         const uint16_t *q, const uint16_t *summ, const qasp_score *scores, int32_t *sel,
+                         int32_t *sel_count, int32_t max_sel, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  if (max_sel < max_sel_of(*lay, *pol, bat->max_pages)) return QASP_ERR_MAX_SEL;
+  if (bat->batch == 0) return QASP_OK;
+  if (!sel || !sel_count) return QASP_ERR_NULL_ARG;
+  if (!all_static(*lay, *pol) && (!q || !summ || !scores)) return QASP_ERR_NULL_ARG;
+  return status_of(launch_select_topk(*lay, *bat, *pol, q, summ, scores, sel, sel_count, max_sel, nullptr,
+                                      (hipStream_t)stream));
+}
+
+int32_t qasp_sparse_paged_decode(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                                 const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                 const int32_t *sel, const int32_t *sel_count, int32_t max_sel, float scale,
+                                 float *out, void *workspace, size_t workspace_bytes_given, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  if (bat->batch == 0) return QASP_OK;
+  if (!q || !k_pool || !sel || !sel_count || !out || !workspace) return QASP_ERR_NULL_ARG;
+  if (!lay->v_from_k && !v_pool) return QASP_ERR_NULL_ARG;
+  if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
+  return status_of(launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel, sel_count, max_sel, scale,
+                                        out, ws, (hipStream_t)stream));
+}
+
+int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                         const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                         uint16_t *v_pool, uint16_t *summ, float scale, float *out, int32_t *sel,
+                         int32_t *sel_count, int32_t max_sel, void *workspace, size_t workspace_bytes_given,
+                         void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  if (max_sel < max_sel_of(*lay, *pol, bat->max_pages)) return QASP_ERR_MAX_SEL;
+  if (bat->batch == 0) return QASP_OK;
+  if (!q || !k_pool || !out || !workspace) return QASP_ERR_NULL_ARG;
+  if (!lay->v_from_k && !v_pool) return QASP_ERR_NULL_ARG;
+  const bool scored = !all_static(*lay, *pol);
+  if (scored && !summ) return QASP_ERR_NULL_ARG;
+  if (k_new && !lay->v_from_k && !v_new) return QASP_ERR_NULL_ARG;
+  if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
+  if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t *sel_out = sel ? sel : ws.sel;
+  int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
+  hipError_t e = hipSuccess;
+  if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
+  if (e == hipSuccess && scored) e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s);
+  if (e == hipSuccess)
+    e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, ws.counters, s);
+  if (e == hipSuccess)
+    e = launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
+  return status_of(e);
+}
+
+}  // extern "C"

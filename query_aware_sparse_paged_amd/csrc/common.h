@@ -1,0 +1,109 @@
+// Device-side helpers shared by the qasp kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qasp.h"
+
+namespace qasp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 bit tricks
+// ---------------------------------------------------------------------------
+
+// Order-preserving signed key of a bf16 pattern: numeric order, -0 below +0.
+// Negative patterns have their magnitude bits flipped so that a larger
+// magnitude gives a smaller key.
+__device__ __forceinline__ int bf16_order_key(uint32_t bits16) {
+  int s = (int)(int16_t)(uint16_t)bits16;
+  return s >= 0 ? s : (s ^ 0x7fff);
+}
+__device__ __forceinline__ uint32_t bf16_from_order_key(int key) {
+  int s = key >= 0 ? key : (key ^ 0x7fff);
+  return (uint32_t)(uint16_t)(int16_t)s;
+}
+
+// Two bf16 in a dword: keep each half whose sign bit is set / clear.
+__device__ __forceinline__ uint32_t bf16x2_negative_part(uint32_t w) {
+  uint32_t m = ((w & 0x80008000u) >> 15) * 0xffffu;
+  return w & m;
+}
+__device__ __forceinline__ uint32_t bf16x2_positive_part(uint32_t w) {
+  uint32_t m = ((w & 0x80008000u) >> 15) * 0xffffu;
+  return w & ~m;
+}
+__device__ __forceinline__ uint32_t bf16x2_abs(uint32_t w) { return w & 0x7fff7fffu; }
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (operands as raw dwords)
+// ---------------------------------------------------------------------------
+
+// D(16x16) += A(16x32) B(32x16), bf16 in, fp32 accumulate.  Lane l holds row
+// (l % 16) of A and column (l % 16) of B, eight consecutive k each; the k
+// blocks of lanes l and l' pair up when l / 16 == l' / 16.
+__device__ __forceinline__ floatx4 mfma16x16x32(uint4 a, uint4 b, floatx4 c) {
+  bf16x8 av = __builtin_bit_cast(bf16x8, a);
+  bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x16) B(16x16), bf16 in, fp32 accumulate, four k per lane.
+// Output layout: lane l holds D[4 * (l / 16) + r][l % 16], r = 0..3.
+__device__ __forceinline__ floatx4 mfma16x16x16(uint2 a, uint2 b, floatx4 c) {
+  short4v av = __builtin_bit_cast(short4v, a);
+  short4v bv = __builtin_bit_cast(short4v, b);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions (wave64)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    int lo = __shfl_xor((int)(uint32_t)(uint64_t)v, o, kWave);
+    int hi = __shfl_xor((int)(uint32_t)((uint64_t)v >> 32), o, kWave);
+    v += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// geometry
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int num_pages_of(int L, int ps) { return L <= 0 ? 0 : (L + ps - 1) / ps; }
+
+__device__ __forceinline__ bool head_is_static(uint64_t mask, int g) {
+  return (mask >> g) & 1ull;
+}
+
+}  // namespace qasp

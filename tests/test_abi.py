@@ -1,0 +1,127 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from query_aware_sparse_paged_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qasp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qasp_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(api.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return api.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert "qasp_decode_step" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(api.EXPORTS)
+
+
+def test_version_and_status_strings(L):
+    assert re.match(r"^\d+\.\d+\.\d+$", api.version())
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert api.status_string(s) != "unknown status"
+    assert api.status_string(-99) == "unknown status"
+
+
+GQA = api.Layout(512, 16, 8, 128, 128)
+MLA = api.Layout(64, 64, 1, 576, 512, True)
+
+
+def _batch(B=1, Hq=32, stride=300, max_pages=256, pt=0x1000, sl=0x2000):
+    return api.CBatch(B, Hq, stride, max_pages, pt, sl)
+
+
+def _call(fn, *args):
+    return getattr(api.lib(), fn)(*args)
+
+
+def test_null_and_shape_errors(L):
+    b = ctypes.byref
+    lay, pol = GQA.c(), api.Policy(1, 4, 32).c()
+    bat = _batch()
+    assert _call("qasp_build_summaries", None, b(bat), 1, 1, None) == api.ERR_NULL_ARG
+    assert _call("qasp_build_summaries", b(lay), None, 1, 1, None) == api.ERR_NULL_ARG
+    assert _call("qasp_build_summaries", b(lay), b(bat), None, 1, None) == api.ERR_NULL_ARG
+    bad = api.CLayout(0, 16, 8, 128, 128, 0)
+    assert _call("qasp_build_summaries", b(bad), b(bat), 1, 1, None) == api.ERR_BAD_SHAPE
+    for shape in [(512, 32, 8, 128, 128, 0), (512, 16, 8, 64, 64, 0), (512, 64, 1, 576, 512, 0),
+                  (512, 16, 80, 128, 128, 0)]:
+        assert _call("qasp_build_summaries", b(api.CLayout(*shape)), b(bat), 1, 1, None) == api.ERR_UNSUPPORTED
+    assert _call("qasp_score_pages", b(lay), b(_batch(Hq=30)), b(pol), 1, 1, 1, None) == api.ERR_BAD_SHAPE
+    assert _call("qasp_score_pages", b(lay), b(_batch(Hq=8 * 17)), b(pol), 1, 1, 1, None) == api.ERR_UNSUPPORTED
+    assert _call("qasp_score_pages", b(lay), b(_batch(stride=100)), b(pol), 1, 1, 1, None) == api.ERR_BAD_SHAPE
+    assert _call("qasp_score_pages", b(lay), b(_batch(max_pages=20000, stride=20000)), b(pol), 1, 1, 1,
+                 None) == api.ERR_UNSUPPORTED
+    neg = api.Policy(1, -1, 3).c()
+    assert _call("qasp_score_pages", b(lay), b(bat), b(neg), 1, 1, 1, None) == api.ERR_BAD_SHAPE
+    stray = api.CPolicy(1, 1, 3, 0, 0, 1 << 9)   # static bit beyond the 8 KV heads
+    assert _call("qasp_score_pages", b(lay), b(bat), b(stray), 1, 1, 1, None) == api.ERR_BAD_SHAPE
+    assert _call("qasp_score_pages", b(lay), b(bat), b(pol), None, 1, 1, None) == api.ERR_NULL_ARG
+    # MLA needs 128 q heads per latent head
+    assert _call("qasp_score_pages", b(MLA.c()), b(_batch(Hq=64)), b(pol), 1, 1, 1, None) == api.ERR_UNSUPPORTED
+
+
+def test_max_sel_and_workspace_checks(L):
+    b = ctypes.byref
+    lay = GQA.c()
+    pol = api.Policy(1, 4, 32)
+    assert api.max_sel(GQA, pol, 256) == 37
+    assert api.max_sel(GQA, pol, 20) == 20
+    assert api.max_sel(GQA, api.Policy(1, 8, 55, 4, 1024, [1, 1, 1, 1, 0, 0, 0, 0]), 4097) == 66
+    bat = _batch()
+    # select with max_sel below the bound
+    assert _call("qasp_select_topk", b(lay), b(bat), b(pol.c()), 1, 1, 1, 1, 1, 36, None) == api.ERR_MAX_SEL
+    assert _call("qasp_decode_step", b(lay), b(bat), b(pol.c()), 1, None, None, 1, 1, 1, 1.0, 1, None, None,
+                 36, 1, 1 << 30, None) == api.ERR_MAX_SEL
+    need = _call("qasp_workspace_bytes", b(lay), b(bat), b(pol.c()), 37)
+    assert need > 0
+    assert _call("qasp_sparse_paged_decode", b(lay), b(bat), b(pol.c()), 1, 1, 1, 1, 1, 37, 1.0, 1, 1,
+                 need - 1, None) == api.ERR_WORKSPACE
+    assert _call("qasp_decode_step", b(lay), b(bat), b(pol.c()), 1, None, None, 1, 1, 1, 1.0, 1, None, None,
+                 37, 1, need - 1, None) == api.ERR_WORKSPACE
+    # sel and sel_count come together
+    assert _call("qasp_decode_step", b(lay), b(bat), b(pol.c()), 1, None, None, 1, 1, 1, 1.0, 1, 1, None,
+                 37, 1, need, None) == api.ERR_NULL_ARG
+    assert _call("qasp_workspace_bytes", None, b(bat), b(pol.c()), 37) == 0
+
+
+def test_static_only_heads_need_no_summaries(L):
+    b = ctypes.byref
+    lay = GQA.c()
+    pol = api.Policy(0, 0, 0, 4, 64, [1] * 8).c()
+    # empty batch: valid and returns before any launch, even with NULL summaries
+    empty = _batch(B=0)
+    assert _call("qasp_decode_step", b(lay), b(empty), b(pol), 1, None, None, 1, 1, None, 1.0, 1, None, None,
+                 6, 1, 1 << 20, None) == api.OK
+    qa = api.Policy(1, 1, 1).c()
+    assert _call("qasp_decode_step", b(lay), b(_batch()), b(qa), 1, None, None, 1, 1, None, 1.0, 1, None,
+                 None, 256, 1, 1 << 30, None) == api.ERR_NULL_ARG
+    assert _call("qasp_append_kv", b(lay), b(_batch()), b(qa), 1, 1, 1, 1, None, None) == api.ERR_NULL_ARG
+
+
+def test_empty_batch_is_a_no_op(L):
+    b = ctypes.byref
+    lay, pol = GQA.c(), api.Policy(1, 4, 32).c()
+    empty = _batch(B=0)
+    assert _call("qasp_build_summaries", b(lay), b(empty), None, None, None) == api.OK
+    assert _call("qasp_score_pages", b(lay), b(empty), b(pol), None, None, None, None) == api.OK
+    assert _call("qasp_select_topk", b(lay), b(empty), b(pol), None, None, None, None, None, 37, None) == api.OK
+    assert _call("qasp_sparse_paged_decode", b(lay), b(empty), b(pol), None, None, None, None, None, 37, 1.0,
+                 None, None, 0, None) == api.OK

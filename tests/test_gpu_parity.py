@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: summaries and selected page ids bit-exact, every fp32 score within its
+own error bound of the exact score, attention outputs within 5e-3 max-abs.
+Small cases run the oracle on everything; full-size workloads run the oracle
+on sampled sequences and check size-independent properties on the rest.
+"""
+import numpy as np
+import pytest
+import torch
+
+from query_aware_sparse_paged_amd import api, workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_cases import DEV, compare, gpu_summaries_of, run_gpu, run_oracle
+
+
+def _small(name, **kw):
+    return workloads.make(name, device="cpu", **kw)
+
+
+def _check_full(w, g, seqs):
+    r = run_oracle(w, api.policy_of(w), g.max_sel, seqs=seqs)
+    assert np.array_equal(gpu_summaries_of(g, w, seqs, r), r.summ), "summaries differ"
+    return compare(g, r, seqs=seqs, what=w.spec.name)
+
+
+# ----------------------------------------------------------------------------
+# small cases: oracle on every sequence
+# ----------------------------------------------------------------------------
+
+def test_tiny_config_exact():
+    w = _small("tiny_b1_4k")
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    k_phys = w.page_table[0, :256].long()
+    assert np.array_equal(workloads.bits(g.summ.cpu()[k_phys]), r.summ[k_phys.numpy()])
+    compare(g, r, what="tiny_b1_4k")
+    assert (g.cnt == 37).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_llama_shape_ragged_small(seed):
+    w = _small("llama8b_b32_32k", seed=seed, batch=3, seq_len=3001, seq_len_min=1500)
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="llama small")
+
+
+def test_needles_small_all_found():
+    w = _small("needle_b8_128k", batch=2, seq_len=12000)
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="needle small")
+    for b in range(2):
+        pages = set((w.needle_pos[b] // 16).tolist())
+        for h in range(8):
+            assert pages <= set(g.sel[b, h, :g.cnt[b, h]].tolist())
+
+
+def test_ragged_mixed_static_small():
+    w = _small("ragged_b64_mixed", batch=5, seq_len=4000, seq_len_min=1)
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="ragged small")
+
+
+@pytest.mark.parametrize("lens,pol", [
+    ([1, 16, 17, 33], api.Policy(1, 1, 2)),
+    ([5, 40, 129, 300], api.Policy(0, 0, 3)),
+    ([200, 201, 64, 95], api.Policy(3, 2, 0)),
+    ([250, 7, 90, 1000], api.Policy(1, 4, 1000)),
+    ([513, 700, 31, 48], api.Policy(2, 1, 5, 3, 40, [1, 0, 1, 0, 0, 0, 1, 1])),
+])
+def test_edges(lens, pol):
+    w = _small("tiny_b1_4k", batch=len(lens), seq_len=max(lens))
+    w.seq_lens[:] = torch.tensor(lens, dtype=torch.int32)
+    # the new token of each sequence is the one at its (new) last position
+    ps = 16
+    for b, L in enumerate(lens):
+        phys = int(w.page_table[b, (L - 1) // ps])
+        w.k_new[b] = w.k_pool[phys, :, (L - 1) % ps, :]
+        w.v_new[b] = w.v_pool[phys, :, :, (L - 1) % ps]
+    g = run_gpu(w, pol=pol)
+    r = run_oracle(w, pol, g.max_sel)
+    compare(g, r, what="edge %s" % lens)
+
+
+def test_all_static_heads_without_summaries():
+    w = _small("ragged_b64_mixed", batch=3, seq_len=3000, seq_len_min=10)
+    pol = api.Policy(0, 0, 0, 4, 100, [1] * 8)
+    g = run_gpu(w, pol=pol, use_summ=False)
+    r = run_oracle(w, pol, g.max_sel)
+    compare(g, r, check_scores=False, what="all static")
+
+
+def test_zero_query_ties_go_to_lowest_ids():
+    w = _small("llama8b_b32_32k", batch=2, seq_len=3000)
+    w.q.zero_()
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="zero query")
+    P = 188
+    want = list(range(0, 1 + 119)) + list(range(P - 8, P))
+    assert g.sel[0, 0, :128].tolist() == want
+
+
+def test_integer_keys_many_ties():
+    w = _small("tiny_b1_4k", batch=2, seq_len=1500)
+    gen = torch.Generator().manual_seed(3)
+    w.k_pool.copy_(torch.randint(-2, 3, w.k_pool.shape, generator=gen).to(torch.bfloat16))
+    w.q.copy_(torch.randint(-1, 2, w.q.shape, generator=gen).to(torch.bfloat16))
+    for b in range(2):
+        L = int(w.seq_lens[b])
+        w.k_new[b] = w.k_pool[int(w.page_table[b, (L - 1) // 16]), :, (L - 1) % 16, :]
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="integer ties")
+
+
+def test_exact_rescore_needs_tiny_terms():
+    """Pages whose bounds differ only through a term 2^-80 below the others:
+    the exact re-score must keep it (1 + 2^-53 + 2^-80 rounds up, 1 + 2^-53
+    ties to even and rounds down)."""
+    w = _small("tiny_b1_4k", batch=1, seq_len=16 * 12)
+    w.q.zero_()
+    w.k_pool.zero_()
+    f = lambda x: torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+    # q head 0 of KV head 0: channel 0 = 1, channel 1 = 2^-27, channel 2 = 2^-40
+    w.q[0, 0, 0], w.q[0, 0, 1], w.q[0, 0, 2] = f(1.0), f(2.0 ** -27), f(2.0 ** -40)
+    pt = w.page_table[0]
+    # page 3: 1 + 2^-53 + 2^-80 -> 1 + 2^-52 ; page 5: 1 + 2^-53 -> 1 ;
+    # page 7: 1 + 2^-52 exactly (2^-26 * 2^-26) -> ties with page 3, lower id wins
+    for j, (c1, c2) in {3: (2.0 ** -26, 2.0 ** -40), 5: (2.0 ** -26, 0.0)}.items():
+        w.k_pool[int(pt[j]), 0, :, 0] = f(1.0)
+        w.k_pool[int(pt[j]), 0, :, 1] = f(c1)
+        w.k_pool[int(pt[j]), 0, :, 2] = f(c2)
+    w.k_pool[int(pt[7]), 0, :, 0] = f(1.0)
+    w.k_pool[int(pt[7]), 0, :, 1] = f(2.0 ** -25)
+    w.k_new.zero_()
+    pol = api.Policy(1, 1, 1)
+    g = run_gpu(w, pol=pol, append=False)
+    r = run_oracle(w, pol, g.max_sel)
+    compare(g, r, what="tiny terms")
+    assert g.sel[0, 0, :3].tolist() == [0, 3, 11]
+
+
+def test_append_updates_summaries_incrementally():
+    """Append 16 tokens one at a time (at most one new page per sequence, the
+    spare one the generator maps); summaries must equal a rebuild."""
+    w = _small("llama8b_b32_32k", batch=3, seq_len=100, seq_len_min=40)
+    lay, pol = api.layout_of(w), api.policy_of(w)
+    kp, vp = w.k_pool.to(DEV), w.v_pool.to(DEV)
+    pt = w.page_table.to(DEV)
+    lens = w.seq_lens.clone()
+    summ = torch.zeros((lay.num_pool_pages, 8, 2, 128), dtype=torch.bfloat16, device=DEV)
+    api.build_summaries(lay, api.Batch(pt, lens.to(DEV), 32), kp, summ)
+    gen = torch.Generator().manual_seed(9)
+    for step in range(16):
+        kn = torch.randn((3, 8, 128), generator=gen).to(torch.bfloat16)
+        vn = torch.randn((3, 8, 128), generator=gen).to(torch.bfloat16)
+        # the spare page covers a crossing into a new page
+        api.append_kv(lay, api.Batch(pt, lens.to(DEV), 32), pol, kn.to(DEV), vn.to(DEV), kp, vp, summ)
+        lens += 1
+    torch.cuda.synchronize()
+    rebuilt = torch.zeros_like(summ)
+    api.build_summaries(lay, api.Batch(pt, lens.to(DEV), 32), kp, rebuilt)
+    torch.cuda.synchronize()
+    used = []
+    for b in range(3):
+        used += w.page_table[b, :(int(lens[b]) + 15) // 16].tolist()
+    used = torch.tensor(used, device=DEV)
+    assert torch.equal(summ[used].view(torch.int16), rebuilt[used].view(torch.int16))
+    import oracle
+    from gpu_cases import olayout
+    osumm = oracle.summaries(olayout(lay), w.page_table.numpy(), lens.numpy(), 32, workloads.bits(kp))
+    assert np.array_equal(workloads.bits(summ[used]), osumm[used.cpu().numpy()])
+
+
+def test_split_entry_points_match_decode_step():
+    w = _small("llama8b_b32_32k", batch=2, seq_len=2500)
+    lay, pol = api.layout_of(w), api.policy_of(w)
+    g = run_gpu(w)
+    q, kp, vp = w.q.to(DEV), w.k_pool.to(DEV), w.v_pool.to(DEV)
+    bat = api.Batch(w.page_table.to(DEV), w.seq_lens.to(DEV), 32)
+    sc = api.score_pages(lay, bat, pol, q, g.summ)
+    sel, cnt = api.select_topk(lay, bat, pol, q, g.summ, sc)
+    ws = api.new_workspace(lay, bat, pol, sel.shape[2], DEV)
+    out = api.sparse_paged_decode(lay, bat, pol, q, kp, vp, sel, cnt, w.scale, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), g.sel)
+    assert np.array_equal(out.cpu().numpy(), g.out)
+
+
+def test_repeated_calls_are_deterministic():
+    w = _small("llama8b_b32_32k", batch=4, seq_len=4000)
+    a = run_gpu(w)
+    b = run_gpu(w)
+    assert np.array_equal(a.sel, b.sel) and np.array_equal(a.out, b.out)
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads: sampled sequences against the oracle
+# ----------------------------------------------------------------------------
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_full_llama8b_b32_32k():
+    w = workloads.make("llama8b_b32_32k", device=DEV)
+    g = run_gpu(w)
+    assert (g.cnt == 128).all()
+    assert (np.diff(g.sel, axis=2) > 0).all()
+    _check_full(w, g, [0, 17, 31])
+    del w, g
+    _free()
+
+
+def test_full_needle_b8_128k():
+    w = workloads.make("needle_b8_128k", device=DEV)
+    g = run_gpu(w, with_scores=False)
+    assert (g.cnt == 256).all()
+    for b in range(8):
+        pages = set((w.needle_pos[b] // 16).tolist())
+        for h in range(8):
+            assert pages <= set(g.sel[b, h].tolist())
+    _check_full(w, g, [5])
+    del w, g
+    _free()
+
+
+def test_full_ragged_b64_mixed():
+    w = workloads.make("ragged_b64_mixed", device=DEV)
+    g = run_gpu(w, with_scores=False)
+    assert (g.cnt[:, 4:] == 64).all()
+    assert ((g.cnt[:, :4] >= 65) & (g.cnt[:, :4] <= 66)).all()
+    lens = w.seq_lens.cpu().numpy()
+    _check_full(w, g, [int(np.argmin(lens)), int(np.argmax(lens)), 7])
+    del w, g
+    _free()
