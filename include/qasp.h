@@ -132,9 +132,9 @@ const char *qasp_status_string(int32_t status);
  * Returns a negative status for invalid arguments. */
 int32_t qasp_max_sel(const qasp_layout *lay, const qasp_policy *pol, int32_t max_pages);
 
-/* Bytes of device workspace qasp_decode_step and qasp_sparse_paged_decode need.
- * The workspace must be zero-filled once after it is allocated (every call
- * leaves its counters at zero again).  Returns 0 on invalid arguments. */
+/* Bytes of device workspace qasp_decode_step and qasp_sparse_paged_decode need
+ * (scores, selections and the split partials of the attention).  Its content
+ * needs no initialisation.  Returns 0 on invalid arguments. */
 size_t qasp_workspace_bytes(const qasp_layout *lay, const qasp_batch *bat,
                             const qasp_policy *pol, int32_t max_sel);
 
@@ -181,7 +181,7 @@ int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat,
  * head's selected pages (static heads: only the sink and window tokens),
  * split across pages and merged: out [batch][num_q_heads][head_dim_v] fp32.
  * scale multiplies q.k before the softmax.  A head with no token gets 0.
- * workspace: >= qasp_workspace_bytes, zero-filled once at allocation. */
+ * workspace: >= qasp_workspace_bytes. */
 int32_t qasp_sparse_paged_decode(const qasp_layout *lay, const qasp_batch *bat,
                                  const qasp_policy *pol, const uint16_t *q,
                                  const uint16_t *k_pool, const uint16_t *v_pool,

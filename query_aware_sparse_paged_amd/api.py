@@ -16,7 +16,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqasp.so")
+# QASP_LIB may point at another build of the same library (e.g. a tuning build)
+LIB_PATH = os.environ.get("QASP_LIB") or os.path.join(_HERE, "libqasp.so")
 
 OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MAX_SEL, ERR_LAUNCH = 0, -1, -2, -3, -4, -5, -6
 
@@ -179,11 +180,11 @@ def workspace_bytes(layout: Layout, batch: Batch, policy: Policy, max_sel_n: int
 
 
 def new_workspace(layout: Layout, batch: Batch, policy: Policy, max_sel_n: int, device) -> torch.Tensor:
-    """Zero-filled workspace (the counters in it must start at zero)."""
+    """Workspace of qasp_workspace_bytes bytes (no initialisation needed)."""
     n = workspace_bytes(layout, batch, policy, max_sel_n)
     if n == 0:
         raise ValueError("invalid arguments for the workspace size")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def _u16(t):

@@ -77,22 +77,30 @@ static int32_t max_sel_of(const qasp_layout &lay, const qasp_policy &pol, int32_
   return (int32_t)m;
 }
 
-int decode_splits(const qasp_layout &lay, int max_sel) {
-  const int per = family_of(lay) == kFamilyMla ? kMlaPagesPerSplit : kGqaPagesPerSplit;
-  const int s = (max_sel + per - 1) / per;
-  return s < 1 ? 1 : s;
+// Splits per (sequence, KV head) unit: enough blocks to fill the chip, at
+// most 64 pages per wave, at least one page per split.
+int decode_splits(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
+  if (family_of(lay) == kFamilyMla) {
+    const int s = (max_sel + kMlaPagesPerSplit - 1) / kMlaPagesPerSplit;
+    return s < 1 ? 1 : s;
+  }
+  const long units = (long)bat.batch * lay.num_kv_heads;
+  long s = units > 0 ? (kGqaTargetBlocks + units - 1) / units : 1;
+  const long min_s = (max_sel + 64L * kGqaDecodeWaves - 1) / (64L * kGqaDecodeWaves);
+  if (s < min_s) s = min_s;
+  if (s > max_sel) s = max_sel;
+  return s < 1 ? 1 : (int)s;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
   const size_t units = (size_t)bat.batch * lay.num_kv_heads;
-  const size_t splits = (size_t)decode_splits(lay, max_sel);
+  const size_t splits = (size_t)decode_splits(lay, bat, max_sel);
   size_t n = 0;
   n += align256(units * (size_t)bat.max_pages * sizeof(qasp_score));
   n += align256(units * (size_t)max_sel * sizeof(int32_t));
   n += align256(units * sizeof(int32_t));
-  n += align256(units * sizeof(uint32_t));
   n += align256((size_t)bat.batch * bat.num_q_heads * splits * lay.head_dim_v * sizeof(float));
   n += align256((size_t)bat.batch * bat.num_q_heads * splits * sizeof(float2));
   return n;
@@ -101,7 +109,7 @@ size_t workspace_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_se
 Workspace carve_workspace(const qasp_layout &lay, const qasp_batch &bat, int max_sel, void *base) {
   Workspace w;
   const size_t units = (size_t)bat.batch * lay.num_kv_heads;
-  w.splits = decode_splits(lay, max_sel);
+  w.splits = decode_splits(lay, bat, max_sel);
   char *p = (char *)base;
   w.scores = (qasp_score *)p;
   p += align256(units * (size_t)bat.max_pages * sizeof(qasp_score));
@@ -109,25 +117,10 @@ Workspace carve_workspace(const qasp_layout &lay, const qasp_batch &bat, int max
   p += align256(units * (size_t)max_sel * sizeof(int32_t));
   w.sel_count = (int32_t *)p;
   p += align256(units * sizeof(int32_t));
-  w.counters = (uint32_t *)p;
-  p += align256(units * sizeof(uint32_t));
   w.partial = (float *)p;
   p += align256((size_t)bat.batch * bat.num_q_heads * w.splits * lay.head_dim_v * sizeof(float));
   w.partial_ml = (float2 *)p;
   return w;
-}
-
-__global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t value) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = value;
-}
-
-hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t value, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, value);
-  return hipGetLastError();
 }
 
 hipError_t launch_sparse_decode(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
@@ -229,7 +222,7 @@ int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (bat->batch == 0) return QASP_OK;
   if (!sel || !sel_count) return QASP_ERR_NULL_ARG;
   if (!all_static(*lay, *pol) && (!q || !summ || !scores)) return QASP_ERR_NULL_ARG;
-  return status_of(launch_select_topk(*lay, *bat, *pol, q, summ, scores, sel, sel_count, max_sel, nullptr,
+  return status_of(launch_select_topk(*lay, *bat, *pol, q, summ, scores, sel, sel_count, max_sel,
                                       (hipStream_t)stream));
 }
 
@@ -278,7 +271,7 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
   if (e == hipSuccess && scored) e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s);
   if (e == hipSuccess)
-    e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, ws.counters, s);
+    e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
   if (e == hipSuccess)
     e = launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
   return status_of(e);

@@ -6,15 +6,17 @@
 // page's score is max over the heads h that share the KV head.  The split
 // form is one dot product of length 2*D between [q^-, q^+] and the summary
 // row [lo, hi], so a 16-page group against up to 16 heads is a chain of
-// 16x16x32 bf16 MFMAs; the products of two bf16 are exact and the
-// accumulation is fp32.  Alongside, the same MFMAs on absolute values give
-// S_h(j) = sum_d |q_d| |x_d|, from which a rigorous bound on the fp32
-// accumulation error follows:
-//     |U_fp32 - U| <= 2 * (2D) * 2^-23 * S * 1.001 + 2^-90
-// (one rounding per product and per addition at most, unit roundoff taken as
-// 2^-23 so a faithful rather than nearest rounding is also covered, and an
-// absolute term for flushed subnormal products).  The selection step uses
-// this bound to decide which pages it must re-score exactly.
+// 16x16x32 bf16 MFMAs.  Each MFMA starts from zero and its 32-product result
+// is added in fp64, so the only fp32 rounding is inside one MFMA.  Alongside,
+// chained MFMAs on absolute values give S_h(j) = sum_d |q_d| |x_d|, from
+// which a rigorous bound on the error of the fp32 score follows:
+//     |U_fp32 - U| <= 65 * 2^-23 * S * 1.01 + 2^-50
+// (per MFMA at most one rounding per product and per addition, unit roundoff
+// taken as 2^-23 so that a faithful rather than nearest rounding is covered;
+// the fp64 additions and the final rounding to fp32 add less than 2^-23 S;
+// the absolute term covers flushed subnormal operands and products when
+// |q|, |k| <= 2^64).  The selection step uses this bound to decide which
+// pages it must re-score exactly.
 //
 // Candidates are the pages between the sink and the local window; every
 // other slot of a row gets value -inf, err 0.
@@ -26,7 +28,7 @@ namespace qasp {
 namespace {
 
 constexpr int kScoreWaves = 4;
-constexpr int kScoreGroupsPerWave = 2;   // 16-page groups per wave
+constexpr int kScoreGroupsPerWave = 4;   // 16-page groups per wave
 constexpr int kScorePagesPerBlock = kScoreWaves * kScoreGroupsPerWave * 16;
 
 __device__ __forceinline__ uint4 map4(uint4 v, int mode) {
@@ -48,7 +50,8 @@ __device__ __forceinline__ uint4 map4(uint4 v, int mode) {
 
 // Grouped-query scoring, head_dim D (128).  Grid: (page blocks, Hkv, B);
 // block = 4 waves; wave w scores kScoreGroupsPerWave groups of 16 consecutive
-// logical pages.  Lane l: page column n = l % 16, k block kg = l / 16.
+// logical pages, loading group i+1 while it computes group i.  Lane l: page
+// column n = l % 16, k block kg = l / 16.
 template <int D>
 __global__ __launch_bounds__(256) void score_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ summ,
@@ -57,6 +60,8 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
     int ps, int n_sink, int n_local, uint64_t static_mask) {
   constexpr int K2 = 2 * D;
   constexpr int KSTEPS = K2 / 32;
+  constexpr int GPW = kScoreGroupsPerWave;
+  constexpr int PTR = (GPW * 16 + kWave - 1) / kWave;  // page-table registers per lane
   const int b = blockIdx.z, g = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n = lane & 15, kg = lane >> 4;
@@ -65,6 +70,28 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
   const int P = num_pages_of(L, ps);
   const int cand_lo = min(n_sink, P), cand_hi = max(cand_lo, P - n_local);
   qasp_score *row = scores + ((size_t)b * Hkv + g) * max_pages;
+  const int wave_first = (blockIdx.x * kScoreWaves + wave) * GPW * 16;
+  if (wave_first >= max_pages) return;
+
+  // physical page of each of the wave's pages (-1: not a candidate)
+  int phys_r[PTR];
+#pragma unroll
+  for (int r = 0; r < PTR; r++) {
+    const int j = wave_first + kWave * r + lane;
+    phys_r[r] = (!is_static && j >= cand_lo && j < cand_hi) ? page_table[(size_t)b * pt_stride + j] : -1;
+  }
+  auto phys_of = [&](int grp) {
+    const int idx = grp * 16 + n;
+    return __shfl(phys_r[idx / kWave], idx % kWave, kWave);
+  };
+  uint4 bs[2][KSTEPS];
+  auto load_group = [&](int grp, uint4 *dst) {
+    const int phys = phys_of(grp);
+    const uint16_t *sp = summ + ((size_t)(phys < 0 ? 0 : phys) * Hkv + g) * K2 + 8 * kg;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; i++) dst[i] = phys >= 0 ? *(const uint4 *)(sp + 32 * i) : make_uint4(0, 0, 0, 0);
+  };
+  load_group(0, bs[0]);
 
   // A operands: row m = head g*G + m of [q^-, q^+] and of its absolute value.
   uint4 aq[KSTEPS], aa[KSTEPS];
@@ -81,58 +108,48 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
     }
   }
 
-  const int wave_first = blockIdx.x * kScorePagesPerBlock + wave * kScoreGroupsPerWave * 16;
-  // issue every summary load of the wave before the first MFMA
-  uint4 bs[kScoreGroupsPerWave][KSTEPS];
-  bool cand[kScoreGroupsPerWave];
+  constexpr float kErrRel = 65.0f * 1.1920928955078125e-07f * 1.01f;  // 65 * 2^-23 * 1.01
+  constexpr float kErrAbs = 8.8817841970012523e-16f;                   // 2^-50
 #pragma unroll
-  for (int grp = 0; grp < kScoreGroupsPerWave; grp++) {
-    const int j = wave_first + grp * 16 + n;
-    cand[grp] = !is_static && j >= cand_lo && j < cand_hi;
-    const uint16_t *s = summ;
-    if (cand[grp]) {
-      const int phys = page_table[(size_t)b * pt_stride + j];
-      s = summ + ((size_t)phys * Hkv + g) * K2;
-    }
-#pragma unroll
-    for (int i = 0; i < KSTEPS; i++)
-      bs[grp][i] = cand[grp] ? *(const uint4 *)(s + 32 * i + 8 * kg) : make_uint4(0, 0, 0, 0);
-  }
-
-  constexpr float kErrRel = 2.0f * K2 * 1.1920928955078125e-07f * 1.001f;  // 2 * 2D * 2^-23
-  constexpr float kErrAbs = 8.0779356694631609e-28f;                         // 2^-90
-#pragma unroll
-  for (int grp = 0; grp < kScoreGroupsPerWave; grp++) {
+  for (int grp = 0; grp < GPW; grp++) {
     const int j0 = wave_first + grp * 16;
     if (j0 >= max_pages) break;
-    floatx4 u = {0.f, 0.f, 0.f, 0.f}, sa = {0.f, 0.f, 0.f, 0.f};
+    if (grp + 1 < GPW) load_group(grp + 1, bs[(grp + 1) & 1]);
+    const uint4 *cur = bs[grp & 1];
+    double u64[4] = {0.0, 0.0, 0.0, 0.0};
+    floatx4 sa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < KSTEPS; i++) {
-      u = mfma16x16x32(aq[i], bs[grp][i], u);
-      sa = mfma16x16x32(aa[i], map4(bs[grp][i], 2), sa);
+      const floatx4 ui = mfma16x16x32(aq[i], cur[i], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; r++) u64[r] += (double)ui[r];
+      sa = mfma16x16x32(aa[i], map4(cur[i], 2), sa);
     }
     // lane (n, kg) holds heads 4kg + r of page j0 + n
-    float best = -INFINITY, bound = 0.f;
+    double best = -INFINITY;
+    float bound = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       if (4 * kg + r < G) {
-        best = fmaxf(best, u[r]);
+        best = fmax(best, u64[r]);
         bound = fmaxf(bound, sa[r]);
       }
     }
-    best = fmaxf(best, __shfl_xor(best, 16, kWave));
-    best = fmaxf(best, __shfl_xor(best, 32, kWave));
+    best = fmax(best, __shfl_xor(best, 16, kWave));
+    best = fmax(best, __shfl_xor(best, 32, kWave));
     bound = fmaxf(bound, __shfl_xor(bound, 16, kWave));
     bound = fmaxf(bound, __shfl_xor(bound, 32, kWave));
     const int j = j0 + n;
+    const bool is_cand = phys_of(grp) >= 0;  // cross-lane read: outside the divergent branch
     if (kg == 0 && j < max_pages) {
       qasp_score sc;
-      if (cand[grp]) {
+      if (is_cand) {
+        const float v = (float)best;
         const float err = kErrRel * bound + kErrAbs;
-        if (isfinite(best) && isfinite(err)) {
-          sc.value = best == 0.f ? 0.f : best;  // no -0
+        if (isfinite(v) && isfinite(err)) {
+          sc.value = v == 0.f ? 0.f : v;  // no -0
           sc.err = err;
-        } else {                                 // overflowed: let selection re-score it
+        } else {                           // overflowed: let selection re-score it
           sc.value = 0.f;
           sc.err = INFINITY;
         }

@@ -45,12 +45,16 @@ __device__ __forceinline__ uint64_t f64_order(double d) {
 // block-wide helpers (256 threads)
 // ---------------------------------------------------------------------------
 
+constexpr int kQStageBytes = 8192;  // q rows of a group staged in LDS for exact re-scoring
+
 struct SelShared {
   int hist[256];
   int ired[kSelWaves];
   float fred[kSelWaves];
   uint32_t ured[kSelWaves];
+  uint64_t ared[kSelWaves], ored[kSelWaves];
   int digit, rem;
+  uint16_t qstage[kQStageBytes / 2];
 };
 
 __device__ int block_sum_int(int v, SelShared &sh) {
@@ -138,47 +142,70 @@ __device__ void find_digit_from_top(int kk, SelShared &sh) {
   __syncthreads();
 }
 
-// k-th largest (1-based) of keys[0..n) (LDS), 8 bits per pass.
-__device__ uint32_t kth_largest_u32(const uint32_t *keys, int n, int k, SelShared &sh) {
-  uint32_t prefix = 0, pmask = 0;
-  int kk = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    sh.hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-      const uint32_t u = keys[i];
-      if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    find_digit_from_top(kk, sh);
-    prefix |= (uint32_t)sh.digit << shift;
-    pmask |= 255u << shift;
-    kk = sh.rem;
-    __syncthreads();
-  }
-  return prefix;
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const int lo = __shfl_xor((int)(uint32_t)v, o, kWave);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), o, kWave);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// k-th largest 64-bit order key among the band pages (keys64 indexed by
-// candidate index, band membership in band_bits).
-__device__ uint64_t kth_largest_band_u64(const uint64_t *keys64, const uint32_t *band_bits, int n,
-                                         int k, SelShared &sh) {
-  uint64_t prefix = 0, pmask = 0;
+// Block-wide AND and OR of 64-bit values.
+__device__ void block_and_or(uint64_t &a, uint64_t &o, SelShared &sh) {
+  for (int s = 32; s > 0; s >>= 1) {
+    a &= shfl_xor_u64(a, s);
+    o |= shfl_xor_u64(o, s);
+  }
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    sh.ared[threadIdx.x / kWave] = a;
+    sh.ored[threadIdx.x / kWave] = o;
+  }
+  __syncthreads();
+  a = ~0ull;
+  o = 0;
+  for (int w = 0; w < kSelWaves; w++) {
+    a &= sh.ared[w];
+    o |= sh.ored[w];
+  }
+}
+
+// k-th largest (1-based) of the keys whose member bit is set (all keys when
+// member_bits is null), keys in LDS.  The bits above the highest bit where
+// the members differ are common to all of them and are skipped; the rest is
+// resolved 8 bits per histogram pass, from the top.
+template <typename U>
+__device__ U kth_largest(const U *keys, const uint32_t *member_bits, int n, int k, SelShared &sh) {
+  constexpr int kBits = 8 * sizeof(U);
+  uint64_t a = ~0ull, o = 0;
+  for (int i = threadIdx.x; i < n; i += kSelThreads) {
+    if (member_bits && !((member_bits[i >> 5] >> (i & 31)) & 1u)) continue;
+    a &= (uint64_t)keys[i];
+    o |= (uint64_t)keys[i];
+  }
+  block_and_or(a, o, sh);
+  const U all_and = (U)a, diff = (U)(a ^ o);
+  if (diff == 0) return all_and;
+  int hb = kBits - 1;
+  while (!((diff >> hb) & 1)) hb--;
+  U pmask = hb + 1 >= kBits ? (U)0 : (U)(~(U)0 << (hb + 1));
+  U prefix = all_and & pmask;
   int kk = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  while (hb >= 0) {
+    const int lo = hb >= 7 ? hb - 7 : 0;
+    const U dmask = (U)((1u << (hb - lo + 1)) - 1u);
     sh.hist[threadIdx.x] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += kSelThreads) {
-      if (!((band_bits[i >> 5] >> (i & 31)) & 1u)) continue;
-      const uint64_t u = keys64[i];
-      if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1);
+      if (member_bits && !((member_bits[i >> 5] >> (i & 31)) & 1u)) continue;
+      const U u = keys[i];
+      if ((u & pmask) == prefix) atomicAdd(&sh.hist[(int)((u >> lo) & dmask)], 1);
     }
     __syncthreads();
     find_digit_from_top(kk, sh);
-    prefix |= (uint64_t)sh.digit << shift;
-    pmask |= 255ull << shift;
+    prefix |= (U)sh.digit << lo;
+    pmask |= dmask << lo;
     kk = sh.rem;
     __syncthreads();
+    hb = lo - 1;
   }
   return prefix;
 }
@@ -199,17 +226,21 @@ __device__ __forceinline__ void bf16_split(uint32_t bits, int &m, int &e) {
   }
 }
 
-// Signed significand and exponent of the channel-d term q_d * (q_d < 0 ? lo_d : hi_d).
-__device__ __forceinline__ void bound_term(const uint16_t *qh, const uint16_t *lo, const uint16_t *hi,
-                                           int d, int &M, int &E) {
-  const uint32_t qb = qh[d];
-  const uint32_t xb = (qb & 0x8000u) ? lo[d] : hi[d];
+// Signed significand and exponent of the term q_d * x_d (bit patterns).
+__device__ __forceinline__ void term_of(uint32_t qb, uint32_t xb, int &M, int &E) {
   int mq, eq, mx, ex;
   bf16_split(qb, mq, eq);
   bf16_split(xb, mx, ex);
   M = mq * mx;
   E = eq + ex;
   if ((qb ^ xb) & 0x8000u) M = -M;
+}
+
+// Channel-d term q_d * (q_d < 0 ? lo_d : hi_d).
+__device__ __forceinline__ void bound_term(const uint16_t *qh, const uint16_t *lo, const uint16_t *hi,
+                                           int d, int &M, int &E) {
+  const uint32_t qb = qh[d];
+  term_of(qb, (qb & 0x8000u) ? lo[d] : hi[d], M, E);
 }
 
 __device__ __forceinline__ double i64_to_f64_rn(int64_t x) {
@@ -277,10 +308,12 @@ __device__ double exact_head_bound_digits(const uint16_t *qh, const uint16_t *lo
 }
 
 // Correctly rounded fp64 value of the exact sum_d q_d * (q_d < 0 ? lo_d : hi_d).
-// Wave-wide: lane l takes channels l, l+64, ...; the terms are placed on one
-// 64-bit integer grid just below the largest term and summed exactly.
+// Wave-wide: lane l holds channels l, l+64, ... of the page rows (xl, xh, bit
+// patterns); the terms are placed on one 64-bit integer grid just below the
+// largest term and summed exactly across the wave.  qh may point to LDS.
 template <int D>
-__device__ double exact_head_bound(const uint16_t *qh, const uint16_t *lo, const uint16_t *hi, int lane) {
+__device__ double exact_head_bound(const uint16_t *qh, const uint32_t *xl, const uint32_t *xh,
+                                   const uint16_t *lo, const uint16_t *hi, int lane) {
   constexpr int PER = (D + kWave - 1) / kWave;
   constexpr int LOGD = D <= 128 ? 7 : (D <= 1024 ? 10 : 16);
   constexpr int HEADROOM = 62 - 16 - LOGD;  // |sum| < D * 2^16 * 2^HEADROOM <= 2^62
@@ -292,7 +325,8 @@ __device__ double exact_head_bound(const uint16_t *qh, const uint16_t *lo, const
     Ms[s] = 0;
     Es[s] = 0;
     if (d < D) {
-      bound_term(qh, lo, hi, d, Ms[s], Es[s]);
+      const uint32_t qb = qh[d];
+      term_of(qb, (qb & 0x8000u) ? xl[s] : xh[s], Ms[s], Es[s]);
       if (Ms[s] != 0) emax = max(emax, Es[s]);
     }
   }
@@ -315,6 +349,22 @@ __device__ double exact_head_bound(const uint16_t *qh, const uint16_t *lo, const
   return ldexp(i64_to_f64_rn(acc), base);
 }
 
+// Exact group score of one page: max over the G heads (wave-wide).
+template <int D>
+__device__ double exact_page_key(const uint16_t *qg, int G, const uint16_t *lo, const uint16_t *hi, int lane) {
+  constexpr int PER = (D + kWave - 1) / kWave;
+  uint32_t xl[PER], xh[PER];
+#pragma unroll
+  for (int s = 0; s < PER; s++) {
+    const int d = lane + kWave * s;
+    xl[s] = d < D ? lo[d] : 0u;
+    xh[s] = d < D ? hi[d] : 0u;
+  }
+  double best = -INFINITY;
+  for (int m = 0; m < G; m++) best = fmax(best, exact_head_bound<D>(qg + (size_t)m * D, xl, xh, lo, hi, lane));
+  return best;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -326,7 +376,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ summ,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     const qasp_score *__restrict__ scores, int32_t *__restrict__ sel,
-    int32_t *__restrict__ sel_count, uint32_t *__restrict__ counters, int pt_stride, int max_pages,
+    int32_t *__restrict__ sel_count, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int ps, int n_sink, int n_local, int top_k,
     int sink_tokens, int window_tokens, uint64_t static_mask) {
   extern __shared__ uint64_t dyn[];
@@ -346,7 +396,6 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     sel_bits[w] = 0;
     band_bits[w] = 0;
   }
-  if (counters != nullptr && tid == 0) counters[unit] = 0;
   __syncthreads();
 
   if (head_is_static(static_mask, g)) {
@@ -373,7 +422,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         e_loc = fmaxf(e_loc, s.err);
       }
       const float emax = block_max_float(e_loc, sh);   // has a barrier before reading keys
-      const uint32_t uk = kth_largest_u32(keys32, n, k, sh);
+      const uint32_t uk = kth_largest<uint32_t>(keys32, nullptr, n, k, sh);
       int c_ge = 0;
       uint32_t below = 0;
       for (int i = tid; i < n; i += kSelThreads) {
@@ -412,6 +461,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         // exact scores of the band pages, one page per wave at a time
         __syncthreads();  // keys32 is dead from here; keys64 reuses the space
         const uint16_t *qb = q + ((size_t)b * Hq + (size_t)g * G) * D;
+        if ((size_t)G * D * 2 <= kQStageBytes) {  // stage the group's q rows in LDS
+          for (int i = tid; i < G * D / 2; i += kSelThreads)
+            ((uint32_t *)sh.qstage)[i] = ((const uint32_t *)qb)[i];
+          __syncthreads();
+          qb = sh.qstage;
+        }
         int seen = 0;
         for (int w = 0; w < (n + 31) / 32; w++) {
           uint32_t bits = band_bits[w];
@@ -423,13 +478,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
             const int phys = page_table[(size_t)b * pt_stride + j];
             const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
             const uint16_t *hi = lo + D;
-            double best = -INFINITY;
-            for (int m = 0; m < G; m++) best = fmax(best, exact_head_bound<D>(qb + (size_t)m * D, lo, hi, lane));
+            const double best = exact_page_key<D>(qb, G, lo, hi, lane);
             if (lane == 0) keys64[i] = f64_order(best);
           }
         }
         __syncthreads();
-        const uint64_t kth = kth_largest_band_u64(keys64, band_bits, n, need, sh);
+        const uint64_t kth = kth_largest<uint64_t>(keys64, band_bits, n, need, sh);
         // all band pages above kth, then the lowest ids among those equal to it
         int above = 0;
         for (int i = tid; i < n; i += kSelThreads)
@@ -482,14 +536,14 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
 hipError_t launch_select_topk(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
                               const qasp_score *scores, int32_t *sel, int32_t *sel_count,
-                              int max_sel, uint32_t *counters_to_clear, hipStream_t stream) {
+                              int max_sel, hipStream_t stream) {
   if (bat.batch == 0) return hipSuccess;
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = (size_t)mp * 8 + 2 * (size_t)((mp + 31) / 32) * 4;
   dim3 grid(lay.num_kv_heads, bat.batch);
 #define QASP_SELECT_ARGS                                                                        \
-  q, summ, bat.page_table, bat.seq_lens, scores, sel, sel_count, counters_to_clear,             \
+  q, summ, bat.page_table, bat.seq_lens, scores, sel, sel_count,                                \
       bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G, lay.page_size,          \
       pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens, pol.window_tokens,        \
       pol.static_head_mask
