@@ -125,52 +125,43 @@ def main():
     w0 = layers[0]["w"]
     spec = w0.spec
 
-    def step(L, ev=None):
+    def step(L):
         w = L["w"]
-        api.append_kv(L["lay"], L["bat_before"], L["pol"], w.k_new, w.v_new, w.k_pool, w.v_pool, L["summ"])
-        if ev: ev[0].record(stream)
-        api.score_pages(L["lay"], L["bat"], L["pol"], w.q, L["summ"], L["scores"])
-        if ev: ev[1].record(stream)
-        sel, cnt = L["sel"], L["cnt"]
-        api.select_topk(L["lay"], L["bat"], L["pol"], w.q, L["summ"], L["scores"], sel=sel, sel_count=cnt)
-        if ev: ev[2].record(stream)
-        api.sparse_paged_decode(L["lay"], L["bat"], L["pol"], w.q, w.k_pool, w.v_pool, sel, cnt, w.scale,
-                                L["ws"], out=L["out"])
-        if ev: ev[3].record(stream)
+        api.decode_step(L["lay"], L["bat"], L["pol"], w.q, w.k_pool, w.v_pool, L["summ"], w.scale, L["ws"],
+                        L["msel"], k_new=w.k_new, v_new=w.v_new, out=L["out"], sel=L["sel"], sel_count=L["cnt"])
 
     for i in range(args.warmup):
         step(layers[i % len(layers)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # HIP events on the launch stream around every step; with many units the
+    # step is one kernel (append + score + select + attend), so these bracket
+    # exactly that kernel's launches
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        e = evs[i]
-        e[4].record(stream)
-        step(layers[i % len(layers)], ev=e)
+        evs[i][0].record(stream)
+        step(layers[i % len(layers)])
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    score_ms = [e[4].elapsed_time(e[1]) - e[4].elapsed_time(e[0]) for e in evs]
-    select_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    decode_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    step_ms = [e[4].elapsed_time(e[3]) for e in evs]
+    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
     med = statistics.median
     counts = layers[0]["cnt"].cpu().tolist()
     b_score, b_decode = step_bytes(w0, counts)
     total_bytes = b_score + b_decode
-    kern = {"score_pages": (med(score_ms), b_score), "sparse_paged_decode": (med(decode_ms), b_decode)}
-    dom = max(kern, key=lambda k: kern[k][0])
-    dom_ms, dom_bytes = kern[dom]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    units = spec.batch * spec.num_kv_heads
+    one_kernel = units >= 200 and w0.max_pages <= 4096 and not spec.v_from_k
+    kernel = "fused_step_gqa_kernel" if one_kernel else "decode_step (several kernels)"
+    dom_ms = med(step_ms)
+    achieved = total_bytes / (dom_ms * 1e-3) / 1e9
     tokens_per_s = spec.batch / (ms_per_step * 1e-3)
     gbps = total_bytes / (ms_per_step * 1e-3) / 1e9
-    log("step events: median %.1f us (p10 %.1f, p90 %.1f); score %.1f us, select %.1f us, decode %.1f us"
-        % (med(step_ms) * 1e3, sorted(step_ms)[len(step_ms) // 10] * 1e3,
-           sorted(step_ms)[(9 * len(step_ms)) // 10] * 1e3, med(score_ms) * 1e3, med(select_ms) * 1e3,
-           med(decode_ms) * 1e3))
+    log("step events: median %.1f us (p10 %.1f, p90 %.1f), wall %.1f us/step"
+        % (dom_ms * 1e3, step_ms[len(step_ms) // 10] * 1e3, step_ms[(9 * len(step_ms)) // 10] * 1e3,
+           ms_per_step * 1e3))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -199,9 +190,9 @@ def main():
         "kv_gbps": round(gbps, 1),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "step_bytes": total_bytes,
-        "kernel_us": {"score_pages": round(med(score_ms) * 1e3, 2), "select_topk": round(med(select_ms) * 1e3, 2),
-                      "sparse_paged_decode": round(med(decode_ms) * 1e3, 2)},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+        "step_us_events": {"median": round(dom_ms * 1e3, 2), "p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
+                           "p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2)},
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
         "cpu_baseline": cpu,
     }

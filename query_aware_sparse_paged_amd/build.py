@@ -20,7 +20,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["api.hip", "summaries.hip", "score.hip", "select.hip", "decode_gqa.hip", "decode_mla.hip"]
+SOURCES = ["api.hip", "summaries.hip", "score.hip", "select.hip", "decode_gqa.hip", "decode_mla.hip",
+           "fused_gqa.hip"]
 
 
 def _compile(src: str) -> str:

@@ -263,8 +263,14 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (k_new && !lay->v_from_k && !v_new) return QASP_ERR_NULL_ARG;
   if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
   if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
-  const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
   hipStream_t s = (hipStream_t)stream;
+  // many units: the whole step as one kernel per (sequence, KV head) block
+  const long units = (long)bat->batch * lay->num_kv_heads;
+  if (family_of(*lay) == kFamilyGqa && units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages &&
+      fused_lds_bytes(*lay, *bat, max_sel) <= 160 * 1024)
+    return status_of(launch_fused_step_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out,
+                                           sel, sel_count, max_sel, s));
+  const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
   int32_t *sel_out = sel ? sel : ws.sel;
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   hipError_t e = hipSuccess;

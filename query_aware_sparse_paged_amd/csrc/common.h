@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "../../include/qasp.h"
@@ -94,6 +95,72 @@ __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
     v += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
   }
   return v;
+}
+
+// ---------------------------------------------------------------------------
+// DPP wave scans and reductions (GFX9 data-parallel primitives: row_shr
+// within rows of 16 lanes, then row_bcast15 / row_bcast31 across rows).
+// Each step is one VALU op with a DPP source, not a round trip through LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_or(int identity, int x) {
+  return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += dpp_or<kDppRowShr1>(0, x);
+  x += dpp_or<kDppRowShr2>(0, x);
+  x += dpp_or<kDppRowShr4>(0, x);
+  x += dpp_or<kDppRowShr8>(0, x);
+  x += dpp_or<kDppRowBcast15, 0xa>(0, x);
+  x += dpp_or<kDppRowBcast31, 0xc>(0, x);
+  return x;
+}
+
+// Sum / max over the wave, returned to every lane.
+__device__ __forceinline__ int wave_sum_dpp(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_sum(x), 63);
+}
+__device__ __forceinline__ int wave_max_dpp(int x) {
+  x = max(x, dpp_or<kDppRowShr1>(INT_MIN, x));
+  x = max(x, dpp_or<kDppRowShr2>(INT_MIN, x));
+  x = max(x, dpp_or<kDppRowShr4>(INT_MIN, x));
+  x = max(x, dpp_or<kDppRowShr8>(INT_MIN, x));
+  x = max(x, dpp_or<kDppRowBcast15, 0xa>(INT_MIN, x));
+  x = max(x, dpp_or<kDppRowBcast31, 0xc>(INT_MIN, x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+// max over floats without NaN: order-preserving int map, then integer max
+__device__ __forceinline__ float wave_max_dpp(float f) {
+  const int u = __float_as_int(f);
+  const int key = u >= 0 ? u : (u ^ 0x7fffffff);
+  const int m = wave_max_dpp(key);
+  return __int_as_float(m >= 0 ? m : (m ^ 0x7fffffff));
+}
+__device__ __forceinline__ uint32_t wave_and_dpp(uint32_t x) {
+  int v = (int)x;
+  v &= dpp_or<kDppRowShr1>(-1, v);
+  v &= dpp_or<kDppRowShr2>(-1, v);
+  v &= dpp_or<kDppRowShr4>(-1, v);
+  v &= dpp_or<kDppRowShr8>(-1, v);
+  v &= dpp_or<kDppRowBcast15, 0xa>(-1, v);
+  v &= dpp_or<kDppRowBcast31, 0xc>(-1, v);
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_or_dpp(uint32_t x) {
+  int v = (int)x;
+  v |= dpp_or<kDppRowShr1>(0, v);
+  v |= dpp_or<kDppRowShr2>(0, v);
+  v |= dpp_or<kDppRowShr4>(0, v);
+  v |= dpp_or<kDppRowShr8>(0, v);
+  v |= dpp_or<kDppRowBcast15, 0xa>(0, v);
+  v |= dpp_or<kDppRowBcast31, 0xc>(0, v);
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 
 // ---------------------------------------------------------------------------

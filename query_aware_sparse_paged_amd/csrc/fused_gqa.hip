@@ -1,0 +1,219 @@
+// One whole decode step for grouped-query heads in a single kernel, used when
+// every (sequence, KV head) unit can have a block of its own (units >= CUs):
+//   append   the current token's key/value and its page summary (head g only);
+//   score    every candidate page from the summaries (score_core.h);
+//   select   sink + local + certified top-k, exact on ties (select_core.h);
+//   attend   softmax attention over the selected pages (attend_core.h).
+// The scores and the selection stay in LDS: no round trip through HBM and no
+// kernel boundary between the steps.  Each unit's data is touched by its own
+// block only, so no inter-block synchronisation is needed.
+#include "attend_core.h"
+#include "launch.h"
+#include "score_core.h"
+#include "select_core.h"
+
+namespace qasp {
+
+constexpr int kFusedWaves = 8;
+
+// Dynamic LDS layout of the fused kernel (bytes).
+struct FusedLds {
+  size_t keys, bits, list, merge, total;
+  __host__ __device__ FusedLds(int max_pages, int max_sel, int G) {
+    const int nwords = (max_pages + 31) / 32;
+    keys = 0;                                                       // uint64 [max_pages]
+    bits = keys + (size_t)max_pages * 8;                            // 2 x uint32 [nwords]
+    list = bits + (size_t)2 * nwords * 4;                           // int32 [max_sel]
+    merge = (list + (size_t)max_sel * 4 + 15) & ~(size_t)15;        // float merge area
+    total = merge + (size_t)attend::merge_lds_floats(kFusedWaves, G, 128) * 4;
+  }
+};
+
+template <int D, int DV, int PS, int W>
+__global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    uint16_t *__restrict__ k_pool, uint16_t *__restrict__ v_pool, uint16_t *__restrict__ summ,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, float *__restrict__ out,
+    int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
+    int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
+    int window_tokens, uint64_t static_mask, float scale_log2) {
+  constexpr int NW = W, T = W * kWave;
+  constexpr int KSTEPS = 2 * D / 32;
+  extern __shared__ uint64_t dyn[];
+  __shared__ sel::SelShared<NW> sh;
+  const FusedLds lay(max_pages, max_sel, G);
+  uint64_t *keys64 = dyn;
+  uint32_t *keys32 = (uint32_t *)dyn;
+  const int nwords = (max_pages + 31) / 32;
+  uint32_t *sel_bits = (uint32_t *)((char *)dyn + lay.bits);
+  uint32_t *band_bits = sel_bits + nwords;
+  int32_t *list = (int32_t *)((char *)dyn + lay.list);
+  float *merge_area = (float *)((char *)dyn + lay.merge);
+
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n_col = lane & 15, kg = lane >> 4;
+  const int unit = b * Hkv + g;
+  const int L = seq_lens[b];
+  const int P = num_pages_of(L, PS);
+  const int32_t *pt_row = page_table + (size_t)b * pt_stride;
+  const bool is_static = head_is_static(static_mask, g);
+  const int cand_lo = min(n_sink, P), cand_hi = max(cand_lo, P - n_local);
+  const int n = cand_hi - cand_lo;
+  const int k = top_k;
+  const bool ranked = !is_static && k > 0 && k < n;
+  const size_t head0 = (size_t)b * Hq + (size_t)g * G;
+
+  // ---- append: the token at position L-1, head g (key row, value column,
+  // summary: slot 0 starts it, later slots widen it)
+  if (k_new != nullptr && L > 0) {
+    const int pos = L - 1, t = pos % PS;
+    const size_t ph = (size_t)pt_row[pos / PS] * Hkv + g;
+    const uint32_t *kn = (const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D);
+    for (int w = tid; w < D / 2; w += T) {
+      const uint32_t kv = kn[w];
+      ((uint32_t *)k_pool)[(ph * PS + t) * (D / 2) + w] = kv;
+      if (summ != nullptr) {
+        uint32_t *s = (uint32_t *)summ + ph * D;
+        uint32_t lo = kv, hi = kv;
+        if (t != 0) {
+          lo = s[w];
+          hi = s[D / 2 + w];
+          const int v0 = bf16_order_key(kv & 0xffffu), v1 = bf16_order_key(kv >> 16);
+          lo = bf16_from_order_key(min(v0, bf16_order_key(lo & 0xffffu))) |
+               (bf16_from_order_key(min(v1, bf16_order_key(lo >> 16))) << 16);
+          hi = bf16_from_order_key(max(v0, bf16_order_key(hi & 0xffffu))) |
+               (bf16_from_order_key(max(v1, bf16_order_key(hi >> 16))) << 16);
+        }
+        s[w] = lo;
+        s[D / 2 + w] = hi;
+      }
+    }
+    const uint16_t *vn = v_new + ((size_t)b * Hkv + g) * DV;
+    for (int dv = tid; dv < DV; dv += T) v_pool[(ph * DV + dv) * PS + t] = vn[dv];
+    __threadfence_block();
+  }
+  for (int w = tid; w < nwords; w += T) {
+    sel_bits[w] = 0;
+    band_bits[w] = 0;
+  }
+  if (tid == 0) sh.nlist = 0;
+  __syncthreads();
+
+  // ---- score the candidates: wave w takes 16-page groups w, w+W, ...; the
+  // page-table entries of the next group and its summaries are loaded while
+  // the current group is computed
+  float e_loc = 0.f;
+  uint32_t k_and = ~0u, k_or = 0;
+  if (ranked) {
+    const int ngroups = (n + 15) / 16;
+    const int my_groups = ngroups > wave ? (ngroups - wave + W - 1) / W : 0;
+    score::QOperands<D> op;
+    score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
+    auto page_of = [&](int gi) {  // physical page of this lane's column in the wave's gi-th group, -1 if none
+      const int i = (wave + gi * W) * 16 + n_col;
+      const bool ok = gi < my_groups && i < n;
+      const int phys = pt_row[cand_lo + (ok ? i : 0)];  // always issued: static wait counts
+      return ok ? phys : -1;
+    };
+    uint4 bs[2][KSTEPS];
+    int phys_cur = page_of(0);
+    int phys_next = page_of(1);
+    score::load_group<D>(bs[0], summ, max(phys_cur, 0), Hkv, g, lane);
+    for (int gi = 0; gi < my_groups; gi += 2) {
+#pragma unroll
+      for (int half = 0; half < 2; half++) {
+        const int gcur = gi + half;
+        uint4 *cur = bs[half];
+        // prefetch: summaries of group gcur+1, page-table entry of gcur+2
+        score::load_group<D>(bs[half ^ 1], summ, max(phys_next, 0), Hkv, g, lane);
+        const int phys_after = page_of(gcur + 2);
+        if (phys_cur < 0) {
+#pragma unroll
+          for (int i = 0; i < KSTEPS; i++) cur[i] = make_uint4(0, 0, 0, 0);
+        }
+        double best;
+        float bound;
+        score::score_group<D>(op, cur, G, lane, best, bound);
+        const int i = (wave + gcur * W) * 16 + n_col;
+        if (kg == 0 && gcur < my_groups && i < n) {
+          const qasp_score sc = score::make_score(best, bound);
+          const uint32_t o = sel::f32_order(sc.value);
+          keys32[i] = o;
+          k_and &= o;
+          k_or |= o;
+          e_loc = fmaxf(e_loc, sc.err);
+        }
+        phys_cur = phys_next;
+        phys_next = phys_after;
+      }
+    }
+  }
+
+  // ---- select
+  if (is_static) {
+    const int sink_end = min(sink_tokens, L);
+    const int win_begin = max(0, L - window_tokens);
+    for (int j = tid; j < P; j += T) {
+      const int a = j * PS, e = min(a + PS, L);
+      if (a < sink_end || e > win_begin) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+    }
+  } else {
+    for (int j = tid; j < P; j += T)
+      if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+    if (ranked) {
+      sel::block_max_and_or(e_loc, k_and, k_or, sh);
+      sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_and, k_or,
+                                    q + head0 * D, G, summ, pt_row, Hkv, g);
+    }
+  }
+  __syncthreads();
+  const int count = sel::emit_selection(sh, sel_bits, nwords,
+                                        sel_out ? sel_out + (size_t)unit * max_sel : nullptr, list, max_sel);
+  if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
+  __syncthreads();
+
+  // ---- attend: wave w takes selected pages w, w+W, ...
+  const int npg = count > wave ? (count - wave + W - 1) / W : 0;
+  int my_j = 0, my_phys = 0;
+  if (lane < npg) {
+    my_j = list[wave + W * lane];
+    my_phys = pt_row[my_j];
+  }
+  const int sink_end = is_static ? min(sink_tokens, L) : 0;
+  const int win_begin = is_static ? max(0, L - window_tokens) : 0;
+  uint4 bq[D / 32];
+  attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
+  attend::WaveState st;
+  attend::init_state(st);
+  attend::attend_pages<PS, D, DV>(st, k_pool, v_pool, Hkv, g, bq, npg, my_j, my_phys, L, is_static, sink_end,
+                                  win_begin, scale_log2, lane);
+  attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
+    (void)M;
+    out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
+  });
+}
+
+size_t fused_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
+  const int G = bat.num_q_heads / lay.num_kv_heads;
+  return FusedLds(bat.max_pages > 0 ? bat.max_pages : 1, max_sel, G).total + sizeof(sel::SelShared<kFusedWaves>);
+}
+
+hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                 const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                 uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
+                                 int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream) {
+  const int G = bat.num_q_heads / lay.num_kv_heads;
+  const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
+  const size_t lds = FusedLds(mp, max_sel, G).total;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid(lay.num_kv_heads, bat.batch);
+  hipLaunchKernelGGL((fused_step_gqa_kernel<128, 128, 16, kFusedWaves>), grid, dim3(kFusedWaves * 64), lds,
+                     stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, out, sel,
+                     sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G,
+                     pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens, pol.window_tokens,
+                     pol.static_head_mask, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace qasp

@@ -50,6 +50,14 @@ hipError_t launch_sparse_decode(const qasp_layout &lay, const qasp_batch &bat,
                                 const uint16_t *k_pool, const uint16_t *v_pool,
                                 const int32_t *sel, const int32_t *sel_count, int max_sel,
                                 float scale, float *out, const Workspace &ws, hipStream_t stream);
+// The single-kernel decode step (grouped-query family), for many units.
+constexpr int kFusedMinUnits = 200;
+constexpr int kFusedMaxPages = 4096;
+size_t fused_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel);
+hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                 const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                 uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
+                                 int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream);
 hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,
                                hipStream_t stream);
 

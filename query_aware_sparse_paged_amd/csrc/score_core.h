@@ -1,0 +1,128 @@
+// Device building blocks of score_pages: the per-page upper bound on q.k
+// from the page summaries, on MFMA.
+//
+// For query head h and page j with summary (lo, hi):
+//     U_h(j) = sum_d max(q_d lo_d, q_d hi_d) = q_h^- . lo_j + q_h^+ . hi_j
+// (q^- keeps the negative channels of q, q^+ the positive ones), and the
+// page's score is max over the heads h that share the KV head.  The split
+// form is one dot product of length 2*D between [q^-, q^+] and the summary
+// row [lo, hi], so a 16-page group against up to 16 heads is a chain of
+// 16x16x32 bf16 MFMAs.  Each MFMA starts from zero and its 32-product result
+// is added in fp64, so the only fp32 rounding is inside one MFMA.  Alongside,
+// chained MFMAs on absolute values give S_h(j) = sum_d |q_d| |x_d|, from
+// which a rigorous bound on the error of the fp32 score follows:
+//     |U_fp32 - U| <= 65 * 2^-23 * S * 1.01 + 2^-50
+// (per MFMA at most one rounding per product and per addition, unit roundoff
+// taken as 2^-23 so that a faithful rather than nearest rounding is covered;
+// the fp64 additions and the final rounding to fp32 add less than 2^-23 S;
+// the absolute term covers flushed subnormal operands and products when
+// |q|, |k| <= 2^64).  The selection uses this bound to decide which pages it
+// must re-score exactly.
+#pragma once
+
+#include "common.h"
+
+namespace qasp {
+namespace score {
+
+constexpr float kErrRel = 65.0f * 1.1920928955078125e-07f * 1.01f;  // 65 * 2^-23 * 1.01
+constexpr float kErrAbs = 8.8817841970012523e-16f;                   // 2^-50
+
+__device__ __forceinline__ uint4 map4(uint4 v, int mode) {
+  // mode 0: negative part, 1: positive part, 2: absolute value
+  uint4 r;
+  if (mode == 0) {
+    r.x = bf16x2_negative_part(v.x); r.y = bf16x2_negative_part(v.y);
+    r.z = bf16x2_negative_part(v.z); r.w = bf16x2_negative_part(v.w);
+  } else if (mode == 1) {
+    r.x = bf16x2_positive_part(v.x); r.y = bf16x2_positive_part(v.y);
+    r.z = bf16x2_positive_part(v.z); r.w = bf16x2_positive_part(v.w);
+  } else {
+    r.x = bf16x2_abs(v.x); r.y = bf16x2_abs(v.y); r.z = bf16x2_abs(v.z); r.w = bf16x2_abs(v.w);
+  }
+  return r;
+}
+
+// A operands of one wave: row m = head m of the group, k = [q^-, q^+] and its
+// absolute value.  Lane l holds row l % 16, k block l / 16.
+template <int D>
+struct QOperands {
+  static constexpr int KSTEPS = 2 * D / 32;
+  uint4 aq[KSTEPS], aa[KSTEPS];
+};
+
+// qg: the group's first q row; heads m >= G (or an inactive group) get zeros.
+template <int D>
+__device__ __forceinline__ void load_q_operands(QOperands<D> &op, const uint16_t *qg, int G, bool active,
+                                                int lane) {
+  const int m = lane & 15, kg = lane >> 4;
+  const uint16_t *qh = qg + (size_t)(m < G ? m : 0) * D;
+#pragma unroll
+  for (int i = 0; i < QOperands<D>::KSTEPS; i++) {
+    const int k0 = 32 * i + 8 * kg;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (m < G && active) v = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
+    op.aq[i] = map4(v, k0 < D ? 0 : 1);
+    op.aa[i] = map4(op.aq[i], 2);
+  }
+}
+
+// Summary rows of physical page `phys` (>= 0) for KV head g, in the B-operand
+// layout: lane l holds page column l % 16 ... the caller passes the lane's page.
+template <int D>
+__device__ __forceinline__ void load_group(uint4 *dst, const uint16_t *summ, int phys, int Hkv, int g, int lane) {
+  const uint16_t *sp = summ + ((size_t)phys * Hkv + g) * (2 * D) + 8 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < 2 * D / 32; i++) dst[i] = *(const uint4 *)(sp + 32 * i);
+}
+
+// Scores of a 16-page group: on return every lane of page column l % 16 holds
+// the group score (max over the G heads, fp64 sum of the MFMA steps) and the
+// largest S of its heads.
+template <int D>
+__device__ __forceinline__ void score_group(const QOperands<D> &op, const uint4 *cur, int G, int lane,
+                                            double &best, float &bound) {
+  const int kg = lane >> 4;
+  double u64[4] = {0.0, 0.0, 0.0, 0.0};
+  floatx4 sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < QOperands<D>::KSTEPS; i++) {
+    const floatx4 ui = mfma16x16x32(op.aq[i], cur[i], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int r = 0; r < 4; r++) u64[r] += (double)ui[r];
+    sa = mfma16x16x32(op.aa[i], map4(cur[i], 2), sa);
+  }
+  // lane (n, kg) holds heads 4kg + r of page n
+  best = -INFINITY;
+  bound = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    if (4 * kg + r < G) {
+      best = fmax(best, u64[r]);
+      bound = fmaxf(bound, sa[r]);
+    }
+  }
+  best = fmax(best, __shfl_xor(best, 16, kWave));
+  best = fmax(best, __shfl_xor(best, 32, kWave));
+  bound = fmaxf(bound, __shfl_xor(bound, 16, kWave));
+  bound = fmaxf(bound, __shfl_xor(bound, 32, kWave));
+}
+
+// The stored score of a candidate page: fp32 value and error bound; an
+// overflow becomes (0, inf) so that selection re-scores the page exactly.
+__device__ __forceinline__ qasp_score make_score(double best, float bound) {
+  const float v = (float)best;
+  const float err = kErrRel * bound + kErrAbs;
+  qasp_score sc;
+  if (isfinite(v) && isfinite(err)) {
+    sc.value = v == 0.f ? 0.f : v;  // no -0
+    sc.err = err;
+  } else {
+    sc.value = 0.f;
+    sc.err = INFINITY;
+  }
+  return sc;
+}
+
+}  // namespace score
+}  // namespace qasp

@@ -1,0 +1,605 @@
+// Device building blocks of select_topk: per (sequence, KV head) block, the
+// sink + local + top-k page selection with exact tie handling.
+//
+// The top-k of the query-aware heads must be exactly the top-k of the exact
+// group scores (largest first, equal scores to the lower page id).  The fp32
+// scores carry an error bound e, so with E the largest bound among the
+// candidates and v_k, v_k1 the k-th and (k+1)-th largest fp32 values:
+//   v_j > v_k1 + 2E  -> certainly selected (at most k-1 pages can beat it),
+//   v_j < v_k  - 2E  -> certainly not selected (k pages certainly beat it),
+//   otherwise        -> in doubt ("band").
+// The band pages get their exact score, the correctly rounded fp64 value of
+// the exact real sum (an integer sum of the exact bf16 products, then one
+// rounding), and the remaining places go to the best band pages by that
+// score and then by lower page id.  The usual band is empty or a few pages.
+#pragma once
+
+#include "common.h"
+
+namespace qasp {
+namespace sel {
+
+constexpr int kQStageBytes = 8192;  // q rows of a group staged in LDS for exact re-scoring
+constexpr int kSmallBand = 64;      // bands up to this size are ranked by one wave
+
+// Order-preserving unsigned keys of fp32 / fp64 values (one zero).
+__device__ __forceinline__ uint32_t f32_order(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ uint64_t f64_order(double d) {
+  if (d == 0.0) d = 0.0;
+  uint64_t u = (uint64_t)__double_as_longlong(d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const int lo = __shfl_xor((int)(uint32_t)v, o, kWave);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), o, kWave);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+template <int NW>
+struct SelShared {
+  int hist[NW][256];          // one digit histogram per wave
+  int red[NW][4];             // per-wave partials of block reductions
+  int digit, rem, nlist;
+  int list[kSmallBand];
+  double lkey[kSmallBand];
+  uint32_t rows[NW][128];     // one page's summary rows per wave (2 x 128 bf16)
+  uint16_t qstage[kQStageBytes / 2];
+};
+
+// ---------------------------------------------------------------------------
+// block-wide helpers: DPP inside a wave, one LDS exchange across waves
+// ---------------------------------------------------------------------------
+
+template <int NW>
+__device__ void block_sum2(int &a, int &b, SelShared<NW> &sh) {
+  a = wave_sum_dpp(a);
+  b = wave_sum_dpp(b);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    sh.red[threadIdx.x / kWave][0] = a;
+    sh.red[threadIdx.x / kWave][1] = b;
+  }
+  __syncthreads();
+  a = b = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    a += sh.red[w][0];
+    b += sh.red[w][1];
+  }
+}
+
+// sum of c, max of m
+template <int NW>
+__device__ void block_sum_max(int &c, int &m, SelShared<NW> &sh) {
+  c = wave_sum_dpp(c);
+  m = wave_max_dpp(m);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    sh.red[threadIdx.x / kWave][0] = c;
+    sh.red[threadIdx.x / kWave][1] = m;
+  }
+  __syncthreads();
+  c = 0;
+  m = INT_MIN;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    c += sh.red[w][0];
+    m = max(m, sh.red[w][1]);
+  }
+}
+
+// max of f, AND and OR of the 32-bit a / o
+template <int NW>
+__device__ void block_max_and_or(float &f, uint32_t &a, uint32_t &o, SelShared<NW> &sh) {
+  f = wave_max_dpp(f);
+  a = wave_and_dpp(a);
+  o = wave_or_dpp(o);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    sh.red[threadIdx.x / kWave][0] = __float_as_int(f);
+    sh.red[threadIdx.x / kWave][1] = (int)a;
+    sh.red[threadIdx.x / kWave][2] = (int)o;
+  }
+  __syncthreads();
+  f = __int_as_float(sh.red[0][0]);
+  a = ~0u;
+  o = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    f = fmaxf(f, __int_as_float(sh.red[w][0]));
+    a &= (uint32_t)sh.red[w][1];
+    o |= (uint32_t)sh.red[w][2];
+  }
+}
+
+// AND and OR of 64-bit values
+template <int NW>
+__device__ void block_and_or64(uint64_t &a, uint64_t &o, SelShared<NW> &sh) {
+  const uint32_t alo = wave_and_dpp((uint32_t)a), ahi = wave_and_dpp((uint32_t)(a >> 32));
+  const uint32_t olo = wave_or_dpp((uint32_t)o), ohi = wave_or_dpp((uint32_t)(o >> 32));
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    int *r = sh.red[threadIdx.x / kWave];
+    r[0] = (int)alo; r[1] = (int)ahi; r[2] = (int)olo; r[3] = (int)ohi;
+  }
+  __syncthreads();
+  a = ~0ull;
+  o = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    a &= ((uint64_t)(uint32_t)sh.red[w][1] << 32) | (uint32_t)sh.red[w][0];
+    o |= ((uint64_t)(uint32_t)sh.red[w][3] << 32) | (uint32_t)sh.red[w][2];
+  }
+}
+
+// Exclusive prefix of v over threads in order; *total gets the sum.
+template <int NW>
+__device__ int block_exclusive_scan(int v, int *total, SelShared<NW> &sh) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int incl = wave_incl_sum(v);
+  __syncthreads();
+  if (lane == kWave - 1) sh.red[wave][0] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    if (w < wave) base += sh.red[w][0];
+    tot += sh.red[w][0];
+  }
+  *total = tot;
+  return base + incl - v;
+}
+
+// With the per-wave histograms filled, finds the digit holding rank kk
+// (1-based, from the top): sh.digit, and the rank inside it: sh.rem.  Wave 0:
+// lane l owns digits 255-4l .. 252-4l, summed over the waves' histograms.
+template <int NW>
+__device__ void find_digit_from_top(int kk, SelShared<NW> &sh) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int c[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int bin = 255 - 4 * lane - i;
+      int t = 0;
+#pragma unroll
+      for (int w = 0; w < NW; w++) t += sh.hist[w][bin];
+      c[i] = t;
+      s += t;
+    }
+    const int incl = wave_incl_sum(s);
+    const int excl = incl - s;
+    if (excl < kk && incl >= kk) {  // exactly one lane
+      int cum = excl;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (cum + c[i] >= kk) {
+          sh.digit = 255 - 4 * lane - i;
+          sh.rem = kk - cum;
+          break;
+        }
+        cum += c[i];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// k-th largest (1-based) of the keys whose member bit is set (all keys when
+// member_bits is null); all_and / all_or are the AND and OR of the member
+// keys.  The bits above the highest bit where the members differ are common
+// to all of them; the rest is resolved 8 bits per histogram pass.
+template <typename U, int NW>
+__device__ U kth_largest(const U *keys, const uint32_t *member_bits, int n, int k, U all_and, U all_or,
+                         SelShared<NW> &sh) {
+  constexpr int kBits = 8 * sizeof(U);
+  const U diff = all_and ^ all_or;
+  if (diff == 0) return all_and;
+  int hb = kBits - 1;
+  while (!((diff >> hb) & 1)) hb--;
+  U pmask = hb + 1 >= kBits ? (U)0 : (U)(~(U)0 << (hb + 1));
+  U prefix = all_and & pmask;
+  int kk = k;
+  int *myhist = sh.hist[threadIdx.x / kWave];
+  while (hb >= 0) {
+    const int lo = hb >= 7 ? hb - 7 : 0;
+    const U dmask = (U)((1u << (hb - lo + 1)) - 1u);
+    for (int i = threadIdx.x % kWave; i < 256; i += kWave) myhist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += NW * kWave) {
+      if (member_bits && !((member_bits[i >> 5] >> (i & 31)) & 1u)) continue;
+      const U u = keys[i];
+      if ((u & pmask) == prefix) atomicAdd(&myhist[(int)((u >> lo) & dmask)], 1);
+    }
+    __syncthreads();
+    find_digit_from_top(kk, sh);
+    prefix |= (U)sh.digit << lo;
+    pmask |= dmask << lo;
+    kk = sh.rem;
+    hb = lo - 1;
+  }
+  return prefix;
+}
+
+// ---------------------------------------------------------------------------
+// exact page bound
+// ---------------------------------------------------------------------------
+
+// bf16 pattern -> (significand, exponent): value = m * 2^e, m < 2^8.
+__device__ __forceinline__ void bf16_split(uint32_t bits, int &m, int &e) {
+  const int ef = (bits >> 7) & 0xff, mant = bits & 0x7f;
+  if (ef == 0) {
+    m = mant;
+    e = -133;
+  } else {
+    m = mant | 0x80;
+    e = ef - 134;
+  }
+}
+
+// Signed significand and exponent of the term q_d * x_d (bit patterns).
+__device__ __forceinline__ void term_of(uint32_t qb, uint32_t xb, int &M, int &E) {
+  int mq, eq, mx, ex;
+  bf16_split(qb, mq, eq);
+  bf16_split(xb, mx, ex);
+  M = mq * mx;
+  E = eq + ex;
+  if ((qb ^ xb) & 0x8000u) M = -M;
+}
+
+// Channel-d term q_d * (q_d < 0 ? lo_d : hi_d).
+__device__ __forceinline__ void bound_term(const uint16_t *qh, const uint16_t *lo, const uint16_t *hi,
+                                           int d, int &M, int &E) {
+  const uint32_t qb = qh[d];
+  term_of(qb, (qb & 0x8000u) ? lo[d] : hi[d], M, E);
+}
+
+__device__ __forceinline__ double i64_to_f64_rn(int64_t x) {
+  // both parts are exact doubles; their sum is rounded once
+  const int32_t hi = (int32_t)(x >> 32);
+  const uint32_t lo = (uint32_t)x;
+  return (double)hi * 4294967296.0 + (double)lo;
+}
+
+// Exact sum with 32-bit digits; every lane runs it (rare path: some term is
+// too small for the 64-bit window of exact_head_bound).
+template <int D>
+__device__ double exact_head_bound_digits(const uint16_t *qh, const uint16_t *lo, const uint16_t *hi) {
+  constexpr int kDigits = 22;
+  constexpr int kLow = -288;   // weight of bit 0 of digit 0: below 2^-266, the smallest term
+  int64_t dg[kDigits];
+  for (int i = 0; i < kDigits; i++) dg[i] = 0;
+  for (int d = 0; d < D; d++) {
+    int M, E;
+    bound_term(qh, lo, hi, d, M, E);
+    if (M == 0) continue;
+    const int off = E - kLow;
+    const int di = off >> 5, sh = off & 31;
+    const int64_t v = (int64_t)M * ((int64_t)1 << sh);
+    const int64_t low = v & 0xffffffffll;
+    dg[di] += low;
+    dg[di + 1] += (v - low) / ((int64_t)1 << 32);
+  }
+  // carries: digits into [0, 2^32), the top one keeps the sign
+  for (int i = 0; i + 1 < kDigits; i++) {
+    const int64_t low = dg[i] & 0xffffffffll;
+    dg[i + 1] += (dg[i] - low) / ((int64_t)1 << 32);
+    dg[i] = low;
+  }
+  bool neg = dg[kDigits - 1] < 0;
+  if (neg) {
+    for (int i = 0; i < kDigits; i++) dg[i] = -dg[i];
+    for (int i = 0; i + 1 < kDigits; i++) {
+      const int64_t low = dg[i] & 0xffffffffll;
+      dg[i + 1] += (dg[i] - low) / ((int64_t)1 << 32);
+      dg[i] = low;
+    }
+  }
+  int top = kDigits - 1;
+  while (top >= 0 && dg[top] == 0) top--;
+  if (top < 0) return 0.0;
+  // 64-bit window ending at the leading one; lower bits fold into a sticky bit
+  const int lead = 32 * top + 31 - __builtin_clz((uint32_t)dg[top]);
+  double r;
+  if (lead < 64) {
+    const uint64_t x = (uint64_t)dg[0] | ((uint64_t)dg[1] << 32);
+    r = ldexp((double)(uint32_t)(x >> 32) * 4294967296.0 + (double)(uint32_t)x, kLow);
+  } else {
+    const int lo_bit = lead - 63;
+    const int di = lo_bit >> 5, sh = lo_bit & 31;
+    const uint64_t w0 = (uint64_t)dg[di] | ((uint64_t)dg[di + 1] << 32);
+    const uint64_t w2 = di + 2 < kDigits ? (uint64_t)dg[di + 2] : 0;
+    uint64_t x = sh == 0 ? w0 : ((w0 >> sh) | (w2 << (64 - sh)));
+    bool sticky = sh != 0 && (dg[di] & ((1ll << sh) - 1)) != 0;
+    for (int i = 0; i < di; i++) sticky |= dg[i] != 0;
+    if (sticky) x |= 1;  // 11 bits below the rounding point: the sticky bit keeps RNE exact
+    r = ldexp((double)(uint32_t)(x >> 32) * 4294967296.0 + (double)(uint32_t)x, lo_bit + kLow);
+  }
+  return neg ? -r : r;
+}
+
+// Correctly rounded fp64 value of the exact sum_d q_d * (q_d < 0 ? lo_d : hi_d).
+// Wave-wide: lane l holds channels l, l+64, ... of the page rows (xl, xh, bit
+// patterns); the terms are placed on one 64-bit integer grid just below the
+// largest term and summed exactly across the wave.  qh may point to LDS.
+template <int D>
+__device__ double exact_head_bound(const uint16_t *qh, const uint32_t *xl, const uint32_t *xh,
+                                   const uint16_t *lo, const uint16_t *hi, int lane) {
+  constexpr int PER = (D + kWave - 1) / kWave;
+  constexpr int LOGD = D <= 128 ? 7 : (D <= 1024 ? 10 : 16);
+  constexpr int HEADROOM = 62 - 16 - LOGD;  // |sum| < D * 2^16 * 2^HEADROOM <= 2^62
+  int Ms[PER], Es[PER];
+  int emax = INT_MIN;
+#pragma unroll
+  for (int s = 0; s < PER; s++) {
+    const int d = lane + kWave * s;
+    Ms[s] = 0;
+    Es[s] = 0;
+    if (d < D) {
+      const uint32_t qb = qh[d];
+      term_of(qb, (qb & 0x8000u) ? xl[s] : xh[s], Ms[s], Es[s]);
+      if (Ms[s] != 0) emax = max(emax, Es[s]);
+    }
+  }
+  emax = wave_max_int(emax);
+  if (emax == INT_MIN) return 0.0;
+  const int base = emax - HEADROOM;
+  int64_t acc = 0;
+  int tiny = 0;
+#pragma unroll
+  for (int s = 0; s < PER; s++) {
+    if (Ms[s] == 0) continue;
+    const int sh = Es[s] - base;
+    if (sh >= 0)
+      acc += (int64_t)Ms[s] * ((int64_t)1 << sh);
+    else
+      tiny = 1;
+  }
+  if (__any(tiny)) return exact_head_bound_digits<D>(qh, lo, hi);
+  acc = wave_sum_i64(acc);
+  return ldexp(i64_to_f64_rn(acc), base);
+}
+
+// Exact group score of one page: max over the G heads (wave-wide).
+template <int D>
+__device__ double exact_page_key(const uint16_t *qg, int G, const uint16_t *lo, const uint16_t *hi, int lane) {
+  constexpr int PER = (D + kWave - 1) / kWave;
+  uint32_t xl[PER], xh[PER];
+#pragma unroll
+  for (int s = 0; s < PER; s++) {
+    const int d = lane + kWave * s;
+    xl[s] = d < D ? lo[d] : 0u;
+    xh[s] = d < D ? hi[d] : 0u;
+  }
+  double best = -INFINITY;
+  for (int m = 0; m < G; m++) best = fmax(best, exact_head_bound<D>(qg + (size_t)m * D, xl, xh, lo, hi, lane));
+  return best;
+}
+
+// Exact group score of one page for up to 16 heads at once: lane l works on
+// head l / 4 and channels (l % 4) + 4t of the page rows (rows: lo then hi,
+// bf16 pairs in LDS); the four lanes of a head sum exactly on a common 64-bit
+// grid, then the wave takes the max over heads.  Falls back to the per-head
+// digit sum when some term lies below the grid.
+template <int D>
+__device__ double exact_page_key_heads16(const uint16_t *qg, int G, const uint16_t *rows,
+                                         const uint16_t *lo_g, const uint16_t *hi_g, int lane) {
+  constexpr int NP = 4, PER = D / NP;
+  constexpr int LOGD = D <= 128 ? 7 : (D <= 1024 ? 10 : 16);
+  constexpr int HEADROOM = 62 - 16 - LOGD;
+  const int m = lane / NP, part = lane % NP;
+  const bool live = m < G;
+  const uint16_t *qh = qg + (size_t)(live ? m : 0) * D;
+  int emax = INT_MIN;
+#pragma unroll 8
+  for (int t = 0; t < PER; t++) {
+    const int d = part + NP * t;
+    const uint32_t qb = qh[d];
+    int M, E;
+    term_of(qb, (qb & 0x8000u) ? rows[d] : rows[D + d], M, E);
+    if (live && M != 0) emax = max(emax, E);
+  }
+  emax = max(emax, __shfl_xor(emax, 1, kWave));
+  emax = max(emax, __shfl_xor(emax, 2, kWave));
+  const int base = emax - HEADROOM;
+  int64_t acc = 0;
+  int tiny = 0;
+  if (live && emax != INT_MIN) {
+#pragma unroll 8
+    for (int t = 0; t < PER; t++) {
+      const int d = part + NP * t;
+      const uint32_t qb = qh[d];
+      int M, E;
+      term_of(qb, (qb & 0x8000u) ? rows[d] : rows[D + d], M, E);
+      if (M == 0) continue;
+      const int sh = E - base;
+      if (sh >= 0)
+        acc += (int64_t)M * ((int64_t)1 << sh);
+      else
+        tiny = 1;
+    }
+  }
+  if (__any(tiny)) {
+    double best = -INFINITY;
+    for (int h = 0; h < G; h++) best = fmax(best, exact_head_bound_digits<D>(qg + (size_t)h * D, lo_g, hi_g));
+    return best;
+  }
+  acc += (int64_t)shfl_xor_u64((uint64_t)acc, 1);
+  acc += (int64_t)shfl_xor_u64((uint64_t)acc, 2);
+  double v = -INFINITY;
+  if (live) v = emax == INT_MIN ? 0.0 : ldexp(i64_to_f64_rn(acc), base);
+  for (int o = 4; o < kWave; o <<= 1) v = fmax(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Marks the top-k candidates in sel_bits.  Called by every thread of the
+// block.  Preconditions: keys32[0..n) hold the candidates' order keys (LDS,
+// visible to all threads); band_bits is zero; sh.nlist is zero; emax, k_and
+// and k_or are the block-wide max error bound, AND and OR of the keys;
+// 0 < k < n.  Candidate i is logical page cand_lo + i; pt_row is the
+// sequence's page-table row; qg the group's first q row (global).  keys64
+// aliases keys32 (8 bytes per candidate) for large bands.
+template <int D, int NW>
+__device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t *keys64, uint32_t *sel_bits,
+                                  uint32_t *band_bits, int n, int k, int cand_lo, float emax, uint32_t k_and,
+                                  uint32_t k_or, const uint16_t *qg, int G, const uint16_t *summ,
+                                  const int32_t *pt_row, int Hkv, int g) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const uint32_t uk = kth_largest<uint32_t, NW>(keys32, nullptr, n, k, k_and, k_or, sh);
+  // (k+1)-th largest: uk again if more than k keys reach it, else the largest below it
+  int c_ge = 0;
+  int below = INT_MIN;  // unsigned order keys, biased into the signed range
+  for (int i = tid; i < n; i += NW * kWave) {
+    const uint32_t u = keys32[i];
+    c_ge += u >= uk;
+    if (u < uk) below = max(below, (int)(u ^ 0x80000000u));
+  }
+  block_sum_max(c_ge, below, sh);
+  const float vk = f32_from_order(uk);
+  const float vk1 = c_ge > k ? vk : f32_from_order((uint32_t)below ^ 0x80000000u);
+  const double t_in = (double)vk1 + 2.0 * (double)emax;
+  const double t_out = (double)vk - 2.0 * (double)emax;
+  int n_in = 0, n_band = 0;
+  for (int i = tid; i < n; i += NW * kWave) {
+    const double v = (double)f32_from_order(keys32[i]);
+    const int j = cand_lo + i;
+    if (v > t_in) {
+      atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+      n_in++;
+    } else if (!(v < t_out)) {
+      atomicOr(&band_bits[i >> 5], 1u << (i & 31));
+      n_band++;
+    }
+  }
+  block_sum2(n_in, n_band, sh);
+  const int need = k - n_in;
+  if (need > 0 && need >= n_band) {
+    for (int i = tid; i < n; i += NW * kWave)
+      if ((band_bits[i >> 5] >> (i & 31)) & 1u) {
+        const int j = cand_lo + i;
+        atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+      }
+  } else if (need > 0) {
+    // exact scores of the band pages
+    const uint16_t *qb = qg;
+    if ((size_t)G * D * 2 <= kQStageBytes) {  // stage the group's q rows in LDS
+      for (int i = tid; i < G * D / 2; i += NW * kWave) ((uint32_t *)sh.qstage)[i] = ((const uint32_t *)qb)[i];
+      qb = sh.qstage;
+    }
+    if (n_band <= kSmallBand) {
+      // compact list of the band, exact keys (one page per wave), rank by one wave
+      for (int i = tid; i < n; i += NW * kWave)
+        if ((band_bits[i >> 5] >> (i & 31)) & 1u) sh.list[atomicAdd(&sh.nlist, 1)] = i;
+      __syncthreads();
+      for (int e = wave; e < n_band; e += NW) {
+        const int i = sh.list[e];
+        const int phys = pt_row[cand_lo + i];
+        const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
+        double key;
+        if (D == 128 && G <= 16) {
+          for (int x = lane; x < D; x += kWave) sh.rows[wave][x] = ((const uint32_t *)lo)[x];
+          key = exact_page_key_heads16<D>(qb, G, (const uint16_t *)sh.rows[wave], lo, lo + D, lane);
+        } else {
+          key = exact_page_key<D>(qb, G, lo, lo + D, lane);
+        }
+        if (lane == 0) sh.lkey[e] = key;
+      }
+      __syncthreads();
+      if (wave == 0 && lane < n_band) {
+        const double kl = sh.lkey[lane];
+        const int il = sh.list[lane];
+        int rank = 0;  // band pages that beat this one: larger key, or equal key and lower id
+        for (int e = 0; e < n_band; e++) {
+          const double ke = sh.lkey[e];
+          rank += ke > kl || (ke == kl && sh.list[e] < il);
+        }
+        if (rank < need) {
+          const int j = cand_lo + il;
+          atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+        }
+      }
+    } else {
+      __syncthreads();  // keys32 is dead from here; keys64 reuses the space
+      uint64_t b_and = ~0ull, b_or = 0;
+      int seen = 0;
+      for (int w = 0; w < (n + 31) / 32; w++) {
+        uint32_t bits = band_bits[w];
+        while (bits) {
+          const int i = w * 32 + __builtin_ctz(bits);
+          bits &= bits - 1;
+          if ((seen++ % NW) != wave) continue;
+          const int phys = pt_row[cand_lo + i];
+          const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
+          const uint64_t o = f64_order(exact_page_key<D>(qb, G, lo, lo + D, lane));
+          if (lane == 0) keys64[i] = o;
+          b_and &= o;
+          b_or |= o;
+        }
+      }
+      block_and_or64(b_and, b_or, sh);
+      const uint64_t kth = kth_largest<uint64_t, NW>(keys64, band_bits, n, need, b_and, b_or, sh);
+      // all band pages above kth, then the lowest ids among those equal to it
+      int above = 0, zero = 0;
+      for (int i = tid; i < n; i += NW * kWave)
+        if (((band_bits[i >> 5] >> (i & 31)) & 1u) && keys64[i] > kth) {
+          const int j = cand_lo + i;
+          atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+          above++;
+        }
+      block_sum2(above, zero, sh);
+      int take = need - above;
+      for (int i0 = 0; i0 < n && take > 0; i0 += NW * kWave) {
+        const int i = i0 + tid;
+        const int tie = i < n && ((band_bits[i >> 5] >> (i & 31)) & 1u) && keys64[i] == kth;
+        int total;
+        const int before = block_exclusive_scan(tie, &total, sh);
+        if (tie && before < take) {
+          const int j = cand_lo + i;
+          atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+        }
+        take -= min(total, take);
+      }
+    }
+  }
+}
+
+// Writes the pages marked in sel_bits, in ascending order, to out_global
+// (followed by -1 up to max_sel) and/or out_lds.  Returns the count.
+template <int NW>
+__device__ int emit_selection(SelShared<NW> &sh, const uint32_t *sel_bits, int nwords, int32_t *out_global,
+                              int32_t *out_lds, int max_sel) {
+  constexpr int T = NW * kWave;
+  const int tid = threadIdx.x;
+  int written = 0;
+  for (int w0 = 0; w0 < nwords; w0 += T) {
+    const int w = w0 + tid;
+    const uint32_t bits = w < nwords ? sel_bits[w] : 0u;
+    int total;
+    int pos = written + block_exclusive_scan(__popc(bits), &total, sh);
+    uint32_t x = bits;
+    while (x) {
+      const int j = w * 32 + __builtin_ctz(x);
+      x &= x - 1;
+      if (pos < max_sel) {
+        if (out_global) out_global[pos] = j;
+        if (out_lds) out_lds[pos] = j;
+      }
+      pos++;
+    }
+    written += total;
+  }
+  const int count = min(written, max_sel);
+  if (out_global)
+    for (int i = count + tid; i < max_sel; i += T) out_global[i] = -1;
+  return count;
+}
+
+}  // namespace sel
+}  // namespace qasp

@@ -194,6 +194,62 @@ def test_split_entry_points_match_decode_step():
     assert np.array_equal(out.cpu().numpy(), g.out)
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("llama8b_b32_32k", dict(batch=32, seq_len=2500, seq_len_min=300)),      # 256 units: one-kernel step
+    ("ragged_b64_mixed", dict(batch=26, seq_len=3000, seq_len_min=1)),       # 208 units, static heads
+])
+def test_single_kernel_step_matches_oracle_and_kernel_chain(name, kw):
+    """Many units: qasp_decode_step runs the whole step as one kernel; it must
+    match the oracle and the score -> select -> decode kernel chain."""
+    w = _small(name, **kw)
+    lay, pol = api.layout_of(w), api.policy_of(w)
+    assert w.spec.batch * lay.num_kv_heads >= 200
+    g = run_gpu(w)
+    r = run_oracle(w, pol, g.max_sel)
+    compare(g, r, what="one-kernel step " + name)
+    q, kp, vp = w.q.to(DEV), w.k_pool.to(DEV), w.v_pool.to(DEV)
+    bat = api.Batch(w.page_table.to(DEV), w.seq_lens.to(DEV), w.spec.num_q_heads)
+    sc = api.score_pages(lay, bat, pol, q, g.summ)
+    sel, cnt = api.select_topk(lay, bat, pol, q, g.summ, sc, max_sel_n=g.max_sel)
+    ws = api.new_workspace(lay, bat, pol, g.max_sel, DEV)
+    out = api.sparse_paged_decode(lay, bat, pol, q, kp, vp, sel, cnt, w.scale, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), g.sel) and np.array_equal(cnt.cpu().numpy(), g.cnt)
+    assert np.abs(out.cpu().numpy() - g.out).max() <= 1e-5
+
+
+def test_single_kernel_step_appends():
+    """The one-kernel step writes the token at L-1 and updates its summary."""
+    w = _small("llama8b_b32_32k", batch=32, seq_len=700, seq_len_min=600)
+    lay, pol = api.layout_of(w), api.policy_of(w)
+    gen = torch.Generator().manual_seed(5)
+    new_k = torch.randn(w.k_new.shape, generator=gen).to(torch.bfloat16)
+    new_v = torch.randn(w.v_new.shape, generator=gen).to(torch.bfloat16)
+    kp, vp = w.k_pool.to(DEV), w.v_pool.to(DEV)
+    bat = api.Batch(w.page_table.to(DEV), w.seq_lens.to(DEV), 32)
+    summ = torch.zeros((lay.num_pool_pages, 8, 2, 128), dtype=torch.bfloat16, device=DEV)
+    # summaries of the cache before the new token: lengths L-1
+    api.build_summaries(lay, api.Batch(bat.page_table, (bat.seq_lens - 1).contiguous(), 32), kp, summ)
+    msel = api.max_sel(lay, pol, bat.max_pages)
+    ws = api.new_workspace(lay, bat, pol, msel, DEV)
+    out = api.decode_step(lay, bat, pol, w.q.to(DEV), kp, vp, summ, w.scale, ws, msel,
+                          k_new=new_k.to(DEV), v_new=new_v.to(DEV))
+    torch.cuda.synchronize()
+    # the oracle sees the pool with the token written and summaries from scratch
+    for b in range(32):
+        L = int(w.seq_lens[b])
+        phys = int(w.page_table[b, (L - 1) // 16])
+        w.k_pool[phys, :, (L - 1) % 16, :] = new_k[b]
+        w.v_pool[phys, :, :, (L - 1) % 16] = new_v[b]
+    assert torch.equal(kp.cpu().view(torch.int16), w.k_pool.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), w.v_pool.view(torch.int16))
+    r = run_oracle(w, pol, msel)
+    used = w.page_table[:, :44].reshape(-1).long()
+    used = used[used >= 0]
+    assert np.array_equal(workloads.bits(summ.cpu()[used]), r.summ[used.numpy()])
+    assert np.abs(out.cpu().numpy().astype(np.float64) - r.out).max() <= 5e-3
+
+
 def test_repeated_calls_are_deterministic():
     w = _small("llama8b_b32_32k", batch=4, seq_len=4000)
     a = run_gpu(w)
