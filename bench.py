@@ -24,6 +24,31 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 
 
+def kernel_source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "query_aware_sparse_paged_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter record, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel.replace("_kernel", ""), workload))
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -70,12 +95,17 @@ def cpu_baseline(w, msel, n_seqs, threads):
     lay = oracle.Layout(int(phys.numel()), s.page_size, s.num_kv_heads, s.head_dim_k, s.head_dim_v, s.v_from_k)
     pol = oracle.Policy(s.n_sink_pages, s.n_local_pages, s.top_k, s.sink_tokens, s.window_tokens, s.static_heads)
     summ = oracle.summaries(lay, pt, sl, s.num_q_heads, k)
-    t0 = time.perf_counter()
-    oracle.decode(lay, pt, sl, q, k, v, summ, pol, w.scale, num_threads=threads, max_sel_n=msel)
-    dt = time.perf_counter() - t0
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < 1.0 and len(times) < 50):
+        t0 = time.perf_counter()
+        oracle.decode(lay, pt, sl, q, k, v, summ, pol, w.scale, num_threads=threads, max_sel_n=msel)
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
     return {"value": len(seqs) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d sequences (all %d KV heads), one decode step over precomputed summaries, "
-                      "%.2f s wall" % (len(seqs), s.batch, s.num_kv_heads, dt)}
+            "sample": "%d of %d sequences (all %d KV heads), one decode step over precomputed summaries; "
+                      "median of %d runs, %.3f s wall each, %.1f s total" % (
+                          len(seqs), s.batch, s.num_kv_heads, len(times), dt, sum(times))}
 
 
 def main():
@@ -87,6 +117,8 @@ def main():
     ap.add_argument("--layers", type=int, default=3, help="independent layer caches rotated over")
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (a known-size kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -121,6 +153,15 @@ def main():
         log("layer %d ready: pool %.2f GB" % (i, (w.k_pool.numel() + (0 if w.v_pool is None else w.v_pool.numel()))
                                                * 2 / 1e9))
     torch.cuda.synchronize()
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # one elementwise kernel: n bytes read, n bytes written
+        torch.cuda.synchronize()
+        log("calibration kernel (neg): %d bytes read, %d bytes written" % (n, n))
+        del src, dst
     stream = torch.cuda.current_stream()
     w0 = layers[0]["w"]
     spec = w0.spec
@@ -193,7 +234,9 @@ def main():
         "step_us_events": {"median": round(dom_ms * 1e3, 2), "p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
                            "p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2)},
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": profiled_traffic(kernel, spec.name) if one_kernel else None,
+                     "algorithmic_bytes": total_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
