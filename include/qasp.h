@@ -68,7 +68,7 @@ typedef enum {
  *   grouped-query: page_size 16, head_dim_k = head_dim_v = 128,
  *                  1 <= num_q_heads / num_kv_heads <= 16, num_kv_heads <= 64;
  *   latent (MLA):  page_size 64, head_dim_k 576, head_dim_v 512, v_from_k = 1,
- *                  num_q_heads / num_kv_heads = 128.                         */
+ *                  num_kv_heads = 1, num_q_heads = 128.                      */
 typedef struct {
     int32_t num_pool_pages;
     int32_t page_size;

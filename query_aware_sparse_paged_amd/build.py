@@ -20,7 +20,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["api.hip", "summaries.hip", "score.hip", "select.hip", "decode_gqa.hip", "decode_mla.hip",
+SOURCES = ["api.hip", "summaries.hip", "score.hip", "score_mla.hip", "select.hip", "decode_gqa.hip", "decode_mla.hip",
            "fused_gqa.hip"]
 
 

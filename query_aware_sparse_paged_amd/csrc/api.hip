@@ -36,6 +36,7 @@ static int32_t check_layout(const qasp_layout *lay) {
   if (lay->v_from_k && lay->head_dim_v > lay->head_dim_k) return QASP_ERR_BAD_SHAPE;
   if (lay->num_kv_heads > 64) return QASP_ERR_UNSUPPORTED;
   if (family_of(*lay) == kFamilyNone) return QASP_ERR_UNSUPPORTED;
+  if (family_of(*lay) == kFamilyMla && lay->num_kv_heads != 1) return QASP_ERR_UNSUPPORTED;
   return QASP_OK;
 }
 

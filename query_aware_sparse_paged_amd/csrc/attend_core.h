@@ -83,12 +83,14 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const uint16_t *__re
     const int j = __shfl(my_j, min(it, npg - 1), kWave);
     float sv[4];
     float tmax = -INFINITY;
+    uint32_t keep[2] = {0u, 0u};  // value bits of the attended tokens 4kg + r
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int pos = j * PS + 4 * kg + r;
-      const bool ok = real && pos < L && (!is_static || pos < sink_end || pos >= win_begin);
+      const bool ok = real & (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
       sv[r] = ok ? s[r] * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, sv[r]);
+      keep[r >> 1] |= ok ? (0xffffu << (16 * (r & 1))) : 0u;
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
@@ -111,11 +113,14 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const uint16_t *__re
     const uint2 ph = pack_bf16x4(p[0], p[1], p[2], p[3]);
     const uint2 pl = pack_bf16x4(p[0] - bf16_round_f32(p[0]), p[1] - bf16_round_f32(p[1]),
                                  p[2] - bf16_round_f32(p[2]), p[3] - bf16_round_f32(p[3]));
+    // values of tokens that are not attended are zeroed: a zero weight times
+    // a stale non-finite pool entry would still be NaN
 #pragma unroll
     for (int i = 0; i < DV / 16; i++) {
+      const uint2 v = make_uint2(vt[i].x & keep[0], vt[i].y & keep[1]);
       st.acc[i] *= alpha;
-      st.acc[i] = mfma16x16x16(vt[i], ph, st.acc[i]);
-      st.acc[i] = mfma16x16x16(vt[i], pl, st.acc[i]);
+      st.acc[i] = mfma16x16x16(v, ph, st.acc[i]);
+      st.acc[i] = mfma16x16x16(v, pl, st.acc[i]);
     }
   };
   // page it computes from (kc, vc) after prefetching page it+2 into (kn, vn)

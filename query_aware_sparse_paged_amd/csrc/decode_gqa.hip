@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float *__restri
     if (M != -INFINITY) {
       for (int s = 0; s < splits; s++) {
         const float2 ml = partial_ml[base + s];
+        if (ml.x == -INFINITY) continue;  // empty split
         const float f = __builtin_amdgcn_exp2f(ml.x - M);
         a += f * partial[(base + s) * dv_dim + dv];
         lsum += f * ml.y;

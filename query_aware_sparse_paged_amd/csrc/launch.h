@@ -41,6 +41,8 @@ hipError_t launch_append_kv(const qasp_layout &lay, const qasp_batch &bat, int p
 hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
                               qasp_score *scores, hipStream_t stream);
+hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                            const uint16_t *q, const uint16_t *summ, qasp_score *scores, hipStream_t stream);
 hipError_t launch_select_topk(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
                               const qasp_score *scores, int32_t *sel, int32_t *sel_count,

@@ -84,6 +84,8 @@ hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
                        bat.seq_lens, scores, bat.pt_stride, bat.max_pages, bat.num_q_heads,
                        lay.num_kv_heads, G, lay.page_size, pol.n_sink_pages, pol.n_local_pages,
                        pol.static_head_mask);
+  } else if (lay.head_dim_k == 576) {
+    return launch_score_mla(lay, bat, pol, q, summ, scores, stream);
   } else {
     return hipErrorInvalidValue;
   }

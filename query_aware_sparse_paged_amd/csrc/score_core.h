@@ -45,25 +45,26 @@ __device__ __forceinline__ uint4 map4(uint4 v, int mode) {
 
 // A operands of one wave: row m = head m of the group, k = [q^-, q^+] and its
 // absolute value.  Lane l holds row l % 16, k block l / 16.
-template <int D>
+// ABS: also keep |q'| for the contraction on absolute values.
+template <int D, bool ABS = true>
 struct QOperands {
   static constexpr int KSTEPS = 2 * D / 32;
-  uint4 aq[KSTEPS], aa[KSTEPS];
+  uint4 aq[KSTEPS], aa[ABS ? KSTEPS : 1];
 };
 
 // qg: the group's first q row; heads m >= G (or an inactive group) get zeros.
-template <int D>
-__device__ __forceinline__ void load_q_operands(QOperands<D> &op, const uint16_t *qg, int G, bool active,
+template <int D, bool ABS = true>
+__device__ __forceinline__ void load_q_operands(QOperands<D, ABS> &op, const uint16_t *qg, int G, bool active,
                                                 int lane) {
   const int m = lane & 15, kg = lane >> 4;
   const uint16_t *qh = qg + (size_t)(m < G ? m : 0) * D;
 #pragma unroll
-  for (int i = 0; i < QOperands<D>::KSTEPS; i++) {
+  for (int i = 0; i < QOperands<D, ABS>::KSTEPS; i++) {
     const int k0 = 32 * i + 8 * kg;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (m < G && active) v = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
     op.aq[i] = map4(v, k0 < D ? 0 : 1);
-    op.aa[i] = map4(op.aq[i], 2);
+    if (ABS) op.aa[i] = map4(op.aq[i], 2);
   }
 }
 

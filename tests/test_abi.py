@@ -76,6 +76,9 @@ def test_null_and_shape_errors(L):
     assert _call("qasp_score_pages", b(lay), b(bat), b(pol), None, 1, 1, None) == api.ERR_NULL_ARG
     # MLA needs 128 q heads per latent head
     assert _call("qasp_score_pages", b(MLA.c()), b(_batch(Hq=64)), b(pol), 1, 1, 1, None) == api.ERR_UNSUPPORTED
+    # and exactly one latent KV head
+    mla2 = api.CLayout(64, 64, 2, 576, 512, 1)
+    assert _call("qasp_score_pages", b(mla2), b(_batch(Hq=256)), b(pol), 1, 1, 1, None) == api.ERR_UNSUPPORTED
 
 
 def test_max_sel_and_workspace_checks(L):

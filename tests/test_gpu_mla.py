@@ -1,0 +1,125 @@
+"""GPU parity of the latent-head (MLA) family: 128 query heads over one
+576-channel latent KV head, value = its first 512 channels, pages of 64.
+
+Same bar as the grouped-query tests: summaries and selections bit-exact,
+scores inside their bounds, outputs within 5e-3 max-abs of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from query_aware_sparse_paged_amd import api, workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_cases import DEV, compare, gpu_summaries_of, run_gpu, run_oracle
+
+PS = 64
+
+
+def _small(**kw):
+    return workloads.make("mla_b16_64k", device="cpu", **kw)
+
+
+def _set_lengths(w, lens):
+    """Shorter lengths inside the generated pages; the appended token is the
+    one at each sequence's new last position."""
+    w.seq_lens[:] = torch.tensor(lens, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        phys = int(w.page_table[b, (L - 1) // PS])
+        w.k_new[b] = w.k_pool[phys, :, (L - 1) % PS, :]
+
+
+def test_mla_small_ragged():
+    w = _small(batch=3, seq_len=3000, seq_len_min=1000)
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="mla small")
+    pages = (w.seq_lens.numpy() + PS - 1) // PS
+    assert (g.cnt[:, 0] == np.minimum(32, pages)).all()
+
+
+@pytest.mark.parametrize("lens,pol", [
+    ([1, 63, 64, 65], api.Policy(1, 2, 29)),              # below one page .. one token into page 2
+    ([191, 192, 193, 2000], api.Policy(1, 2, 29)),        # k >= candidates, page-size edges
+    ([700, 1500, 129, 4000], api.Policy(0, 1, 5)),        # no sink, few pages: many empty splits
+    ([900, 3000, 64, 2049], api.Policy(2, 0, 0)),         # no top-k
+])
+def test_mla_edges(lens, pol):
+    w = _small(batch=len(lens), seq_len=max(lens))
+    _set_lengths(w, lens)
+    g = run_gpu(w, pol=pol)
+    r = run_oracle(w, pol, g.max_sel)
+    compare(g, r, what="mla edge %s" % lens)
+
+
+def test_mla_static_head_sink_and_window():
+    w = _small(batch=3, seq_len=2500, seq_len_min=100)
+    pol = api.Policy(0, 0, 0, 40, 300, [1])
+    g = run_gpu(w, pol=pol, use_summ=False)
+    r = run_oracle(w, pol, g.max_sel)
+    compare(g, r, check_scores=False, what="mla static")
+
+
+def test_mla_reference_max_too_low_starts_again():
+    """A token whose score lies ~100 (log2 units) above the first chunk of its
+    block: the kernel must redo the block from the larger reference max."""
+    w = _small(batch=1, seq_len=64 * 40)
+    q0 = w.q[0, 0].float()
+    needle = (40.0 * q0 / q0.norm()).to(torch.bfloat16)
+    pos = 64 * 20 + 40                       # second chunk of logical page 20
+    phys = int(w.page_table[0, pos // PS])
+    w.k_pool[phys, 0, pos % PS] = needle
+    scale_log2 = w.scale * 1.4426950408889634
+    assert float(needle.float() @ q0) * scale_log2 > 64 + 20
+    g = run_gpu(w)
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="mla restart")
+    assert 20 in g.sel[0, 0].tolist()
+    # head 0 attends the needle almost alone
+    assert np.abs(g.out[0, 0] - needle[:512].float().numpy()).max() < 1e-2
+
+
+def test_mla_stale_non_finite_tail_is_not_read():
+    """Pool slots past each length hold NaN: the output must not see them."""
+    w = _small(batch=3, seq_len=2000, seq_len_min=1000)
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
+    for b in range(3):
+        L = int(w.seq_lens[b])
+        if L % PS:
+            phys = int(w.page_table[b, (L - 1) // PS])
+            w.k_pool[phys, 0, L % PS:] = nan
+    g = run_gpu(w)
+    assert np.isfinite(g.out).all()
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="mla NaN tail")
+
+
+def test_mla_split_entry_points_match_decode_step():
+    w = _small(batch=2, seq_len=5000, seq_len_min=3000)
+    lay, pol = api.layout_of(w), api.policy_of(w)
+    g = run_gpu(w)
+    q, kp = w.q.to(DEV), w.k_pool.to(DEV)
+    bat = api.Batch(w.page_table.to(DEV), w.seq_lens.to(DEV), 128)
+    sc = api.score_pages(lay, bat, pol, q, g.summ)
+    sel, cnt = api.select_topk(lay, bat, pol, q, g.summ, sc, max_sel_n=g.max_sel)
+    ws = api.new_workspace(lay, bat, pol, g.max_sel, DEV)
+    out = api.sparse_paged_decode(lay, bat, pol, q, kp, None, sel, cnt, w.scale, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), g.sel) and np.array_equal(cnt.cpu().numpy(), g.cnt)
+    assert np.array_equal(out.cpu().numpy(), g.out)
+
+
+def test_full_mla_b16_64k():
+    w = workloads.make("mla_b16_64k", device=DEV)
+    g = run_gpu(w)
+    assert (g.cnt == 32).all()
+    assert (np.diff(g.sel, axis=2) > 0).all()
+    seqs = [0, 9, 15]
+    r = run_oracle(w, api.policy_of(w), g.max_sel, seqs=seqs)
+    assert np.array_equal(gpu_summaries_of(g, w, seqs, r), r.summ), "summaries differ"
+    compare(g, r, seqs=seqs, what="mla_b16_64k")
+    del w, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()

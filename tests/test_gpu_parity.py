@@ -250,6 +250,24 @@ def test_single_kernel_step_appends():
     assert np.abs(out.cpu().numpy().astype(np.float64) - r.out).max() <= 5e-3
 
 
+@pytest.mark.parametrize("batch", [3, 32])   # kernel chain; one-kernel step
+def test_stale_non_finite_tail_is_not_read(batch):
+    """Pool slots past each length hold NaN keys and values: the output must
+    not see them."""
+    w = _small("llama8b_b32_32k", batch=batch, seq_len=900, seq_len_min=400)
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
+    for b in range(batch):
+        L = int(w.seq_lens[b])
+        if L % 16:
+            phys = int(w.page_table[b, (L - 1) // 16])
+            w.k_pool[phys, :, L % 16:, :] = nan
+            w.v_pool[phys, :, :, L % 16:] = nan
+    g = run_gpu(w)
+    assert np.isfinite(g.out).all()
+    r = run_oracle(w, api.policy_of(w), g.max_sel)
+    compare(g, r, what="NaN tail")
+
+
 def test_repeated_calls_are_deterministic():
     w = _small("llama8b_b32_32k", batch=4, seq_len=4000)
     a = run_gpu(w)
