@@ -22,6 +22,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "llama8b_b32_32k"
+METRIC = "decode tokens/s and achieved KV GB/s (% of MI355X HBM peak), 32K ctx, batch 32"
 
 
 def kernel_source_hash():
@@ -113,7 +115,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b_b32_32k")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=3, help="independent layer caches rotated over")
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,7 +146,7 @@ def main():
         ws = api.new_workspace(lay, bat, pol, msel, dev)
         B = w.spec.batch
         layers.append(dict(w=w, lay=lay, pol=pol, bat=bat, bat_before=bat_before, msel=msel, summ=summ, ws=ws,
-                           scores=torch.empty((B, lay.num_kv_heads, bat.max_pages, 2), dtype=torch.float32,
+                           scores=torch.empty((B, lay.num_kv_heads, bat.max_pages, 4), dtype=torch.float32,
                                               device=dev),
                            sel=torch.empty((B, lay.num_kv_heads, msel), dtype=torch.int32, device=dev),
                            cnt=torch.empty((B, lay.num_kv_heads), dtype=torch.int32, device=dev),
@@ -211,7 +213,8 @@ def main():
         log("cpu oracle: %s" % cpu["sample"])
 
     line = {
-        "metric": "decode tokens/s and achieved KV GB/s (% of MI355X HBM peak), 32K ctx, batch 32",
+        "metric": METRIC if spec.name == DEFAULT_WORKLOAD else
+                  "decode tokens/s and achieved GB/s (%% of MI355X HBM peak), %s" % spec.name,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -113,11 +113,17 @@ typedef struct {
 } qasp_policy;
 
 /* Scores as produced by qasp_score_pages: an fp32 approximation of the exact
- * group score and a bound on its error, |value - exact| <= err.  Pages that
- * are not candidates hold value = -inf, err = 0. */
+ * group score and a bound on its error, |value - exact| <= err.  head is the
+ * index, inside the KV head's group, of the query head that certainly
+ * attains the group maximum (its approximate bound leads every other head's
+ * by more than twice the error bound), or -1 when that is not certain; the
+ * exact re-scoring in qasp_select_topk then evaluates only that head.
+ * Pages that are not candidates hold value = -inf, err = 0, head = -1. */
 typedef struct {
     float value;
     float err;
+    int32_t head;
+    int32_t reserved;  /* 0 */
 } qasp_score;
 
 /* Library version, "major.minor.patch". */

@@ -210,14 +210,18 @@ def append_kv(layout: Layout, batch_before: Batch, policy: Policy, k_new, v_new,
 
 
 def score_pages(layout: Layout, batch: Batch, policy: Policy, q, summ, scores=None) -> torch.Tensor:
-    """Returns float32 [B][Hkv][max_pages][2]: (fp32 score, error bound)."""
+    """Returns float32 [B][Hkv][max_pages][4], one qasp_score per page: (fp32
+    score, error bound, certified leading head, 0); the last two are int32 bit
+    patterns (view the tensor as int32 to read them)."""
     _dev(q, torch.bfloat16, "q", 3)
     _dev(summ, torch.bfloat16, "summ", 4)
     B = batch.seq_lens.shape[0]
     if scores is None:
-        scores = torch.empty((B, layout.num_kv_heads, batch.max_pages, 2), dtype=torch.float32,
+        scores = torch.empty((B, layout.num_kv_heads, batch.max_pages, 4), dtype=torch.float32,
                              device=batch.seq_lens.device)
     _dev(scores, torch.float32, "scores", 4)
+    if scores.shape[-1] != 4:
+        raise ValueError("scores: last dimension must be 4 (one qasp_score per page)")
     _check(lib().qasp_score_pages(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
                                   _ptr(q), _ptr(summ), _ptr(scores), _stream()), "qasp_score_pages")
     return scores

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     if (ranked) {
       sel::block_max_and_or(e_loc, k_and, k_or, sh);
       sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_and, k_or,
-                                    q + head0 * D, G, summ, pt_row, Hkv, g);
+                                    q + head0 * D, G, summ, pt_row, Hkv, g, nullptr);
     }
   }
   __syncthreads();

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
     float bound;
     score::score_group<D>(op, cur, G, lane, best, bound);
     const int j = j0 + n;
-    if (kg == 0 && j < max_pages) row[j] = is_cand ? score::make_score(best, bound) : qasp_score{-INFINITY, 0.f};
+    if (kg == 0 && j < max_pages) row[j] = is_cand ? score::make_score(best, bound) : qasp_score{-INFINITY, 0.f, -1, 0};
   }
 }
 

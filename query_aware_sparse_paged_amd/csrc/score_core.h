@@ -111,16 +111,23 @@ __device__ __forceinline__ void score_group(const QOperands<D> &op, const uint4 
 
 // The stored score of a candidate page: fp32 value and error bound; an
 // overflow becomes (0, inf) so that selection re-scores the page exactly.
-__device__ __forceinline__ qasp_score make_score(double best, float bound) {
+// With the runner-up head's value (second) and the leading head (arg), the
+// leader is certified when it beats the runner-up by more than twice the
+// error bound of every head's value.
+__device__ __forceinline__ qasp_score make_score(double best, float bound, double second = INFINITY,
+                                                 int arg = -1) {
   const float v = (float)best;
   const float err = kErrRel * bound + kErrAbs;
   qasp_score sc;
+  sc.reserved = 0;
   if (isfinite(v) && isfinite(err)) {
     sc.value = v == 0.f ? 0.f : v;  // no -0
     sc.err = err;
+    sc.head = best - second > 2.0 * (double)err ? arg : -1;
   } else {
     sc.value = 0.f;
     sc.err = INFINITY;
+    sc.head = -1;
   }
   return sc;
 }

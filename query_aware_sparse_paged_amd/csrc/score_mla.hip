@@ -30,14 +30,27 @@ constexpr int kRecBytes = kMlaK2 * 2 + 16;    // padded LDS row of one page reco
 constexpr int kGroupBytes = 16 * kRecBytes;
 
 struct MlaScoreShared {
-  double best[kMlaWaves][16];
-  float norm2[16];
+  double best[kMlaWaves][16];    // per wave and page: largest head value,
+  double second[kMlaWaves][16];  // the runner-up,
+  int arg[kMlaWaves][16];        // and the leading head
+  float norm2[kMlaWaves][16];  // partial page norms per wave
   float qnorm[kMlaWaves];
   int phys[3][16];   // physical pages of groups gid, gid+1, gid+2 (slot gid % 3); -1 = not a candidate
 };
 
 constexpr int kRecU4 = kMlaK2 / 8;                                      // 144 uint4 per record
 constexpr int kLoadsPerThread = (16 * kRecU4 + kMlaWaves * 64 - 1) / (kMlaWaves * 64);  // 5
+
+// Merges the top two (b1 >= b2, leader a1) with another top two.
+__device__ __forceinline__ void top2_merge(double &b1, double &b2, int &a1, double ob1, double ob2, int oa) {
+  if (ob1 > b1) {
+    b2 = fmax(b1, ob2);
+    b1 = ob1;
+    a1 = oa;
+  } else {
+    b2 = fmax(b2, ob1);
+  }
+}
 
 }  // namespace
 
@@ -107,16 +120,20 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const int buf = (gid - first) & 1;
     int b, j0, cand_hi;
     group_pages(gid, b, j0, cand_hi);
-    if (b != cur_b) {  // this wave's 16 heads of the sequence's query, and their norms
+    if (b != cur_b) {  // this wave's 16 heads of the sequence's query, and the largest |q_h|
       cur_b = b;
       const uint16_t *qg = q + ((size_t)b * Hq + (size_t)wave * 16) * kMlaD;
 #pragma unroll
       for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qg + (size_t)n * kMlaD + 32 * i + 8 * kg);
-      float s2 = 0.f;  // |q_h|^2 for head n of the wave, over this lane's quarter of the channels
-      const uint16_t *qh = qg + (size_t)n * kMlaD;
-      for (int d = kg; d < kMlaD; d += 4) {
-        const float x = __uint_as_float((uint32_t)qh[d] << 16);
-        s2 += x * x;
+      float s2 = 0.f;  // |q_h|^2 of head n over this lane's quarter of the channels
+#pragma unroll
+      for (int i = 0; i < kMlaD / 32; i++) {
+        const uint32_t w4[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float a = bf16_lo_to_f32(w4[k]), c = bf16_hi_to_f32(w4[k]);
+          s2 += a * a + c * c;
+        }
       }
       s2 += __shfl_xor(s2, 16, kWave);
       s2 += __shfl_xor(s2, 32, kWave);
@@ -128,17 +145,24 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const int phys_ahead = tid < 16 ? phys_of(gid + 2) : -1;
     if (gid + 1 < last) load_regs((gid + 1) % 3, regs);
     const char *rec = (const char *)stage + (size_t)buf * kGroupBytes;
-    // page norms N_j^2 (wave 0): lane (page n, quarter kg)
-    if (wave == 0) {
+    // page norms N_j^2 = sum_d max(lo_d^2, hi_d^2): wave w adds channel blocks
+    // 32i + 8kg .. (i = w, w + 8, ...) of page n; the blocks sum in LDS below
+    {
+      const char *rp = rec + (size_t)n * kRecBytes + 16 * kg;
       float a = 0.f;
-      const uint16_t *r = (const uint16_t *)(rec + (size_t)n * kRecBytes);
-      for (int d = kg; d < kMlaD; d += 4) {
-        const float lo = __uint_as_float((uint32_t)r[d] << 16), hi = __uint_as_float((uint32_t)r[kMlaD + d] << 16);
-        a += fmaxf(lo * lo, hi * hi);
+      for (int i = wave; i < kMlaD / 32; i += kMlaWaves) {
+        const uint4 lo4 = *(const uint4 *)(rp + 64 * i), hi4 = *(const uint4 *)(rp + 2 * kMlaD + 64 * i);
+        const uint32_t lw[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, hw[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float l0 = bf16_lo_to_f32(lw[k]), l1 = bf16_hi_to_f32(lw[k]);
+          const float h0 = bf16_lo_to_f32(hw[k]), h1 = bf16_hi_to_f32(hw[k]);
+          a += fmaxf(l0 * l0, h0 * h0) + fmaxf(l1 * l1, h1 * h1);
+        }
       }
       a += __shfl_xor(a, 16, kWave);
       a += __shfl_xor(a, 32, kWave);
-      if (kg == 0) sh.norm2[n] = a;
+      if (kg == 0) sh.norm2[wave][n] = a;
     }
     // contraction over [lo, hi]: step i < 18 pairs q^- with lo channels
     // 32i + 8kg ..., step 18 + i pairs q^+ with the same hi channels
@@ -153,25 +177,47 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       for (int r = 0; r < 4; r++) u64[r] += (double)ui[r];
     }
     // lane (n, kg) holds heads 16 wave + 4kg + r of page n: max over the wave's heads
-    double best = fmax(fmax(u64[0], u64[1]), fmax(u64[2], u64[3]));
-    best = fmax(best, __shfl_xor(best, 16, kWave));
-    best = fmax(best, __shfl_xor(best, 32, kWave));
-    if (kg == 0) sh.best[wave][n] = best;
+    // top two of the wave's heads for page n: value, runner-up, leading head
+    double b1 = -INFINITY, b2 = -INFINITY;
+    int a1 = -1;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (u64[r] > b1) {
+        b2 = b1;
+        b1 = u64[r];
+        a1 = 16 * wave + 4 * kg + r;
+      } else {
+        b2 = fmax(b2, u64[r]);
+      }
+    }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const double ob1 = __shfl_xor(b1, o, kWave), ob2 = __shfl_xor(b2, o, kWave);
+      const int oa = __shfl_xor(a1, o, kWave);
+      top2_merge(b1, b2, a1, ob1, ob2, oa);
+    }
+    if (kg == 0) {
+      sh.best[wave][n] = b1;
+      sh.second[wave][n] = b2;
+      sh.arg[wave][n] = a1;
+    }
     if (gid + 1 < last) store_regs(buf ^ 1, regs);
     if (tid < 16) sh.phys[(gid + 2) % 3][tid] = phys_ahead;
     __syncthreads();
     if (wave == 0 && lane < 16) {
       const int j = j0 + lane;
       if (j < cand_hi) {
-        double m = sh.best[0][lane];
-        float qn = sh.qnorm[0];
+        double m = sh.best[0][lane], m2 = sh.second[0][lane];
+        int arg = sh.arg[0][lane];
+        float qn = sh.qnorm[0], n2 = sh.norm2[0][lane];
 #pragma unroll
         for (int w = 1; w < kMlaWaves; w++) {
-          m = fmax(m, sh.best[w][lane]);
+          top2_merge(m, m2, arg, sh.best[w][lane], sh.second[w][lane], sh.arg[w][lane]);
           qn = fmaxf(qn, sh.qnorm[w]);
+          n2 += sh.norm2[w][lane];
         }
-        const float bound = qn * sqrtf(sh.norm2[lane]) * 1.01f;  // >= every head's S
-        scores[((size_t)b * Hkv + g) * max_pages + j] = score::make_score(m, bound);
+        const float bound = qn * sqrtf(n2) * 1.01f;  // >= every head's S
+        scores[((size_t)b * Hkv + g) * max_pages + j] = score::make_score(m, bound, m2, arg);
       }
     }
   }
@@ -180,7 +226,7 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
 // Fills every row with (-inf, 0); the candidates are overwritten by the scoring kernel.
 __global__ void fill_scores_kernel(qasp_score *scores, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    scores[i] = qasp_score{-INFINITY, 0.f};
+    scores[i] = qasp_score{-INFINITY, 0.f, -1, 0};
 }
 
 hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,

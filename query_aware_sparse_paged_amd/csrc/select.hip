@@ -46,7 +46,7 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
         const int i = i0 + u * THREADS + tid;
-        sc[u] = i < n ? row[i] : qasp_score{-INFINITY, 0.f};
+        sc[u] = i < n ? row[i] : qasp_score{-INFINITY, 0.f, -1, 0};
       }
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
       sel::block_max_and_or(e_loc, k_and, k_or, sh);
       sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_and, k_or,
                                     q + ((size_t)b * Hq + (size_t)g * G) * D, G, summ,
-                                    page_table + (size_t)b * pt_stride, Hkv, g);
+                                    page_table + (size_t)b * pt_stride, Hkv, g, row);
     }
   }
   __syncthreads();

@@ -445,12 +445,14 @@ __device__ double exact_page_key_heads16(const uint16_t *qg, int G, const uint16
 // and k_or are the block-wide max error bound, AND and OR of the keys;
 // 0 < k < n.  Candidate i is logical page cand_lo + i; pt_row is the
 // sequence's page-table row; qg the group's first q row (global).  keys64
-// aliases keys32 (8 bytes per candidate) for large bands.
+// aliases keys32 (8 bytes per candidate) for large bands.  cand_scores (may
+// be null) holds the candidates' stored scores: a certified leading head
+// reduces a page's exact re-score to that one head.
 template <int D, int NW>
 __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t *keys64, uint32_t *sel_bits,
                                   uint32_t *band_bits, int n, int k, int cand_lo, float emax, uint32_t k_and,
                                   uint32_t k_or, const uint16_t *qg, int G, const uint16_t *summ,
-                                  const int32_t *pt_row, int Hkv, int g) {
+                                  const int32_t *pt_row, int Hkv, int g, const qasp_score *cand_scores) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const uint32_t uk = kth_largest<uint32_t, NW>(keys32, nullptr, n, k, k_and, k_or, sh);
   // (k+1)-th largest: uk again if more than k keys reach it, else the largest below it
@@ -503,7 +505,10 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
         const int phys = pt_row[cand_lo + i];
         const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
         double key;
-        if (D == 128 && G <= 16) {
+        const int lead = cand_scores ? cand_scores[i].head : -1;
+        if (lead >= 0) {
+          key = exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane);
+        } else if (D == 128 && G <= 16) {
           for (int x = lane; x < D; x += kWave) sh.rows[wave][x] = ((const uint32_t *)lo)[x];
           key = exact_page_key_heads16<D>(qb, G, (const uint16_t *)sh.rows[wave], lo, lo + D, lane);
         } else {
@@ -537,7 +542,9 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
           if ((seen++ % NW) != wave) continue;
           const int phys = pt_row[cand_lo + i];
           const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
-          const uint64_t o = f64_order(exact_page_key<D>(qb, G, lo, lo + D, lane));
+          const int lead = cand_scores ? cand_scores[i].head : -1;
+          const uint64_t o = f64_order(lead >= 0 ? exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane)
+                                                 : exact_page_key<D>(qb, G, lo, lo + D, lane));
           if (lane == 0) keys64[i] = o;
           b_and &= o;
           b_or |= o;

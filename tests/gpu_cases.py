@@ -29,7 +29,7 @@ class GpuRun:
     out: np.ndarray       # fp32 [B][Hq][Dv]
     sel: np.ndarray       # int32 [B][Hkv][max_sel]
     cnt: np.ndarray       # int32 [B][Hkv]
-    scores: np.ndarray    # fp32 [B][Hkv][max_pages][2] or None
+    scores: np.ndarray    # fp32 [B][Hkv][max_pages][4] (qasp_score records) or None
     summ: torch.Tensor    # device summary pool
     max_sel: int
 

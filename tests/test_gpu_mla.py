@@ -13,7 +13,8 @@ from query_aware_sparse_paged_amd import api, workloads
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from gpu_cases import DEV, compare, gpu_summaries_of, run_gpu, run_oracle
+    import oracle
+    from gpu_cases import DEV, compare, gpu_summaries_of, olayout, opolicy, run_gpu, run_oracle
 
 PS = 64
 
@@ -38,6 +39,34 @@ def test_mla_small_ragged():
     compare(g, r, what="mla small")
     pages = (w.seq_lens.numpy() + PS - 1) // PS
     assert (g.cnt[:, 0] == np.minimum(32, pages)).all()
+
+
+def test_mla_certified_leading_head_is_the_maximiser():
+    """Where the scores name a certified leading head, that head's exact
+    bound alone equals the exact group score (checked with the oracle on a
+    query whose 128 heads are all that head)."""
+    w = _small(batch=3, seq_len=3000, seq_len_min=1000)
+    g = run_gpu(w)
+    pol = api.policy_of(w)
+    r = run_oracle(w, pol, g.max_sel)
+    head = g.scores.view(np.int32)[..., 2]
+    mp = r.scores.shape[-1]
+    head = head[..., :mp]
+    cand = np.isfinite(r.scores)
+    cert = head >= 0
+    assert not (cert & ~cand).any()
+    assert cert.sum() >= 0.5 * cand.sum()
+    olay, opol = olayout(api.layout_of(w)), opolicy(pol)
+    qb = workloads.bits(w.q)
+    checked = 0
+    for b in range(3):
+        for a in np.unique(head[b, 0][cert[b, 0]]):
+            q1 = np.repeat(qb[b:b + 1, a:a + 1], 128, axis=1)
+            s1 = oracle.scores(olay, w.page_table[b:b + 1].numpy(), w.seq_lens[b:b + 1].numpy(), q1, r.summ, opol)
+            pages = np.where(cert[b, 0] & (head[b, 0] == a))[0]
+            assert np.array_equal(s1[0, 0, pages], r.scores[b, 0, pages])
+            checked += len(pages)
+    assert checked == cert.sum()
 
 
 @pytest.mark.parametrize("lens,pol", [
