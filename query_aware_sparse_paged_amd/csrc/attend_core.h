@@ -34,9 +34,13 @@ __device__ __forceinline__ float bf16_round_f32(float a) { return __uint_as_floa
 template <int D>
 __device__ __forceinline__ void load_q_columns(uint4 *bq, const uint16_t *qg, int G, int lane) {
   const int n = lane & 15, kg = lane >> 4;
+  const uint32_t keep = n < G ? ~0u : 0u;  // unconditional loads (row clamped), then masked
+  const uint16_t *qh = qg + (size_t)(n < G ? n : 0) * D + 8 * kg;
 #pragma unroll
-  for (int i = 0; i < D / 32; i++)
-    bq[i] = n < G ? *(const uint4 *)(qg + (size_t)n * D + 32 * i + 8 * kg) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < D / 32; i++) {
+    const uint4 v = *(const uint4 *)(qh + 32 * i);
+    bq[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+  }
 }
 
 struct WaveState {

@@ -18,11 +18,12 @@ constexpr int kFusedWaves = 8;
 
 // Dynamic LDS layout of the fused kernel (bytes).
 struct FusedLds {
-  size_t keys, bits, list, merge, total;
+  size_t keys, phys, bits, list, merge, total;
   __host__ __device__ FusedLds(int max_pages, int max_sel, int G) {
     const int nwords = (max_pages + 31) / 32;
     keys = 0;                                                       // uint64 [max_pages]
-    bits = keys + (size_t)max_pages * 8;                            // 2 x uint32 [nwords]
+    phys = keys + (size_t)max_pages * 8;                            // int32 [max_pages]: candidates' pages
+    bits = phys + (size_t)max_pages * 4;                            // 2 x uint32 [nwords]
     list = bits + (size_t)2 * nwords * 4;                           // int32 [max_sel]
     merge = (list + (size_t)max_sel * 4 + 15) & ~(size_t)15;        // float merge area
     total = merge + (size_t)attend::merge_lds_floats(kFusedWaves, G, 128) * 4;
@@ -48,9 +49,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   uint32_t *sel_bits = (uint32_t *)((char *)dyn + lay.bits);
   uint32_t *band_bits = sel_bits + nwords;
   int32_t *list = (int32_t *)((char *)dyn + lay.list);
+  int32_t *cand_phys = (int32_t *)((char *)dyn + lay.phys);
   float *merge_area = (float *)((char *)dyn + lay.merge);
 
-  const int g = blockIdx.x, b = blockIdx.y;
+  const int b = blockIdx.x, g = blockIdx.y;  // consecutive blocks (one per XCD in turn) take different sequences
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n_col = lane & 15, kg = lane >> 4;
   const int unit = b * Hkv + g;
@@ -97,14 +99,19 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     sel_bits[w] = 0;
     band_bits[w] = 0;
   }
+  for (int w = tid; w < NW * 256; w += T) (&sh.hist[0][0])[w] = 0;
   if (tid == 0) sh.nlist = 0;
+  // the group's q rows in LDS, for the exact re-scoring of undecided pages
+  const bool q_in_lds = (size_t)G * D * 2 <= sel::kQStageBytes;
+  if (q_in_lds)
+    for (int w = tid; w < G * D / 2; w += T) ((uint32_t *)sh.qstage)[w] = ((const uint32_t *)(q + head0 * D))[w];
   __syncthreads();
 
   // ---- score the candidates: wave w takes 16-page groups w, w+W, ...; the
   // page-table entries of the next group and its summaries are loaded while
   // the current group is computed
   float e_loc = 0.f;
-  uint32_t k_and = ~0u, k_or = 0;
+  uint32_t k_min = ~0u, k_max = 0;
   if (ranked) {
     const int ngroups = (n + 15) / 16;
     const int my_groups = ngroups > wave ? (ngroups - wave + W - 1) / W : 0;
@@ -140,8 +147,9 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
           const qasp_score sc = score::make_score(best, bound);
           const uint32_t o = sel::f32_order(sc.value);
           keys32[i] = o;
-          k_and &= o;
-          k_or |= o;
+          cand_phys[i] = phys_cur;
+          k_min = min(k_min, o);
+          k_max = max(k_max, o);
           e_loc = fmaxf(e_loc, sc.err);
         }
         phys_cur = phys_next;
@@ -162,9 +170,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     for (int j = tid; j < P; j += T)
       if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     if (ranked) {
-      sel::block_max_and_or(e_loc, k_and, k_or, sh);
-      sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_and, k_or,
-                                    q + head0 * D, G, summ, pt_row, Hkv, g, nullptr);
+      sel::block_max_min_max(e_loc, k_min, k_max, sh);
+      sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min, k_max,
+                                    q_in_lds ? sh.qstage : q + head0 * D, G, summ, pt_row, Hkv, g, nullptr,
+                                    cand_phys);
     }
   }
   __syncthreads();
@@ -207,7 +216,7 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = FusedLds(mp, max_sel, G).total;
   const float scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid(lay.num_kv_heads, bat.batch);
+  dim3 grid(bat.batch, lay.num_kv_heads);
   hipLaunchKernelGGL((fused_step_gqa_kernel<128, 128, 16, kFusedWaves>), grid, dim3(kFusedWaves * 64), lds,
                      stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, out, sel,
                      sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G,

@@ -56,13 +56,18 @@ struct QOperands {
 template <int D, bool ABS = true>
 __device__ __forceinline__ void load_q_operands(QOperands<D, ABS> &op, const uint16_t *qg, int G, bool active,
                                                 int lane) {
+  // active is uniform over the wave (q may be null when it is false); inside,
+  // every lane loads (row clamped) and masks, so no per-lane branch
+  // serialises the loads
   const int m = lane & 15, kg = lane >> 4;
   const uint16_t *qh = qg + (size_t)(m < G ? m : 0) * D;
+  const uint32_t keep = m < G ? ~0u : 0u;
 #pragma unroll
   for (int i = 0; i < QOperands<D, ABS>::KSTEPS; i++) {
     const int k0 = 32 * i + 8 * kg;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < G && active) v = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
+    if (active) v = *(const uint4 *)(qh + (k0 < D ? k0 : k0 - D));
+    v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     op.aq[i] = map4(v, k0 < D ? 0 : 1);
     if (ABS) op.aa[i] = map4(op.aq[i], 2);
   }

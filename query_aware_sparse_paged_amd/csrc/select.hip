@@ -39,7 +39,7 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
   constexpr int kLoadUnroll = 8;
   const qasp_score *row = scores + (size_t)unit * max_pages + cand_lo;
   float e_loc = 0.f;
-  uint32_t k_and = ~0u, k_or = 0;
+  uint32_t k_min = ~0u, k_max = 0;
   if (ranked) {
     for (int i0 = 0; i0 < n; i0 += kLoadUnroll * THREADS) {
       qasp_score sc[kLoadUnroll];
@@ -54,8 +54,8 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
         if (i < n) {
           const uint32_t o = sel::f32_order(sc[u].value);
           keys32[i] = o;
-          k_and &= o;
-          k_or |= o;
+          k_min = min(k_min, o);
+          k_max = max(k_max, o);
           e_loc = fmaxf(e_loc, sc[u].err);
         }
       }
@@ -65,6 +65,7 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
     sel_bits[w] = 0;
     band_bits[w] = 0;
   }
+  for (int w = tid; w < NW * 256; w += THREADS) (&sh.hist[0][0])[w] = 0;
   if (tid == 0) sh.nlist = 0;
   __syncthreads();
 
@@ -79,10 +80,10 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
     for (int j = tid; j < P; j += THREADS)
       if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     if (ranked) {
-      sel::block_max_and_or(e_loc, k_and, k_or, sh);
-      sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_and, k_or,
+      sel::block_max_min_max(e_loc, k_min, k_max, sh);
+      sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min, k_max,
                                     q + ((size_t)b * Hq + (size_t)g * G) * D, G, summ,
-                                    page_table + (size_t)b * pt_stride, Hkv, g, row);
+                                    page_table + (size_t)b * pt_stride, Hkv, g, row, nullptr);
     }
   }
   __syncthreads();

@@ -46,8 +46,13 @@ template <int NW>
 struct SelShared {
   int hist[NW][256];          // one digit histogram per wave
   int red[NW][4];             // per-wave partials of block reductions
-  int digit, rem, nlist;
+  int digit, rem, nlist, bincnt;
+  int n_in, n_band, nsel;
+  int kbin[2], krem[2], kcnt[2], nk[2];
+  uint32_t uk, uk1;
   int list[kSmallBand];
+  uint32_t klist[kSmallBand];   // keys of one histogram bin
+  uint32_t klist1[kSmallBand];  // keys of a second bin
   double lkey[kSmallBand];
   uint32_t rows[NW][128];     // one page's summary rows per wave (2 x 128 bf16)
   uint16_t qstage[kQStageBytes / 2];
@@ -117,6 +122,31 @@ __device__ void block_max_and_or(float &f, uint32_t &a, uint32_t &o, SelShared<N
     a &= (uint32_t)sh.red[w][1];
     o |= (uint32_t)sh.red[w][2];
   }
+}
+
+// max of f, min and max of the unsigned keys lo / hi
+template <int NW>
+__device__ void block_max_min_max(float &f, uint32_t &lo, uint32_t &hi, SelShared<NW> &sh) {
+  f = wave_max_dpp(f);
+  const int nlo = wave_max_dpp((int)(~lo ^ 0x80000000u));  // max of ~lo = ~min(lo), biased to signed
+  const int nhi = wave_max_dpp((int)(hi ^ 0x80000000u));
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    sh.red[threadIdx.x / kWave][0] = __float_as_int(f);
+    sh.red[threadIdx.x / kWave][1] = nlo;
+    sh.red[threadIdx.x / kWave][2] = nhi;
+  }
+  __syncthreads();
+  f = __int_as_float(sh.red[0][0]);
+  int a = INT_MIN, b = INT_MIN;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    f = fmaxf(f, __int_as_float(sh.red[w][0]));
+    a = max(a, sh.red[w][1]);
+    b = max(b, sh.red[w][2]);
+  }
+  lo = ~((uint32_t)a ^ 0x80000000u);
+  hi = (uint32_t)b ^ 0x80000000u;
 }
 
 // AND and OR of 64-bit values
@@ -226,6 +256,192 @@ __device__ U kth_largest(const U *keys, const uint32_t *member_bits, int n, int 
     hb = lo - 1;
   }
   return prefix;
+}
+
+// k-th largest (1-based) of the 32-bit keys, all of which lie in [lo, hi].
+// One pass spreads the keys of [lo, hi] over NW*256 equal bins (a shared
+// LDS histogram: few keys per bin, so the atomics rarely collide), finds the
+// bin holding rank k from the top, and either ranks that bin's keys in one
+// wave (up to kSmallBand of them) or narrows [lo, hi] to the bin and repeats.
+template <int NW>
+__device__ uint32_t kth_largest_range(const uint32_t *keys, int n, int k, uint32_t lo, uint32_t hi,
+                                      SelShared<NW> &sh) {
+  constexpr int T = NW * kWave, NB = 4 * T;
+  static_assert(NB * sizeof(int) <= sizeof(sh.hist), "histogram size");
+  int *hist = &sh.hist[0][0];
+  const int tid = threadIdx.x;
+  int kk = k;
+  for (;;) {
+    if (lo == hi) return lo;
+    int shift = 0;
+    while (((hi - lo) >> shift) >= (uint32_t)NB) shift++;
+    for (int i = tid; i < NB; i += T) hist[i] = 0;
+    if (tid == 0) sh.nlist = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += T) {
+      const uint32_t u = keys[i];
+      if (u >= lo && u <= hi) atomicAdd(&hist[(u - lo) >> shift], 1);
+    }
+    __syncthreads();
+    // thread t owns bins NB-1-4t .. NB-4-4t, scanned from the top
+    int c[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      c[j] = hist[NB - 1 - 4 * tid - j];
+      s += c[j];
+    }
+    int total;
+    const int excl = block_exclusive_scan(s, &total, sh);
+    if (excl < kk && excl + s >= kk) {  // exactly one thread
+      int cum = excl;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (cum + c[j] >= kk) {
+          sh.digit = NB - 1 - 4 * tid - j;
+          sh.rem = kk - cum;
+          sh.bincnt = c[j];
+          break;
+        }
+        cum += c[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t blo = lo + ((uint32_t)sh.digit << shift);
+    const uint32_t bhi = shift == 0 ? blo : min(hi, blo + ((1u << shift) - 1u));
+    const int cnt = sh.bincnt;
+    kk = sh.rem;
+    if (shift == 0) return blo;
+    if (cnt > kSmallBand) {
+      lo = blo;
+      hi = bhi;
+      continue;
+    }
+    // the bin's keys, ranked by one wave: the kk-th largest of them
+    for (int i = tid; i < n; i += T) {
+      const uint32_t u = keys[i];
+      if (u >= blo && u <= bhi) sh.klist[atomicAdd(&sh.nlist, 1)] = u;
+    }
+    __syncthreads();
+    if (tid == 0) sh.nlist = 0;  // free for the band list
+    if (tid < kWave) {
+      const uint32_t mine = tid < cnt ? sh.klist[tid] : 0u;
+      int greater = 0, ge = 0;
+      for (int e = 0; e < cnt; e++) {
+        const uint32_t o = sh.klist[e];
+        greater += o > mine;
+        ge += o >= mine;
+      }
+      if (tid < cnt && greater < kk && ge >= kk) sh.digit = (int)mine;  // equal keys write the same value
+    }
+    __syncthreads();
+    return (uint32_t)sh.digit;
+  }
+}
+
+// The key of rank r (1-based, from the top) among the cnt <= 64 keys held
+// one per lane (mine, lanes < cnt); lane-to-lane reads go through SGPRs.
+__device__ __forceinline__ uint32_t rank_in_wave(uint32_t mine, int cnt, int r, int lane) {
+  int greater = 0, ge = 0;
+  for (int e = 0; e < cnt; e++) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, e);
+    greater += o > mine;
+    ge += o >= mine;
+  }
+  const uint64_t hit = __ballot(lane < cnt && greater < r && ge >= r);  // equal keys: same value
+  return (uint32_t)__shfl((int)mine, hit ? (int)__builtin_ctzll(hit) : 0, kWave);
+}
+
+// The k-th and (k+1)-th largest (1-based) of the n > k keys in [lo, hi].
+// The block spreads the keys over NB = NW*256 equal bins (shared LDS
+// histogram, which the caller has zeroed; few keys per bin, so the atomics
+// rarely collide); a suffix scan over the bins locates the bins of ranks k
+// and k+1; their keys are gathered and ranked by wave 0.  Five barriers.
+// Bins of more than 64 keys (many equal or very close keys) fall back to
+// kth_largest_range and a counting pass.
+template <int NW>
+__device__ void kth_pair(const uint32_t *keys, int n, int k, uint32_t lo, uint32_t hi, SelShared<NW> &sh,
+                         uint32_t &uk, uint32_t &uk1) {
+  constexpr int T = NW * kWave, NB = 4 * T;
+  int *hist = &sh.hist[0][0];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  if (lo == hi) {  // block-uniform
+    __syncthreads();
+    uk = uk1 = lo;
+    return;
+  }
+  int shift = 0;
+  while (((hi - lo) >> shift) >= (uint32_t)NB) shift++;
+  if (tid == 0) sh.nk[0] = sh.nk[1] = 0;
+  for (int i = tid; i < n; i += T) atomicAdd(&hist[(keys[i] - lo) >> shift], 1);
+  __syncthreads();
+  // thread t owns bins NB-1-4t .. NB-4-4t, counted from the top
+  int c[4], s = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    c[j] = hist[NB - 1 - 4 * tid - j];
+    s += c[j];
+  }
+  const int incl = wave_incl_sum(s);
+  if (lane == kWave - 1) sh.red[wave][3] = incl;
+  __syncthreads();
+  int excl = incl - s;
+#pragma unroll
+  for (int w = 0; w < NW; w++)
+    if (w < wave) excl += sh.red[w][3];
+#pragma unroll
+  for (int x = 0; x < 2; x++) {
+    const int r = k + x;
+    if (excl < r && excl + s >= r) {
+      int cum = excl;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (cum + c[j] >= r) {
+          sh.kbin[x] = NB - 1 - 4 * tid - j;
+          sh.krem[x] = r - cum;
+          sh.kcnt[x] = c[j];
+          break;
+        }
+        cum += c[j];
+      }
+    }
+  }
+  __syncthreads();
+  const int bin0 = sh.kbin[0], bin1 = sh.kbin[1];
+  const int cnt0 = sh.kcnt[0], cnt1 = bin1 == bin0 ? 0 : sh.kcnt[1];
+  if (cnt0 <= kWave && cnt1 <= kWave) {  // block-uniform
+    for (int i = tid; i < n; i += T) {
+      const uint32_t u = keys[i];
+      const int b = (int)((u - lo) >> shift);
+      if (b == bin0) sh.klist[atomicAdd(&sh.nk[0], 1)] = u;
+      else if (b == bin1) sh.klist1[atomicAdd(&sh.nk[1], 1)] = u;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t k0 = lane < cnt0 ? sh.klist[lane] : 0u;
+      const uint32_t a = rank_in_wave(k0, cnt0, sh.krem[0], lane);
+      const uint32_t k1 = bin1 == bin0 ? k0 : (lane < cnt1 ? sh.klist1[lane] : 0u);
+      const uint32_t b1 = rank_in_wave(k1, bin1 == bin0 ? cnt0 : cnt1, sh.krem[1], lane);
+      if (lane == 0) {
+        sh.uk = a;
+        sh.uk1 = b1;
+      }
+    }
+    __syncthreads();
+    uk = sh.uk;
+    uk1 = sh.uk1;
+    return;
+  }
+  uk = kth_largest_range<NW>(keys, n, k, lo, hi, sh);
+  // (k+1)-th largest: uk again if more than k keys reach it, else the largest below it
+  int c_ge = 0;
+  int below = INT_MIN;  // unsigned order keys, biased into the signed range
+  for (int i = tid; i < n; i += T) {
+    const uint32_t u = keys[i];
+    c_ge += u >= uk;
+    if (u < uk) below = max(below, (int)(u ^ 0x80000000u));
+  }
+  block_sum_max(c_ge, below, sh);
+  uk1 = c_ge > k ? uk : ((uint32_t)below ^ 0x80000000u);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,45 +599,41 @@ __device__ double exact_page_key(const uint16_t *qg, int G, const uint16_t *lo, 
   return best;
 }
 
-// Exact group score of one page for up to 16 heads at once: lane l works on
-// head l / 4 and channels (l % 4) + 4t of the page rows (rows: lo then hi,
-// bf16 pairs in LDS); the four lanes of a head sum exactly on a common 64-bit
-// grid, then the wave takes the max over heads.  Falls back to the per-head
-// digit sum when some term lies below the grid.
-template <int D>
-__device__ double exact_page_key_heads16(const uint16_t *qg, int G, const uint16_t *rows,
-                                         const uint16_t *lo_g, const uint16_t *hi_g, int lane) {
-  constexpr int NP = 4, PER = D / NP;
+// Exact group score of one page for up to 64 / NP heads at once: lane l
+// works on head l / NP and channels (l % NP) + NP t of the page rows (rows:
+// lo then hi, bf16 pairs in LDS); the NP lanes of a head sum exactly on a
+// common 64-bit grid, then the wave takes the max over heads.  Falls back to
+// the per-head digit sum when some term lies below the grid.
+template <int D, int NP>
+__device__ double exact_page_key_heads(const uint16_t *qg, int G, const uint16_t *rows,
+                                       const uint16_t *lo_g, const uint16_t *hi_g, int lane) {
+  constexpr int PER = D / NP;
   constexpr int LOGD = D <= 128 ? 7 : (D <= 1024 ? 10 : 16);
-  constexpr int HEADROOM = 62 - 16 - LOGD;
+  constexpr int HEADROOM = 62 - 16 - LOGD;  // |sum of D terms| < 2^62
   const int m = lane / NP, part = lane % NP;
   const bool live = m < G;
   const uint16_t *qh = qg + (size_t)(live ? m : 0) * D;
+  int Ms[PER], Es[PER];
   int emax = INT_MIN;
-#pragma unroll 8
+#pragma unroll
   for (int t = 0; t < PER; t++) {
     const int d = part + NP * t;
     const uint32_t qb = qh[d];
-    int M, E;
-    term_of(qb, (qb & 0x8000u) ? rows[d] : rows[D + d], M, E);
-    if (live && M != 0) emax = max(emax, E);
+    term_of(qb, (qb & 0x8000u) ? rows[d] : rows[D + d], Ms[t], Es[t]);
+    if (live && Ms[t] != 0) emax = max(emax, Es[t]);
   }
-  emax = max(emax, __shfl_xor(emax, 1, kWave));
-  emax = max(emax, __shfl_xor(emax, 2, kWave));
+#pragma unroll
+  for (int o = 1; o < NP; o <<= 1) emax = max(emax, __shfl_xor(emax, o, kWave));
   const int base = emax - HEADROOM;
   int64_t acc = 0;
   int tiny = 0;
   if (live && emax != INT_MIN) {
-#pragma unroll 8
+#pragma unroll
     for (int t = 0; t < PER; t++) {
-      const int d = part + NP * t;
-      const uint32_t qb = qh[d];
-      int M, E;
-      term_of(qb, (qb & 0x8000u) ? rows[d] : rows[D + d], M, E);
-      if (M == 0) continue;
-      const int sh = E - base;
+      if (Ms[t] == 0) continue;
+      const int sh = Es[t] - base;
       if (sh >= 0)
-        acc += (int64_t)M * ((int64_t)1 << sh);
+        acc += (int64_t)Ms[t] * ((int64_t)1 << sh);
       else
         tiny = 1;
     }
@@ -431,56 +643,58 @@ __device__ double exact_page_key_heads16(const uint16_t *qg, int G, const uint16
     for (int h = 0; h < G; h++) best = fmax(best, exact_head_bound_digits<D>(qg + (size_t)h * D, lo_g, hi_g));
     return best;
   }
-  acc += (int64_t)shfl_xor_u64((uint64_t)acc, 1);
-  acc += (int64_t)shfl_xor_u64((uint64_t)acc, 2);
+#pragma unroll
+  for (int o = 1; o < NP; o <<= 1) acc += (int64_t)shfl_xor_u64((uint64_t)acc, o);
   double v = -INFINITY;
   if (live) v = emax == INT_MIN ? 0.0 : ldexp(i64_to_f64_rn(acc), base);
-  for (int o = 4; o < kWave; o <<= 1) v = fmax(v, __shfl_xor(v, o, kWave));
+  for (int o = NP; o < kWave; o <<= 1) v = fmax(v, __shfl_xor(v, o, kWave));
   return v;
 }
 
 // Marks the top-k candidates in sel_bits.  Called by every thread of the
 // block.  Preconditions: keys32[0..n) hold the candidates' order keys (LDS,
-// visible to all threads); band_bits is zero; sh.nlist is zero; emax, k_and
-// and k_or are the block-wide max error bound, AND and OR of the keys;
+// visible to all threads); band_bits and sh.hist are zero; emax, k_min and k_max are the
+// block-wide max error bound and the smallest and largest key;
 // 0 < k < n.  Candidate i is logical page cand_lo + i; pt_row is the
 // sequence's page-table row; qg the group's first q row (global).  keys64
 // aliases keys32 (8 bytes per candidate) for large bands.  cand_scores (may
 // be null) holds the candidates' stored scores: a certified leading head
-// reduces a page's exact re-score to that one head.
+// reduces a page's exact re-score to that one head.  cand_phys (may be null,
+// then pt_row is read) holds the candidates' physical pages.  qg may already
+// point to sh.qstage.
 template <int D, int NW>
 __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t *keys64, uint32_t *sel_bits,
-                                  uint32_t *band_bits, int n, int k, int cand_lo, float emax, uint32_t k_and,
-                                  uint32_t k_or, const uint16_t *qg, int G, const uint16_t *summ,
-                                  const int32_t *pt_row, int Hkv, int g, const qasp_score *cand_scores) {
+                                  uint32_t *band_bits, int n, int k, int cand_lo, float emax, uint32_t k_min,
+                                  uint32_t k_max, const uint16_t *qg, int G, const uint16_t *summ,
+                                  const int32_t *pt_row, int Hkv, int g, const qasp_score *cand_scores,
+                                  const int32_t *cand_phys) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const uint32_t uk = kth_largest<uint32_t, NW>(keys32, nullptr, n, k, k_and, k_or, sh);
-  // (k+1)-th largest: uk again if more than k keys reach it, else the largest below it
-  int c_ge = 0;
-  int below = INT_MIN;  // unsigned order keys, biased into the signed range
-  for (int i = tid; i < n; i += NW * kWave) {
-    const uint32_t u = keys32[i];
-    c_ge += u >= uk;
-    if (u < uk) below = max(below, (int)(u ^ 0x80000000u));
-  }
-  block_sum_max(c_ge, below, sh);
-  const float vk = f32_from_order(uk);
-  const float vk1 = c_ge > k ? vk : f32_from_order((uint32_t)below ^ 0x80000000u);
+  uint32_t uk, uk1;
+  if (tid == 0) sh.n_in = sh.n_band = 0;  // ordered before use by the barriers inside kth_pair
+  kth_pair<NW>(keys32, n, k, k_min, k_max, sh, uk, uk1);
+  const float vk = f32_from_order(uk), vk1 = f32_from_order(uk1);
   const double t_in = (double)vk1 + 2.0 * (double)emax;
   const double t_out = (double)vk - 2.0 * (double)emax;
-  int n_in = 0, n_band = 0;
+  int c_in = 0, c_band = 0;
   for (int i = tid; i < n; i += NW * kWave) {
     const double v = (double)f32_from_order(keys32[i]);
     const int j = cand_lo + i;
     if (v > t_in) {
       atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-      n_in++;
+      c_in++;
     } else if (!(v < t_out)) {
       atomicOr(&band_bits[i >> 5], 1u << (i & 31));
-      n_band++;
+      c_band++;
     }
   }
-  block_sum2(n_in, n_band, sh);
+  c_in = wave_sum_dpp(c_in);
+  c_band = wave_sum_dpp(c_band);
+  if (lane == 0) {
+    if (c_in) atomicAdd(&sh.n_in, c_in);
+    if (c_band) atomicAdd(&sh.n_band, c_band);
+  }
+  __syncthreads();
+  const int n_in = sh.n_in, n_band = sh.n_band;
   const int need = k - n_in;
   if (need > 0 && need >= n_band) {
     for (int i = tid; i < n; i += NW * kWave)
@@ -491,7 +705,7 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
   } else if (need > 0) {
     // exact scores of the band pages
     const uint16_t *qb = qg;
-    if ((size_t)G * D * 2 <= kQStageBytes) {  // stage the group's q rows in LDS
+    if (qg != sh.qstage && (size_t)G * D * 2 <= kQStageBytes) {  // stage the group's q rows in LDS
       for (int i = tid; i < G * D / 2; i += NW * kWave) ((uint32_t *)sh.qstage)[i] = ((const uint32_t *)qb)[i];
       qb = sh.qstage;
     }
@@ -502,7 +716,7 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
       __syncthreads();
       for (int e = wave; e < n_band; e += NW) {
         const int i = sh.list[e];
-        const int phys = pt_row[cand_lo + i];
+        const int phys = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
         const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
         double key;
         const int lead = cand_scores ? cand_scores[i].head : -1;
@@ -510,7 +724,10 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
           key = exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane);
         } else if (D == 128 && G <= 16) {
           for (int x = lane; x < D; x += kWave) sh.rows[wave][x] = ((const uint32_t *)lo)[x];
-          key = exact_page_key_heads16<D>(qb, G, (const uint16_t *)sh.rows[wave], lo, lo + D, lane);
+          const uint16_t *rows = (const uint16_t *)sh.rows[wave];
+          key = G <= 4 ? exact_page_key_heads<D, 16>(qb, G, rows, lo, lo + D, lane)
+                       : (G <= 8 ? exact_page_key_heads<D, 8>(qb, G, rows, lo, lo + D, lane)
+                                 : exact_page_key_heads<D, 4>(qb, G, rows, lo, lo + D, lane));
         } else {
           key = exact_page_key<D>(qb, G, lo, lo + D, lane);
         }
@@ -540,7 +757,7 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
           const int i = w * 32 + __builtin_ctz(bits);
           bits &= bits - 1;
           if ((seen++ % NW) != wave) continue;
-          const int phys = pt_row[cand_lo + i];
+          const int phys = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
           const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
           const int lead = cand_scores ? cand_scores[i].head : -1;
           const uint64_t o = f64_order(lead >= 0 ? exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane)
@@ -579,28 +796,40 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
 
 // Writes the pages marked in sel_bits, in ascending order, to out_global
 // (followed by -1 up to max_sel) and/or out_lds.  Returns the count.
+// Each thread takes one bit word per round; a wave prefix sum and the wave
+// totals in LDS give the word's first slot.
 template <int NW>
 __device__ int emit_selection(SelShared<NW> &sh, const uint32_t *sel_bits, int nwords, int32_t *out_global,
                               int32_t *out_lds, int max_sel) {
   constexpr int T = NW * kWave;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   int written = 0;
   for (int w0 = 0; w0 < nwords; w0 += T) {
     const int w = w0 + tid;
     const uint32_t bits = w < nwords ? sel_bits[w] : 0u;
-    int total;
-    int pos = written + block_exclusive_scan(__popc(bits), &total, sh);
-    uint32_t x = bits;
-    while (x) {
-      const int j = w * 32 + __builtin_ctz(x);
-      x &= x - 1;
+    const int c = __popc(bits);
+    const int incl = wave_incl_sum(c);
+    if (lane == kWave - 1) sh.red[wave][2] = incl;
+    __syncthreads();
+    int pos = written + incl - c, round = 0;
+#pragma unroll
+    for (int x = 0; x < NW; x++) {
+      const int t = sh.red[x][2];
+      if (x < wave) pos += t;
+      round += t;
+    }
+    uint32_t m = bits;
+    while (m) {
+      const int j = w * 32 + __builtin_ctz(m);
+      m &= m - 1;
       if (pos < max_sel) {
         if (out_global) out_global[pos] = j;
         if (out_lds) out_lds[pos] = j;
       }
       pos++;
     }
-    written += total;
+    written += round;
+    if (w0 + T < nwords) __syncthreads();  // sh.red is rewritten next round
   }
   const int count = min(written, max_sel);
   if (out_global)
