@@ -101,6 +101,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   }
   for (int w = tid; w < NW * 256; w += T) (&sh.hist[0][0])[w] = 0;
   if (tid == 0) sh.nlist = 0;
+  // the candidates' physical pages, read once, coalesced (the scoring loop
+  // takes them from LDS, so its summary loads depend on no global load)
+  if (ranked)
+    for (int i = tid; i < n; i += T) cand_phys[i] = pt_row[cand_lo + i];
   // the group's q rows in LDS, for the exact re-scoring of undecided pages
   const bool q_in_lds = (size_t)G * D * 2 <= sel::kQStageBytes;
   if (q_in_lds)
@@ -108,8 +112,8 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   __syncthreads();
 
   // ---- score the candidates: wave w takes 16-page groups w, w+W, ...; the
-  // page-table entries of the next group and its summaries are loaded while
-  // the current group is computed
+  // summaries of the next group are in flight while the current group is
+  // computed (past the last group the prefetch reads page 0, unused)
   float e_loc = 0.f;
   uint32_t k_min = ~0u, k_max = 0;
   if (ranked) {
@@ -119,22 +123,19 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
     auto page_of = [&](int gi) {  // physical page of this lane's column in the wave's gi-th group, -1 if none
       const int i = (wave + gi * W) * 16 + n_col;
-      const bool ok = gi < my_groups && i < n;
-      const int phys = pt_row[cand_lo + (ok ? i : 0)];  // always issued: static wait counts
-      return ok ? phys : -1;
+      return gi < my_groups && i < n ? cand_phys[i] : -1;
     };
     uint4 bs[2][KSTEPS];
     int phys_cur = page_of(0);
-    int phys_next = page_of(1);
     score::load_group<D>(bs[0], summ, max(phys_cur, 0), Hkv, g, lane);
     for (int gi = 0; gi < my_groups; gi += 2) {
 #pragma unroll
       for (int half = 0; half < 2; half++) {
         const int gcur = gi + half;
         uint4 *cur = bs[half];
-        // prefetch: summaries of group gcur+1, page-table entry of gcur+2
+        // prefetch: summaries of group gcur+1
+        const int phys_next = page_of(gcur + 1);
         score::load_group<D>(bs[half ^ 1], summ, max(phys_next, 0), Hkv, g, lane);
-        const int phys_after = page_of(gcur + 2);
         if (phys_cur < 0) {
 #pragma unroll
           for (int i = 0; i < KSTEPS; i++) cur[i] = make_uint4(0, 0, 0, 0);
@@ -147,13 +148,11 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
           const qasp_score sc = score::make_score(best, bound);
           const uint32_t o = sel::f32_order(sc.value);
           keys32[i] = o;
-          cand_phys[i] = phys_cur;
           k_min = min(k_min, o);
           k_max = max(k_max, o);
           e_loc = fmaxf(e_loc, sc.err);
         }
         phys_cur = phys_next;
-        phys_next = phys_after;
       }
     }
   }
