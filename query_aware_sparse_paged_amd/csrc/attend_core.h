@@ -55,22 +55,20 @@ __device__ __forceinline__ void init_state(WaveState &st) {
   for (int i = 0; i < 8; i++) st.acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Attends npg page-heads.  Lane i (< npg) holds the i-th page's logical id
-// (my_j) and physical page (my_phys).  Tokens t of a page are used when
-// t < L and, for a static head, t < sink_end or t >= win_begin.
+// Loading and computing one page-head for a wave (the two halves of the
+// pipelined loops below).
 template <int PS, int D, int DV>
-__device__ __forceinline__ void attend_pages(WaveState &st, const uint16_t *__restrict__ k_pool,
-                                             const uint16_t *__restrict__ v_pool, int Hkv, int g,
-                                             const uint4 *bq, int npg, int my_j, int my_phys, int L,
-                                             bool is_static, int sink_end, int win_begin, float scale_log2,
-                                             int lane) {
+struct PageWork {
   static_assert(PS == 16 && D == 128 && DV == 128, "tile shapes");
-  if (npg <= 0) return;
-  const int n = lane & 15, kg = lane >> 4;
-  uint4 kA[D / 32], kB[D / 32], kC[D / 32];
-  uint2 vA[DV / 16], vB[DV / 16], vC[DV / 16];
-  auto load_page = [&](int it, uint4 *kk, uint2 *vv) {
-    const int phys = __shfl(my_phys, min(it, npg - 1), kWave);
+  const uint16_t *__restrict__ k_pool;
+  const uint16_t *__restrict__ v_pool;
+  const uint4 *bq;
+  int Hkv, g, L, sink_end, win_begin;
+  bool is_static;
+  float scale_log2;
+
+  __device__ __forceinline__ void load(int phys, uint4 *kk, uint2 *vv, int lane) const {
+    const int n = lane & 15, kg = lane >> 4;
     const size_t ph = (size_t)phys * Hkv + g;
     const uint16_t *kp = k_pool + (ph * PS + n) * D + 8 * kg;
     const uint16_t *vp = v_pool + ph * DV * PS + (size_t)n * PS + 4 * kg;
@@ -78,13 +76,15 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const uint16_t *__re
     for (int i = 0; i < D / 32; i++) kk[i] = *(const uint4 *)(kp + 32 * i);
 #pragma unroll
     for (int i = 0; i < DV / 16; i++) vv[i] = *(const uint2 *)(vp + 16 * i * PS);
-  };
-  auto compute_page = [&](int it, const uint4 *kt, const uint2 *vt) {
+  }
+
+  // page with logical id j; real = false computes it fully masked
+  __device__ __forceinline__ void compute(WaveState &st, bool real, int j, const uint4 *kt, const uint2 *vt,
+                                          int lane) const {
+    const int kg = lane >> 4;
     floatx4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < D / 32; i++) s = mfma16x16x32(kt[i], bq[i], s);
-    const bool real = it < npg;
-    const int j = __shfl(my_j, min(it, npg - 1), kWave);
     float sv[4];
     float tmax = -INFINITY;
     uint32_t keep[2] = {0u, 0u};  // value bits of the attended tokens 4kg + r
@@ -126,6 +126,23 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const uint16_t *__re
       st.acc[i] = mfma16x16x16(v, ph, st.acc[i]);
       st.acc[i] = mfma16x16x16(v, pl, st.acc[i]);
     }
+  }
+};
+
+// Attends npg page-heads.  Lane i (< npg) holds the i-th page's logical id
+// (my_j) and physical page (my_phys).  Tokens t of a page are used when
+// t < L and, for a static head, t < sink_end or t >= win_begin.
+template <int PS, int D, int DV>
+__device__ __forceinline__ void attend_pages(WaveState &st, const PageWork<PS, D, DV> &pw, int npg, int my_j,
+                                             int my_phys, int lane) {
+  if (npg <= 0) return;
+  uint4 kA[D / 32], kB[D / 32], kC[D / 32];
+  uint2 vA[DV / 16], vB[DV / 16], vC[DV / 16];
+  auto load_page = [&](int it, uint4 *kk, uint2 *vv) {
+    pw.load(__shfl(my_phys, min(it, npg - 1), kWave), kk, vv, lane);
+  };
+  auto compute_page = [&](int it, const uint4 *kt, const uint2 *vt) {
+    pw.compute(st, it < npg, __shfl(my_j, min(it, npg - 1), kWave), kt, vt, lane);
   };
   // page it computes from (kc, vc) after prefetching page it+2 into (kn, vn)
   auto page_step = [&](int it, const uint4 *kc, const uint2 *vc, uint4 *kn, uint2 *vn) {
@@ -138,6 +155,51 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const uint16_t *__re
     page_step(it, kA, vA, kC, vC);
     page_step(it + 1, kB, vB, kA, vA);
     page_step(it + 2, kC, vC, kB, vB);
+  }
+}
+
+// Attends the pages list[0 .. count) (logical ids; page_phys[j] is the
+// physical page of id j), shared by the block's waves through the LDS
+// counter *next: each wave takes the next unclaimed entry whenever it issues
+// a prefetch, so waves that see faster memory take more pages.  Two pages
+// are in flight per wave as in attend_pages; claims past the end load the
+// last page again and are not computed.
+template <int PS, int D, int DV>
+__device__ __forceinline__ void attend_pages_queue(WaveState &st, const PageWork<PS, D, DV> &pw, int *next,
+                                                   const int32_t *list, const int32_t *page_phys, int count,
+                                                   int lane) {
+  if (count <= 0) return;
+  uint4 kA[D / 32], kB[D / 32], kC[D / 32];
+  uint2 vA[DV / 16], vB[DV / 16], vC[DV / 16];
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  // loads entry idx (clamped) and returns its logical id
+  auto load_entry = [&](int idx, uint4 *kk, uint2 *vv) {
+    const int j = list[min(idx, count - 1)];
+    pw.load(page_phys[j], kk, vv, lane);
+    return j;
+  };
+  int ia = claim(), ib = claim();
+  int ja = load_entry(ia, kA, vA), jb = load_entry(ib, kB, vB);
+  while (ia < count) {
+    const int ic = claim();
+    const int jc = load_entry(ic, kC, vC);
+    pw.compute(st, true, ja, kA, vA, lane);
+    if (ib >= count) break;
+    const int id = claim();
+    const int jd = load_entry(id, kA, vA);
+    pw.compute(st, true, jb, kB, vB, lane);
+    if (ic >= count) break;
+    const int ie = claim();
+    const int je = load_entry(ie, kB, vB);
+    pw.compute(st, true, jc, kC, vC, lane);
+    ia = id;
+    ja = jd;
+    ib = ie;
+    jb = je;
   }
 }
 

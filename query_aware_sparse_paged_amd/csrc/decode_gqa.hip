@@ -49,8 +49,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
   attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
   attend::WaveState st;
   attend::init_state(st);
-  attend::attend_pages<PS, D, DV>(st, k_pool, v_pool, Hkv, g, bq, npg, my_j, my_phys, L, is_static, sink_end,
-                                  win_begin, scale_log2, lane);
+  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
   attend::merge_waves<WAVES, DV>(lds, st, G, [&](int h, int dv, float a, float lsum, float M) {
     if (splits == 1) {
       out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;

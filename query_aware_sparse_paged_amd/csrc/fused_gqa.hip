@@ -22,7 +22,7 @@ struct FusedLds {
   __host__ __device__ FusedLds(int max_pages, int max_sel, int G) {
     const int nwords = (max_pages + 31) / 32;
     keys = 0;                                                       // uint64 [max_pages]
-    phys = keys + (size_t)max_pages * 8;                            // int32 [max_pages]: candidates' pages
+    phys = keys + (size_t)max_pages * 8;                            // int32 [max_pages]: pages of the sequence
     bits = phys + (size_t)max_pages * 4;                            // 2 x uint32 [nwords]
     list = bits + (size_t)2 * nwords * 4;                           // int32 [max_sel]
     merge = (list + (size_t)max_sel * 4 + 15) & ~(size_t)15;        // float merge area
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   constexpr int KSTEPS = 2 * D / 32;
   extern __shared__ uint64_t dyn[];
   __shared__ sel::SelShared<NW> sh;
+  __shared__ int attend_next;
   const FusedLds lay(max_pages, max_sel, G);
   uint64_t *keys64 = dyn;
   uint32_t *keys32 = (uint32_t *)dyn;
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   uint32_t *sel_bits = (uint32_t *)((char *)dyn + lay.bits);
   uint32_t *band_bits = sel_bits + nwords;
   int32_t *list = (int32_t *)((char *)dyn + lay.list);
-  int32_t *cand_phys = (int32_t *)((char *)dyn + lay.phys);
+  int32_t *page_phys = (int32_t *)((char *)dyn + lay.phys);
   float *merge_area = (float *)((char *)dyn + lay.merge);
 
   const int b = blockIdx.x, g = blockIdx.y;  // consecutive blocks (one per XCD in turn) take different sequences
@@ -101,10 +102,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   }
   for (int w = tid; w < NW * 256; w += T) (&sh.hist[0][0])[w] = 0;
   if (tid == 0) sh.nlist = 0;
-  // the candidates' physical pages, read once, coalesced (the scoring loop
-  // takes them from LDS, so its summary loads depend on no global load)
-  if (ranked)
-    for (int i = tid; i < n; i += T) cand_phys[i] = pt_row[cand_lo + i];
+  // the sequence's physical pages, read once, coalesced: scoring, exact
+  // re-scoring and attention take them from LDS, so no load waits on a
+  // page-table load
+  for (int j = tid; j < P; j += T) page_phys[j] = pt_row[j];
   // the group's q rows in LDS, for the exact re-scoring of undecided pages
   const bool q_in_lds = (size_t)G * D * 2 <= sel::kQStageBytes;
   if (q_in_lds)
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
     auto page_of = [&](int gi) {  // physical page of this lane's column in the wave's gi-th group, -1 if none
       const int i = (wave + gi * W) * 16 + n_col;
-      return gi < my_groups && i < n ? cand_phys[i] : -1;
+      return gi < my_groups && i < n ? page_phys[cand_lo + i] : -1;
     };
     uint4 bs[2][KSTEPS];
     int phys_cur = page_of(0);
@@ -172,30 +173,25 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
       sel::block_max_min_max(e_loc, k_min, k_max, sh);
       sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min, k_max,
                                     q_in_lds ? sh.qstage : q + head0 * D, G, summ, pt_row, Hkv, g, nullptr,
-                                    cand_phys);
+                                    page_phys + cand_lo);
     }
   }
   __syncthreads();
   const int count = sel::emit_selection(sh, sel_bits, nwords,
                                         sel_out ? sel_out + (size_t)unit * max_sel : nullptr, list, max_sel);
   if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
+  if (tid == 0) attend_next = 0;
   __syncthreads();
 
-  // ---- attend: wave w takes selected pages w, w+W, ...
-  const int npg = count > wave ? (count - wave + W - 1) / W : 0;
-  int my_j = 0, my_phys = 0;
-  if (lane < npg) {
-    my_j = list[wave + W * lane];
-    my_phys = pt_row[my_j];
-  }
+  // ---- attend: the waves claim selected pages from a shared counter
   const int sink_end = is_static ? min(sink_tokens, L) : 0;
   const int win_begin = is_static ? max(0, L - window_tokens) : 0;
   uint4 bq[D / 32];
   attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
   attend::WaveState st;
   attend::init_state(st);
-  attend::attend_pages<PS, D, DV>(st, k_pool, v_pool, Hkv, g, bq, npg, my_j, my_phys, L, is_static, sink_end,
-                                  win_begin, scale_log2, lane);
+  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  attend::attend_pages_queue<PS, D, DV>(st, pw, &attend_next, list, page_phys, count, lane);
   attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
     (void)M;
     out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
