@@ -8,17 +8,20 @@
 //   S^T = K q^T   16x16x32, A = 16 key rows (tokens), B = q^T (16 heads);
 //   O^T += V^T P^T  16x16x32, A = V^T (16 value channels x 32 tokens), B = P^T.
 //
-// Block (split, g, b) takes the selected pages [2 split, 2 split + 2) of unit
-// (b, g) and all 128 heads; wave w owns heads 32w .. 32w+31 (two 16-head
-// column blocks), keeps their q^T (B operand) in registers and their O^T
-// (32 heads x 512 channels, 256 floats per lane) in the accumulation
-// registers.  Tokens go through in chunks of 32, each read from HBM once per
-// block and staged twice in LDS (double-buffered, the next chunk's loads in
-// flight while the current one is computed):
-//   Ktok  token-major rows, row stride padded to spread the 16 rows of an
-//         A fragment over the banks;
-//   Vt    the 512 value channels channel-major (32 tokens per row), made by
-//         a 4x8 transpose in registers, so a V^T fragment is two 8-byte reads.
+// Block (split, g, b) takes the selected pages [P split, P split + P) of
+// unit (b, g) and all 128 heads; wave w (of 8) owns heads 16w .. 16w+15,
+// keeps their q^T (the B operand, 72 registers) and their O^T (16 heads x
+// 512 channels, 128 accumulators per lane).  Two waves share each SIMD, so
+// one wave's LDS reads overlap the other's MFMAs.  Tokens go through in
+// chunks of 32, read from HBM once per block into registers and stored to
+// LDS token-major (rows padded so the 16 rows of an A fragment fall on
+// different banks); the next chunk is loaded while the current one is
+// computed.  The V^T fragments come straight from the token-major rows
+// through the transposing LDS read of gfx950 (ds_read_b64_tr_b16): within a
+// group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces that
+// lanes 4j + i / 4 address (j = 0..3), so pointing lane l' at token
+// 4G + l' / 4, channels dv0 + 4 (l' % 4) gives lane i the 4 tokens
+// 4G .. 4G+3 of channel dv0 + i, the layout of the MFMA A operand.
 // Tokens that are not attended (past the length, outside a static head's
 // sink and window) are zeroed while staging, so stale pool contents never
 // reach the products.
@@ -27,10 +30,10 @@
 // 16-token S^T blocks come out of the QK product, so P^T needs no shuffle.
 // P is split into bf16 hi + lo parts (two MFMAs) to keep ~16 significant bits.
 // Softmax in the exp2 domain against a fixed reference max per head (the max
-// of the first attended chunk), so the 256 accumulators are never rescaled:
+// of the first attended chunk), so the accumulators are never rescaled:
 // weights stay below 2^64 unless a later chunk's max lies further above the
 // reference, and then the block starts its pages again with the largest max
-// seen as reference (at most once per chunk, almost never in practice).
+// seen as reference (almost never in practice).
 // Several splits per unit are combined by merge_splits_kernel.
 #include "launch.h"
 #include "common.h"
@@ -42,25 +45,20 @@ hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_di
 
 namespace {
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
 constexpr int kD = 576, kDV = 512, kPS = 64, kG = 128;
 constexpr int kChunk = 32;                       // tokens per staged chunk
-constexpr int kHB = 2;                           // 16-head column blocks per wave
-constexpr int kWaves = kG / (16 * kHB);          // 4
-constexpr int kThreads = kWaves * kWave;         // 256
-constexpr int kKRow = kD * 2 + 16;               // bytes per Ktok row (padded)
-constexpr int kVRow = kChunk * 2 + 8;            // bytes per Vt row (padded)
-constexpr int kKBytes = kChunk * kKRow;          // 37376
-constexpr int kVBytes = kDV * kVRow;             // 36864
-constexpr int kBufBytes = kKBytes + kVBytes;     // 74240 per buffer
+constexpr int kWaves = kG / 16;                  // 8, one 16-head block each
+constexpr int kThreads = kWaves * kWave;         // 512
+constexpr int kKRow = kD * 2 + 16;               // bytes per LDS row (padded): 1168
+constexpr int kBufBytes = kChunk * kKRow;        // 37376 per buffer
+constexpr int kRowU4 = kD / 8;                   // 72 uint4 per row
+constexpr int kStage = (kChunk * kRowU4 + kThreads - 1) / kThreads;  // 5 loads per thread per chunk
 constexpr int kMaxChunks = kMlaPagesPerSplit * (kPS / kChunk);
 constexpr float kHeadroom = 64.f;                // weights stay below 2^64 (log2 units)
-static_assert((kChunk / 4) * (kDV / 8) == 2 * kThreads, "two V items (4 tokens x 8 channels) per thread");
-static_assert(kChunk * (kD - kDV) / 8 == kThreads, "one 16-byte rope load per thread");
-static_assert(kBufBytes % 16 == 0 && kKBytes % 16 == 0, "LDS alignment");
-
-__device__ __forceinline__ uint32_t word_of(const uint4 &v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
-}
+static_assert(kBufBytes % 16 == 0 && kKRow % 16 == 0, "LDS alignment");
 
 __device__ __forceinline__ uint4 pack_bf16x8(const float *a, const float *b) {
   return make_uint4(f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16),
@@ -70,6 +68,12 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float *a, const float *b) {
 }
 
 __device__ __forceinline__ float bf16_round(float a) { return __uint_as_float(f32_to_bf16_rne(a) << 16); }
+
+// Transposing 8-byte LDS read (see the file comment for its lane layout).
+__device__ __forceinline__ uint2 lds_read_tr16(const char *p) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)p);
+  return __builtin_bit_cast(uint2, v);
+}
 
 }  // namespace
 
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   extern __shared__ uint4 lds_u4[];
   char *lds = (char *)lds_u4;
   __shared__ int2 chunks[kMaxChunks];  // (physical page, position of the chunk's first token)
-  __shared__ int nchunks_sh;
+  __shared__ int nchunks_sh, overflow;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane & 15, kg = lane >> 4;
@@ -93,10 +97,6 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   const int win_begin = is_static ? max(0, L - window_tokens) : 0;
   auto attended = [&](int pos) {  // branch-free: evaluated per element in the hot loop
     return (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
-  };
-  auto keep_if = [](uint4 v, bool keep) {
-    const uint32_t k = keep ? ~0u : 0u;
-    return make_uint4(v.x & k, v.y & k, v.z & k, v.w & k);
   };
 
   // the block's chunks: halves of its pages that hold an attended position
@@ -114,192 +114,140 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
       }
     }
     nchunks_sh = nc;
+    overflow = 0;
   }
 
-  // q^T of the wave's heads: column n of block hb = head 32 wave + 16 hb + n
-  const size_t head0 = (size_t)b * Hq + (size_t)g * kG + 32 * wave;
-  uint4 qB[kHB][kD / 32];
+  // q^T of the wave's heads: column n = head 16 wave + n, channels 32i + 8kg ..
+  const size_t head0 = (size_t)b * Hq + (size_t)g * kG + 16 * wave;
+  uint4 qB[kD / 32];
 #pragma unroll
-  for (int hb = 0; hb < kHB; hb++)
-#pragma unroll
-    for (int i = 0; i < kD / 32; i++)
-      qB[hb][i] = *(const uint4 *)(q + (head0 + 16 * hb + n) * kD + 32 * i + 8 * kg);
+  for (int i = 0; i < kD / 32; i++) qB[i] = *(const uint4 *)(q + (head0 + n) * kD + 32 * i + 8 * kg);
   __syncthreads();
   const int nchunks = nchunks_sh;
 
-  // staging in two parts, each a set of loads held in registers until stored:
-  // part 0 = V item 0, part 1 = V item 1 and the rope channels.  A V item is
-  // (token quad a, channel block cb): four 16-byte loads, one per token.
-  uint4 rv[4], rr;
-  auto load_part = [&](int c, int part) {
+  // staging: thread loads the 16-byte pieces e = tid + 512 u of the chunk
+  // (token e / 72, channels 8 (e % 72) ..), consecutive lanes along a row
+  uint4 stg[kStage];
+  auto load_chunk = [&](int c) {
     const int2 ch = chunks[c];
-    const uint16_t *base = k_pool + (((size_t)ch.x * Hkv + g) * kPS + (ch.y % kPS)) * kD;
-    const int e = tid + part * kThreads, a = e & 7, cb = e >> 3;
+    const uint4 *base = (const uint4 *)(k_pool + (((size_t)ch.x * Hkv + g) * kPS + (ch.y % kPS)) * kD);
 #pragma unroll
-    for (int y = 0; y < 4; y++) rv[y] = *(const uint4 *)(base + (size_t)(4 * a + y) * kD + 8 * cb);
-    if (part == 1) {
-      const int t = tid >> 3, rb = kDV / 8 + (tid & 7);
-      rr = *(const uint4 *)(base + (size_t)t * kD + 8 * rb);
-    }
+    for (int u = 0; u < kStage; u++) stg[u] = base[min(tid + u * kThreads, kChunk * kRowU4 - 1)];
   };
-  auto store_part = [&](int c, int buf, int part) {
+  auto store_chunk = [&](int c, int buf) {
     const int pos0 = chunks[c].y;
     char *kb = lds + (size_t)buf * kBufBytes;
-    char *vb = kb + kKBytes;
-    const int e = tid + part * kThreads, a = e & 7, cb = e >> 3;
-    uint4 r[4];
 #pragma unroll
-    for (int y = 0; y < 4; y++) {
-      r[y] = keep_if(rv[y], attended(pos0 + 4 * a + y));
-      *(uint4 *)(kb + (4 * a + y) * kKRow + 16 * cb) = r[y];
-    }
-    // channel 8 cb + 2w (+1), tokens 4a .. 4a+3
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      const uint32_t d0 = word_of(r[0], w), d1 = word_of(r[1], w), d2 = word_of(r[2], w), d3 = word_of(r[3], w);
-      const uint2 lo = make_uint2((d0 & 0xffffu) | (d1 << 16), (d2 & 0xffffu) | (d3 << 16));
-      const uint2 hi = make_uint2((d0 >> 16) | (d1 & 0xffff0000u), (d2 >> 16) | (d3 & 0xffff0000u));
-      *(uint2 *)(vb + (8 * cb + 2 * w) * kVRow + 8 * a) = lo;
-      *(uint2 *)(vb + (8 * cb + 2 * w + 1) * kVRow + 8 * a) = hi;
-    }
-    if (part == 1) {
-      const int t = tid >> 3, rb = kDV / 8 + (tid & 7);
-      *(uint4 *)(kb + t * kKRow + 16 * rb) = keep_if(rr, attended(pos0 + t));
+    for (int u = 0; u < kStage; u++) {
+      const int e = tid + u * kThreads;
+      if (e < kChunk * kRowU4) {
+        const int t = e / kRowU4, cb = e % kRowU4;
+        const uint32_t k = attended(pos0 + t) ? ~0u : 0u;
+        *(uint4 *)(kb + t * kKRow + 16 * cb) = make_uint4(stg[u].x & k, stg[u].y & k, stg[u].z & k, stg[u].w & k);
+      }
     }
   };
+  // lane's transposing-read address inside a buffer: token 4kg + n/4, channels 4 (n % 4) ..
+  const int tr_off = (4 * kg + n / 4) * kKRow + 8 * (n % 4);
 
-  floatx4 acc[kHB][kDV / 16];
-  float m[kHB], l[kHB], seen[kHB];  // reference max, sum, largest score seen (log2 units)
-#pragma unroll
-  for (int hb = 0; hb < kHB; hb++) {
-    m[hb] = -INFINITY;
-    seen[hb] = -INFINITY;
-  }
-  __shared__ int overflow;
-  if (tid == 0) overflow = 0;
-  // one pass over the block's chunks with reference m (fixed per head once set)
+  floatx4 acc[kDV / 16];
+  float m = -INFINITY, l = 0.f, seen = -INFINITY;  // per head column n (log2 units)
+  // one pass over the block's chunks with reference m (fixed once set)
   auto run_pass = [&]() {
+    l = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < kHB; hb++) {
-      l[hb] = 0.f;
-#pragma unroll
-      for (int d = 0; d < kDV / 16; d++) acc[hb][d] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int d = 0; d < kDV / 16; d++) acc[d] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (nchunks > 0) {
-      load_part(0, 0);
-      store_part(0, 0, 0);
-      load_part(0, 1);
-      store_part(0, 0, 1);
+      load_chunk(0);
+      store_chunk(0, 0);
     }
+    if (nchunks > 1) load_chunk(1);
     __syncthreads();
     for (int c = 0; c < nchunks; c++) {
       const int buf = c & 1;
-      const bool more = c + 1 < nchunks;
-      if (more) load_part(c + 1, 0);
       const char *kb = lds + (size_t)buf * kBufBytes;
-      const char *vb = kb + kKBytes;
       const int pos0 = chunks[c].y;
 
-      // S^T: token 16 tb + 4 kg + r of column n, head block hb
-      floatx4 s[2][kHB];
+      // S^T: token 16 tb + 4 kg + r of head column n
+      floatx4 s[2];
 #pragma unroll
       for (int tb = 0; tb < 2; tb++) {
-#pragma unroll
-        for (int hb = 0; hb < kHB; hb++) s[tb][hb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        s[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
         const char *kr = kb + (16 * tb + n) * kKRow + 16 * kg;
 #pragma unroll
-        for (int i = 0; i < kD / 32; i++) {
-          const uint4 a = *(const uint4 *)(kr + 64 * i);
-#pragma unroll
-          for (int hb = 0; hb < kHB; hb++) s[tb][hb] = mfma16x16x32(a, qB[hb][i], s[tb][hb]);
-        }
-      }
-
-      if (more) {
-        store_part(c + 1, buf ^ 1, 0);
-        load_part(c + 1, 1);
+        for (int i = 0; i < kD / 32; i++) s[tb] = mfma16x16x32(*(const uint4 *)(kr + 64 * i), qB[i], s[tb]);
       }
 
       // softmax weights against the reference max; P^T hi / lo as the B operand
-      uint4 phi[kHB], plo[kHB];
-      bool over = false;
+      float sv[2][4];
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int hb = 0; hb < kHB; hb++) {
-        float sv[2][4];
-        float tmax = -INFINITY;
+      for (int tb = 0; tb < 2; tb++)
 #pragma unroll
-        for (int tb = 0; tb < 2; tb++)
+        for (int r = 0; r < 4; r++) {
+          const bool ok = attended(pos0 + 16 * tb + 4 * kg + r);
+          sv[tb][r] = ok ? s[tb][r] * scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, sv[tb][r]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      seen = fmaxf(seen, tmax);
+      if (m == -INFINITY) m = tmax;  // first attended chunk: nothing accumulated yet
+      if (__any(tmax > m + kHeadroom) && lane == 0) overflow = 1;
+      float p[2][4], pl[2][4];
+      float psum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; r++) {
-            const bool ok = attended(pos0 + 16 * tb + 4 * kg + r);
-            sv[tb][r] = ok ? s[tb][hb][r] * scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, sv[tb][r]);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        seen[hb] = fmaxf(seen[hb], tmax);
-        if (m[hb] == -INFINITY) m[hb] = tmax;  // first attended chunk: nothing accumulated yet
-        over |= tmax > m[hb] + kHeadroom;
-        float p[2][4], pl[2][4];
-        float psum = 0.f;
+      for (int tb = 0; tb < 2; tb++)
 #pragma unroll
-        for (int tb = 0; tb < 2; tb++)
-#pragma unroll
-          for (int r = 0; r < 4; r++) {
-            p[tb][r] = sv[tb][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][r] - m[hb]);
-            psum += p[tb][r];
-            pl[tb][r] = p[tb][r] - bf16_round(p[tb][r]);
-          }
-        psum += __shfl_xor(psum, 16, kWave);
-        psum += __shfl_xor(psum, 32, kWave);
-        l[hb] += psum;
-        phi[hb] = pack_bf16x8(p[0], p[1]);
-        plo[hb] = pack_bf16x8(pl[0], pl[1]);
-      }
-      if (__any(over) && lane == 0) overflow = 1;
+        for (int r = 0; r < 4; r++) {
+          p[tb][r] = sv[tb][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][r] - m);
+          psum += p[tb][r];
+          pl[tb][r] = p[tb][r] - bf16_round(p[tb][r]);
+        }
+      psum += __shfl_xor(psum, 16, kWave);
+      psum += __shfl_xor(psum, 32, kWave);
+      l += psum;
+      const uint4 phi = pack_bf16x8(p[0], p[1]);
+      const uint4 plo = pack_bf16x8(pl[0], pl[1]);
 
-      // O^T += V^T P^T: A = channels 16 d + n, tokens 4kg..4kg+3 and 16+4kg..16+4kg+3
+      // O^T += V^T P^T over value channels 16 d + n
+      const char *vb = kb + tr_off;
 #pragma unroll
       for (int d = 0; d < kDV / 16; d++) {
-        const char *vr = vb + (16 * d + n) * kVRow + 8 * kg;
-        const uint2 x0 = *(const uint2 *)vr, x1 = *(const uint2 *)(vr + 32);
+        const uint2 x0 = lds_read_tr16(vb + 32 * d), x1 = lds_read_tr16(vb + 16 * kKRow + 32 * d);
         const uint4 a = make_uint4(x0.x, x0.y, x1.x, x1.y);
-#pragma unroll
-        for (int hb = 0; hb < kHB; hb++) {
-          acc[hb][d] = mfma16x16x32(a, phi[hb], acc[hb][d]);
-          acc[hb][d] = mfma16x16x32(a, plo[hb], acc[hb][d]);
-        }
+        acc[d] = mfma16x16x32(a, phi, acc[d]);
+        acc[d] = mfma16x16x32(a, plo, acc[d]);
       }
 
-      if (more) store_part(c + 1, buf ^ 1, 1);
-      __syncthreads();
+      __syncthreads();  // every wave is done with buffer buf
+      if (c + 1 < nchunks) {
+        store_chunk(c + 1, buf ^ 1);  // loaded while chunk c was computed
+        if (c + 2 < nchunks) load_chunk(c + 2);
+        __syncthreads();
+      }
     }
   };
   run_pass();
   if (overflow) {  // some weight could exceed 2^kHeadroom: again, from the largest score seen
-#pragma unroll
-    for (int hb = 0; hb < kHB; hb++) m[hb] = seen[hb];
+    m = seen;
     run_pass();
   }
 
   // lane (n, kg) holds O^T rows 16 d + 4 kg + r of head column n
+  const size_t row = head0 + n;
+  if (splits == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int hb = 0; hb < kHB; hb++) {
-    const size_t row = head0 + 16 * hb + n;
-    if (splits == 1) {
-      const float inv = l[hb] > 0.f ? 1.f / l[hb] : 0.f;
+    for (int d = 0; d < kDV / 16; d++)
+      *(float4 *)(out + row * kDV + 16 * d + 4 * kg) =
+          make_float4(acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv);
+  } else {
+    const size_t ps_idx = row * splits + split;
 #pragma unroll
-      for (int d = 0; d < kDV / 16; d++)
-        *(float4 *)(out + row * kDV + 16 * d + 4 * kg) =
-            make_float4(acc[hb][d][0] * inv, acc[hb][d][1] * inv, acc[hb][d][2] * inv, acc[hb][d][3] * inv);
-    } else {
-      const size_t ps_idx = row * splits + split;
-#pragma unroll
-      for (int d = 0; d < kDV / 16; d++)
-        *(float4 *)(partial + ps_idx * kDV + 16 * d + 4 * kg) =
-            make_float4(acc[hb][d][0], acc[hb][d][1], acc[hb][d][2], acc[hb][d][3]);
-      if (kg == 0) partial_ml[ps_idx] = make_float2(m[hb], l[hb]);
-    }
+    for (int d = 0; d < kDV / 16; d++)
+      *(float4 *)(partial + ps_idx * kDV + 16 * d + 4 * kg) = make_float4(acc[d][0], acc[d][1], acc[d][2], acc[d][3]);
+    if (kg == 0) partial_ml[ps_idx] = make_float2(m, l);
   }
 }
 
@@ -309,15 +257,12 @@ hipError_t launch_decode_mla(const qasp_layout &lay, const qasp_batch &bat, cons
                              const Workspace &ws, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = 2 * (size_t)kBufBytes;
-  hipError_t e = hipFuncSetAttribute((const void *)decode_mla_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   dim3 grid(ws.splits, lay.num_kv_heads, bat.batch);
   hipLaunchKernelGGL(decode_mla_kernel, grid, dim3(kThreads), lds, stream, q, k_pool, bat.page_table,
                      bat.seq_lens, sel, sel_count, ws.partial, ws.partial_ml, out, bat.pt_stride, max_sel,
                      bat.num_q_heads, lay.num_kv_heads, ws.splits, scale_log2, pol.sink_tokens,
                      pol.window_tokens, pol.static_head_mask);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || ws.splits == 1) return e;
   return launch_merge_splits(ws, bat.batch, bat.num_q_heads, kDV, out, stream);
 }

@@ -18,7 +18,10 @@ namespace qasp {
 #endif
 constexpr int kGqaDecodeWaves = QASP_GQA_WAVES;         // waves per decode block
 constexpr int kGqaTargetBlocks = QASP_GQA_TARGET_BLOCKS; // split units until this many blocks
-constexpr int kMlaPagesPerSplit = 2;
+#ifndef QASP_MLA_PAGES_PER_SPLIT
+#define QASP_MLA_PAGES_PER_SPLIT 2
+#endif
+constexpr int kMlaPagesPerSplit = QASP_MLA_PAGES_PER_SPLIT;  // selected pages per latent-head decode block
 
 struct Workspace {
   qasp_score *scores;   // [B][Hkv][max_pages]
