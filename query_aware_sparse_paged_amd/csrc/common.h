@@ -169,6 +169,15 @@ __device__ __forceinline__ uint32_t wave_or_dpp(uint32_t x) {
 
 __device__ __forceinline__ int num_pages_of(int L, int ps) { return L <= 0 ? 0 : (L + ps - 1) / ps; }
 
+// Work item of block `blk` (of `total`) when consecutive items should share
+// an XCD: blocks are dealt to the 8 XCDs in turn (block b runs on XCD b % 8),
+// so XCD x is given the contiguous items [x total / 8, (x + 1) total / 8).
+// Identity when total is not a multiple of 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous_item(int blk, int total) {
+  return total % kXcds == 0 ? (blk % kXcds) * (total / kXcds) + blk / kXcds : blk;
+}
+
 __device__ __forceinline__ bool head_is_static(uint64_t mask, int g) {
   return (mask >> g) & 1ull;
 }

@@ -63,8 +63,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
 }
 
 // Combines the split partials of every (sequence, query head):
-// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(256) void merge_splits_kernel(const float *__restrict__ partial,
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.  One block per
+// (sequence, head); a thread owns 4 consecutive channels and reads four
+// splits' partials per step (16-byte loads, several in flight).
+__global__ __launch_bounds__(128) void merge_splits_kernel(const float *__restrict__ partial,
                                                            const float2 *__restrict__ partial_ml,
                                                            float *__restrict__ out, int Hq, int splits,
                                                            int dv_dim) {
@@ -72,24 +74,51 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float *__restri
   const size_t base = ((size_t)b * Hq + h) * splits;
   float M = -INFINITY;
   for (int s = 0; s < splits; s++) M = fmaxf(M, partial_ml[base + s].x);
-  for (int dv = threadIdx.x; dv < dv_dim; dv += blockDim.x) {
-    float a = 0.f, lsum = 0.f;
+  for (int c = 4 * threadIdx.x; c < dv_dim; c += 4 * blockDim.x) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.f;
     if (M != -INFINITY) {
-      for (int s = 0; s < splits; s++) {
+      int s = 0;
+      for (; s + 4 <= splits; s += 4) {
+        float4 v[4];
+        float f[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) v[u] = *(const float4 *)(partial + (base + s + u) * dv_dim + c);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const float2 ml = partial_ml[base + s + u];
+          f[u] = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);  // empty split: no weight
+          lsum += ml.x == -INFINITY ? 0.f : f[u] * ml.y;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          if (f[u] == 0.f) continue;
+          a.x += f[u] * v[u].x;
+          a.y += f[u] * v[u].y;
+          a.z += f[u] * v[u].z;
+          a.w += f[u] * v[u].w;
+        }
+      }
+      for (; s < splits; s++) {
         const float2 ml = partial_ml[base + s];
-        if (ml.x == -INFINITY) continue;  // empty split
+        if (ml.x == -INFINITY) continue;
         const float f = __builtin_amdgcn_exp2f(ml.x - M);
-        a += f * partial[(base + s) * dv_dim + dv];
+        const float4 v = *(const float4 *)(partial + (base + s) * dv_dim + c);
+        a.x += f * v.x;
+        a.y += f * v.y;
+        a.z += f * v.z;
+        a.w += f * v.w;
         lsum += f * ml.y;
       }
     }
-    out[((size_t)b * Hq + h) * dv_dim + dv] = lsum > 0.f ? a / lsum : 0.f;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    *(float4 *)(out + ((size_t)b * Hq + h) * dv_dim + c) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
   }
 }
 
 hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(Hq, batch), dim3(dv_dim <= 128 ? 128 : 256), 0, stream,
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(Hq, batch), dim3(dv_dim >= 512 ? 128 : dv_dim / 4), 0, stream,
                      ws.partial, ws.partial_ml, out, Hq, ws.splits, dv_dim);
   return hipGetLastError();
 }

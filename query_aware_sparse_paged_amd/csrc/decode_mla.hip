@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   char *lds = (char *)lds_u4;
   __shared__ int2 chunks[kMaxChunks];  // (physical page, position of the chunk's first token)
   __shared__ int nchunks_sh, overflow;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // the splits of a unit run on one XCD, which then reads its q once into L2
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
+  const int split = item % splits, g = (item / splits) % Hkv, b = item / (splits * Hkv);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane & 15, kg = lane >> 4;
   const int unit = b * Hkv + g;
@@ -257,7 +259,7 @@ hipError_t launch_decode_mla(const qasp_layout &lay, const qasp_batch &bat, cons
                              const Workspace &ws, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = 2 * (size_t)kBufBytes;
-  dim3 grid(ws.splits, lay.num_kv_heads, bat.batch);
+  dim3 grid((unsigned)ws.splits * lay.num_kv_heads * bat.batch);
   hipLaunchKernelGGL(decode_mla_kernel, grid, dim3(kThreads), lds, stream, q, k_pool, bat.page_table,
                      bat.seq_lens, sel, sel_count, ws.partial, ws.partial_ml, out, bat.pt_stride, max_sel,
                      bat.num_q_heads, lay.num_kv_heads, ws.splits, scale_log2, pol.sink_tokens,

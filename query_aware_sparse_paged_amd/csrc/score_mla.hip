@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   const int n = lane & 15, kg = lane >> 4;
   const int g = 0;  // one latent KV head
   const int total = batch * groups_per_seq;
-  const int first = blockIdx.x * groups_per_block;
+  // the blocks of a sequence run on one XCD, which then reads its q once into L2
+  const int first = xcd_contiguous_item(blockIdx.x, gridDim.x) * groups_per_block;
   const int last = min(first + groups_per_block, total);
   if (first >= last) return;
 
