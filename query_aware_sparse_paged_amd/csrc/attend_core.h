@@ -158,51 +158,6 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const PageWork<PS, D
   }
 }
 
-// Attends the pages list[0 .. count) (logical ids; page_phys[j] is the
-// physical page of id j), shared by the block's waves through the LDS
-// counter *next: each wave takes the next unclaimed entry whenever it issues
-// a prefetch, so waves that see faster memory take more pages.  Two pages
-// are in flight per wave as in attend_pages; claims past the end load the
-// last page again and are not computed.
-template <int PS, int D, int DV>
-__device__ __forceinline__ void attend_pages_queue(WaveState &st, const PageWork<PS, D, DV> &pw, int *next,
-                                                   const int32_t *list, const int32_t *page_phys, int count,
-                                                   int lane) {
-  if (count <= 0) return;
-  uint4 kA[D / 32], kB[D / 32], kC[D / 32];
-  uint2 vA[DV / 16], vB[DV / 16], vC[DV / 16];
-  auto claim = [&]() {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(next, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  // loads entry idx (clamped) and returns its logical id
-  auto load_entry = [&](int idx, uint4 *kk, uint2 *vv) {
-    const int j = list[min(idx, count - 1)];
-    pw.load(page_phys[j], kk, vv, lane);
-    return j;
-  };
-  int ia = claim(), ib = claim();
-  int ja = load_entry(ia, kA, vA), jb = load_entry(ib, kB, vB);
-  while (ia < count) {
-    const int ic = claim();
-    const int jc = load_entry(ic, kC, vC);
-    pw.compute(st, true, ja, kA, vA, lane);
-    if (ib >= count) break;
-    const int id = claim();
-    const int jd = load_entry(id, kA, vA);
-    pw.compute(st, true, jb, kB, vB, lane);
-    if (ic >= count) break;
-    const int ie = claim();
-    const int je = load_entry(ie, kB, vB);
-    pw.compute(st, true, jc, kC, vC, lane);
-    ia = id;
-    ja = jd;
-    ib = ie;
-    jb = je;
-  }
-}
-
 // LDS footprint of merge_waves for W waves and G heads (floats).
 __host__ __device__ constexpr int merge_lds_floats(int W, int G, int DV) { return 2 * W * G + W * G * (DV + 4); }
 

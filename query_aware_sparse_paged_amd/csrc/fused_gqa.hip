@@ -42,7 +42,6 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   constexpr int KSTEPS = 2 * D / 32;
   extern __shared__ uint64_t dyn[];
   __shared__ sel::SelShared<NW> sh;
-  __shared__ int attend_next;
   const FusedLds lay(max_pages, max_sel, G);
   uint64_t *keys64 = dyn;
   uint32_t *keys32 = (uint32_t *)dyn;
@@ -180,10 +179,16 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const int count = sel::emit_selection(sh, sel_bits, nwords,
                                         sel_out ? sel_out + (size_t)unit * max_sel : nullptr, list, max_sel);
   if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
-  if (tid == 0) attend_next = 0;
   __syncthreads();
 
-  // ---- attend: the waves claim selected pages from a shared counter
+  // ---- attend: wave w takes selected pages w, w+W, ... (a fixed assignment,
+  // so the result does not depend on timing)
+  const int npg = count > wave ? (count - wave + W - 1) / W : 0;
+  int my_j = 0, my_phys = 0;
+  if (lane < npg) {
+    my_j = list[wave + W * lane];
+    my_phys = page_phys[my_j];
+  }
   const int sink_end = is_static ? min(sink_tokens, L) : 0;
   const int win_begin = is_static ? max(0, L - window_tokens) : 0;
   uint4 bq[D / 32];
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   attend::WaveState st;
   attend::init_state(st);
   const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
-  attend::attend_pages_queue<PS, D, DV>(st, pw, &attend_next, list, page_phys, count, lane);
+  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
   attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
     (void)M;
     out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
