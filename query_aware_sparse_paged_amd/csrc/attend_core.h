@@ -55,6 +55,14 @@ __device__ __forceinline__ void init_state(WaveState &st) {
   for (int i = 0; i < 8; i++) st.acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
+// One page-head's fragments for a wave (keys as MFMA A operands, values as
+// V^T fragments), held in registers.
+template <int D, int DV>
+struct PageRegs {
+  uint4 k[D / 32];
+  uint2 v[DV / 16];
+};
+
 // Loading and computing one page-head for a wave (the two halves of the
 // pipelined loops below).
 template <int PS, int D, int DV>
@@ -76,6 +84,11 @@ struct PageWork {
     for (int i = 0; i < D / 32; i++) kk[i] = *(const uint4 *)(kp + 32 * i);
 #pragma unroll
     for (int i = 0; i < DV / 16; i++) vv[i] = *(const uint2 *)(vp + 16 * i * PS);
+  }
+  __device__ __forceinline__ PageRegs<D, DV> load(int phys, int lane) const {
+    PageRegs<D, DV> r;
+    load(phys, r.k, r.v, lane);
+    return r;
   }
 
   // page with logical id j; real = false computes it fully masked
@@ -131,10 +144,12 @@ struct PageWork {
 
 // Attends npg page-heads.  Lane i (< npg) holds the i-th page's logical id
 // (my_j) and physical page (my_phys).  Tokens t of a page are used when
-// t < L and, for a static head, t < sink_end or t >= win_begin.
+// t < L and, for a static head, t < sink_end or t >= win_begin.  When pre is
+// set, first already holds page 0 (loaded by the caller earlier).
 template <int PS, int D, int DV>
 __device__ __forceinline__ void attend_pages(WaveState &st, const PageWork<PS, D, DV> &pw, int npg, int my_j,
-                                             int my_phys, int lane) {
+                                             int my_phys, int lane, bool pre = false,
+                                             PageRegs<D, DV> first = PageRegs<D, DV>()) {
   if (npg <= 0) return;
   uint4 kA[D / 32], kB[D / 32], kC[D / 32];
   uint2 vA[DV / 16], vB[DV / 16], vC[DV / 16];
@@ -149,7 +164,14 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const PageWork<PS, D
     load_page(it + 2, kn, vn);
     compute_page(it, kc, vc);
   };
-  load_page(0, kA, vA);
+  if (pre) {
+#pragma unroll
+    for (int i = 0; i < D / 32; i++) kA[i] = first.k[i];
+#pragma unroll
+    for (int i = 0; i < DV / 16; i++) vA[i] = first.v[i];
+  } else {
+    load_page(0, kA, vA);
+  }
   load_page(1, kB, vB);
   for (int it = 0; it < npg; it += 3) {
     page_step(it, kA, vA, kC, vC);

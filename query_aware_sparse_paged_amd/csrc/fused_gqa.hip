@@ -42,6 +42,8 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   constexpr int KSTEPS = 2 * D / 32;
   extern __shared__ uint64_t dyn[];
   __shared__ sel::SelShared<NW> sh;
+  __shared__ uint32_t sh_kmin, sh_kmax;
+  __shared__ int sh_emax;
   const FusedLds lay(max_pages, max_sel, G);
   uint64_t *keys64 = dyn;
   uint32_t *keys32 = (uint32_t *)dyn;
@@ -100,7 +102,12 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     band_bits[w] = 0;
   }
   for (int w = tid; w < NW * 256; w += T) (&sh.hist[0][0])[w] = 0;
-  if (tid == 0) sh.nlist = 0;
+  if (tid == 0) {
+    sh.nlist = 0;
+    sh_kmin = ~0u;
+    sh_kmax = 0u;
+    sh_emax = 0;
+  }
   // the sequence's physical pages, read once, coalesced: scoring, exact
   // re-scoring and attention take them from LDS, so no load waits on a
   // page-table load
@@ -155,7 +162,33 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
         phys_cur = phys_next;
       }
     }
+    // block-wide key range and largest error bound through LDS atomics (the
+    // barrier before the selection orders them)
+    k_min = ~(uint32_t)wave_max_dpp((int)(~k_min ^ 0x80000000u)) ^ 0x80000000u;
+    k_max = (uint32_t)wave_max_dpp((int)(k_max ^ 0x80000000u)) ^ 0x80000000u;
+    e_loc = wave_max_dpp(e_loc);
+    if (lane == 0) {
+      atomicMin(&sh_kmin, k_min);
+      atomicMax(&sh_kmax, k_max);
+      atomicMax(&sh_emax, __float_as_int(e_loc));  // non-negative floats order as integers
+    }
   }
+
+  // ---- attention order: the sink and local pages of a ranked unit are known
+  // before its selection, so they come first and each wave loads its first
+  // one now, under the selection; the top-k pages follow.  Attention position
+  // p maps to position map_pos(p) of the ascending selection list.
+  const int n_known = ranked ? cand_lo + (P - cand_hi) : 0;
+  const int sink_end = is_static ? min(sink_tokens, L) : 0;
+  const int win_begin = is_static ? max(0, L - window_tokens) : 0;
+  uint4 bq[D / 32];
+  attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
+  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  const bool pre = wave < n_known;  // wave-uniform
+  // issued by every wave (a valid page when there is nothing to preload), so
+  // the registers are always defined and the load is never waited on here
+  const attend::PageRegs<D, DV> first =
+      pw.load(pre ? page_phys[wave < cand_lo ? wave : cand_hi + (wave - cand_lo)] : (P > 0 ? page_phys[0] : 0), lane);
 
   // ---- select
   if (is_static) {
@@ -169,7 +202,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     for (int j = tid; j < P; j += T)
       if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     if (ranked) {
-      sel::block_max_min_max(e_loc, k_min, k_max, sh);
+      __syncthreads();
+      k_min = sh_kmin;
+      k_max = sh_kmax;
+      e_loc = __int_as_float(sh_emax);
       sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min, k_max,
                                     q_in_lds ? sh.qstage : q + head0 * D, G, summ, pt_row, Hkv, g, nullptr,
                                     page_phys + cand_lo);
@@ -181,22 +217,21 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
   __syncthreads();
 
-  // ---- attend: wave w takes selected pages w, w+W, ... (a fixed assignment,
-  // so the result does not depend on timing)
+  // ---- attend: wave w takes attention positions w, w+W, ... (a fixed
+  // assignment, so the result does not depend on timing)
+  auto map_pos = [&](int p) {
+    if (p >= n_known) return cand_lo + (p - n_known);           // top-k, ascending
+    return p < cand_lo ? p : count - (P - cand_hi) + (p - cand_lo);  // sink, then local
+  };
   const int npg = count > wave ? (count - wave + W - 1) / W : 0;
   int my_j = 0, my_phys = 0;
   if (lane < npg) {
-    my_j = list[wave + W * lane];
+    my_j = list[n_known > 0 ? map_pos(wave + W * lane) : wave + W * lane];
     my_phys = page_phys[my_j];
   }
-  const int sink_end = is_static ? min(sink_tokens, L) : 0;
-  const int win_begin = is_static ? max(0, L - window_tokens) : 0;
-  uint4 bq[D / 32];
-  attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
   attend::WaveState st;
   attend::init_state(st);
-  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
-  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
+  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane, pre && npg > 0, first);
   attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
     (void)M;
     out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
