@@ -38,6 +38,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
     int window_tokens, uint64_t static_mask, float scale_log2) {
+  static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
   extern __shared__ uint64_t dyn[];
@@ -68,35 +69,6 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const bool ranked = !is_static && k > 0 && k < n;
   const size_t head0 = (size_t)b * Hq + (size_t)g * G;
 
-  // ---- append: the token at position L-1, head g (key row, value column,
-  // summary: slot 0 starts it, later slots widen it)
-  if (k_new != nullptr && L > 0) {
-    const int pos = L - 1, t = pos % PS;
-    const size_t ph = (size_t)pt_row[pos / PS] * Hkv + g;
-    const uint32_t *kn = (const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D);
-    for (int w = tid; w < D / 2; w += T) {
-      const uint32_t kv = kn[w];
-      ((uint32_t *)k_pool)[(ph * PS + t) * (D / 2) + w] = kv;
-      if (summ != nullptr) {
-        uint32_t *s = (uint32_t *)summ + ph * D;
-        uint32_t lo = kv, hi = kv;
-        if (t != 0) {
-          lo = s[w];
-          hi = s[D / 2 + w];
-          const int v0 = bf16_order_key(kv & 0xffffu), v1 = bf16_order_key(kv >> 16);
-          lo = bf16_from_order_key(min(v0, bf16_order_key(lo & 0xffffu))) |
-               (bf16_from_order_key(min(v1, bf16_order_key(lo >> 16))) << 16);
-          hi = bf16_from_order_key(max(v0, bf16_order_key(hi & 0xffffu))) |
-               (bf16_from_order_key(max(v1, bf16_order_key(hi >> 16))) << 16);
-        }
-        s[w] = lo;
-        s[D / 2 + w] = hi;
-      }
-    }
-    const uint16_t *vn = v_new + ((size_t)b * Hkv + g) * DV;
-    for (int dv = tid; dv < DV; dv += T) v_pool[(ph * DV + dv) * PS + t] = vn[dv];
-    __threadfence_block();
-  }
   for (int w = tid; w < nwords; w += T) {
     sel_bits[w] = 0;
     band_bits[w] = 0;
@@ -108,15 +80,81 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     sh_kmax = 0u;
     sh_emax = 0;
   }
-  // the sequence's physical pages, read once, coalesced: scoring, exact
-  // re-scoring and attention take them from LDS, so no load waits on a
-  // page-table load
-  for (int j = tid; j < P; j += T) page_phys[j] = pt_row[j];
-  // the group's q rows in LDS, for the exact re-scoring of undecided pages
+  // ---- the sequence's physical pages and the group's q rows to LDS (the
+  // scoring, the exact re-scoring and the attention read them there); every
+  // load of a round is issued before its results are stored
   const bool q_in_lds = (size_t)G * D * 2 <= sel::kQStageBytes;
-  if (q_in_lds)
-    for (int w = tid; w < G * D / 2; w += T) ((uint32_t *)sh.qstage)[w] = ((const uint32_t *)(q + head0 * D))[w];
+  {
+    const int nq = q_in_lds ? G * D / 2 : 0;  // q words
+    const uint32_t *qsrc = (const uint32_t *)(q + head0 * D);
+    for (int r0 = 0; r0 < P || r0 < 4 * nq; r0 += 4 * T) {  // 4 page-table entries and 1 q word per thread a round
+      int v[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int j = r0 + r * T + tid;
+        v[r] = j < P ? pt_row[j] : 0;
+      }
+      const int wq = r0 / 4 + tid;
+      const uint32_t qv = wq < nq ? qsrc[wq] : 0u;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int j = r0 + r * T + tid;
+        if (j < P) page_phys[j] = v[r];
+      }
+      if (wq < nq) ((uint32_t *)sh.qstage)[wq] = qv;
+    }
+  }
   __syncthreads();
+
+  // ---- append of the token at position L-1, head g, by the last wave (its
+  // key row, value column and the page summary: slot 0 starts it, later slots
+  // widen it).  Its loads are issued here, the stores after the scoring, so
+  // their latency is hidden; the barrier after the scoring orders them
+  // before any read of the page.
+  const bool appending = k_new != nullptr && L > 0;  // block-uniform
+  const bool my_append = appending && wave == W - 1;
+  const int a_t = appending ? (L - 1) % PS : 0;
+  size_t a_ph = 0;
+  uint32_t a_k = 0, a_lo = 0, a_hi = 0;
+  uint16_t a_v0 = 0, a_v1 = 0;
+  if (my_append) {
+    a_ph = (size_t)page_phys[(L - 1) / PS] * Hkv + g;
+    a_k = ((const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D))[lane];  // D / 2 = 64 words: one per lane
+    const uint16_t *vn = v_new + ((size_t)b * Hkv + g) * DV;
+    a_v0 = vn[lane];
+    a_v1 = vn[lane + kWave];
+    if (summ != nullptr) {
+      const uint32_t *sp = (const uint32_t *)summ + a_ph * D;
+      a_lo = sp[lane];
+      a_hi = sp[D / 2 + lane];
+    }
+  }
+  auto append_stores = [&]() {
+    ((uint32_t *)k_pool)[(a_ph * PS + a_t) * (D / 2) + lane] = a_k;
+    v_pool[(a_ph * DV + lane) * PS + a_t] = a_v0;
+    v_pool[(a_ph * DV + lane + kWave) * PS + a_t] = a_v1;
+    if (summ != nullptr) {
+      uint32_t lo = a_k, hi = a_k;
+      if (a_t != 0) {
+        const int v0 = bf16_order_key(a_k & 0xffffu), v1 = bf16_order_key(a_k >> 16);
+        lo = bf16_from_order_key(min(v0, bf16_order_key(a_lo & 0xffffu))) |
+             (bf16_from_order_key(min(v1, bf16_order_key(a_lo >> 16))) << 16);
+        hi = bf16_from_order_key(max(v0, bf16_order_key(a_hi & 0xffffu))) |
+             (bf16_from_order_key(max(v1, bf16_order_key(a_hi >> 16))) << 16);
+      }
+      uint32_t *sp = (uint32_t *)summ + a_ph * D;
+      sp[lane] = lo;
+      sp[D / 2 + lane] = hi;
+    }
+    __threadfence_block();
+  };
+  // a last page that is itself a candidate is scored with the new token in
+  // its summary, so then the append completes first
+  const bool early_append = appending && ranked && cand_hi == P;  // block-uniform
+  if (early_append) {
+    if (my_append) append_stores();
+    __syncthreads();
+  }
 
   // ---- score the candidates: wave w takes 16-page groups w, w+W, ...; the
   // summaries of the next group are in flight while the current group is
@@ -173,6 +211,9 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
       atomicMax(&sh_emax, __float_as_int(e_loc));  // non-negative floats order as integers
     }
   }
+  if (!early_append && my_append) append_stores();
+  // the append is complete and the key range / error bound are final
+  __syncthreads();
 
   // ---- attention order: the sink and local pages of a ranked unit are known
   // before its selection, so they come first and each wave loads its first
@@ -202,7 +243,6 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     for (int j = tid; j < P; j += T)
       if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     if (ranked) {
-      __syncthreads();
       k_min = sh_kmin;
       k_max = sh_kmax;
       e_loc = __int_as_float(sh_emax);

@@ -218,12 +218,17 @@ def test_single_kernel_step_matches_oracle_and_kernel_chain(name, kw):
     assert np.abs(out.cpu().numpy() - g.out).max() <= 1e-5
 
 
-def test_single_kernel_step_appends():
-    """The one-kernel step writes the token at L-1 and updates its summary."""
+@pytest.mark.parametrize("local,boost", [(None, 1.0), (0, 6.0)])
+def test_single_kernel_step_appends(local, boost):
+    """The one-kernel step writes the token at L-1 and updates its summary.
+    With no local window the last page is a candidate, and a large new key
+    makes it the best page: it must be scored with the new token."""
     w = _small("llama8b_b32_32k", batch=32, seq_len=700, seq_len_min=600)
     lay, pol = api.layout_of(w), api.policy_of(w)
+    if local is not None:
+        pol = api.Policy(pol.n_sink_pages, local, pol.top_k)
     gen = torch.Generator().manual_seed(5)
-    new_k = torch.randn(w.k_new.shape, generator=gen).to(torch.bfloat16)
+    new_k = (torch.randn(w.k_new.shape, generator=gen) * boost).to(torch.bfloat16)
     new_v = torch.randn(w.v_new.shape, generator=gen).to(torch.bfloat16)
     kp, vp = w.k_pool.to(DEV), w.v_pool.to(DEV)
     bat = api.Batch(w.page_table.to(DEV), w.seq_lens.to(DEV), 32)
@@ -232,8 +237,10 @@ def test_single_kernel_step_appends():
     api.build_summaries(lay, api.Batch(bat.page_table, (bat.seq_lens - 1).contiguous(), 32), kp, summ)
     msel = api.max_sel(lay, pol, bat.max_pages)
     ws = api.new_workspace(lay, bat, pol, msel, DEV)
+    sel = torch.full((32, lay.num_kv_heads, msel), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((32, lay.num_kv_heads), -7, dtype=torch.int32, device=DEV)
     out = api.decode_step(lay, bat, pol, w.q.to(DEV), kp, vp, summ, w.scale, ws, msel,
-                          k_new=new_k.to(DEV), v_new=new_v.to(DEV))
+                          k_new=new_k.to(DEV), v_new=new_v.to(DEV), sel=sel, sel_count=cnt)
     torch.cuda.synchronize()
     # the oracle sees the pool with the token written and summaries from scratch
     for b in range(32):
@@ -247,7 +254,12 @@ def test_single_kernel_step_appends():
     used = w.page_table[:, :44].reshape(-1).long()
     used = used[used >= 0]
     assert np.array_equal(workloads.bits(summ.cpu()[used]), r.summ[used.numpy()])
+    assert np.array_equal(cnt.cpu().numpy(), r.cnt) and np.array_equal(sel.cpu().numpy(), r.sel)
     assert np.abs(out.cpu().numpy().astype(np.float64) - r.out).max() <= 5e-3
+    if local == 0:  # the test is only sensitive if the boosted last pages are chosen
+        last = (w.seq_lens.numpy() - 1) // 16
+        chosen = (r.sel == last[:, None, None]).any(-1)
+        assert chosen.mean() > 0.5
 
 
 @pytest.mark.parametrize("batch", [3, 32])   # kernel chain; one-kernel step
