@@ -18,12 +18,13 @@ constexpr int kFusedWaves = 8;
 
 // Dynamic LDS layout of the fused kernel (bytes).
 struct FusedLds {
-  size_t keys, phys, bits, list, merge, total;
+  size_t keys, phys, order, bits, list, merge, total;
   __host__ __device__ FusedLds(int max_pages, int max_sel, int G) {
     const int nwords = (max_pages + 31) / 32;
     keys = 0;                                                       // uint64 [max_pages]
     phys = keys + (size_t)max_pages * 8;                            // int32 [max_pages]: pages of the sequence
-    bits = phys + (size_t)max_pages * 4;                            // 2 x uint32 [nwords]
+    order = phys + (size_t)max_pages * 4;                           // int32 [max_pages]: scoring order
+    bits = order + (size_t)max_pages * 4;                           // 2 x uint32 [nwords]
     list = bits + (size_t)2 * nwords * 4;                           // int32 [max_sel]
     merge = (list + (size_t)max_sel * 4 + 15) & ~(size_t)15;        // float merge area
     total = merge + (size_t)attend::merge_lds_floats(kFusedWaves, G, 128) * 4;
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, float *__restrict__ out,
     int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
-    int window_tokens, uint64_t static_mask, float scale_log2) {
+    int window_tokens, uint64_t static_mask, float scale_log2, int pool_pages) {
   static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   uint32_t *band_bits = sel_bits + nwords;
   int32_t *list = (int32_t *)((char *)dyn + lay.list);
   int32_t *page_phys = (int32_t *)((char *)dyn + lay.phys);
+  int32_t *order = (int32_t *)((char *)dyn + lay.order);
   float *merge_area = (float *)((char *)dyn + lay.merge);
 
   const int b = blockIdx.x, g = blockIdx.y;  // consecutive blocks (one per XCD in turn) take different sequences
@@ -156,30 +158,80 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     __syncthreads();
   }
 
-  // ---- score the candidates: wave w takes 16-page groups w, w+W, ...; the
-  // summaries of the next group are in flight while the current group is
-  // computed (past the last group the prefetch reads page 0, unused)
+  // ---- scoring order: each wave's first 16-page group is in candidate
+  // order and its summaries are loaded now; the other candidates follow by
+  // physical page, bucketed into 256 equal ranges of the pool (a counting
+  // sort while those loads are in flight; the order inside a bucket is
+  // whatever the LDS atomics give, which changes no result).  Every block then
+  // sweeps the summary pool from low to high addresses at about the pace of
+  // the others, which the memory serves faster than records in random order.
+  const int ngroups = (n + 15) / 16;
+  const int my_groups = ngroups > wave ? (ngroups - wave + W - 1) / W : 0;
+  const int s0 = min(n, W * 16);  // positions below s0 keep candidate order
+  auto cand_of = [&](int gi) {    // candidate of this lane's column in the wave's gi-th group, -1 if none
+    const int s = (wave + gi * W) * 16 + n_col;
+    return gi < my_groups && s < n ? (s < s0 ? s : order[s]) : -1;
+  };
+  auto page_of = [&](int c) { return c >= 0 ? page_phys[cand_lo + c] : -1; };
+  score::QOperands<D> op;
+  uint4 bs[2][KSTEPS];
+  int c_cur = -1, phys_cur = -1;
+  if (ranked) {
+    score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
+    c_cur = cand_of(0);
+    phys_cur = page_of(c_cur);
+    score::load_group<D>(bs[0], summ, max(phys_cur, 0), Hkv, g, lane);
+    constexpr int NB = 256;
+    int *cnt = &sh.hist[0][0];  // zero here; zeroed again before the selection uses it
+    for (int i0 = s0; i0 < n; i0 += 4 * T) {
+      int bk[4], rk[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int i = i0 + r * T + tid;
+        bk[r] = i < n ? min(max((int)(((long long)page_phys[cand_lo + i] * NB) / pool_pages), 0), NB - 1) : 0;
+        rk[r] = i < n ? atomicAdd(&cnt[bk[r]], 1) : 0;
+      }
+      __syncthreads();
+      if (wave == 0) {  // exclusive scan of the bucket counts, in place (4 per lane)
+        int c[4], t = 0;
+#pragma unroll
+        for (int x = 0; x < 4; x++) {
+          c[x] = cnt[4 * lane + x];
+          t += c[x];
+        }
+        int e = wave_incl_sum(t) - t;
+#pragma unroll
+        for (int x = 0; x < 4; x++) {
+          cnt[4 * lane + x] = e;
+          e += c[x];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int i = i0 + r * T + tid;
+        if (i < n) order[i0 + cnt[bk[r]] + rk[r]] = i;
+      }
+      __syncthreads();
+      for (int x = tid; x < NB; x += T) cnt[x] = 0;
+      if (i0 + 4 * T < n) __syncthreads();  // the next round counts again
+    }
+  }
+
+  // ---- score the candidates in that order: wave w takes 16-page groups w,
+  // w+W, ...; the summaries of the next group are in flight while the current
+  // group is computed (past the last group the prefetch reads page 0, unused)
   float e_loc = 0.f;
   uint32_t k_min = ~0u, k_max = 0;
   if (ranked) {
-    const int ngroups = (n + 15) / 16;
-    const int my_groups = ngroups > wave ? (ngroups - wave + W - 1) / W : 0;
-    score::QOperands<D> op;
-    score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
-    auto page_of = [&](int gi) {  // physical page of this lane's column in the wave's gi-th group, -1 if none
-      const int i = (wave + gi * W) * 16 + n_col;
-      return gi < my_groups && i < n ? page_phys[cand_lo + i] : -1;
-    };
-    uint4 bs[2][KSTEPS];
-    int phys_cur = page_of(0);
-    score::load_group<D>(bs[0], summ, max(phys_cur, 0), Hkv, g, lane);
     for (int gi = 0; gi < my_groups; gi += 2) {
 #pragma unroll
       for (int half = 0; half < 2; half++) {
         const int gcur = gi + half;
         uint4 *cur = bs[half];
         // prefetch: summaries of group gcur+1
-        const int phys_next = page_of(gcur + 1);
+        const int c_next = cand_of(gcur + 1);
+        const int phys_next = page_of(c_next);
         score::load_group<D>(bs[half ^ 1], summ, max(phys_next, 0), Hkv, g, lane);
         if (phys_cur < 0) {
 #pragma unroll
@@ -188,16 +240,16 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
         double best;
         float bound;
         score::score_group<D>(op, cur, G, lane, best, bound);
-        const int i = (wave + gcur * W) * 16 + n_col;
-        if (kg == 0 && gcur < my_groups && i < n) {
+        if (kg == 0 && c_cur >= 0) {
           const qasp_score sc = score::make_score(best, bound);
           const uint32_t o = sel::f32_order(sc.value);
-          keys32[i] = o;
+          keys32[c_cur] = o;
           k_min = min(k_min, o);
           k_max = max(k_max, o);
           e_loc = fmaxf(e_loc, sc.err);
         }
         phys_cur = phys_next;
+        c_cur = c_next;
       }
     }
     // block-wide key range and largest error bound through LDS atomics (the
@@ -296,7 +348,7 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
                      stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, out, sel,
                      sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G,
                      pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens, pol.window_tokens,
-                     pol.static_head_mask, scale_log2);
+                     pol.static_head_mask, scale_log2, lay.num_pool_pages);
   return hipGetLastError();
 }
 
