@@ -38,7 +38,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, float *__restrict__ out,
     int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
-    int window_tokens, uint64_t static_mask, float scale_log2, int pool_pages) {
+    int window_tokens, uint64_t static_mask, float scale_log2, uint32_t bucket_mul) {
   static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
@@ -110,27 +110,29 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
 
   // ---- append of the token at position L-1, head g, by the last wave (its
   // key row, value column and the page summary: slot 0 starts it, later slots
-  // widen it).  Its loads are issued here, the stores after the scoring, so
-  // their latency is hidden; the barrier after the scoring orders them
-  // before any read of the page.
+  // widen it).  Its loads are issued with the wave's first summary loads and
+  // its stores after the scoring, so their latency is hidden; the barrier
+  // after the scoring orders them before any read of the page.
   const bool appending = k_new != nullptr && L > 0;  // block-uniform
   const bool my_append = appending && wave == W - 1;
   const int a_t = appending ? (L - 1) % PS : 0;
-  size_t a_ph = 0;
-  uint32_t a_k = 0, a_lo = 0, a_hi = 0;
-  uint16_t a_v0 = 0, a_v1 = 0;
-  if (my_append) {
+  // set and used only under my_append (no merge with other values where the
+  // branches join, so nothing waits for these loads before the stores)
+  size_t a_ph;
+  uint32_t a_k, a_lo, a_hi;
+  uint16_t a_v0, a_v1;
+  auto append_loads = [&]() {
     a_ph = (size_t)page_phys[(L - 1) / PS] * Hkv + g;
-    a_k = ((const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D))[lane];  // D / 2 = 64 words: one per lane
+    const uint32_t *krow = (const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D);  // D / 2 = 64 words
+    a_k = krow[lane];
     const uint16_t *vn = v_new + ((size_t)b * Hkv + g) * DV;
     a_v0 = vn[lane];
     a_v1 = vn[lane + kWave];
-    if (summ != nullptr) {
-      const uint32_t *sp = (const uint32_t *)summ + a_ph * D;
-      a_lo = sp[lane];
-      a_hi = sp[D / 2 + lane];
-    }
-  }
+    // the summary rows (without summaries, the key row again: read, unused)
+    const uint32_t *sl = summ != nullptr ? (const uint32_t *)summ + a_ph * D : krow;
+    a_lo = sl[lane];
+    a_hi = sl[(summ != nullptr ? D / 2 : 0) + lane];
+  };
   auto append_stores = [&]() {
     ((uint32_t *)k_pool)[(a_ph * PS + a_t) * (D / 2) + lane] = a_k;
     v_pool[(a_ph * DV + lane) * PS + a_t] = a_v0;
@@ -154,7 +156,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   // its summary, so then the append completes first
   const bool early_append = appending && ranked && cand_hi == P;  // block-uniform
   if (early_append) {
-    if (my_append) append_stores();
+    if (my_append) {
+      append_loads();
+      append_stores();
+    }
     __syncthreads();
   }
 
@@ -177,10 +182,15 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   uint4 bs[2][KSTEPS];
   int c_cur = -1, phys_cur = -1;
   if (ranked) {
-    score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
     c_cur = cand_of(0);
     phys_cur = page_of(c_cur);
     score::load_group<D>(bs[0], summ, max(phys_cur, 0), Hkv, g, lane);
+    // the q operands from the LDS copy of the q rows when there is one
+    if (q_in_lds)
+      score::load_q_operands<D>(op, sh.qstage, G, true, lane);
+    else
+      score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
+    if (my_append && !early_append) append_loads();
     constexpr int NB = 256;
     int *cnt = &sh.hist[0][0];  // zero here; zeroed again before the selection uses it
     for (int i0 = s0; i0 < n; i0 += 4 * T) {
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int i = i0 + r * T + tid;
-        bk[r] = i < n ? min(max((int)(((long long)page_phys[cand_lo + i] * NB) / pool_pages), 0), NB - 1) : 0;
+        bk[r] = i < n ? min((int)__umulhi((uint32_t)page_phys[cand_lo + i], bucket_mul), NB - 1) : 0;
         rk[r] = i < n ? atomicAdd(&cnt[bk[r]], 1) : 0;
       }
       __syncthreads();
@@ -216,6 +226,8 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
       for (int x = tid; x < NB; x += T) cnt[x] = 0;
       if (i0 + 4 * T < n) __syncthreads();  // the next round counts again
     }
+  } else if (my_append) {
+    append_loads();
   }
 
   // ---- score the candidates in that order: wave w takes 16-page groups w,
@@ -343,12 +355,14 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = FusedLds(mp, max_sel, G).total;
   const float scale_log2 = scale * 1.4426950408889634f;
+  // physical page p falls in scoring bucket (p * bucket_mul) >> 32, monotone in p and below 256
+  const uint32_t bucket_mul = (uint32_t)std::min<uint64_t>((256ull << 32) / (uint64_t)lay.num_pool_pages, 0xffffffffull);
   dim3 grid(bat.batch, lay.num_kv_heads);
   hipLaunchKernelGGL((fused_step_gqa_kernel<128, 128, 16, kFusedWaves>), grid, dim3(kFusedWaves * 64), lds,
                      stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, out, sel,
                      sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G,
                      pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens, pol.window_tokens,
-                     pol.static_head_mask, scale_log2, lay.num_pool_pages);
+                     pol.static_head_mask, scale_log2, bucket_mul);
   return hipGetLastError();
 }
 
