@@ -295,7 +295,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const attend::PageRegs<D, DV> first =
       pw.load(pre ? page_phys[wave < cand_lo ? wave : cand_hi + (wave - cand_lo)] : (P > 0 ? page_phys[0] : 0), lane);
 
-  // ---- select
+  // ---- select (usually no page is in doubt: then the selection is the k
+  // largest keys and the list is written straight from them)
+  bool fast = false;
+  uint32_t uk_fast = 0;
   if (is_static) {
     const int sink_end = min(sink_tokens, L);
     const int win_begin = max(0, L - window_tokens);
@@ -304,20 +307,22 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
       if (a < sink_end || e > win_begin) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     }
   } else {
-    for (int j = tid; j < P; j += T)
-      if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     if (ranked) {
       k_min = sh_kmin;
       k_max = sh_kmax;
       e_loc = __int_as_float(sh_emax);
-      sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min, k_max,
-                                    q_in_lds ? sh.qstage : q + head0 * D, G, summ, pt_row, Hkv, g, nullptr,
-                                    page_phys + cand_lo);
+      fast = sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min,
+                                           k_max, q_in_lds ? sh.qstage : q + head0 * D, G, summ, pt_row, Hkv, g,
+                                           nullptr, page_phys + cand_lo, &uk_fast);
     }
+    if (!fast)
+      for (int j = tid; j < P; j += T)
+        if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
-  const int count = sel::emit_selection(sh, sel_bits, nwords,
-                                        sel_out ? sel_out + (size_t)unit * max_sel : nullptr, list, max_sel);
+  int32_t *sel_row = sel_out ? sel_out + (size_t)unit * max_sel : nullptr;
+  const int count = fast ? sel::emit_by_threshold(sh, keys32, n, uk_fast, cand_lo, cand_hi, P, sel_row, list, max_sel)
+                         : sel::emit_selection(sh, sel_bits, nwords, sel_row, list, max_sel);
   if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
   __syncthreads();
 

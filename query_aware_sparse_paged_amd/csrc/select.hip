@@ -69,6 +69,8 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
   if (tid == 0) sh.nlist = 0;
   __syncthreads();
 
+  bool fast = false;
+  uint32_t uk_fast = 0;
   if (is_static) {
     const int sink_end = min(sink_tokens, L);
     const int win_begin = max(0, L - window_tokens);
@@ -77,17 +79,21 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
       if (a < sink_end || e > win_begin) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     }
   } else {
-    for (int j = tid; j < P; j += THREADS)
-      if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
     if (ranked) {
       sel::block_max_min_max(e_loc, k_min, k_max, sh);
-      sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min, k_max,
-                                    q + ((size_t)b * Hq + (size_t)g * G) * D, G, summ,
-                                    page_table + (size_t)b * pt_stride, Hkv, g, row, nullptr);
+      fast = sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min,
+                                           k_max, q + ((size_t)b * Hq + (size_t)g * G) * D, G, summ,
+                                           page_table + (size_t)b * pt_stride, Hkv, g, row, nullptr, &uk_fast);
     }
+    if (!fast)
+      for (int j = tid; j < P; j += THREADS)
+        if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
-  const int count = sel::emit_selection(sh, sel_bits, nwords, sel + (size_t)unit * max_sel, nullptr, max_sel);
+  // without pages in doubt the list comes straight from the keys
+  int32_t *sel_row = sel + (size_t)unit * max_sel;
+  const int count = fast ? sel::emit_by_threshold(sh, keys32, n, uk_fast, cand_lo, cand_hi, P, sel_row, nullptr, max_sel)
+                         : sel::emit_selection(sh, sel_bits, nwords, sel_row, nullptr, max_sel);
   if (tid == 0) sel_count[unit] = count;
 }
 

@@ -651,8 +651,11 @@ __device__ double exact_page_key_heads(const uint16_t *qg, int G, const uint16_t
   return v;
 }
 
-// Marks the top-k candidates in sel_bits.  Called by every thread of the
-// block.  Preconditions: keys32[0..n) hold the candidates' order keys (LDS,
+// Marks the top-k candidates in sel_bits, or returns true without marking
+// anything when no candidate is in doubt (the k-th value beats the (k+1)-th
+// by more than twice the largest error bound): then the top k are exactly the
+// candidates whose key is >= *uk_fast (see emit_by_threshold).  Called by
+// every thread of the block.  Preconditions: keys32[0..n) hold the candidates' order keys (LDS,
 // visible to all threads); band_bits and sh.hist are zero; emax, k_min and k_max are the
 // block-wide max error bound and the smallest and largest key;
 // 0 < k < n.  Candidate i is logical page cand_lo + i; pt_row is the
@@ -663,11 +666,11 @@ __device__ double exact_page_key_heads(const uint16_t *qg, int G, const uint16_t
 // then pt_row is read) holds the candidates' physical pages.  qg may already
 // point to sh.qstage.
 template <int D, int NW>
-__device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t *keys64, uint32_t *sel_bits,
+__device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t *keys64, uint32_t *sel_bits,
                                   uint32_t *band_bits, int n, int k, int cand_lo, float emax, uint32_t k_min,
                                   uint32_t k_max, const uint16_t *qg, int G, const uint16_t *summ,
                                   const int32_t *pt_row, int Hkv, int g, const qasp_score *cand_scores,
-                                  const int32_t *cand_phys) {
+                                  const int32_t *cand_phys, uint32_t *uk_fast) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   uint32_t uk, uk1;
   if (tid == 0) sh.n_in = sh.n_band = 0;  // ordered before use by the barriers inside kth_pair
@@ -675,6 +678,12 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
   const float vk = f32_from_order(uk), vk1 = f32_from_order(uk1);
   const double t_in = (double)vk1 + 2.0 * (double)emax;
   const double t_out = (double)vk - 2.0 * (double)emax;
+  // block-uniform: every value >= vk is above t_in and every value <= vk1
+  // below t_out, so no page is in doubt and the k keys >= uk are the top k
+  if ((double)vk > t_in && (double)vk1 < t_out) {
+    *uk_fast = uk;
+    return true;
+  }
   int c_in = 0, c_band = 0;
   for (int i = tid; i < n; i += NW * kWave) {
     const double v = (double)f32_from_order(keys32[i]);
@@ -792,6 +801,59 @@ __device__ void select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
       }
     }
   }
+  return false;
+}
+
+// The ascending selection when select_candidates returned true: the sink
+// pages [0, cand_lo), the candidates whose key is >= uk, the local pages
+// [cand_hi, P).  Written to out_global (followed by -1 up to max_sel) and/or
+// out_lds; returns the count.  Thread t takes candidates 4t .. 4t+3 of a
+// round of 4T; a wave prefix sum and the wave totals in LDS give their
+// slots.  No bit map is built.
+template <int NW>
+__device__ int emit_by_threshold(SelShared<NW> &sh, const uint32_t *keys32, int n, uint32_t uk, int cand_lo,
+                                 int cand_hi, int P, int32_t *out_global, int32_t *out_lds, int max_sel) {
+  constexpr int T = NW * kWave;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  auto put = [&](int pos, int j) {
+    if (pos < max_sel) {
+      if (out_global) out_global[pos] = j;
+      if (out_lds) out_lds[pos] = j;
+    }
+  };
+  for (int j = tid; j < cand_lo; j += T) put(j, j);  // sink pages
+  int base = cand_lo;
+  for (int i0 = 0; i0 < n; i0 += 4 * T) {
+    const int i = i0 + 4 * tid;
+    uint32_t m = 0;  // bit r: candidate i + r is selected
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      if (i + r < n && keys32[i + r] >= uk) m |= 1u << r;
+    const int c = __popc(m);
+    const int incl = wave_incl_sum(c);
+    if (lane == kWave - 1) sh.red[wave][2] = incl;
+    __syncthreads();
+    int pos = base + incl - c, round = 0;
+#pragma unroll
+    for (int x = 0; x < NW; x++) {
+      const int t = sh.red[x][2];
+      if (x < wave) pos += t;
+      round += t;
+    }
+    while (m) {
+      const int r = __builtin_ctz(m);
+      m &= m - 1;
+      put(pos++, cand_lo + i + r);
+    }
+    base += round;
+    if (i0 + 4 * T < n) __syncthreads();  // sh.red is rewritten next round
+  }
+  const int nloc = P - cand_hi;
+  for (int x = tid; x < nloc; x += T) put(base + x, cand_hi + x);  // local pages
+  const int count = min(base + nloc, max_sel);
+  if (out_global)
+    for (int x = count + tid; x < max_sel; x += T) out_global[x] = -1;
+  return count;
 }
 
 // Writes the pages marked in sel_bits, in ascending order, to out_global
