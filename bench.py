@@ -56,22 +56,23 @@ def log(*a):
 
 
 def step_bytes(w, msel_counts):
-    """Algorithmic bytes of one step, split by kernel."""
+    """Algorithmic bytes of one step (what the method must move), split into
+    the scoring side (the 512 B summary of every candidate page-head, and each
+    sequence's page-table row once) and the attention side (the K and V tiles
+    of every selected page-head, q once, the fp32 output)."""
     s = w.spec
-    G = s.num_q_heads // s.num_kv_heads
     lens = w.seq_lens.cpu().tolist()
     summ_b = 2 * s.head_dim_k * 2
     kv_b = s.page_size * (s.head_dim_k + (0 if s.v_from_k else s.head_dim_v)) * 2
     score = decode = 0
     for b, L in enumerate(lens):
         P = (L + s.page_size - 1) // s.page_size
+        score += P * 4
         for g in range(s.num_kv_heads):
-            static = bool(s.static_heads and s.static_heads[g])
-            if not static:
-                C = max(0, P - s.n_sink_pages - s.n_local_pages)
-                score += C * (summ_b + 4 + 8) + G * s.head_dim_k * 2
-            n = int(msel_counts[b][g])
-            decode += n * (kv_b + 4 + 4) + G * s.head_dim_k * 2 + G * s.head_dim_v * 4
+            if not (s.static_heads and s.static_heads[g]):
+                score += max(0, P - s.n_sink_pages - s.n_local_pages) * summ_b
+            decode += int(msel_counts[b][g]) * kv_b
+    decode += s.batch * s.num_q_heads * (s.head_dim_k * 2 + s.head_dim_v * 4)
     return score, decode
 
 
