@@ -182,4 +182,17 @@ __device__ __forceinline__ bool head_is_static(uint64_t mask, int g) {
   return (mask >> g) & 1ull;
 }
 
+// KV heads in dispatch order: the query-aware heads first, then the static
+// ones.  Blocks start in index order as CUs free up, so when the units do not
+// all fit on the chip at once the long (scored) units start first and the
+// short static ones fill in behind them.  Returns the y-th head of that order.
+__device__ __forceinline__ int head_in_dispatch_order(uint64_t static_mask, int Hkv, int y) {
+  const uint64_t all = Hkv >= 64 ? ~0ull : ((1ull << Hkv) - 1);
+  const uint64_t qa = all & ~static_mask, st = all & static_mask;
+  const int n_qa = __popcll(qa);
+  uint64_t m = y < n_qa ? qa : st;
+  for (int r = y < n_qa ? y : y - n_qa; r > 0; r--) m &= m - 1;  // drop the r lowest set bits
+  return __ffsll((long long)m) - 1;
+}
+
 }  // namespace qasp

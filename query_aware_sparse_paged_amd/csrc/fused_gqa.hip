@@ -57,7 +57,8 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   int32_t *order = (int32_t *)((char *)dyn + lay.order);
   float *merge_area = (float *)((char *)dyn + lay.merge);
 
-  const int b = blockIdx.x, g = blockIdx.y;  // consecutive blocks (one per XCD in turn) take different sequences
+  // consecutive blocks (one per XCD in turn) take different sequences
+  const int b = blockIdx.x, g = head_in_dispatch_order(static_mask, Hkv, blockIdx.y);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n_col = lane & 15, kg = lane >> 4;
   const int unit = b * Hkv + g;
