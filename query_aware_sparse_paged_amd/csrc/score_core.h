@@ -120,9 +120,9 @@ __device__ __forceinline__ void score_group(const QOperands<D> &op, const uint4 
 // leader is certified when it beats the runner-up by more than twice the
 // error bound of every head's value.
 __device__ __forceinline__ qasp_score make_score(double best, float bound, double second = INFINITY,
-                                                 int arg = -1) {
+                                                 int arg = -1, float rel = kErrRel) {
   const float v = (float)best;
-  const float err = kErrRel * bound + kErrAbs;
+  const float err = rel * bound + kErrAbs;
   qasp_score sc;
   sc.reserved = 0;
   if (isfinite(v) && isfinite(err)) {

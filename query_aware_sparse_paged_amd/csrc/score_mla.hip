@@ -3,18 +3,25 @@
 //
 // The page bound is the one of score_core.h, U_h(j) = q_h^- . lo_j + q_h^+ .
 // hi_j, here a real contraction: 128 heads x 1152 channels against every
-// page.  A block of 8 waves stages the summary records of 16 pages in LDS
-// (row stride padded by 16 bytes so the 16 page columns fall on different
-// banks) and each wave contracts its 16 heads ([q^-, q^+] held as the MFMA A
-// operand, 36 steps of 16x16x32) against them; every 32-product MFMA result
-// is added in fp64.  The error bound uses Cauchy-Schwarz instead of a second
-// contraction on absolute values:
-//     S_h(j) = sum_d |q_hd| |x_hd| <= |q_h|_2 * N_j,  N_j^2 = sum_d max(lo_d^2, hi_d^2),
-//     |U_fp32 - U| <= 65 * 2^-23 * 1.01 * max_h |q_h|_2 * N_j * 1.01 + 2^-50
-// (the last 1.01 covers the fp32 evaluation of the norms).
-// Blocks are persistent over the 16-page groups of the batch, in sequence
-// order, with the next group's records loading while the current one is
-// contracted.
+// page.  A block of 8 waves stages the summary records of 16 pages in LDS and
+// each wave contracts its 16 heads ([q^-, q^+] formed from q on the fly as
+// the MFMA A operand, 36 steps of 16x16x32) against them.  The 32-product
+// MFMA results are summed in fp32 six at a time and the six partial sums in
+// fp64: per MFMA at most 64 roundings of unit 2^-23 on terms bounded by its
+// S, five fp32 additions per partial sum, exact fp64 conversions and
+// negligible fp64 additions, then the final rounding to fp32, so
+//     |U_fp32 - U| <= 71 * 2^-23 * 1.01 * S + 2^-50.
+// S comes from Cauchy-Schwarz instead of a second contraction on absolute
+// values:
+//     S_h(j) = sum_d |q_hd| |x_hd| <= |q_h|_2 * N_j,  N_j^2 = sum_d max(lo_d^2, hi_d^2)
+// (times 1.01 for the fp32 evaluation of the norms).
+// A block takes up to kMlaGroups consecutive 16-page groups of one sequence
+// and issues the loads of all their summary records at once, straight into
+// one LDS slab per group (global_load_lds, 16 bytes per lane; about 148 KB in
+// flight per CU, no registers held).  Chunk c (16 bytes) of page row n sits
+// at slot c ^ (n % 16) of the row, so the 16 rows of an MFMA B fragment fall
+// on different banks.  The block also writes the row's non-candidate slots
+// (-inf), so the score row needs no separate fill.
 #include "launch.h"
 #include "score_core.h"
 
@@ -24,10 +31,12 @@ namespace {
 
 constexpr int kMlaD = 576;
 constexpr int kMlaK2 = 2 * kMlaD;             // 1152 channels of [lo, hi]
-constexpr int kMlaSteps = kMlaK2 / 32;        // 36 MFMA steps
 constexpr int kMlaWaves = 8;                  // 8 x 16 = 128 heads
-constexpr int kRecBytes = kMlaK2 * 2 + 16;    // padded LDS row of one page record
+constexpr int kRecBytes = kMlaK2 * 2;         // LDS row of one page record (chunks swizzled)
 constexpr int kGroupBytes = 16 * kRecBytes;
+constexpr int kMlaGroups = 4;                 // 16-page groups per block (4 slabs: 144 KiB of LDS)
+constexpr int kMlaChunk = 6;                  // MFMA results summed in fp32 before the fp64 sum
+constexpr float kErrRelMla = 71.0f * 1.1920928955078125e-07f * 1.01f;  // see the file comment
 
 struct MlaScoreShared {
   double best[kMlaWaves][16];    // per wave and page: largest head value,
@@ -35,11 +44,16 @@ struct MlaScoreShared {
   int arg[kMlaWaves][16];        // and the leading head
   float norm2[kMlaWaves][16];  // partial page norms per wave
   float qnorm[kMlaWaves];
-  int phys[3][16];   // physical pages of groups gid, gid+1, gid+2 (slot gid % 3); -1 = not a candidate
+  int phys[kMlaGroups][16];  // physical pages of the block's groups; -1 = not a candidate
 };
 
-constexpr int kRecU4 = kMlaK2 / 8;                                      // 144 uint4 per record
-constexpr int kLoadsPerThread = (16 * kRecU4 + kMlaWaves * 64 - 1) / (kMlaWaves * 64);  // 5
+constexpr int kRecU4 = kMlaK2 / 8;            // 144 chunks of 16 bytes per record
+constexpr int kDmaPerGroup = 16 * kRecU4 / 64;  // 36 wave-wide 1 KB transfers per group
+static_assert(kRecU4 % 16 == 0 && (16 * kRecU4) % 64 == 0, "swizzle and transfer granularity");
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte offset of chunk c of row n inside a slab
+__device__ __forceinline__ int slab_off(int n, int c) { return n * kRecBytes + 16 * (c ^ (n & 15)); }
 
 // Merges the top two (b1 >= b2, leader a1) with another top two.
 __device__ __forceinline__ void top2_merge(double &b1, double &b2, int &a1, double ob1, double ob2, int oa) {
@@ -58,101 +72,94 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ summ,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     qasp_score *__restrict__ scores, int batch, int pt_stride, int max_pages, int Hq, int Hkv, int ps,
-    int n_sink, int n_local, uint64_t static_mask, int groups_per_seq, int groups_per_block) {
-  extern __shared__ uint4 stage[];  // 2 x kGroupBytes
+    int n_sink, int n_local, uint64_t static_mask, int groups_per_seq) {
+  extern __shared__ uint4 stage[];  // kMlaGroups x kGroupBytes
   __shared__ MlaScoreShared sh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane & 15, kg = lane >> 4;
   const int g = 0;  // one latent KV head
-  const int total = batch * groups_per_seq;
+  const int blocks_per_seq = (groups_per_seq + kMlaGroups - 1) / kMlaGroups;
   // the blocks of a sequence run on one XCD, which then reads its q once into L2
-  const int first = xcd_contiguous_item(blockIdx.x, gridDim.x) * groups_per_block;
-  const int last = min(first + groups_per_block, total);
-  if (first >= last) return;
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
+  const int b = item / blocks_per_seq;
+  if (b >= batch) return;
+  const int gfirst = (item % blocks_per_seq) * kMlaGroups;
+  const int ng = min(kMlaGroups, groups_per_seq - gfirst);
+  // the page-table entries of the block's groups are read together with the
+  // length (assuming the usual cand_lo = n_sink; re-read if it is not)
+  int pv = -1;
+  {
+    const int j = n_sink + gfirst * 16 + tid;
+    if (tid < 16 * kMlaGroups && j < max_pages) pv = page_table[(size_t)b * pt_stride + j];
+  }
+  const int L = seq_lens[b];
+  const int P = num_pages_of(L, ps);
+  const int cand_lo = min(n_sink, P);
+  const int cand_hi = head_is_static(static_mask, g) ? cand_lo : max(cand_lo, P - n_local);
+  qasp_score *row = scores + ((size_t)b * Hkv + g) * max_pages;
+  const qasp_score none = {-INFINITY, 0.f, -1, 0};
+  if (gfirst == 0) {  // the row's slots outside the candidates: sink pages, local pages, past the sequence
+    for (int j = tid; j < cand_lo && j < max_pages; j += kMlaWaves * 64) row[j] = none;
+    for (int j = cand_hi + tid; j < max_pages; j += kMlaWaves * 64) row[j] = none;
+  }
 
-  // group -> (sequence, first logical page, end of the candidates)
-  auto group_pages = [&](int gid, int &b, int &j0, int &cand_hi) {
-    b = gid / groups_per_seq;
-    const int L = seq_lens[b];
-    const int P = num_pages_of(L, ps);
-    const int cand_lo = min(n_sink, P);
-    cand_hi = head_is_static(static_mask, g) ? cand_lo : max(cand_lo, P - n_local);
-    j0 = cand_lo + (gid % groups_per_seq) * 16;
-  };
-  // page-table entry of page tid (< 16) of group gid
-  auto phys_of = [&](int gid) {
-    if (gid >= last) return -1;
-    int b, j0, cand_hi;
-    group_pages(gid, b, j0, cand_hi);
-    const int j = j0 + tid;
-    return j < cand_hi ? page_table[(size_t)b * pt_stride + j] : -1;
-  };
-  // the group's 16 summary records, read into registers (5 uint4 per thread)
-  auto load_regs = [&](int slot, uint4 *r) {
+  // physical pages of the block's groups (page j0 + 16 x + t of group x)
+  const int j0 = cand_lo + gfirst * 16;
+  if (tid < 16 * kMlaGroups) {
+    const int x = tid / 16, j = j0 + tid;
+    if (cand_lo != n_sink && j < max_pages) pv = page_table[(size_t)b * pt_stride + j];  // short sequence
+    sh.phys[x][tid % 16] = x < ng && j < cand_hi ? pv : -1;
+  }
+  // q of the wave's 16 heads: column n = head 16 wave + n, channels 32i + 8kg ..
+  uint4 qraw[kMlaD / 32];
+  {
+    const uint16_t *qg = q + ((size_t)b * Hq + (size_t)wave * 16) * kMlaD;
 #pragma unroll
-    for (int u = 0; u < kLoadsPerThread; u++) {
-      const int e = tid + u * kMlaWaves * 64;
-      const int p = e / kRecU4, c = e % kRecU4;
-      const int phys = e < 16 * kRecU4 ? sh.phys[slot][p] : -1;
-      r[u] = phys >= 0 ? *((const uint4 *)(summ + ((size_t)phys * Hkv + g) * kMlaK2) + c) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_regs = [&](int buf, const uint4 *r) {
-    char *dst = (char *)stage + (size_t)buf * kGroupBytes;
-#pragma unroll
-    for (int u = 0; u < kLoadsPerThread; u++) {
-      const int e = tid + u * kMlaWaves * 64;
-      if (e < 16 * kRecU4) *(uint4 *)(dst + (size_t)(e / kRecU4) * kRecBytes + (e % kRecU4) * 16) = r[u];
-    }
-  };
-
-  if (tid < 16) {
-    sh.phys[first % 3][tid] = phys_of(first);
-    sh.phys[(first + 1) % 3][tid] = phys_of(first + 1);
+    for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qg + (size_t)n * kMlaD + 32 * i + 8 * kg);
   }
   __syncthreads();
-  uint4 regs[kLoadsPerThread];
-  load_regs(first % 3, regs);
-  store_regs(0, regs);
-
-  uint4 qraw[kMlaD / 32];  // q of head 16 wave + (l % 16), channels 32i + 8(l / 16) ...
-  int cur_b = -1;
-  for (int gid = first; gid < last; gid++) {
-    const int buf = (gid - first) & 1;
-    int b, j0, cand_hi;
-    group_pages(gid, b, j0, cand_hi);
-    if (b != cur_b) {  // this wave's 16 heads of the sequence's query, and the largest |q_h|
-      cur_b = b;
-      const uint16_t *qg = q + ((size_t)b * Hq + (size_t)wave * 16) * kMlaD;
-#pragma unroll
-      for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qg + (size_t)n * kMlaD + 32 * i + 8 * kg);
-      float s2 = 0.f;  // |q_h|^2 of head n over this lane's quarter of the channels
-#pragma unroll
-      for (int i = 0; i < kMlaD / 32; i++) {
-        const uint32_t w4[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          const float a = bf16_lo_to_f32(w4[k]), c = bf16_hi_to_f32(w4[k]);
-          s2 += a * a + c * c;
-        }
-      }
-      s2 += __shfl_xor(s2, 16, kWave);
-      s2 += __shfl_xor(s2, 32, kWave);
-      const float qmax = wave_max(sqrtf(s2));
-      if (lane == 0) sh.qnorm[wave] = qmax;
+  // every record of every group, straight to LDS: transfer t of group x
+  // fills slots 64 t .. 64 t + 63 of slab x (row slot / 144), lane l loading
+  // the chunk whose swizzled slot is 64 t + l; rows past the candidates read
+  // page 0 (their columns are never stored)
+  for (int x = 0; x < ng; x++) {
+    char *slab = (char *)stage + (size_t)x * kGroupBytes;
+    for (int t = wave; t < kDmaPerGroup; t += kMlaWaves) {
+      const int slot = 64 * t + lane, r = slot / kRecU4, sl = slot % kRecU4;
+      const int ph = max(sh.phys[x][r], 0);
+      const uint16_t *src = summ + ((size_t)ph * Hkv + g) * kMlaK2 + 8 * (sl ^ (r & 15));
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(slab + 1024 * t), 16, 0, 0);
     }
-    __syncthreads();  // stage `buf` and sh.phys of gid+1 are complete
-    // prefetch: page-table entries of gid+2, summary records of gid+1
-    const int phys_ahead = tid < 16 ? phys_of(gid + 2) : -1;
-    if (gid + 1 < last) load_regs((gid + 1) % 3, regs);
-    const char *rec = (const char *)stage + (size_t)buf * kGroupBytes;
+  }
+  // the largest |q_h| of the wave's heads
+  {
+    float s2 = 0.f;  // |q_h|^2 of head n over this lane's quarter of the channels
+#pragma unroll
+    for (int i = 0; i < kMlaD / 32; i++) {
+      const uint32_t w4[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const float a = bf16_lo_to_f32(w4[k]), c = bf16_hi_to_f32(w4[k]);
+        s2 += a * a + c * c;
+      }
+    }
+    s2 += __shfl_xor(s2, 16, kWave);
+    s2 += __shfl_xor(s2, 32, kWave);
+    const float qmax = wave_max(sqrtf(s2));
+    if (lane == 0) sh.qnorm[wave] = qmax;
+  }
+
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's transfers have landed (the barrier below publishes them)
+  for (int x = 0; x < ng; x++) {
+    const char *rec = (const char *)stage + (size_t)x * kGroupBytes;
+    __syncthreads();  // every slab has landed; the previous group's results are read
     // page norms N_j^2 = sum_d max(lo_d^2, hi_d^2): wave w adds channel blocks
     // 32i + 8kg .. (i = w, w + 8, ...) of page n; the blocks sum in LDS below
     {
-      const char *rp = rec + (size_t)n * kRecBytes + 16 * kg;
       float a = 0.f;
       for (int i = wave; i < kMlaD / 32; i += kMlaWaves) {
-        const uint4 lo4 = *(const uint4 *)(rp + 64 * i), hi4 = *(const uint4 *)(rp + 2 * kMlaD + 64 * i);
+        const uint4 lo4 = *(const uint4 *)(rec + slab_off(n, 4 * i + kg));
+        const uint4 hi4 = *(const uint4 *)(rec + slab_off(n, kMlaD / 8 + 4 * i + kg));
         const uint32_t lw[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, hw[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
 #pragma unroll
         for (int k = 0; k < 4; k++) {
@@ -165,20 +172,29 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       a += __shfl_xor(a, 32, kWave);
       if (kg == 0) sh.norm2[wave][n] = a;
     }
-    // contraction over [lo, hi]: step i < 18 pairs q^- with lo channels
-    // 32i + 8kg ..., step 18 + i pairs q^+ with the same hi channels
+    // contraction over [lo, hi]: q^- with lo channels 32i + 8kg ... and q^+
+    // (the rest of q's bits) with the same hi channels, for i = 0 .. 17
     double u64[4] = {0.0, 0.0, 0.0, 0.0};
-    const char *bp = rec + (size_t)n * kRecBytes + 16 * kg;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kMlaSteps; i++) {
-      const uint4 bfrag = *(const uint4 *)(bp + 64 * i);
-      const uint4 afrag = score::map4(qraw[i % (kMlaD / 32)], i < kMlaD / 32 ? 0 : 1);
-      const floatx4 ui = mfma16x16x32(afrag, bfrag, floatx4{0.f, 0.f, 0.f, 0.f});
+    for (int i = 0; i < kMlaD / 32; i++) {
+      const uint4 qn = score::map4(qraw[i], 0);
+      const uint4 qp = make_uint4(qraw[i].x ^ qn.x, qraw[i].y ^ qn.y, qraw[i].z ^ qn.z, qraw[i].w ^ qn.w);
+      const floatx4 un = mfma16x16x32(qn, *(const uint4 *)(rec + slab_off(n, 4 * i + kg)), floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 up =
+          mfma16x16x32(qp, *(const uint4 *)(rec + slab_off(n, kMlaD / 8 + 4 * i + kg)), floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int r = 0; r < 4; r++) u64[r] += (double)ui[r];
+      for (int r = 0; r < 4; r++) part[r] = (part[r] + un[r]) + up[r];
+      if ((2 * i + 2) % kMlaChunk == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          u64[r] += (double)part[r];
+          part[r] = 0.f;
+        }
+      }
     }
-    // lane (n, kg) holds heads 16 wave + 4kg + r of page n: max over the wave's heads
-    // top two of the wave's heads for page n: value, runner-up, leading head
+    // lane (n, kg) holds heads 16 wave + 4kg + r of page n: top two of the
+    // wave's heads for page n (value, runner-up, leading head)
     double b1 = -INFINITY, b2 = -INFINITY;
     int a1 = -1;
 #pragma unroll
@@ -202,11 +218,9 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       sh.second[wave][n] = b2;
       sh.arg[wave][n] = a1;
     }
-    if (gid + 1 < last) store_regs(buf ^ 1, regs);
-    if (tid < 16) sh.phys[(gid + 2) % 3][tid] = phys_ahead;
     __syncthreads();
     if (wave == 0 && lane < 16) {
-      const int j = j0 + lane;
+      const int j = j0 + 16 * x + lane;
       if (j < cand_hi) {
         double m = sh.best[0][lane], m2 = sh.second[0][lane];
         int arg = sh.arg[0][lane];
@@ -218,35 +232,25 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
           n2 += sh.norm2[w][lane];
         }
         const float bound = qn * sqrtf(n2) * 1.01f;  // >= every head's S
-        scores[((size_t)b * Hkv + g) * max_pages + j] = score::make_score(m, bound, m2, arg);
+        row[j] = score::make_score(m, bound, m2, arg, kErrRelMla);
       }
     }
   }
 }
 
-// Fills every row with (-inf, 0); the candidates are overwritten by the scoring kernel.
-__global__ void fill_scores_kernel(qasp_score *scores, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    scores[i] = qasp_score{-INFINITY, 0.f, -1, 0};
-}
-
 hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                             const uint16_t *q, const uint16_t *summ, qasp_score *scores, hipStream_t stream) {
-  const size_t n = (size_t)bat.batch * lay.num_kv_heads * bat.max_pages;
-  size_t fill_blocks = (n + 255) / 256;
-  if (fill_blocks > 2048) fill_blocks = 2048;
-  hipLaunchKernelGGL(fill_scores_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, scores, n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int groups_per_seq = (bat.max_pages + 15) / 16;
-  const int total = bat.batch * groups_per_seq;
-  int per_block = (total + 255) / 256;  // about one block per CU
-  if (per_block < 1) per_block = 1;
-  const int blocks = (total + per_block - 1) / per_block;
-  hipLaunchKernelGGL(score_mla_kernel, dim3(blocks), dim3(kMlaWaves * 64), 2 * kGroupBytes, stream, q, summ,
-                     bat.page_table, bat.seq_lens, scores, bat.batch, bat.pt_stride, bat.max_pages,
+  if (bat.batch == 0 || bat.max_pages == 0) return hipSuccess;
+  // groups cover [cand_lo, cand_lo + 16 groups_per_seq), which holds every
+  // candidate: cand_hi - cand_lo <= max_pages - n_sink - n_local when there are any
+  const int max_cand = std::max(0, bat.max_pages - pol.n_sink_pages - pol.n_local_pages);
+  const int groups_per_seq = std::max(1, (max_cand + 15) / 16);
+  const int blocks_per_seq = (groups_per_seq + kMlaGroups - 1) / kMlaGroups;
+  const int blocks = bat.batch * blocks_per_seq;
+  hipLaunchKernelGGL(score_mla_kernel, dim3(blocks), dim3(kMlaWaves * 64), kMlaGroups * kGroupBytes, stream, q,
+                     summ, bat.page_table, bat.seq_lens, scores, bat.batch, bat.pt_stride, bat.max_pages,
                      bat.num_q_heads, lay.num_kv_heads, lay.page_size, pol.n_sink_pages, pol.n_local_pages,
-                     pol.static_head_mask, groups_per_seq, per_block);
+                     pol.static_head_mask, groups_per_seq);
   return hipGetLastError();
 }
 
