@@ -192,41 +192,8 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     else
       score::load_q_operands<D>(op, q + head0 * D, G, true, lane);
     if (my_append && !early_append) append_loads();
-    constexpr int NB = 256;
-    int *cnt = &sh.hist[0][0];  // zero here; zeroed again before the selection uses it
-    for (int i0 = s0; i0 < n; i0 += 4 * T) {
-      int bk[4], rk[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int i = i0 + r * T + tid;
-        bk[r] = i < n ? min((int)__umulhi((uint32_t)page_phys[cand_lo + i], bucket_mul), NB - 1) : 0;
-        rk[r] = i < n ? atomicAdd(&cnt[bk[r]], 1) : 0;
-      }
-      __syncthreads();
-      if (wave == 0) {  // exclusive scan of the bucket counts, in place (4 per lane)
-        int c[4], t = 0;
-#pragma unroll
-        for (int x = 0; x < 4; x++) {
-          c[x] = cnt[4 * lane + x];
-          t += c[x];
-        }
-        int e = wave_incl_sum(t) - t;
-#pragma unroll
-        for (int x = 0; x < 4; x++) {
-          cnt[4 * lane + x] = e;
-          e += c[x];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int i = i0 + r * T + tid;
-        if (i < n) order[i0 + cnt[bk[r]] + rk[r]] = i;
-      }
-      __syncthreads();
-      for (int x = tid; x < NB; x += T) cnt[x] = 0;
-      if (i0 + 4 * T < n) __syncthreads();  // the next round counts again
-    }
+    // (sh.hist is zero here and zero again after the sort)
+    score::bucket_order<T>(order, page_phys + cand_lo, s0, n, bucket_mul, &sh.hist[0][0]);
   } else if (my_append) {
     append_loads();
   }
@@ -237,34 +204,15 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   float e_loc = 0.f;
   uint32_t k_min = ~0u, k_max = 0;
   if (ranked) {
-    for (int gi = 0; gi < my_groups; gi += 2) {
-#pragma unroll
-      for (int half = 0; half < 2; half++) {
-        const int gcur = gi + half;
-        uint4 *cur = bs[half];
-        // prefetch: summaries of group gcur+1
-        const int c_next = cand_of(gcur + 1);
-        const int phys_next = page_of(c_next);
-        score::load_group<D>(bs[half ^ 1], summ, max(phys_next, 0), Hkv, g, lane);
-        if (phys_cur < 0) {
-#pragma unroll
-          for (int i = 0; i < KSTEPS; i++) cur[i] = make_uint4(0, 0, 0, 0);
-        }
-        double best;
-        float bound;
-        score::score_group<D>(op, cur, G, lane, best, bound);
-        if (kg == 0 && c_cur >= 0) {
-          const qasp_score sc = score::make_score(best, bound);
-          const uint32_t o = sel::f32_order(sc.value);
-          keys32[c_cur] = o;
-          k_min = min(k_min, o);
-          k_max = max(k_max, o);
-          e_loc = fmaxf(e_loc, sc.err);
-        }
-        phys_cur = phys_next;
-        c_cur = c_next;
-      }
-    }
+    score::score_groups<D>(op, bs, summ, Hkv, g, G, my_groups, c_cur, phys_cur, lane, cand_of, page_of,
+                           [&](int c, double best, float bound) {
+                             const qasp_score sc = score::make_score(best, bound);
+                             const uint32_t o = sel::f32_order(sc.value);
+                             keys32[c] = o;
+                             k_min = min(k_min, o);
+                             k_max = max(k_max, o);
+                             e_loc = fmaxf(e_loc, sc.err);
+                           });
     // block-wide key range and largest error bound through LDS atomics (the
     // barrier before the selection orders them)
     k_min = ~(uint32_t)wave_max_dpp((int)(~k_min ^ 0x80000000u)) ^ 0x80000000u;
@@ -361,8 +309,7 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = FusedLds(mp, max_sel, G).total;
   const float scale_log2 = scale * 1.4426950408889634f;
-  // physical page p falls in scoring bucket (p * bucket_mul) >> 32, monotone in p and below 256
-  const uint32_t bucket_mul = (uint32_t)std::min<uint64_t>((256ull << 32) / (uint64_t)lay.num_pool_pages, 0xffffffffull);
+  const uint32_t bucket_mul = score::bucket_multiplier(lay.num_pool_pages);
   dim3 grid(bat.batch, lay.num_kv_heads);
   hipLaunchKernelGGL((fused_step_gqa_kernel<128, 128, 16, kFusedWaves>), grid, dim3(kFusedWaves * 64), lds,
                      stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, out, sel,

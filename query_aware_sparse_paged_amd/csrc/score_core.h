@@ -114,6 +114,94 @@ __device__ __forceinline__ void score_group(const QOperands<D> &op, const uint4 
   bound = fmaxf(bound, __shfl_xor(bound, 32, kWave));
 }
 
+// Candidate scoring order by physical page: positions [s0, n) of order[]
+// (LDS) receive the candidates s0 .. n-1 sorted into 256 equal ranges of the
+// pool by their physical page phys[i] (LDS), a counting sort in rounds of 4T
+// (bucket of page p: (p * bucket_mul) >> 32).  The order inside a bucket is
+// whatever the LDS atomics give; callers use the order only to schedule
+// loads, so no result depends on it.  cnt: 256 ints of LDS, zero on entry
+// and on return.  Called by all T threads of the block; ends with a barrier
+// when it sorted anything.
+template <int T>
+__device__ void bucket_order(int32_t *order, const int32_t *phys, int s0, int n, uint32_t bucket_mul, int *cnt) {
+  constexpr int NB = 256;
+  static_assert(T >= NB && T % kWave == 0, "one bucket per thread or more");
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  for (int i0 = s0; i0 < n; i0 += 4 * T) {
+    int bk[4], rk[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int i = i0 + r * T + tid;
+      bk[r] = i < n ? min((int)__umulhi((uint32_t)phys[i], bucket_mul), NB - 1) : 0;
+      rk[r] = i < n ? atomicAdd(&cnt[bk[r]], 1) : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of the bucket counts, in place (4 per lane)
+      int c[4], t = 0;
+#pragma unroll
+      for (int x = 0; x < 4; x++) {
+        c[x] = cnt[4 * lane + x];
+        t += c[x];
+      }
+      int e = wave_incl_sum(t) - t;
+#pragma unroll
+      for (int x = 0; x < 4; x++) {
+        cnt[4 * lane + x] = e;
+        e += c[x];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int i = i0 + r * T + tid;
+      if (i < n) order[i0 + cnt[bk[r]] + rk[r]] = i;
+    }
+    __syncthreads();
+    for (int x = tid; x < NB; x += T) cnt[x] = 0;
+    if (i0 + 4 * T < n) __syncthreads();  // the next round counts again
+  }
+}
+
+// The host-side multiplier of bucket_order for a pool of pool_pages pages.
+__host__ __device__ inline uint32_t bucket_multiplier(int pool_pages) {
+  const unsigned long long m = (256ull << 32) / (unsigned long long)(pool_pages > 0 ? pool_pages : 1);
+  return m > 0xffffffffull ? 0xffffffffu : (uint32_t)m;
+}
+
+// One wave's share of a unit's scoring: the wave's groups 0 .. my_groups-1
+// (16 candidates each; cand_of(gi) is this lane's candidate in its gi-th
+// group, -1 if none, phys_of(c) that candidate's physical page), the next
+// group's summaries in flight while the current one is computed.  bs[0]
+// already holds group 0, whose lane candidate is c_cur (page phys_cur).
+// emit(c, best, bound) runs on the lanes with kg = 0 for every candidate.
+template <int D, typename CandOf, typename PhysOf, typename Emit>
+__device__ __forceinline__ void score_groups(const QOperands<D> &op, uint4 (&bs)[2][2 * D / 32], const uint16_t *summ,
+                                             int Hkv, int g, int G, int my_groups, int c_cur, int phys_cur, int lane,
+                                             CandOf cand_of, PhysOf phys_of, Emit emit) {
+  constexpr int KSTEPS = 2 * D / 32;
+  const int kg = lane >> 4;
+  for (int gi = 0; gi < my_groups; gi += 2) {
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      uint4 *cur = bs[half];
+      // prefetch: summaries of the next group (page 0 past the last)
+      const int c_next = cand_of(gi + half + 1);
+      const int phys_next = phys_of(c_next);
+      load_group<D>(bs[half ^ 1], summ, max(phys_next, 0), Hkv, g, lane);
+      if (phys_cur < 0) {
+#pragma unroll
+        for (int i = 0; i < KSTEPS; i++) cur[i] = make_uint4(0, 0, 0, 0);
+      }
+      double best;
+      float bound;
+      score_group<D>(op, cur, G, lane, best, bound);
+      if (kg == 0 && c_cur >= 0) emit(c_cur, best, bound);
+      phys_cur = phys_next;
+      c_cur = c_next;
+    }
+  }
+}
+
 // The stored score of a candidate page: fp32 value and error bound; an
 // overflow becomes (0, inf) so that selection re-scores the page exactly.
 // With the runner-up head's value (second) and the leading head (arg), the
