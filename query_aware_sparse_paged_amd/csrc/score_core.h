@@ -11,13 +11,15 @@
 // is added in fp64, so the only fp32 rounding is inside one MFMA.  Alongside,
 // chained MFMAs on absolute values give S_h(j) = sum_d |q_d| |x_d|, from
 // which a rigorous bound on the error of the fp32 score follows:
-//     |U_fp32 - U| <= 65 * 2^-23 * S * 1.01 + 2^-50
-// (per MFMA at most one rounding per product and per addition, unit roundoff
-// taken as 2^-23 so that a faithful rather than nearest rounding is covered;
-// the fp64 additions and the final rounding to fp32 add less than 2^-23 S;
-// the absolute term covers flushed subnormal operands and products when
-// |q|, |k| <= 2^64).  The selection uses this bound to decide which pages it
-// must re-score exactly.
+//     |U_fp32 - U| <= 33 * 2^-23 * S * 1.01 + 2^-50
+// The product of two bf16 values (8-bit significands) is exact in fp32, so an
+// MFMA rounds only in its additions: at most 32 of them, each on a partial
+// sum bounded by that step's share of S, with unit roundoff taken as 2^-23 so
+// that a faithful rather than nearest rounding is covered; the exact fp64
+// conversions, the fp64 additions and the final rounding to fp32 add less than
+// 2^-23 S; the absolute term covers flushed subnormal operands and products
+// when |q|, |k| <= 2^64.  The selection uses this bound to decide which pages
+// it must re-score exactly.
 #pragma once
 
 #include "common.h"
@@ -25,7 +27,7 @@
 namespace qasp {
 namespace score {
 
-constexpr float kErrRel = 65.0f * 1.1920928955078125e-07f * 1.01f;  // 65 * 2^-23 * 1.01
+constexpr float kErrRel = 33.0f * 1.1920928955078125e-07f * 1.01f;  // 33 * 2^-23 * 1.01
 constexpr float kErrAbs = 8.8817841970012523e-16f;                   // 2^-50
 
 __device__ __forceinline__ uint4 map4(uint4 v, int mode) {

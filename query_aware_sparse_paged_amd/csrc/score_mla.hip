@@ -7,10 +7,11 @@
 // each wave contracts its 16 heads ([q^-, q^+] formed from q on the fly as
 // the MFMA A operand, 36 steps of 16x16x32) against them.  The 32-product
 // MFMA results are summed in fp32 six at a time and the six partial sums in
-// fp64: per MFMA at most 64 roundings of unit 2^-23 on terms bounded by its
-// S, five fp32 additions per partial sum, exact fp64 conversions and
-// negligible fp64 additions, then the final rounding to fp32, so
-//     |U_fp32 - U| <= 71 * 2^-23 * 1.01 * S + 2^-50.
+// fp64: per MFMA at most 32 roundings of unit 2^-23 (its bf16 products are
+// exact) on partial sums bounded by its S, five fp32 additions per partial
+// sum, exact fp64 conversions and negligible fp64 additions, then the final
+// rounding to fp32, so
+//     |U_fp32 - U| <= 39 * 2^-23 * 1.01 * S + 2^-50.
 // S comes from Cauchy-Schwarz instead of a second contraction on absolute
 // values:
 //     S_h(j) = sum_d |q_hd| |x_hd| <= |q_h|_2 * N_j,  N_j^2 = sum_d max(lo_d^2, hi_d^2)
@@ -36,7 +37,7 @@ constexpr int kRecBytes = kMlaK2 * 2;         // LDS row of one page record (chu
 constexpr int kGroupBytes = 16 * kRecBytes;
 constexpr int kMlaGroups = 4;                 // 16-page groups per block (4 slabs: 144 KiB of LDS)
 constexpr int kMlaChunk = 6;                  // MFMA results summed in fp32 before the fp64 sum
-constexpr float kErrRelMla = 71.0f * 1.1920928955078125e-07f * 1.01f;  // see the file comment
+constexpr float kErrRelMla = 39.0f * 1.1920928955078125e-07f * 1.01f;  // see the file comment
 
 struct MlaScoreShared {
   double best[kMlaWaves][16];    // per wave and page: largest head value,
