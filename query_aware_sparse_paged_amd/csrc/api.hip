@@ -208,7 +208,8 @@ int32_t qasp_score_pages(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (bat->batch == 0 || bat->max_pages == 0) return QASP_OK;
   if (!scores) return QASP_ERR_NULL_ARG;
   if (!all_static(*lay, *pol) && (!q || !summ)) return QASP_ERR_NULL_ARG;
-  return status_of(launch_score_pages(*lay, *bat, *pol, q, summ, scores, (hipStream_t)stream));
+  return status_of(launch_score_pages(*lay, *bat, *pol, q, summ, scores, (hipStream_t)stream,
+                                      token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr)));
 }
 
 int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
@@ -275,8 +276,13 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   int32_t *sel_out = sel ? sel : ws.sel;
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   hipError_t e = hipSuccess;
-  if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
-  if (e == hipSuccess && scored) e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s);
+  // the scoring kernel appends the token when its page is no candidate (a local
+  // page); otherwise the append runs first, so the page is scored with it
+  const bool fold_append = k_new && scored && pol->n_local_pages >= 1;
+  if (k_new && !fold_append) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
+  if (e == hipSuccess && scored)
+    e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s,
+                           token_append(*lay, fold_append ? k_new : nullptr, v_new, k_pool, v_pool, summ));
   if (e == hipSuccess)
     e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
   if (e == hipSuccess)

@@ -178,6 +178,50 @@ __device__ __forceinline__ int xcd_contiguous_item(int blk, int total) {
   return total % kXcds == 0 ? (blk % kXcds) * (total / kXcds) + blk / kXcds : blk;
 }
 
+// The new token of a decode step, appended by one block for the KV heads
+// [g0, g1) of sequence b: its key row and value column go into the page
+// `phys` at slot t, and its key is folded into the page summary (slot 0
+// starts it: elementwise min / max on bf16 order keys, -0 below +0).  The
+// block's threads share the work (tid, nthreads); no synchronisation inside.
+struct TokenAppend {
+  const uint32_t *k_new;  // [B][Hkv][D / 2] bf16 pairs
+  const uint16_t *v_new;  // [B][Hkv][Dv], or null (latent heads)
+  uint32_t *k_pool;       // [pool][Hkv][ps][D / 2]
+  uint16_t *v_pool;       // [pool][Hkv][Dv][ps], or null
+  uint32_t *summ;         // [pool][Hkv][2][D / 2], or null
+  int num_kv_heads, head_dim_k, head_dim_v, ps;
+
+  __device__ void run(int b, int g0, int g1, int phys, int t, int tid, int nthreads) const {
+    const int words = head_dim_k / 2;
+    for (int item = tid; item < (g1 - g0) * words; item += nthreads) {
+      const int g = g0 + item / words, w = item % words;
+      const size_t ph = (size_t)phys * num_kv_heads + g;
+      const uint32_t kv = k_new[((size_t)b * num_kv_heads + g) * words + w];
+      k_pool[(ph * ps + t) * words + w] = kv;
+      if (summ) {
+        uint32_t *s = summ + ph * 2 * words;
+        uint32_t lo = kv, hi = kv;
+        if (t != 0) {
+          const int v0 = bf16_order_key(kv & 0xffffu), v1 = bf16_order_key(kv >> 16);
+          const uint32_t ol = s[w], oh = s[words + w];
+          lo = bf16_from_order_key(min(v0, bf16_order_key(ol & 0xffffu))) |
+               (bf16_from_order_key(min(v1, bf16_order_key(ol >> 16))) << 16);
+          hi = bf16_from_order_key(max(v0, bf16_order_key(oh & 0xffffu))) |
+               (bf16_from_order_key(max(v1, bf16_order_key(oh >> 16))) << 16);
+        }
+        s[w] = lo;
+        s[words + w] = hi;
+      }
+    }
+    if (v_pool)
+      for (int item = tid; item < (g1 - g0) * head_dim_v; item += nthreads) {
+        const int g = g0 + item / head_dim_v, dv = item % head_dim_v;
+        const size_t ph = (size_t)phys * num_kv_heads + g;
+        v_pool[(ph * head_dim_v + dv) * ps + t] = v_new[((size_t)b * num_kv_heads + g) * head_dim_v + dv];
+      }
+  }
+};
+
 __device__ __forceinline__ bool head_is_static(uint64_t mask, int g) {
   return (mask >> g) & 1ull;
 }

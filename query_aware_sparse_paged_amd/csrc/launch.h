@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/qasp.h"
+#include "common.h"
 
 namespace qasp {
 
@@ -41,11 +42,18 @@ hipError_t launch_build_summaries(const qasp_layout &lay, const qasp_batch &bat,
 hipError_t launch_append_kv(const qasp_layout &lay, const qasp_batch &bat, int pos_offset,
                             const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
                             uint16_t *v_pool, uint16_t *summ, hipStream_t stream);
+// The append of a decode step as kernel arguments (null k_new: no append).
+TokenAppend token_append(const qasp_layout &lay, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                         uint16_t *v_pool, uint16_t *summ);
+// Scoring; with ap.k_new set, the first block of every (sequence, KV head)
+// row also appends the step's token at position L-1 (only valid when that
+// page is not a candidate, i.e. n_local_pages >= 1).
 hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
-                              qasp_score *scores, hipStream_t stream);
+                              qasp_score *scores, hipStream_t stream, const TokenAppend &ap);
 hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
-                            const uint16_t *q, const uint16_t *summ, qasp_score *scores, hipStream_t stream);
+                            const uint16_t *q, const uint16_t *summ, qasp_score *scores, hipStream_t stream,
+                            const TokenAppend &ap);
 hipError_t launch_select_topk(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
                               const qasp_score *scores, int32_t *sel, int32_t *sel_count,

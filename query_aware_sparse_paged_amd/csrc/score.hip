@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ summ,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     qasp_score *__restrict__ scores, int pt_stride, int max_pages, int Hq, int Hkv, int G,
-    int ps, int n_sink, int n_local, uint64_t static_mask) {
+    int ps, int n_sink, int n_local, uint64_t static_mask, TokenAppend ap) {
   constexpr int KSTEPS = 2 * D / 32;
   constexpr int GPW = kScoreGroupsPerWave;
   constexpr int PTR = (GPW * 16 + kWave - 1) / kWave;  // page-table registers per lane
@@ -33,6 +33,9 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
   const int P = num_pages_of(L, ps);
   const int cand_lo = min(n_sink, P), cand_hi = max(cand_lo, P - n_local);
   qasp_score *row = scores + ((size_t)b * Hkv + g) * max_pages;
+  // the step's token (page L-1 is not a candidate here), by the row's first block
+  if (ap.k_new != nullptr && blockIdx.x == 0 && L > 0)
+    ap.run(b, g, g + 1, page_table[(size_t)b * pt_stride + (L - 1) / ps], (L - 1) % ps, threadIdx.x, blockDim.x);
   const int wave_first = (blockIdx.x * kScoreWaves + wave) * GPW * 16;
   if (wave_first >= max_pages) return;
 
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
 
 hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
-                              qasp_score *scores, hipStream_t stream) {
+                              qasp_score *scores, hipStream_t stream, const TokenAppend &ap) {
   if (bat.batch == 0 || bat.max_pages == 0) return hipSuccess;
   const int G = bat.num_q_heads / lay.num_kv_heads;
   dim3 grid((bat.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, lay.num_kv_heads,
@@ -83,9 +86,9 @@ hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
     hipLaunchKernelGGL(score_gqa_kernel<128>, grid, dim3(256), 0, stream, q, summ, bat.page_table,
                        bat.seq_lens, scores, bat.pt_stride, bat.max_pages, bat.num_q_heads,
                        lay.num_kv_heads, G, lay.page_size, pol.n_sink_pages, pol.n_local_pages,
-                       pol.static_head_mask);
+                       pol.static_head_mask, ap);
   } else if (lay.head_dim_k == 576) {
-    return launch_score_mla(lay, bat, pol, q, summ, scores, stream);
+    return launch_score_mla(lay, bat, pol, q, summ, scores, stream, ap);
   } else {
     return hipErrorInvalidValue;
   }

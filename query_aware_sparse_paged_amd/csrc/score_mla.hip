@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ summ,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     qasp_score *__restrict__ scores, int batch, int pt_stride, int max_pages, int Hq, int Hkv, int ps,
-    int n_sink, int n_local, uint64_t static_mask, int groups_per_seq) {
+    int n_sink, int n_local, uint64_t static_mask, int groups_per_seq, TokenAppend ap) {
   extern __shared__ uint4 stage[];  // kMlaGroups x kGroupBytes
   __shared__ MlaScoreShared sh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -99,6 +99,9 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   const int cand_hi = head_is_static(static_mask, g) ? cand_lo : max(cand_lo, P - n_local);
   qasp_score *row = scores + ((size_t)b * Hkv + g) * max_pages;
   const qasp_score none = {-INFINITY, 0.f, -1, 0};
+  // the step's token (page L-1 is not a candidate here), by the row's first block
+  if (ap.k_new != nullptr && gfirst == 0 && L > 0)
+    ap.run(b, g, g + 1, page_table[(size_t)b * pt_stride + (L - 1) / ps], (L - 1) % ps, tid, kMlaWaves * 64);
   if (gfirst == 0) {  // the row's slots outside the candidates: sink pages, local pages, past the sequence
     for (int j = tid; j < cand_lo && j < max_pages; j += kMlaWaves * 64) row[j] = none;
     for (int j = cand_hi + tid; j < max_pages; j += kMlaWaves * 64) row[j] = none;
@@ -240,7 +243,8 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
 }
 
 hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
-                            const uint16_t *q, const uint16_t *summ, qasp_score *scores, hipStream_t stream) {
+                            const uint16_t *q, const uint16_t *summ, qasp_score *scores, hipStream_t stream,
+                            const TokenAppend &ap) {
   if (bat.batch == 0 || bat.max_pages == 0) return hipSuccess;
   // groups cover [cand_lo, cand_lo + 16 groups_per_seq), which holds every
   // candidate: cand_hi - cand_lo <= max_pages - n_sink - n_local when there are any
@@ -251,7 +255,7 @@ hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const
   hipLaunchKernelGGL(score_mla_kernel, dim3(blocks), dim3(kMlaWaves * 64), kMlaGroups * kGroupBytes, stream, q,
                      summ, bat.page_table, bat.seq_lens, scores, bat.batch, bat.pt_stride, bat.max_pages,
                      bat.num_q_heads, lay.num_kv_heads, lay.page_size, pol.n_sink_pages, pol.n_local_pages,
-                     pol.static_head_mask, groups_per_seq);
+                     pol.static_head_mask, groups_per_seq, ap);
   return hipGetLastError();
 }
 

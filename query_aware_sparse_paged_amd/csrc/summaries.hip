@@ -45,41 +45,14 @@ __global__ __launch_bounds__(256) void build_summaries_kernel(
 
 // One block per sequence: writes the new token at position seq_lens[b] +
 // pos_offset and folds its key into the page summary (slot 0 starts it).
-__global__ __launch_bounds__(256) void append_kv_kernel(
-    const uint32_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
-    uint32_t *__restrict__ k_pool, uint16_t *__restrict__ v_pool, uint32_t *__restrict__ summ,
-    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, int pos_offset,
-    int pt_stride, int ps, int num_kv_heads, int head_dim_k, int head_dim_v) {
+__global__ __launch_bounds__(256) void append_kv_kernel(TokenAppend ap, const int32_t *__restrict__ page_table,
+                                                        const int32_t *__restrict__ seq_lens, int pos_offset,
+                                                        int pt_stride) {
   const int b = blockIdx.x;
   const int pos = seq_lens[b] + pos_offset;
   if (pos < 0) return;
-  const int phys = page_table[(size_t)b * pt_stride + pos / ps];
-  const int t = pos % ps;
-  const int words = head_dim_k / 2;
-  for (int item = threadIdx.x; item < num_kv_heads * words; item += blockDim.x) {
-    const int g = item / words, w = item % words;
-    const size_t ph = (size_t)phys * num_kv_heads + g;
-    const uint32_t kv = k_new[((size_t)b * num_kv_heads + g) * words + w];
-    k_pool[(ph * ps + t) * words + w] = kv;
-    if (summ) {
-      uint32_t *s = summ + ph * 2 * words;
-      uint32_t lo = kv, hi = kv;
-      if (t != 0) {
-        lo = s[w];
-        hi = s[words + w];
-        minmax_bf16x2(kv, lo, hi);
-      }
-      s[w] = lo;
-      s[words + w] = hi;
-    }
-  }
-  if (v_pool) {
-    for (int item = threadIdx.x; item < num_kv_heads * head_dim_v; item += blockDim.x) {
-      const int g = item / head_dim_v, dv = item % head_dim_v;
-      const size_t ph = (size_t)phys * num_kv_heads + g;
-      v_pool[(ph * head_dim_v + dv) * ps + t] = v_new[((size_t)b * num_kv_heads + g) * head_dim_v + dv];
-    }
-  }
+  const int phys = page_table[(size_t)b * pt_stride + pos / ap.ps];
+  ap.run(b, 0, ap.num_kv_heads, phys, pos % ap.ps, threadIdx.x, blockDim.x);
 }
 
 hipError_t launch_build_summaries(const qasp_layout &lay, const qasp_batch &bat,
@@ -92,15 +65,20 @@ hipError_t launch_build_summaries(const qasp_layout &lay, const qasp_batch &bat,
   return hipGetLastError();
 }
 
+TokenAppend token_append(const qasp_layout &lay, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                         uint16_t *v_pool, uint16_t *summ) {
+  return TokenAppend{(const uint32_t *)k_new, lay.v_from_k ? nullptr : v_new, (uint32_t *)k_pool,
+                     lay.v_from_k ? nullptr : v_pool, (uint32_t *)summ, lay.num_kv_heads, lay.head_dim_k,
+                     lay.head_dim_v, lay.page_size};
+}
+
 hipError_t launch_append_kv(const qasp_layout &lay, const qasp_batch &bat, int pos_offset,
                             const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
                             uint16_t *v_pool, uint16_t *summ, hipStream_t stream) {
   if (bat.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(append_kv_kernel, dim3(bat.batch), dim3(256), 0, stream,
-                     (const uint32_t *)k_new, v_new, (uint32_t *)k_pool,
-                     lay.v_from_k ? (uint16_t *)nullptr : v_pool, (uint32_t *)summ, bat.page_table,
-                     bat.seq_lens, pos_offset, bat.pt_stride, lay.page_size, lay.num_kv_heads,
-                     lay.head_dim_k, lay.head_dim_v);
+                     token_append(lay, k_new, v_new, k_pool, v_pool, summ), bat.page_table, bat.seq_lens,
+                     pos_offset, bat.pt_stride);
   return hipGetLastError();
 }
 

@@ -218,12 +218,15 @@ def test_single_kernel_step_matches_oracle_and_kernel_chain(name, kw):
     assert np.abs(out.cpu().numpy() - g.out).max() <= 1e-5
 
 
+@pytest.mark.parametrize("batch", [32, 3])   # one-kernel step; kernel chain
 @pytest.mark.parametrize("local,boost", [(None, 1.0), (0, 6.0)])
-def test_single_kernel_step_appends(local, boost):
-    """The one-kernel step writes the token at L-1 and updates its summary.
-    With no local window the last page is a candidate, and a large new key
-    makes it the best page: it must be scored with the new token."""
-    w = _small("llama8b_b32_32k", batch=32, seq_len=700, seq_len_min=600)
+def test_step_appends(batch, local, boost):
+    """The decode step writes the token at L-1 and updates its summary (the
+    one-kernel step in its last wave, the chain in its scoring kernel, or in a
+    kernel of its own when the page is a candidate).  With no local window the
+    last page is a candidate, and a large new key makes it the best page: it
+    must be scored with the new token."""
+    w = _small("llama8b_b32_32k", batch=batch, seq_len=700, seq_len_min=600)
     lay, pol = api.layout_of(w), api.policy_of(w)
     if local is not None:
         pol = api.Policy(pol.n_sink_pages, local, pol.top_k)
@@ -237,13 +240,13 @@ def test_single_kernel_step_appends(local, boost):
     api.build_summaries(lay, api.Batch(bat.page_table, (bat.seq_lens - 1).contiguous(), 32), kp, summ)
     msel = api.max_sel(lay, pol, bat.max_pages)
     ws = api.new_workspace(lay, bat, pol, msel, DEV)
-    sel = torch.full((32, lay.num_kv_heads, msel), -7, dtype=torch.int32, device=DEV)
-    cnt = torch.full((32, lay.num_kv_heads), -7, dtype=torch.int32, device=DEV)
+    sel = torch.full((batch, lay.num_kv_heads, msel), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((batch, lay.num_kv_heads), -7, dtype=torch.int32, device=DEV)
     out = api.decode_step(lay, bat, pol, w.q.to(DEV), kp, vp, summ, w.scale, ws, msel,
                           k_new=new_k.to(DEV), v_new=new_v.to(DEV), sel=sel, sel_count=cnt)
     torch.cuda.synchronize()
     # the oracle sees the pool with the token written and summaries from scratch
-    for b in range(32):
+    for b in range(batch):
         L = int(w.seq_lens[b])
         phys = int(w.page_table[b, (L - 1) // 16])
         w.k_pool[phys, :, (L - 1) % 16, :] = new_k[b]
