@@ -17,12 +17,16 @@
 //     S_h(j) = sum_d |q_hd| |x_hd| <= |q_h|_2 * N_j,  N_j^2 = sum_d max(lo_d^2, hi_d^2)
 // (times 1.01 for the fp32 evaluation of the norms).
 // A block takes up to kMlaGroups consecutive 16-page groups of one sequence
-// and issues the loads of all their summary records at once, straight into
-// one LDS slab per group (global_load_lds, 16 bytes per lane; about 148 KB in
-// flight per CU, no registers held).  Chunk c (16 bytes) of page row n sits
-// at slot c ^ (n % 16) of the row, so the 16 rows of an MFMA B fragment fall
-// on different banks.  The block also writes the row's non-candidate slots
-// (-inf), so the score row needs no separate fill.
+// and loads their summary records straight into one LDS slab per group
+// (global_load_lds, 16 bytes per lane, no registers held): the first two
+// slabs, then, once those have landed, the other two, which load while the
+// first two are contracted.  Each slab is an LDS object of its own, so the
+// compiler sees which transfers a read depends on, and the barriers between
+// the steps wait for LDS and for this wave's own transfers explicitly.  Chunk
+// c (16 bytes) of page row n sits at slot c ^ (n % 16) of the row, so the 16
+// rows of an MFMA B fragment fall on different banks.  The block also writes
+// the row's non-candidate slots (-inf), so the score row needs no separate
+// fill.
 #include "launch.h"
 #include "score_core.h"
 
@@ -40,18 +44,49 @@ constexpr int kMlaChunk = 6;                  // MFMA results summed in fp32 bef
 constexpr float kErrRelMla = 39.0f * 1.1920928955078125e-07f * 1.01f;  // see the file comment
 
 struct MlaScoreShared {
-  double best[kMlaWaves][16];    // per wave and page: largest head value,
-  double second[kMlaWaves][16];  // the runner-up,
-  int arg[kMlaWaves][16];        // and the leading head
-  float norm2[kMlaWaves][16];  // partial page norms per wave
+  double best[kMlaGroups][kMlaWaves][16];    // per group, wave and page: largest head value,
+  double second[kMlaGroups][kMlaWaves][16];  // the runner-up,
+  int arg[kMlaGroups][kMlaWaves][16];        // and the leading head
+  float norm2[kMlaGroups][kMlaWaves][16];    // partial page norms per wave
   float qnorm[kMlaWaves];
-  int phys[kMlaGroups][16];  // physical pages of the block's groups; -1 = not a candidate
+  int phys[kMlaGroups][16];        // physical pages of the block's groups; -1 = not a candidate
+  qasp_score out[kMlaGroups][16];  // the block's scores, stored at the end
 };
 
-constexpr int kRecU4 = kMlaK2 / 8;            // 144 chunks of 16 bytes per record
+constexpr int kRecU4 = kMlaK2 / 8;              // 144 chunks of 16 bytes per record
 constexpr int kDmaPerGroup = 16 * kRecU4 / 64;  // 36 wave-wide 1 KB transfers per group
 static_assert(kRecU4 % 16 == 0 && (16 * kRecU4) % 64 == 0, "swizzle and transfer granularity");
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier that waits for this wave's LDS operations (and, with
+// all_vm, for all of its vector memory operations) but not for transfers
+// into LDS still in flight otherwise.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier(bool all_vm) {
+  asm volatile("" ::: "memory");
+  if (all_vm)
+    __builtin_amdgcn_s_waitcnt(0);
+  else  // vmcnt and expcnt at their maximum, lgkmcnt 0
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Negative and non-negative parts of four bf16 pairs: an arithmetic shift of
+// each 16-bit half by 15 gives its sign mask (one packed instruction), so
+// neg = x & mask, pos = x ^ neg.
+__device__ __forceinline__ void split_signs(const uint4 &x, uint4 &neg, uint4 &pos) {
+  typedef short short2v __attribute__((ext_vector_type(2)));
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t n4[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const uint32_t m = __builtin_bit_cast(uint32_t, __builtin_bit_cast(short2v, w[k]) >> (short)15);
+    n4[k] = w[k] & m;
+  }
+  neg = make_uint4(n4[0], n4[1], n4[2], n4[3]);
+  pos = make_uint4(x.x ^ n4[0], x.y ^ n4[1], x.z ^ n4[2], x.w ^ n4[3]);
+}
 
 // LDS byte offset of chunk c of row n inside a slab
 __device__ __forceinline__ int slab_off(int n, int c) { return n * kRecBytes + 16 * (c ^ (n & 15)); }
@@ -74,7 +109,10 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     qasp_score *__restrict__ scores, int batch, int pt_stride, int max_pages, int Hq, int Hkv, int ps,
     int n_sink, int n_local, uint64_t static_mask, int groups_per_seq, TokenAppend ap) {
-  extern __shared__ uint4 stage[];  // kMlaGroups x kGroupBytes
+  // one LDS object per group slab (see the file comment)
+  __shared__ uint4 slab0[kGroupBytes / 16], slab1[kGroupBytes / 16], slab2[kGroupBytes / 16],
+      slab3[kGroupBytes / 16];
+  static_assert(kMlaGroups == 4, "four slabs: two loading while two are contracted");
   __shared__ MlaScoreShared sh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane & 15, kg = lane >> 4;
@@ -121,20 +159,27 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
 #pragma unroll
     for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qg + (size_t)n * kMlaD + 32 * i + 8 * kg);
   }
-  __syncthreads();
-  // every record of every group, straight to LDS: transfer t of group x
-  // fills slots 64 t .. 64 t + 63 of slab x (row slot / 144), lane l loading
-  // the chunk whose swizzled slot is 64 t + l; rows past the candidates read
-  // page 0 (their columns are never stored)
-  for (int x = 0; x < ng; x++) {
-    char *slab = (char *)stage + (size_t)x * kGroupBytes;
+  __syncthreads();  // sh.phys is complete
+
+  // every record of group x, straight to its slab: transfer t fills slots
+  // 64 t .. 64 t + 63 (row slot / 144), lane l loading the chunk whose
+  // swizzled slot is 64 t + l; rows past the candidates read page 0 (their
+  // columns are never stored)
+  auto slab_of = [&](int x) -> char * {
+    return (char *)(x == 0 ? slab0 : x == 1 ? slab1 : x == 2 ? slab2 : slab3);
+  };
+  auto issue_group = [&](int x) {
+    char *slab = slab_of(x);
     for (int t = wave; t < kDmaPerGroup; t += kMlaWaves) {
       const int slot = 64 * t + lane, r = slot / kRecU4, sl = slot % kRecU4;
       const int ph = max(sh.phys[x][r], 0);
       const uint16_t *src = summ + ((size_t)ph * Hkv + g) * kMlaK2 + 8 * (sl ^ (r & 15));
       __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(slab + 1024 * t), 16, 0, 0);
     }
-  }
+  };
+  if (ng > 0) issue_group(0);
+  if (ng > 1) issue_group(1);
+
   // the largest |q_h| of the wave's heads
   {
     float s2 = 0.f;  // |q_h|^2 of head n over this lane's quarter of the channels
@@ -152,11 +197,16 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const float qmax = wave_max(sqrtf(s2));
     if (lane == 0) sh.qnorm[wave] = qmax;
   }
+  // groups 0 and 1 have landed (this wave's part); groups 2 and 3 load while
+  // they are contracted
+  __builtin_amdgcn_s_waitcnt(0);
+  if (ng > 2) issue_group(2);
+  if (ng > 3) issue_group(3);
+  lds_barrier(false);
 
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's transfers have landed (the barrier below publishes them)
-  for (int x = 0; x < ng; x++) {
-    const char *rec = (const char *)stage + (size_t)x * kGroupBytes;
-    __syncthreads();  // every slab has landed; the previous group's results are read
+  // contracts group x: every wave's top two heads and partial norm per page
+  auto contract = [&](int x) {
+    const char *rec = slab_of(x);
     // page norms N_j^2 = sum_d max(lo_d^2, hi_d^2): wave w adds channel blocks
     // 32i + 8kg .. (i = w, w + 8, ...) of page n; the blocks sum in LDS below
     {
@@ -174,28 +224,50 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       }
       a += __shfl_xor(a, 16, kWave);
       a += __shfl_xor(a, 32, kWave);
-      if (kg == 0) sh.norm2[wave][n] = a;
+      if (kg == 0) sh.norm2[x][wave][n] = a;
     }
     // contraction over [lo, hi]: q^- with lo channels 32i + 8kg ... and q^+
-    // (the rest of q's bits) with the same hi channels, for i = 0 .. 17
+    // with the same hi channels, for i = 0 .. 17.  The fragments of three
+    // channel blocks (one fp32 chunk of kMlaChunk MFMA results) are read from
+    // LDS together, one chunk ahead of the MFMAs that use them.
+    static_assert(kMlaChunk == 6 && (kMlaD / 32) % 3 == 0, "three channel blocks per fp32 chunk");
+    constexpr int kChunks = kMlaD / 32 / 3;
     double u64[4] = {0.0, 0.0, 0.0, 0.0};
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    uint4 fl[2][3], fh[2][3];  // [buffer][block in chunk]: lo and hi fragments
+    // chunk 4i + kg of row n is at frag_base[i % 4] + 256 (i / 4), hi chunk
+    // 72 + 4i + kg at frag_base[(i + 2) % 4] + 256 (4 + (i + 2) / 4): four
+    // per-lane bases, the rest immediate offsets
+    static_assert(kMlaD / 8 == 72, "hi half starts at chunk 72");
+    int frag_base[4];
 #pragma unroll
-    for (int i = 0; i < kMlaD / 32; i++) {
-      const uint4 qn = score::map4(qraw[i], 0);
-      const uint4 qp = make_uint4(qraw[i].x ^ qn.x, qraw[i].y ^ qn.y, qraw[i].z ^ qn.z, qraw[i].w ^ qn.w);
-      const floatx4 un = mfma16x16x32(qn, *(const uint4 *)(rec + slab_off(n, 4 * i + kg)), floatx4{0.f, 0.f, 0.f, 0.f});
-      const floatx4 up =
-          mfma16x16x32(qp, *(const uint4 *)(rec + slab_off(n, kMlaD / 8 + 4 * i + kg)), floatx4{0.f, 0.f, 0.f, 0.f});
+    for (int m = 0; m < 4; m++) frag_base[m] = slab_off(n, 4 * m + kg);
+    auto read_chunk = [&](int c, uint4 *l, uint4 *h) {
 #pragma unroll
-      for (int r = 0; r < 4; r++) part[r] = (part[r] + un[r]) + up[r];
-      if ((2 * i + 2) % kMlaChunk == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          u64[r] += (double)part[r];
-          part[r] = 0.f;
-        }
+      for (int j = 0; j < 3; j++) {
+        const int i = 3 * c + j;
+        l[j] = *(const uint4 *)(rec + frag_base[i & 3] + 256 * (i >> 2));
+        h[j] = *(const uint4 *)(rec + frag_base[(i + 2) & 3] + 256 * (4 + ((i + 2) >> 2)));
       }
+    };
+    read_chunk(0, fl[0], fh[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < kChunks; c++) {
+      if (c + 1 < kChunks) read_chunk(c + 1, fl[(c + 1) & 1], fh[(c + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this chunk's MFMAs
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 3; j++) {
+        const int i = 3 * c + j;
+        uint4 qn, qp;  // q^- and q^+ (the rest of q's bits) of channel block i
+        split_signs(qraw[i], qn, qp);
+        const floatx4 un = mfma16x16x32(qn, fl[c & 1][j], floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 up = mfma16x16x32(qp, fh[c & 1][j], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int r = 0; r < 4; r++) part[r] = (part[r] + un[r]) + up[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; r++) u64[r] += (double)part[r];
     }
     // lane (n, kg) holds heads 16 wave + 4kg + r of page n: top two of the
     // wave's heads for page n (value, runner-up, leading head)
@@ -218,27 +290,41 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       top2_merge(b1, b2, a1, ob1, ob2, oa);
     }
     if (kg == 0) {
-      sh.best[wave][n] = b1;
-      sh.second[wave][n] = b2;
-      sh.arg[wave][n] = a1;
+      sh.best[x][wave][n] = b1;
+      sh.second[x][wave][n] = b2;
+      sh.arg[x][wave][n] = a1;
     }
-    __syncthreads();
-    if (wave == 0 && lane < 16) {
-      const int j = j0 + 16 * x + lane;
-      if (j < cand_hi) {
-        double m = sh.best[0][lane], m2 = sh.second[0][lane];
-        int arg = sh.arg[0][lane];
-        float qn = sh.qnorm[0], n2 = sh.norm2[0][lane];
+  };
+  // combines the waves' results of group x into its 16 scores (wave 0)
+  auto finish = [&](int x) {
+    if (wave == 0 && lane < 16 && j0 + 16 * x + lane < cand_hi) {
+      double m = sh.best[x][0][lane], m2 = sh.second[x][0][lane];
+      int arg = sh.arg[x][0][lane];
+      float qn = sh.qnorm[0], n2 = sh.norm2[x][0][lane];
 #pragma unroll
-        for (int w = 1; w < kMlaWaves; w++) {
-          top2_merge(m, m2, arg, sh.best[w][lane], sh.second[w][lane], sh.arg[w][lane]);
-          qn = fmaxf(qn, sh.qnorm[w]);
-          n2 += sh.norm2[w][lane];
-        }
-        const float bound = qn * sqrtf(n2) * 1.01f;  // >= every head's S
-        row[j] = score::make_score(m, bound, m2, arg, kErrRelMla);
+      for (int w = 1; w < kMlaWaves; w++) {
+        top2_merge(m, m2, arg, sh.best[x][w][lane], sh.second[x][w][lane], sh.arg[x][w][lane]);
+        qn = fmaxf(qn, sh.qnorm[w]);
+        n2 += sh.norm2[x][w][lane];
       }
+      const float bound = qn * sqrtf(n2) * 1.01f;  // >= every head's S
+      sh.out[x][lane] = score::make_score(m, bound, m2, arg, kErrRelMla);
     }
+  };
+  if (ng > 0) contract(0);
+  if (ng > 1) contract(1);
+  lds_barrier(true);  // groups 2 and 3 have landed; the results of 0 and 1 are in LDS
+  finish(0);
+  finish(1);
+  if (ng > 2) contract(2);
+  if (ng > 3) contract(3);
+  lds_barrier(false);
+  finish(2);
+  finish(3);
+  lds_barrier(false);
+  for (int t = tid; t < 16 * ng; t += kMlaWaves * 64) {
+    const int j = j0 + t;
+    if (j < cand_hi) row[j] = sh.out[t / 16][t % 16];
   }
 }
 
@@ -252,7 +338,7 @@ hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const
   const int groups_per_seq = std::max(1, (max_cand + 15) / 16);
   const int blocks_per_seq = (groups_per_seq + kMlaGroups - 1) / kMlaGroups;
   const int blocks = bat.batch * blocks_per_seq;
-  hipLaunchKernelGGL(score_mla_kernel, dim3(blocks), dim3(kMlaWaves * 64), kMlaGroups * kGroupBytes, stream, q,
+  hipLaunchKernelGGL(score_mla_kernel, dim3(blocks), dim3(kMlaWaves * 64), 0, stream, q,
                      summ, bat.page_table, bat.seq_lens, scores, bat.batch, bat.pt_stride, bat.max_pages,
                      bat.num_q_heads, lay.num_kv_heads, lay.page_size, pol.n_sink_pages, pol.n_local_pages,
                      pol.static_head_mask, groups_per_seq, ap);
