@@ -80,6 +80,19 @@ static int32_t max_sel_of(const qasp_layout &lay, const qasp_policy &pol, int32_
 
 // Splits per (sequence, KV head) unit: enough blocks to fill the chip, at
 // most 64 pages per wave, at least one page per split.
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static int counts[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
 int decode_splits(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
   if (family_of(lay) == kFamilyMla) {
     const int s = (max_sel + kMlaPagesPerSplit - 1) / kMlaPagesPerSplit;

@@ -31,6 +31,65 @@ struct FusedLds {
   }
 };
 
+// The (sequence, KV head) unit of block i of the one-dimensional grid.
+// Blocks are dispatched in index order, block i to shader engine i % 32
+// (XCD i % 8, engine (i / 8) % 4 of it, 8 CUs each), each waiting for a free
+// CU of its engine, and a block that waits holds up those behind it.
+//  - One round (lpt false: no more units than CUs): block i takes sequence
+//    i % B and the (i / B)-th head of the dispatch order (query-aware heads
+//    first), so consecutive blocks take different sequences and a sequence's
+//    heads share an XCD.
+//  - Several rounds (lpt): the query-aware units come first, ranked by
+//    length (longest first, ties by sequence index) and dealt to the engines
+//    in a snake (rows of 32 blocks alternately left to right and right to
+//    left), so every engine gets the same mix of long and short units and
+//    the engines free their CUs at about the same pace; the static units,
+//    all of about the same size, follow.  Needs B <= T and both unit counts
+//    multiples of 32 (otherwise the one-round order).
+// sm: 2T ints of LDS.  Every thread of the block returns the same unit.
+template <int T>
+__device__ __forceinline__ int2 unit_for_block(int i, const int32_t *seq_lens, int B, int Hkv, uint64_t static_mask,
+                                               bool lpt, int *sm) {
+  constexpr int kEngines = 32;
+  const uint64_t all = Hkv >= 64 ? ~0ull : ((1ull << Hkv) - 1);
+  const uint64_t qa = all & ~static_mask, st = all & static_mask;
+  const int n_qa = __popcll(qa);
+  const int nq = B * n_qa, ns = B * (Hkv - n_qa);
+  if (!lpt || B > T || nq % kEngines != 0 || ns % kEngines != 0)
+    return make_int2(i % B, head_in_dispatch_order(static_mask, Hkv, i / B));
+  const int tid = threadIdx.x;
+  const int len = tid < B ? seq_lens[tid] : 0;
+  if (tid < B) sm[tid] = len;
+  __syncthreads();
+  if (tid < B) {
+    int rank = 0;
+    for (int u = 0; u < B; u++) {
+      const int lu = sm[u];
+      rank += lu > len || (lu == len && u < tid);
+    }
+    sm[T + rank] = tid;  // sequence of each rank
+  }
+  __syncthreads();
+  const int row = i / kEngines, j = i % kEngines;
+  int b, h;
+  uint64_t mask;
+  if (i < nq) {
+    const int item = row * kEngines + (row & 1 ? kEngines - 1 - j : j);  // rank among the query-aware units
+    b = sm[T + item / n_qa];
+    h = item % n_qa;
+    mask = qa;
+  } else {
+    const int item = i - nq;
+    b = item % B;
+    h = item / B;
+    mask = st;
+  }
+  for (; h > 0; h--) mask &= mask - 1;  // drop the h lowest set bits
+  const int g = __ffsll((long long)mask) - 1;
+  __syncthreads();  // sm is free again
+  return make_int2(b, g);
+}
+
 template <int D, int DV, int PS, int W>
 __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
@@ -38,7 +97,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, float *__restrict__ out,
     int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
-    int window_tokens, uint64_t static_mask, float scale_log2, uint32_t bucket_mul) {
+    int window_tokens, uint64_t static_mask, float scale_log2, uint32_t bucket_mul, int lpt) {
   static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
@@ -57,9 +116,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   int32_t *order = (int32_t *)((char *)dyn + lay.order);
   float *merge_area = (float *)((char *)dyn + lay.merge);
 
-  // consecutive blocks (one per XCD in turn) take different sequences
-  const int b = blockIdx.x, g = head_in_dispatch_order(static_mask, Hkv, blockIdx.y);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  __shared__ int rank_sm[2 * T];
+  const int2 bg = unit_for_block<T>(blockIdx.x, seq_lens, gridDim.x / Hkv, Hkv, static_mask, lpt != 0, rank_sm);
+  const int b = bg.x, g = bg.y;
   const int n_col = lane & 15, kg = lane >> 4;
   const int unit = b * Hkv + g;
   const int L = seq_lens[b];
@@ -310,12 +370,15 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   const size_t lds = FusedLds(mp, max_sel, G).total;
   const float scale_log2 = scale * 1.4426950408889634f;
   const uint32_t bucket_mul = score::bucket_multiplier(lay.num_pool_pages);
-  dim3 grid(bat.batch, lay.num_kv_heads);
+  // several rounds of blocks: longest processing time first (see unit_for_block)
+  const int units = bat.batch * lay.num_kv_heads;
+  const int lpt = units > device_cu_count() ? 1 : 0;
+  dim3 grid(units);
   hipLaunchKernelGGL((fused_step_gqa_kernel<128, 128, 16, kFusedWaves>), grid, dim3(kFusedWaves * 64), lds,
                      stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, out, sel,
                      sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G,
                      pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens, pol.window_tokens,
-                     pol.static_head_mask, scale_log2, bucket_mul);
+                     pol.static_head_mask, scale_log2, bucket_mul, lpt);
   return hipGetLastError();
 }
 

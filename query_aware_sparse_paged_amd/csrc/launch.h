@@ -34,6 +34,8 @@ struct Workspace {
 };
 
 int decode_splits(const qasp_layout &lay, const qasp_batch &bat, int max_sel);
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 size_t workspace_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel);
 Workspace carve_workspace(const qasp_layout &lay, const qasp_batch &bat, int max_sel, void *base);
 
