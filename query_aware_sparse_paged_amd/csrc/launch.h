@@ -20,7 +20,7 @@ namespace qasp {
 constexpr int kGqaDecodeWaves = QASP_GQA_WAVES;         // waves per decode block
 constexpr int kGqaTargetBlocks = QASP_GQA_TARGET_BLOCKS; // split units until this many blocks
 #ifndef QASP_MLA_PAGES_PER_SPLIT
-#define QASP_MLA_PAGES_PER_SPLIT 2
+#define QASP_MLA_PAGES_PER_SPLIT 8
 #endif
 constexpr int kMlaPagesPerSplit = QASP_MLA_PAGES_PER_SPLIT;  // selected pages per latent-head decode block
 
