@@ -209,6 +209,26 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat,
                          int32_t max_sel, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* One decode step of a layer that reuses the page selection of an earlier
+ * layer at the same step (cross-layer selection reuse: the OmniKV / DeltaKV
+ * family named in the SparseEngine article's decode-hook paragraph): optional
+ * append of the step's token (when k_new is not NULL; as in
+ * qasp_decode_step, bat->seq_lens counts it), then softmax attention over
+ * the given selection, as qasp_sparse_paged_decode.  No scoring and no
+ * selection: sel / sel_count ([batch][num_kv_heads][max_sel], logical page
+ * ids, read only) come from qasp_decode_step or qasp_select_topk of the
+ * earlier layer and index this layer's page table and pools.  summ (may be
+ * NULL) is this layer's summary pool: when given, the append keeps it
+ * current.  workspace: >= qasp_workspace_bytes.  Errors as
+ * qasp_decode_step. */
+int32_t qasp_decode_step_reuse(const qasp_layout *lay, const qasp_batch *bat,
+                               const qasp_policy *pol, const uint16_t *q,
+                               const uint16_t *k_new, const uint16_t *v_new,
+                               uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ,
+                               float scale, const int32_t *sel, const int32_t *sel_count,
+                               int32_t max_sel, float *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

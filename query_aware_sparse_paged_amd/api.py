@@ -61,6 +61,9 @@ EXPORTS = {
                                                                            ctypes.c_size_t, ctypes.c_void_p]),
     "qasp_decode_step": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 3 +
                          [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qasp_decode_step_reuse": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 2 +
+                               [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                ctypes.c_void_p]),
 }
 
 _lib = None
@@ -292,6 +295,30 @@ def decode_step(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool,
                                   _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(summ),
                                   float(scale), _ptr(out), _ptr(sel), _ptr(sel_count), int(max_sel_n),
                                   _ptr(workspace), workspace.numel(), _stream()), "qasp_decode_step")
+    return out
+
+
+def decode_step_reuse(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, summ, scale: float,
+                      sel, sel_count, workspace: torch.Tensor, k_new=None, v_new=None, out=None) -> torch.Tensor:
+    """A layer that reuses an earlier layer's selection (sel, sel_count of
+    that layer's decode_step at the same step): append (if k_new is given;
+    batch.seq_lens then counts the new token) and attention over the given
+    pages, no scoring or selection.  summ may be None.  Returns out fp32
+    [B][Hq][Dv]."""
+    for t, name, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
+                        (k_new, "k_new", 3), (v_new, "v_new", 3)):
+        _dev(t, torch.bfloat16, name, nd)
+    _dev(sel, torch.int32, "sel", 3)
+    _dev(sel_count, torch.int32, "sel_count", 2)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    B = batch.seq_lens.shape[0]
+    if out is None:
+        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out", 3)
+    _check(lib().qasp_decode_step_reuse(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
+                                        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(summ),
+                                        float(scale), _ptr(sel), _ptr(sel_count), int(sel.shape[2]), _ptr(out),
+                                        _ptr(workspace), workspace.numel(), _stream()), "qasp_decode_step_reuse")
     return out
 
 

@@ -303,4 +303,32 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   return status_of(e);
 }
 
+int32_t qasp_decode_step_reuse(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                               const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                               uint16_t *v_pool, uint16_t *summ, float scale, const int32_t *sel,
+                               const int32_t *sel_count, int32_t max_sel, float *out, void *workspace,
+                               size_t workspace_bytes_given, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  if (bat->batch == 0) return QASP_OK;
+  if (!q || !k_pool || !sel || !sel_count || !out || !workspace) return QASP_ERR_NULL_ARG;
+  if (!lay->v_from_k && !v_pool) return QASP_ERR_NULL_ARG;
+  if (k_new && !lay->v_from_k && !v_new) return QASP_ERR_NULL_ARG;
+  if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const long units = (long)bat->batch * lay->num_kv_heads;
+  if (family_of(*lay) == kFamilyGqa && units >= kFusedMinUnits)
+    return status_of(launch_fused_reuse_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel,
+                                            sel_count, max_sel, s));
+  const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
+  hipError_t e = hipSuccess;
+  if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
+  if (e == hipSuccess)
+    e = launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel, sel_count, max_sel, scale, out, ws, s);
+  return status_of(e);
+}
+
 }  // extern "C"

@@ -356,6 +356,106 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   });
 }
 
+// A decode step of a layer that reuses the page selection of an earlier
+// layer (cross-layer selection reuse, SparseEngine article, decode-hook
+// paragraph: the OmniKV / DeltaKV family), in one kernel per (sequence, KV
+// head) block: the step's token is appended (key row, value column, page
+// summary when there are summaries), then softmax attention over the given
+// selection (this layer's pools, the selection's logical page ids through
+// this layer's page table).  No scoring, no selection.  The token's page is a
+// local page, so the append completes (barrier) before the attention.
+template <int D, int DV, int PS, int W>
+__global__ __launch_bounds__(W * 64) void fused_reuse_gqa_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    uint16_t *__restrict__ k_pool, uint16_t *__restrict__ v_pool, uint16_t *__restrict__ summ,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ sel_count, float *__restrict__ out,
+    int pt_stride, int max_sel, int Hq, int Hkv, int G, int sink_tokens, int window_tokens, uint64_t static_mask,
+    float scale_log2, int lpt) {
+  static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
+  constexpr int T = W * kWave;
+  __shared__ int rank_sm[2 * T];
+  extern __shared__ float merge_area[];  // attend::merge_lds_floats(W, G, DV)
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int2 bg = unit_for_block<T>(blockIdx.x, seq_lens, gridDim.x / Hkv, Hkv, static_mask, lpt != 0, rank_sm);
+  const int b = bg.x, g = bg.y;
+  const int unit = b * Hkv + g;
+  const int L = seq_lens[b];
+  const int32_t *pt_row = page_table + (size_t)b * pt_stride;
+  const bool is_static = head_is_static(static_mask, g);
+  const size_t head0 = (size_t)b * Hq + (size_t)g * G;
+  const int count = min(sel_count[unit], max_sel);
+  const int npg = count > wave ? (count - wave + W - 1) / W : 0;  // positions wave, wave + W, ...
+  // the wave's pages, lane i holding its i-th (issued before the append)
+  int my_j = 0, my_phys = 0;
+  if (lane < npg) my_j = sel[(size_t)unit * max_sel + wave + W * lane];
+  if (lane < npg) my_phys = pt_row[my_j];
+
+  // append of the token at position L-1 by the last wave
+  if (k_new != nullptr && L > 0 && wave == W - 1) {
+    const int a_t = (L - 1) % PS;
+    const size_t a_ph = (size_t)pt_row[(L - 1) / PS] * Hkv + g;
+    const uint32_t *krow = (const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D);  // D / 2 = 64 words
+    const uint32_t a_k = krow[lane];
+    const uint16_t *vn = v_new + ((size_t)b * Hkv + g) * DV;
+    const uint16_t a_v0 = vn[lane], a_v1 = vn[lane + kWave];
+    uint32_t a_lo = 0, a_hi = 0;
+    if (summ != nullptr) {
+      const uint32_t *sl = (const uint32_t *)summ + a_ph * D;
+      a_lo = sl[lane];
+      a_hi = sl[D / 2 + lane];
+    }
+    ((uint32_t *)k_pool)[(a_ph * PS + a_t) * (D / 2) + lane] = a_k;
+    v_pool[(a_ph * DV + lane) * PS + a_t] = a_v0;
+    v_pool[(a_ph * DV + lane + kWave) * PS + a_t] = a_v1;
+    if (summ != nullptr) {
+      uint32_t lo = a_k, hi = a_k;
+      if (a_t != 0) {
+        const int v0 = bf16_order_key(a_k & 0xffffu), v1 = bf16_order_key(a_k >> 16);
+        lo = bf16_from_order_key(min(v0, bf16_order_key(a_lo & 0xffffu))) |
+             (bf16_from_order_key(min(v1, bf16_order_key(a_lo >> 16))) << 16);
+        hi = bf16_from_order_key(max(v0, bf16_order_key(a_hi & 0xffffu))) |
+             (bf16_from_order_key(max(v1, bf16_order_key(a_hi >> 16))) << 16);
+      }
+      uint32_t *sp = (uint32_t *)summ + a_ph * D;
+      sp[lane] = lo;
+      sp[D / 2 + lane] = hi;
+    }
+    __threadfence_block();
+  }
+  __syncthreads();  // the token is in the pools before any wave reads its page
+
+  const int sink_end = is_static ? min(sink_tokens, L) : 0;
+  const int win_begin = is_static ? max(0, L - window_tokens) : 0;
+  uint4 bq[D / 32];
+  attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
+  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  attend::WaveState st;
+  attend::init_state(st);
+  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
+  attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
+    (void)M;
+    out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
+  });
+}
+
+hipError_t launch_fused_reuse_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
+                                  const int32_t *sel, const int32_t *sel_count, int max_sel, hipStream_t stream) {
+  const int G = bat.num_q_heads / lay.num_kv_heads;
+  if (G > 16) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int units = bat.batch * lay.num_kv_heads;
+  const int lpt = units > device_cu_count() ? 1 : 0;
+  const size_t lds = (size_t)attend::merge_lds_floats(kFusedWaves, G, 128) * 4;
+  hipLaunchKernelGGL((fused_reuse_gqa_kernel<128, 128, 16, kFusedWaves>), dim3(units), dim3(kFusedWaves * 64), lds,
+                     stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, sel, sel_count,
+                     out, bat.pt_stride, max_sel, bat.num_q_heads, lay.num_kv_heads, G, pol.sink_tokens,
+                     pol.window_tokens, pol.static_head_mask, scale_log2, lpt);
+  return hipGetLastError();
+}
+
 size_t fused_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
   const int G = bat.num_q_heads / lay.num_kv_heads;
   return FusedLds(bat.max_pages > 0 ? bat.max_pages : 1, max_sel, G).total + sizeof(sel::SelShared<kFusedWaves>);

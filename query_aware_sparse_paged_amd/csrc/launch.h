@@ -73,6 +73,10 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
                                  int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream);
+hipError_t launch_fused_reuse_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
+                                  const int32_t *sel, const int32_t *sel_count, int max_sel, hipStream_t stream);
 hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,
                                hipStream_t stream);
 

@@ -128,3 +128,30 @@ def test_empty_batch_is_a_no_op(L):
     assert _call("qasp_select_topk", b(lay), b(empty), b(pol), None, None, None, None, None, 37, None) == api.OK
     assert _call("qasp_sparse_paged_decode", b(lay), b(empty), b(pol), None, None, None, None, None, 37, 1.0,
                  None, None, 0, None) == api.OK
+
+
+def test_reuse_step_argument_checks(L):
+    """qasp_decode_step_reuse: the given selection is required, summaries are
+    not; the workspace bound and the empty batch behave as in decode_step."""
+    b = ctypes.byref
+    lay, pol = GQA.c(), api.Policy(1, 4, 32).c()
+    bat = _batch()
+    need = _call("qasp_workspace_bytes", b(lay), b(bat), b(pol), 37)
+    # (lay, bat, pol, q, k_new, v_new, k_pool, v_pool, summ, scale, sel, sel_count, max_sel, out, ws, bytes, stream)
+    args = lambda **kw: [kw.get(k, v) for k, v in (("q", 1), ("k_new", None), ("v_new", None), ("k_pool", 1),
+                                                    ("v_pool", 1), ("summ", None), ("scale", 1.0), ("sel", 1),
+                                                    ("sel_count", 1), ("max_sel", 37), ("out", 1), ("ws", 1),
+                                                    ("bytes", need), ("stream", None))]
+    call = lambda lay_=lay, bat_=bat, **kw: _call("qasp_decode_step_reuse", b(lay_), b(bat_), b(pol), *args(**kw))
+    assert call(sel=None) == api.ERR_NULL_ARG
+    assert call(sel_count=None) == api.ERR_NULL_ARG
+    assert call(q=None) == api.ERR_NULL_ARG
+    assert call(out=None) == api.ERR_NULL_ARG
+    assert call(v_pool=None) == api.ERR_NULL_ARG
+    assert call(k_new=1, v_new=None) == api.ERR_NULL_ARG   # a value row goes with the key row
+    assert call(bytes=need - 1) == api.ERR_WORKSPACE
+    assert call(max_sel=-1) == api.ERR_BAD_SHAPE
+    assert call(bat_=_batch(Hq=30)) == api.ERR_BAD_SHAPE
+    # no launch for an empty batch, whatever the pointers
+    assert _call("qasp_decode_step_reuse", b(lay), b(_batch(B=0)), b(pol), None, None, None, None, None, None, 1.0,
+                 None, None, 37, None, None, 0, None) == api.OK
