@@ -10,6 +10,11 @@ independent layer caches so that no step finds the previous step's data in
 the 256 MB Infinity Cache.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+--reuse R measures cross-layer selection reuse instead: a group of R + 1
+layers sharing the page table, where the first layer runs the whole step and
+the next R layers append their token and attend over its selection
+(qasp_decode_step_reuse); one JSON line with the per-layer figures.
 """
 import argparse
 import json
@@ -120,6 +125,8 @@ def main():
     ap.add_argument("--layers", type=int, default=3, help="independent layer caches rotated over")
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reuse", type=int, default=0,
+                    help="cross-layer reuse: per group, 1 selecting layer + this many reusing layers")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (a known-size kernel for HBM counters)")
     args = ap.parse_args()
@@ -133,6 +140,8 @@ def main():
     from query_aware_sparse_paged_amd import api, workloads
 
     dev = torch.device("cuda:0")
+    if args.reuse > 0:
+        return run_reuse(args, torch, api, workloads, dev)
     layers = []
     for i in range(args.layers):
         base = workloads.SPECS[args.workload].seed
@@ -250,6 +259,104 @@ def main():
                      "traffic": profiled_traffic(kernel, spec.name) if one_kernel else None,
                      "algorithmic_bytes": total_bytes},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_reuse(args, torch, api, workloads, dev):
+    """Groups of 1 selecting layer + R reusing layers (same page table and
+    lengths; the reusing layers' pools are the first layer's with the key
+    channels reversed and the values negated, their queries reversed too, so
+    every layer reads its own HBM)."""
+    R = args.reuse
+    w = workloads.make(args.workload, seed=workloads.SPECS[args.workload].seed, device=dev)
+    lay, pol, spec = api.layout_of(w), api.policy_of(w), w.spec
+    bat = api.Batch(w.page_table, w.seq_lens, spec.num_q_heads)
+    msel = api.max_sel(lay, pol, bat.max_pages)
+    ws = api.new_workspace(lay, bat, pol, msel, dev)
+    B = spec.batch
+    sel = torch.empty((B, lay.num_kv_heads, msel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, lay.num_kv_heads), dtype=torch.int32, device=dev)
+    layer = []
+    for r in range(R + 1):
+        if r == 0:
+            kp, vp, q, kn, vn = w.k_pool, w.v_pool, w.q, w.k_new, w.v_new
+        else:
+            kp, q, kn = w.k_pool.flip(-1).contiguous(), w.q.flip(-1).contiguous(), w.k_new.flip(-1).contiguous()
+            vp = None if w.v_pool is None else (-w.v_pool).contiguous()
+            vn = None if w.v_new is None else (-w.v_new).contiguous()
+        summ = torch.zeros((w.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16,
+                           device=dev)
+        api.build_summaries(lay, bat, kp, summ)
+        out = torch.empty((B, spec.num_q_heads, lay.head_dim_v), dtype=torch.float32, device=dev)
+        layer.append(dict(kp=kp, vp=vp, q=q, kn=kn, vn=vn, summ=summ, out=out))
+        log("layer %d ready" % r)
+    torch.cuda.synchronize()
+
+    def full(L):
+        api.decode_step(lay, bat, pol, L["q"], L["kp"], L["vp"], L["summ"], w.scale, ws, msel, k_new=L["kn"],
+                        v_new=L["vn"], out=L["out"], sel=sel, sel_count=cnt)
+
+    def reuse(L):
+        api.decode_step_reuse(lay, bat, pol, L["q"], L["kp"], L["vp"], L["summ"], w.scale, sel, cnt, ws,
+                              k_new=L["kn"], v_new=L["vn"], out=L["out"])
+
+    def group():
+        full(layer[0])
+        for r in range(1, R + 1):
+            reuse(layer[r])
+
+    for _ in range(args.warmup):
+        group()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        group()
+    torch.cuda.synchronize()
+    group_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # HIP events around each layer of a second pass
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for r in range(R + 1):
+            ev[i][r][0].record(stream)
+            (full if r == 0 else reuse)(layer[r])
+            ev[i][r][1].record(stream)
+    torch.cuda.synchronize()
+    med = statistics.median
+    full_ms = med(ev[i][0][0].elapsed_time(ev[i][0][1]) for i in range(args.steps))
+    reuse_ms = med(ev[i][r][0].elapsed_time(ev[i][r][1]) for i in range(args.steps) for r in range(1, R + 1))
+    b_score, b_decode = step_bytes(w, cnt.cpu().tolist())
+    full_bytes, reuse_bytes = b_score + b_decode, b_decode
+    layer_ms = group_ms / (R + 1)
+    gqa = spec.head_dim_k == spec.head_dim_v and not spec.v_from_k
+    rkernel = ("fused_reuse_gqa_kernel" if gqa and B * lay.num_kv_heads >= 200
+               else "append + decode kernels")
+    log("group of %d layers: %.1f us wall; events: selecting layer %.1f us, reusing layer %.1f us"
+        % (R + 1, group_ms * 1e3, full_ms * 1e3, reuse_ms * 1e3))
+    line = {
+        "metric": "decode tokens/s per layer with cross-layer selection reuse (1 selecting + %d reusing layers), %s"
+                  % (R, spec.name),
+        "value": round(B / (layer_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(group_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": B, "seq_len": spec.seq_len, "reusing_layers": R},
+        "layer_us_events": {"selecting": round(full_ms * 1e3, 2), "reusing": round(reuse_ms * 1e3, 2)},
+        "roofline": {"kernel": rkernel, "bound": "hbm", "achieved": round(reuse_bytes / (reuse_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(reuse_bytes / (reuse_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes": reuse_bytes},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
