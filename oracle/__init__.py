@@ -10,6 +10,7 @@ Inputs are numpy arrays: bf16 tensors as ``uint16`` bit patterns, indices as
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 import subprocess
 from dataclasses import dataclass
@@ -74,6 +75,9 @@ def lib():
             "orc_attend": (I32, [P, P, P, P, P, P, P, P, I32, D, P]),
             "orc_decode": (I32, [P, P, P, P, P, P, P, D, P, P, P, I32, I32]),
             "orc_max_sel": (I32, [P, P, I32]),
+            "orc_scores_multi": (I32, [P, P, P, I32, P, P, P, I32]),
+            "orc_select_multi": (I32, [P, P, P, I32, P, I32, P, P, I32]),
+            "orc_attend_multi": (I32, [P, P, P, I32, P, P, P, P, P, I32, D, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(_lib, name)
@@ -243,3 +247,58 @@ def decode(layout: Layout, page_table, seq_lens, q, k_pool, v_pool, summ_pool, p
                             float(scale), _ptr(out), _ptr(sel), _ptr(cnt), max_sel_n,
                             int(num_threads)), "decode")
     return out, sel, cnt
+
+
+# Multi-query step: nq draft tokens per sequence at positions L - nq ... L - 1
+# (seq_lens count them); q [B][nq][Hq][Dk], out [B][nq][Hq][Dv].  The readings
+# are stated in oracle.h beside orc_scores_multi.
+
+def max_sel_multi(layout: Layout, pol: Policy, nq: int, max_pages: int) -> int:
+    """Selection capacity of a multi-query step (static heads read a window of
+    window_tokens + nq - 1 tokens when window_tokens >= 1)."""
+    wide = pol.window_tokens + nq - 1 if pol.window_tokens > 0 else 0
+    return max_sel(layout, dataclasses.replace(pol, window_tokens=wide), max_pages)
+
+
+def scores_multi(layout: Layout, page_table, seq_lens, q, summ_pool, pol: Policy, max_pages=None):
+    keep = _Keep()
+    qq = keep.arr(q, np.uint16)
+    nq = qq.shape[1]
+    s = keep.arr(summ_pool, np.uint16)
+    bat = _batch(keep, page_table, seq_lens, qq.shape[2])
+    if max_pages is None:
+        max_pages = np.asarray(page_table).shape[1]
+    out = np.empty((bat.batch, layout.num_kv_heads, max_pages), np.float64)
+    _check(lib().orc_scores_multi(ctypes.byref(layout.c()), ctypes.byref(bat), ctypes.byref(_policy(keep, pol)),
+                                  nq, _ptr(qq), _ptr(s), _ptr(out), max_pages), "scores_multi")
+    return out
+
+
+def select_multi(layout: Layout, page_table, seq_lens, num_q_heads, nq, scores_arr, pol: Policy, max_sel_n=None):
+    keep = _Keep()
+    sc = keep.arr(scores_arr, np.float64)
+    bat = _batch(keep, page_table, seq_lens, num_q_heads)
+    max_pages = sc.shape[2]
+    if max_sel_n is None:
+        max_sel_n = max_sel_multi(layout, pol, nq, max_pages)
+    sel = np.empty((bat.batch, layout.num_kv_heads, max_sel_n), np.int32)
+    cnt = np.empty((bat.batch, layout.num_kv_heads), np.int32)
+    _check(lib().orc_select_multi(ctypes.byref(layout.c()), ctypes.byref(bat), ctypes.byref(_policy(keep, pol)),
+                                  int(nq), _ptr(sc), max_pages, _ptr(sel), _ptr(cnt), max_sel_n), "select_multi")
+    return sel, cnt
+
+
+def attend_multi(layout: Layout, page_table, seq_lens, q, k_pool, v_pool, sel, cnt, pol: Policy, scale):
+    keep = _Keep()
+    qq = keep.arr(q, np.uint16)
+    nq = qq.shape[1]
+    k = keep.arr(k_pool, np.uint16)
+    v = None if v_pool is None else keep.arr(v_pool, np.uint16)
+    se = keep.arr(sel, np.int32)
+    cn = keep.arr(cnt, np.int32)
+    bat = _batch(keep, page_table, seq_lens, qq.shape[2])
+    out = np.empty((bat.batch, nq, qq.shape[2], layout.head_dim_v), np.float64)
+    _check(lib().orc_attend_multi(ctypes.byref(layout.c()), ctypes.byref(bat), ctypes.byref(_policy(keep, pol)),
+                                  nq, _ptr(qq), _ptr(k), _ptr(v), _ptr(se), _ptr(cn), se.shape[2], float(scale),
+                                  _ptr(out)), "attend_multi")
+    return out

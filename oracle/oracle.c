@@ -286,9 +286,11 @@ int32_t orc_append(const orc_layout *lay, const orc_batch *bat_before,
 /* ------------------------------------------------------------------------ */
 
 /* Group score of every page of the unit: row[j] for j < max_pages.
+ * q holds nq query rows per head: q[b][i][h][:] for i < nq (nq = 1 for a
+ * one-token step); the score is the maximum over every (i, h) of the group.
  * terms: scratch of head_dim_k doubles. */
 static int unit_scores(const orc_layout *lay, const orc_batch *bat,
-                       const orc_policy *pol, const uint16_t *q,
+                       const orc_policy *pol, const uint16_t *q, int32_t nq,
                        const uint16_t *summ_pool, int32_t b, int32_t g,
                        double *row, int32_t max_pages, double *terms)
 {
@@ -305,8 +307,9 @@ static int unit_scores(const orc_layout *lay, const orc_batch *bat,
         const uint16_t *lo = summ_pool + ((int64_t)phys * lay->num_kv_heads + g) * 2 * D;
         const uint16_t *hi = lo + D;
         double best = -INFINITY;
-        for (int32_t h = g * G; h < (g + 1) * G; h++) {
-            const uint16_t *qh = q + ((int64_t)b * bat->num_q_heads + h) * D;
+        for (int32_t r = 0; r < nq * G; r++) {
+            int32_t i = r / G, h = g * G + r % G;
+            const uint16_t *qh = q + (((int64_t)b * nq + i) * bat->num_q_heads + h) * D;
             for (int32_t d = 0; d < D; d++) {
                 double qd = bf16_value(qh[d]);
                 double a = qd * bf16_value(lo[d]);   /* exact: 8-bit x 8-bit significands */
@@ -374,22 +377,26 @@ static int64_t unit_select_flags(const orc_layout *lay, const orc_batch *bat,
     return count;
 }
 
-/* Attention of the query heads of group g over the selected pages. */
+/* Attention of the query heads of group g over the selected pages, for
+ * query i of nq (q and out rows [b][i][h]).  Query i sits at position
+ * L - nq + i and sees the tokens before and at it: it attends as a one-token
+ * step of length L - nq + 1 + i would (nq = 1: the sequence's last token). */
 static void unit_attend(const orc_layout *lay, const orc_batch *bat,
                         const orc_policy *pol, const uint16_t *q,
                         const uint16_t *k_pool, const uint16_t *v_pool,
                         const int32_t *sel, int32_t count, double scale,
-                        int32_t b, int32_t g, double *out, double *s_buf)
+                        int32_t b, int32_t g, int32_t nq, int32_t i,
+                        double *out, double *s_buf)
 {
     const int32_t ps = lay->page_size, D = lay->head_dim_k, Dv = lay->head_dim_v;
     const int32_t G = bat->num_q_heads / lay->num_kv_heads;
-    int32_t L = bat->seq_lens[b];
+    int64_t L = (int64_t)bat->seq_lens[b] - nq + 1 + i;
     int64_t sink_end = pol->sink_tokens < L ? pol->sink_tokens : L;
-    int64_t win_begin = (int64_t)L - pol->window_tokens;
+    int64_t win_begin = L - pol->window_tokens;
     int st = is_static(pol, g);
     for (int32_t h = g * G; h < (g + 1) * G; h++) {
-        const uint16_t *qh = q + ((int64_t)b * bat->num_q_heads + h) * D;
-        double *o = out + ((int64_t)b * bat->num_q_heads + h) * Dv;
+        const uint16_t *qh = q + (((int64_t)b * nq + i) * bat->num_q_heads + h) * D;
+        double *o = out + (((int64_t)b * nq + i) * bat->num_q_heads + h) * Dv;
         /* scores of every attended token, in page then token order */
         int64_t n = 0;
         double m = -INFINITY;
@@ -451,11 +458,11 @@ static int check_policy(const orc_policy *pol)
            pol->sink_tokens >= 0 && pol->window_tokens >= 0;
 }
 
-int32_t orc_scores(const orc_layout *lay, const orc_batch *bat,
-                   const orc_policy *pol, const uint16_t *q,
-                   const uint16_t *summ_pool, double *scores, int32_t max_pages)
+static int32_t scores_nq(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const uint16_t *q,
+                         const uint16_t *summ_pool, double *scores, int32_t max_pages)
 {
-    if (!check_layout(lay) || !check_batch(lay, bat) || !check_policy(pol)) return ORC_ERR_ARG;
+    if (!check_layout(lay) || !check_batch(lay, bat) || !check_policy(pol) || nq < 1) return ORC_ERR_ARG;
     if (bat->batch == 0) return ORC_OK;
     if (!q || !summ_pool || !scores) return ORC_ERR_ARG;
     for (int32_t b = 0; b < bat->batch; b++)
@@ -465,11 +472,25 @@ int32_t orc_scores(const orc_layout *lay, const orc_batch *bat,
     int32_t rc = ORC_OK;
     for (int32_t b = 0; b < bat->batch && rc == ORC_OK; b++)
         for (int32_t g = 0; g < lay->num_kv_heads && rc == ORC_OK; g++)
-            rc = unit_scores(lay, bat, pol, q, summ_pool, b, g,
+            rc = unit_scores(lay, bat, pol, q, nq, summ_pool, b, g,
                              scores + ((int64_t)b * lay->num_kv_heads + g) * max_pages,
                              max_pages, terms);
     free(terms);
     return rc;
+}
+
+int32_t orc_scores(const orc_layout *lay, const orc_batch *bat,
+                   const orc_policy *pol, const uint16_t *q,
+                   const uint16_t *summ_pool, double *scores, int32_t max_pages)
+{
+    return scores_nq(lay, bat, pol, 1, q, summ_pool, scores, max_pages);
+}
+
+int32_t orc_scores_multi(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const uint16_t *q,
+                         const uint16_t *summ_pool, double *scores, int32_t max_pages)
+{
+    return scores_nq(lay, bat, pol, nq, q, summ_pool, scores, max_pages);
 }
 
 int32_t orc_select(const orc_layout *lay, const orc_batch *bat,
@@ -506,13 +527,27 @@ int32_t orc_select(const orc_layout *lay, const orc_batch *bat,
     return rc;
 }
 
-int32_t orc_attend(const orc_layout *lay, const orc_batch *bat,
-                   const orc_policy *pol, const uint16_t *q,
-                   const uint16_t *k_pool, const uint16_t *v_pool,
-                   const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
-                   double scale, double *out)
+/* Draft queries share the unit's selection.  For a static head the page set
+ * is the union of the queries' own sink + window sets; the queries' windows
+ * [L_i - w, L_i) end at L_i = L - nq + 1 ... L, so for w >= 1 they chain
+ * into one window of w + nq - 1 tokens ending at L (w = 0: all empty). */
+int32_t orc_select_multi(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const double *scores, int32_t max_pages,
+                         int32_t *sel, int32_t *sel_count, int32_t max_sel)
 {
-    if (!check_layout(lay) || !check_batch(lay, bat) || !check_policy(pol)) return ORC_ERR_ARG;
+    if (!pol || nq < 1) return ORC_ERR_ARG;
+    orc_policy wide = *pol;
+    if (pol->window_tokens > 0) wide.window_tokens = pol->window_tokens + nq - 1;
+    return orc_select(lay, bat, &wide, scores, max_pages, sel, sel_count, max_sel);
+}
+
+static int32_t attend_nq(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const uint16_t *q,
+                         const uint16_t *k_pool, const uint16_t *v_pool,
+                         const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
+                         double scale, double *out)
+{
+    if (!check_layout(lay) || !check_batch(lay, bat) || !check_policy(pol) || nq < 1) return ORC_ERR_ARG;
     if (bat->batch == 0) return ORC_OK;
     if (!q || !k_pool || (!v_pool && !lay->v_from_k) || !sel || !sel_count || !out) return ORC_ERR_ARG;
     double *s_buf = (double *)malloc(sizeof(double) * ((size_t)max_sel * lay->page_size + 1));
@@ -528,11 +563,30 @@ int32_t orc_attend(const orc_layout *lay, const orc_batch *bat,
             for (int32_t i = 0; i < count; i++)
                 if (row[i] < 0 || row[i] >= P) rc = ORC_ERR_ARG;
             if (rc != ORC_OK) break;
-            unit_attend(lay, bat, pol, q, k_pool, v_pool, row, count, scale, b, g, out, s_buf);
+            for (int32_t i = 0; i < nq; i++)
+                unit_attend(lay, bat, pol, q, k_pool, v_pool, row, count, scale, b, g, nq, i, out, s_buf);
         }
     }
     free(s_buf);
     return rc;
+}
+
+int32_t orc_attend(const orc_layout *lay, const orc_batch *bat,
+                   const orc_policy *pol, const uint16_t *q,
+                   const uint16_t *k_pool, const uint16_t *v_pool,
+                   const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
+                   double scale, double *out)
+{
+    return attend_nq(lay, bat, pol, 1, q, k_pool, v_pool, sel, sel_count, max_sel, scale, out);
+}
+
+int32_t orc_attend_multi(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const uint16_t *q,
+                         const uint16_t *k_pool, const uint16_t *v_pool,
+                         const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
+                         double scale, double *out)
+{
+    return attend_nq(lay, bat, pol, nq, q, k_pool, v_pool, sel, sel_count, max_sel, scale, out);
 }
 
 int32_t orc_decode(const orc_layout *lay, const orc_batch *bat,
@@ -572,7 +626,7 @@ int32_t orc_decode(const orc_layout *lay, const orc_batch *bat,
             if (!ok) continue;
             int32_t b = (int32_t)(u / lay->num_kv_heads), g = (int32_t)(u % lay->num_kv_heads);
             int64_t P = num_pages(bat->seq_lens[b], lay->page_size);
-            int st = unit_scores(lay, bat, pol, q, summ_pool, b, g, row, (int32_t)max_pages, terms);
+            int st = unit_scores(lay, bat, pol, q, 1, summ_pool, b, g, row, (int32_t)max_pages, terms);
             if (st != ORC_OK) {
 #pragma omp critical
                 rc = st;
@@ -591,7 +645,7 @@ int32_t orc_decode(const orc_layout *lay, const orc_batch *bat,
                 for (int64_t i = 0; i < max_sel; i++) sel[u * max_sel + i] = i < n ? list[i] : -1;
                 sel_count[u] = (int32_t)count;
             }
-            unit_attend(lay, bat, pol, q, k_pool, v_pool, list, (int32_t)count, scale, b, g, out, s_buf);
+            unit_attend(lay, bat, pol, q, k_pool, v_pool, list, (int32_t)count, scale, b, g, 1, 0, out, s_buf);
         }
         if (!ok) {
 #pragma omp critical

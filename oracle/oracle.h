@@ -133,6 +133,30 @@ int32_t orc_decode(const orc_layout *lay, const orc_batch *bat,
                    int32_t *sel, int32_t *sel_count, int32_t max_sel,
                    int32_t num_threads);
 
+/* Multi-query step (speculative decoding checks several draft tokens at
+ * once: the llama.cpp SWA-only draft-head fix article on aikeizai.jp, the
+ * section on why it matters, which describes multi-token prediction).  The batch's
+ * seq_lens count the nq draft tokens, which sit at positions L - nq ... L - 1;
+ * q and out hold nq rows per head: q [B][nq][Hq][Dk], out [B][nq][Hq][Dv].
+ * Readings taken: the nq queries share one selection per (sequence, KV head);
+ * a page's group score is the maximum of the bound over every draft query's
+ * heads of the group; query i attends causally, as a one-token step of length
+ * L - nq + 1 + i would over the shared pages; a static head's page set is the
+ * union of the queries' sink + window sets (one window of window_tokens +
+ * nq - 1 tokens ending at L when window_tokens >= 1).  A query with no position (L - nq + 1 + i <= 0)
+ * gets 0.  nq = 1 gives orc_scores / orc_select / orc_attend exactly. */
+int32_t orc_scores_multi(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const uint16_t *q,
+                         const uint16_t *summ_pool, double *scores, int32_t max_pages);
+int32_t orc_select_multi(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const double *scores, int32_t max_pages,
+                         int32_t *sel, int32_t *sel_count, int32_t max_sel);
+int32_t orc_attend_multi(const orc_layout *lay, const orc_batch *bat,
+                         const orc_policy *pol, int32_t nq, const uint16_t *q,
+                         const uint16_t *k_pool, const uint16_t *v_pool,
+                         const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
+                         double scale, double *out);
+
 /* Largest selection any head can need under this policy. */
 int32_t orc_max_sel(const orc_layout *lay, const orc_policy *pol, int32_t max_pages);
 
