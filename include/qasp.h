@@ -229,6 +229,43 @@ int32_t qasp_decode_step_reuse(const qasp_layout *lay, const qasp_batch *bat,
                                int32_t max_sel, float *out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Multi-query decode step: n_query draft tokens per sequence checked at once
+ * (speculative decoding of multi-token-prediction drafts: the llama.cpp
+ * draft-head fix article on aikeizai.jp, the section on why it matters).
+ * Grouped-query layouts only (page 16, head_dim 128), with
+ * (num_q_heads / num_kv_heads) * n_query <= 16 and 1 <= n_query <= 16
+ * (otherwise QASP_ERR_UNSUPPORTED; n_query < 1: QASP_ERR_BAD_SHAPE).
+ *   bat->seq_lens: lengths INCLUDING the drafts, which sit at positions
+ *                  seq_lens[b] - n_query ... seq_lens[b] - 1.
+ *   q     [batch][n_query][num_q_heads][head_dim_k] bf16.
+ *   k_new [batch][n_query][num_kv_heads][head_dim_k], v_new
+ *         [batch][n_query][num_kv_heads][head_dim_v] bf16, or both NULL when
+ *         the drafts are already in the pools; when given they are written
+ *         in order and folded into summ.
+ *   out   [batch][n_query][num_q_heads][head_dim_v] fp32.
+ * The drafts share one selection per (sequence, KV head), scored with the
+ * maximum page bound over every draft query's heads of the group; draft i
+ * attends causally (tokens at positions <= seq_lens[b] - n_query + i of the
+ * selected pages); a static head's page set is the union of the drafts'
+ * sink + window sets, and each draft attends its own window.  A draft with no
+ * position (seq_lens[b] < n_query) is not written and gets 0.
+ * max_sel >= qasp_max_sel_multi; workspace >= qasp_workspace_bytes_multi.
+ * sel / sel_count: optional copy of the shared selection, as
+ * qasp_decode_step.  Other errors as qasp_decode_step. */
+int32_t qasp_max_sel_multi(const qasp_layout *lay, const qasp_policy *pol,
+                           int32_t n_query, int32_t max_pages);
+size_t qasp_workspace_bytes_multi(const qasp_layout *lay, const qasp_batch *bat,
+                                  const qasp_policy *pol, int32_t n_query,
+                                  int32_t max_sel);
+int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat,
+                               const qasp_policy *pol, int32_t n_query,
+                               const uint16_t *q, const uint16_t *k_new,
+                               const uint16_t *v_new, uint16_t *k_pool,
+                               uint16_t *v_pool, uint16_t *summ, float scale,
+                               float *out, int32_t *sel, int32_t *sel_count,
+                               int32_t max_sel, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,11 @@ EXPORTS = {
     "qasp_decode_step_reuse": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 2 +
                                [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p]),
+    "qasp_max_sel_multi": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]),
+    "qasp_workspace_bytes_multi": (ctypes.c_size_t, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32]),
+    "qasp_decode_step_multi": (ctypes.c_int32, [ctypes.c_void_p] * 3 + [ctypes.c_int32] + [ctypes.c_void_p] * 6 +
+                               [ctypes.c_float] + [ctypes.c_void_p] * 3 +
+                               [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -331,3 +336,44 @@ def layout_of(w) -> Layout:
 def policy_of(w) -> Policy:
     s = w.spec
     return Policy(s.n_sink_pages, s.n_local_pages, s.top_k, s.sink_tokens, s.window_tokens, s.static_heads)
+
+
+def max_sel_multi(layout: Layout, policy: Policy, n_query: int, max_pages: int) -> int:
+    r = lib().qasp_max_sel_multi(ctypes.byref(layout.c()), ctypes.byref(policy.c()), int(n_query), int(max_pages))
+    _check(0 if r >= 0 else r, "qasp_max_sel_multi")
+    return r
+
+
+def new_workspace_multi(layout: Layout, batch: Batch, policy: Policy, n_query: int, max_sel_n: int,
+                        device) -> torch.Tensor:
+    """Workspace of qasp_workspace_bytes_multi bytes (no initialisation needed)."""
+    n = int(lib().qasp_workspace_bytes_multi(ctypes.byref(layout.c()), ctypes.byref(batch.c()),
+                                             ctypes.byref(policy.c()), int(n_query), int(max_sel_n)))
+    if n == 0:
+        raise ValueError("invalid arguments for the multi-query workspace size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode_step_multi(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, summ, scale: float,
+                      workspace: torch.Tensor, max_sel_n: int, k_new=None, v_new=None, out=None, sel=None,
+                      sel_count=None) -> torch.Tensor:
+    """n_query = q.shape[1] draft tokens per sequence (batch.seq_lens counts
+    them): append them (if k_new is given, [B][n][Hkv][Dk]), select once per
+    (sequence, KV head) for all drafts, attend causally.  q [B][n][Hq][Dk];
+    returns out fp32 [B][n][Hq][Dv]."""
+    for t, name, nd in ((q, "q", 4), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
+                        (k_new, "k_new", 4), (v_new, "v_new", 4)):
+        _dev(t, torch.bfloat16, name, nd)
+    _dev(sel, torch.int32, "sel", 3)
+    _dev(sel_count, torch.int32, "sel_count", 2)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    B, n = batch.seq_lens.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, n, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out", 4)
+    _check(lib().qasp_decode_step_multi(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
+                                        int(n), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                        _ptr(summ), float(scale), _ptr(out), _ptr(sel), _ptr(sel_count),
+                                        int(max_sel_n), _ptr(workspace), workspace.numel(), _stream()),
+           "qasp_decode_step_multi")
+    return out

@@ -10,7 +10,8 @@ namespace qasp {
 hipError_t launch_decode_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                              const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                              const int32_t *sel, const int32_t *sel_count, int max_sel, float scale,
-                             float *out, const Workspace &ws, hipStream_t stream);
+                             float *out, const Workspace &ws, hipStream_t stream, int nq = 1,
+                             int window_q = 0);
 hipError_t launch_decode_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                              const uint16_t *q, const uint16_t *k_pool, const int32_t *sel,
                              const int32_t *sel_count, int max_sel, float scale, float *out,
@@ -149,6 +150,38 @@ hipError_t launch_sparse_decode(const qasp_layout &lay, const qasp_batch &bat, c
 }
 
 static int32_t status_of(hipError_t e) { return e == hipSuccess ? QASP_OK : QASP_ERR_LAUNCH; }
+
+// Multi-query step: nq draft queries regrouped so that KV head g's group holds
+// G heads per draft query (num_q_heads * nq columns in all); a static head's
+// selection covers the union of the queries' windows (window + nq - 1 tokens
+// ending at L, when the window is not empty).
+constexpr int kMaxDrafts = 16;
+static qasp_batch multi_batch(const qasp_batch &bat, int nq) {
+  qasp_batch b = bat;
+  b.num_q_heads = bat.num_q_heads * nq;
+  return b;
+}
+static qasp_policy multi_policy(const qasp_policy &pol, int nq) {
+  qasp_policy p = pol;
+  if (p.window_tokens > 0) p.window_tokens += nq - 1;
+  return p;
+}
+static int32_t check_multi(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol, int32_t nq) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (nq < 1) return QASP_ERR_BAD_SHAPE;
+  if (nq > kMaxDrafts || family_of(*lay) != kFamilyGqa) return QASP_ERR_UNSUPPORTED;
+  if ((long)(bat->num_q_heads / lay->num_kv_heads) * nq > 16) return QASP_ERR_UNSUPPORTED;
+  if (pol->window_tokens > INT32_MAX - kMaxDrafts) return QASP_ERR_BAD_SHAPE;
+  return QASP_OK;
+}
+static size_t multi_workspace_bytes(const qasp_layout &lay, const qasp_batch &bat, int nq, int max_sel) {
+  const size_t rows = (size_t)bat.batch * nq * bat.num_q_heads;
+  return workspace_bytes(lay, multi_batch(bat, nq), max_sel) + align256(rows * lay.head_dim_k * sizeof(uint16_t)) +
+         align256(rows * lay.head_dim_v * sizeof(float));
+}
 
 }  // namespace qasp
 
@@ -300,6 +333,69 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
     e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
   if (e == hipSuccess)
     e = launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
+  return status_of(e);
+}
+
+int32_t qasp_max_sel_multi(const qasp_layout *lay, const qasp_policy *pol, int32_t n_query, int32_t max_pages) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (max_pages < 0 || n_query < 1 || pol->window_tokens > INT32_MAX - kMaxDrafts) return QASP_ERR_BAD_SHAPE;
+  if (n_query > kMaxDrafts) return QASP_ERR_UNSUPPORTED;
+  return max_sel_of(*lay, multi_policy(*pol, n_query), max_pages);
+}
+
+size_t qasp_workspace_bytes_multi(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                                  int32_t n_query, int32_t max_sel) {
+  if (check_multi(lay, bat, pol, n_query) != QASP_OK || max_sel < 0) return 0;
+  return multi_workspace_bytes(*lay, *bat, n_query, max_sel);
+}
+
+int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                               int32_t n_query, const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                               uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
+                               int32_t *sel, int32_t *sel_count, int32_t max_sel, void *workspace,
+                               size_t workspace_bytes_given, void *stream) {
+  int32_t rc = check_multi(lay, bat, pol, n_query);
+  if (rc != QASP_OK) return rc;
+  const int nq = n_query;
+  const qasp_policy wpol = multi_policy(*pol, nq);
+  if (max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  if (max_sel < max_sel_of(*lay, wpol, bat->max_pages)) return QASP_ERR_MAX_SEL;
+  if (bat->batch == 0) return QASP_OK;
+  if (!q || !k_pool || !v_pool || !out || !workspace) return QASP_ERR_NULL_ARG;
+  const bool scored = !all_static(*lay, *pol);
+  if (scored && !summ) return QASP_ERR_NULL_ARG;
+  if (k_new && !v_new) return QASP_ERR_NULL_ARG;
+  if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
+  if (workspace_bytes_given < multi_workspace_bytes(*lay, *bat, nq, max_sel)) return QASP_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const qasp_batch wbat = multi_batch(*bat, nq);
+  const Workspace ws = carve_workspace(*lay, wbat, max_sel, workspace);
+  const size_t rows = (size_t)bat->batch * wbat.num_q_heads;
+  uint16_t *q_grouped = (uint16_t *)((char *)workspace + workspace_bytes(*lay, wbat, max_sel));
+  float *out_grouped = (float *)((char *)q_grouped + align256(rows * lay->head_dim_k * sizeof(uint16_t)));
+  int32_t *sel_out = sel ? sel : ws.sel;
+  int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
+  const int G = bat->num_q_heads / lay->num_kv_heads;
+  hipError_t e = hipSuccess;
+  if (k_new) e = launch_append_drafts(*lay, *bat, nq, k_new, v_new, k_pool, v_pool, summ, s);
+  // q [B][nq][Hkv][G*Dk] -> [B][Hkv][nq][G*Dk]
+  if (e == hipSuccess)
+    e = launch_swap_rows(q, q_grouped, bat->batch, nq, lay->num_kv_heads,
+                         (size_t)G * lay->head_dim_k * sizeof(uint16_t), s);
+  if (e == hipSuccess && scored)
+    e = launch_score_pages(*lay, wbat, wpol, q_grouped, summ, ws.scores, s,
+                           token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr));
+  if (e == hipSuccess)
+    e = launch_select_topk(*lay, wbat, wpol, q_grouped, summ, ws.scores, sel_out, cnt_out, max_sel, s);
+  if (e == hipSuccess)
+    e = launch_decode_gqa(*lay, wbat, wpol, q_grouped, k_pool, v_pool, sel_out, cnt_out, max_sel, scale,
+                          out_grouped, ws, s, nq, pol->window_tokens);
+  // out [B][Hkv][nq][G*Dv] -> [B][nq][Hkv][G*Dv]
+  if (e == hipSuccess)
+    e = launch_swap_rows(out_grouped, out, bat->batch, lay->num_kv_heads, nq,
+                         (size_t)G * lay->head_dim_v * sizeof(float), s);
   return status_of(e);
 }
 

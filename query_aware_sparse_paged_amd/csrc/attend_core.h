@@ -64,8 +64,12 @@ struct PageRegs {
 };
 
 // Loading and computing one page-head for a wave (the two halves of the
-// pipelined loops below).
-template <int PS, int D, int DV>
+// pipelined loops below).  L, sink_end and win_begin bound the tokens of the
+// unit (their values are read).  With CAUSAL the head columns are draft
+// queries with their own ends: column l % 16 scores only tokens before Lq and,
+// for a static head, at or after winq (its own window) or before sink_end;
+// the unit bounds still decide which value entries are read.
+template <int PS, int D, int DV, bool CAUSAL = false>
 struct PageWork {
   static_assert(PS == 16 && D == 128 && DV == 128, "tile shapes");
   const uint16_t *__restrict__ k_pool;
@@ -74,6 +78,7 @@ struct PageWork {
   int Hkv, g, L, sink_end, win_begin;
   bool is_static;
   float scale_log2;
+  int Lq, winq;  // per lane, CAUSAL only
 
   __device__ __forceinline__ void load(int phys, uint4 *kk, uint2 *vv, int lane) const {
     const int n = lane & 15, kg = lane >> 4;
@@ -105,7 +110,9 @@ struct PageWork {
     for (int r = 0; r < 4; r++) {
       const int pos = j * PS + 4 * kg + r;
       const bool ok = real & (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
-      sv[r] = ok ? s[r] * scale_log2 : -INFINITY;
+      bool use = ok;
+      if constexpr (CAUSAL) use = ok & (pos < Lq) & (!is_static | (pos < sink_end) | (pos >= winq));
+      sv[r] = use ? s[r] * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, sv[r]);
       keep[r >> 1] |= ok ? (0xffffu << (16 * (r & 1))) : 0u;
     }
@@ -146,8 +153,8 @@ struct PageWork {
 // (my_j) and physical page (my_phys).  Tokens t of a page are used when
 // t < L and, for a static head, t < sink_end or t >= win_begin.  When pre is
 // set, first already holds page 0 (loaded by the caller earlier).
-template <int PS, int D, int DV>
-__device__ __forceinline__ void attend_pages(WaveState &st, const PageWork<PS, D, DV> &pw, int npg, int my_j,
+template <int PS, int D, int DV, bool CAUSAL>
+__device__ __forceinline__ void attend_pages(WaveState &st, const PageWork<PS, D, DV, CAUSAL> &pw, int npg, int my_j,
                                              int my_phys, int lane, bool pre = false,
                                              PageRegs<D, DV> first = PageRegs<D, DV>()) {
   if (npg <= 0) return;

@@ -12,12 +12,17 @@
 // writes the output; otherwise it writes a partial (m, l, acc) and
 // merge_splits_kernel combines the partials (a kernel boundary orders the
 // two; no device-wide fences inside a kernel).
+//
+// Multi-query form (CAUSAL): the group's head columns are nq draft queries
+// x G/nq heads (query i's heads are columns i*G/nq ...); query i sits at
+// position L - nq + i and scores only the tokens up to it and, for a static
+// head, its own window of window_q tokens (the selection holds the union).
 #include "attend_core.h"
 #include "launch.h"
 
 namespace qasp {
 
-template <int PS, int D, int DV, int WAVES>
+template <int PS, int D, int DV, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool,
     const uint16_t *__restrict__ v_pool, const int32_t *__restrict__ page_table,
@@ -25,7 +30,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
     const int32_t *__restrict__ sel_count, float *__restrict__ partial,
     float2 *__restrict__ partial_ml, float *__restrict__ out, int pt_stride, int max_sel, int Hq,
     int Hkv, int G, int splits, int pps, float scale_log2, int sink_tokens, int window_tokens,
-    uint64_t static_mask) {
+    uint64_t static_mask, int nq, int window_q) {
   extern __shared__ float lds[];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -49,7 +54,15 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
   attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
   attend::WaveState st;
   attend::init_state(st);
-  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  int Lq = L, winq = 0;
+  if constexpr (CAUSAL) {
+    const int n = lane & 15, per_query = G / nq;
+    const int i = n < G ? n / per_query : nq - 1;
+    Lq = L - (nq - 1 - i);
+    winq = max(0, Lq - window_q);
+  }
+  const attend::PageWork<PS, D, DV, CAUSAL> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin,
+                                               is_static, scale_log2, Lq, winq};
   attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
   attend::merge_waves<WAVES, DV>(lds, st, G, [&](int h, int dv, float a, float lsum, float M) {
     if (splits == 1) {
@@ -126,17 +139,18 @@ hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_di
 hipError_t launch_decode_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                              const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                              const int32_t *sel, const int32_t *sel_count, int max_sel, float scale,
-                             float *out, const Workspace &ws, hipStream_t stream) {
+                             float *out, const Workspace &ws, hipStream_t stream, int nq, int window_q) {
   constexpr int W = kGqaDecodeWaves;
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const float scale_log2 = scale * 1.4426950408889634f;
   const int pps = (max_sel + ws.splits - 1) / ws.splits;
   const size_t lds = (size_t)attend::merge_lds_floats(W, G, 128) * sizeof(float);
   dim3 grid(ws.splits, lay.num_kv_heads, bat.batch);
-  hipLaunchKernelGGL((decode_gqa_kernel<16, 128, 128, W>), grid, dim3(W * 64), lds, stream, q, k_pool,
-                     v_pool, bat.page_table, bat.seq_lens, sel, sel_count, ws.partial, ws.partial_ml, out,
-                     bat.pt_stride, max_sel, bat.num_q_heads, lay.num_kv_heads, G, ws.splits, pps,
-                     scale_log2, pol.sink_tokens, pol.window_tokens, pol.static_head_mask);
+  auto kernel = nq > 1 ? decode_gqa_kernel<16, 128, 128, W, true> : decode_gqa_kernel<16, 128, 128, W, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(W * 64), lds, stream, q, k_pool, v_pool, bat.page_table, bat.seq_lens,
+                     sel, sel_count, ws.partial, ws.partial_ml, out, bat.pt_stride, max_sel, bat.num_q_heads,
+                     lay.num_kv_heads, G, ws.splits, pps, scale_log2, pol.sink_tokens, pol.window_tokens,
+                     pol.static_head_mask, nq, window_q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ws.splits == 1) return e;
   return launch_merge_splits(ws, bat.batch, bat.num_q_heads, lay.head_dim_v, out, stream);

@@ -230,3 +230,17 @@ def from_bits(a, device="cpu") -> torch.Tensor:
     """numpy uint16 bit patterns -> bf16 tensor."""
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def drafts(w: Workload, n: int, seed: int, device="cpu"):
+    """Draft tokens of a multi-query step over workload w: queries
+    [B][n][Hq][Dk], keys [B][n][Hkv][Dk] and values [B][n][Hkv][Dv] (None
+    when values are key channels), N(0,1) in fp32 rounded to bf16, from a
+    CPU generator seeded with `seed`."""
+    s = w.spec
+    gen = torch.Generator().manual_seed(int(seed))
+    B = int(w.seq_lens.shape[0])
+    q = _randn_bf16((B, n, s.num_q_heads, s.head_dim_k), gen, "cpu").to(device)
+    k = _randn_bf16((B, n, s.num_kv_heads, s.head_dim_k), gen, "cpu").to(device)
+    v = None if s.v_from_k else _randn_bf16((B, n, s.num_kv_heads, s.head_dim_v), gen, "cpu").to(device)
+    return q, k, v

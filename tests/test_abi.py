@@ -155,3 +155,43 @@ def test_reuse_step_argument_checks(L):
     # no launch for an empty batch, whatever the pointers
     assert _call("qasp_decode_step_reuse", b(lay), b(_batch(B=0)), b(pol), None, None, None, None, None, None, 1.0,
                  None, None, 37, None, None, 0, None) == api.OK
+
+
+def test_multi_step_argument_checks(L):
+    """qasp_decode_step_multi: draft count limits, the widened selection
+    capacity of static heads, the multi-query workspace, null arguments."""
+    b = ctypes.byref
+    lay, pol = GQA.c(), api.Policy(1, 4, 32).c()
+    bat = _batch(Hq=32)   # 8 KV heads: 4 heads per group, so at most 4 drafts
+    ms = _call("qasp_max_sel_multi", b(lay), b(pol), 4, 256)
+    assert ms == 37
+    need = _call("qasp_workspace_bytes_multi", b(lay), b(bat), b(pol), 4, ms)
+    assert need > _call("qasp_workspace_bytes", b(lay), b(bat), b(pol), ms)
+    # (lay, bat, pol, n, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel, cnt, max_sel, ws, bytes, stream)
+    args = lambda **kw: [kw.get(k, v) for k, v in (("n", 4), ("q", 1), ("k_new", None), ("v_new", None),
+                                                    ("k_pool", 1), ("v_pool", 1), ("summ", 1), ("scale", 1.0),
+                                                    ("out", 1), ("sel", None), ("cnt", None), ("max_sel", ms),
+                                                    ("ws", 1), ("bytes", need), ("stream", None))]
+    call = lambda lay_=lay, bat_=bat, pol_=pol, **kw: _call("qasp_decode_step_multi", b(lay_), b(bat_), b(pol_),
+                                                            *args(**kw))
+    assert call(n=0) == api.ERR_BAD_SHAPE
+    assert call(n=5) == api.ERR_UNSUPPORTED          # 5 drafts x 4 heads > 16 columns
+    assert call(n=17) == api.ERR_UNSUPPORTED
+    assert call(lay_=MLA.c(), bat_=_batch(Hq=128)) == api.ERR_UNSUPPORTED
+    assert call(q=None) == api.ERR_NULL_ARG
+    assert call(summ=None) == api.ERR_NULL_ARG
+    assert call(out=None) == api.ERR_NULL_ARG
+    assert call(v_pool=None) == api.ERR_NULL_ARG
+    assert call(k_new=1, v_new=None) == api.ERR_NULL_ARG
+    assert call(sel=1, cnt=None) == api.ERR_NULL_ARG
+    assert call(bytes=need - 1) == api.ERR_WORKSPACE
+    assert call(max_sel=-1) == api.ERR_BAD_SHAPE
+    # static heads: the drafts' windows widen the page set (window 32 + 3 tokens: up to 4 pages of 16)
+    spol = api.Policy(0, 0, 0, sink_tokens=4, window_tokens=32, static_heads=[1] * 8).c()
+    assert _call("qasp_max_sel", b(lay), b(spol), 256) == 4
+    assert _call("qasp_max_sel_multi", b(lay), b(spol), 4, 256) == 5
+    need_s = _call("qasp_workspace_bytes_multi", b(lay), b(bat), b(spol), 4, 5)
+    assert call(pol_=spol, max_sel=4, bytes=need_s) == api.ERR_MAX_SEL
+    # no launch for an empty batch, whatever the pointers
+    assert _call("qasp_decode_step_multi", b(lay), b(_batch(B=0)), b(pol), 2, None, None, None, None, None, None,
+                 1.0, None, None, None, ms, None, 0, None) == api.OK
