@@ -15,6 +15,10 @@ Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1
 layers sharing the page table, where the first layer runs the whole step and
 the next R layers append their token and attend over its selection
 (qasp_decode_step_reuse); one JSON line with the per-layer figures.
+
+--drafts N measures the multi-query step instead (qasp_decode_step_multi):
+N draft tokens per sequence appended, one shared selection, causal attention
+per draft; value = draft tokens checked per second.
 """
 import argparse
 import json
@@ -127,6 +131,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reuse", type=int, default=0,
                     help="cross-layer reuse: per group, 1 selecting layer + this many reusing layers")
+    ap.add_argument("--drafts", type=int, default=0,
+                    help="multi-query step: this many draft tokens per sequence")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (a known-size kernel for HBM counters)")
     args = ap.parse_args()
@@ -142,6 +148,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.reuse > 0:
         return run_reuse(args, torch, api, workloads, dev)
+    if args.drafts > 0:
+        return run_drafts(args, torch, api, workloads, dev)
     layers = []
     for i in range(args.layers):
         base = workloads.SPECS[args.workload].seed
@@ -259,6 +267,89 @@ def main():
                      "traffic": profiled_traffic(kernel, spec.name) if one_kernel else None,
                      "algorithmic_bytes": total_bytes},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_drafts(args, torch, api, workloads, dev):
+    """Multi-query steps (N draft tokens per sequence) rotated over independent
+    layer caches; each step appends the drafts (the same values every step),
+    scores and selects once per (sequence, KV head) for all drafts and attends
+    causally."""
+    n = args.drafts
+    layers = []
+    for i in range(args.layers):
+        base = workloads.SPECS[args.workload].seed
+        w = workloads.make(args.workload, seed=base + 100 * i, device=dev)
+        lay, pol = api.layout_of(w), api.policy_of(w)
+        bat = api.Batch(w.page_table, w.seq_lens, w.spec.num_q_heads)
+        msel = api.max_sel_multi(lay, pol, n, bat.max_pages)
+        dq, dk, dv = workloads.drafts(w, n, base + 100 * i + 1, device=dev)
+        summ = torch.zeros((w.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16,
+                           device=dev)
+        api.build_summaries(lay, bat, w.k_pool, summ)
+        B = w.spec.batch
+        layers.append(dict(w=w, lay=lay, pol=pol, bat=bat, msel=msel, dq=dq, dk=dk, dv=dv, summ=summ,
+                           ws=api.new_workspace_multi(lay, bat, pol, n, msel, dev),
+                           sel=torch.empty((B, lay.num_kv_heads, msel), dtype=torch.int32, device=dev),
+                           cnt=torch.empty((B, lay.num_kv_heads), dtype=torch.int32, device=dev),
+                           out=torch.empty((B, n, w.spec.num_q_heads, lay.head_dim_v), dtype=torch.float32,
+                                           device=dev)))
+        log("layer %d ready" % i)
+    torch.cuda.synchronize()
+
+    def step(L):
+        api.decode_step_multi(L["lay"], L["bat"], L["pol"], L["dq"], L["w"].k_pool, L["w"].v_pool, L["summ"],
+                              L["w"].scale, L["ws"], L["msel"], k_new=L["dk"], v_new=L["dv"], out=L["out"],
+                              sel=L["sel"], sel_count=L["cnt"])
+
+    for i in range(args.warmup):
+        step(layers[i % len(layers)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(layers[i % len(layers)])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(layers[i % len(layers)])
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+    w0, L0 = layers[0]["w"], layers[0]
+    spec = w0.spec
+    b_score, b_decode = step_bytes(w0, L0["cnt"].cpu().tolist())
+    # the other drafts' queries and outputs, and every draft's key and value row written
+    extra = (n - 1) * spec.batch * spec.num_q_heads * (spec.head_dim_k * 2 + spec.head_dim_v * 4)
+    extra += n * spec.batch * spec.num_kv_heads * (spec.head_dim_k + spec.head_dim_v) * 2
+    total = b_score + b_decode + extra
+    achieved = total / (step_ms * 1e-3) / 1e9
+    log("multi-query step (%d drafts): events median %.1f us, wall %.1f us/step" % (n, step_ms * 1e3,
+                                                                                   ms_per_step * 1e3))
+    line = {
+        "metric": "draft tokens checked per second, multi-query step with %d drafts per sequence, %s" % (n, spec.name),
+        "value": round(spec.batch * n / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.batch, "seq_len": spec.seq_len, "drafts": n,
+                   "layer_caches_rotated": args.layers},
+        "step_us_events": round(step_ms * 1e3, 2),
+        "roofline": {"kernel": "decode_step_multi (several kernels)", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes": total},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

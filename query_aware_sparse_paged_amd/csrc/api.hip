@@ -179,8 +179,7 @@ static int32_t check_multi(const qasp_layout *lay, const qasp_batch *bat, const 
 }
 static size_t multi_workspace_bytes(const qasp_layout &lay, const qasp_batch &bat, int nq, int max_sel) {
   const size_t rows = (size_t)bat.batch * nq * bat.num_q_heads;
-  return workspace_bytes(lay, multi_batch(bat, nq), max_sel) + align256(rows * lay.head_dim_k * sizeof(uint16_t)) +
-         align256(rows * lay.head_dim_v * sizeof(float));
+  return workspace_bytes(lay, multi_batch(bat, nq), max_sel) + align256(rows * lay.head_dim_k * sizeof(uint16_t));
 }
 
 }  // namespace qasp
@@ -372,30 +371,25 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat, co
   hipStream_t s = (hipStream_t)stream;
   const qasp_batch wbat = multi_batch(*bat, nq);
   const Workspace ws = carve_workspace(*lay, wbat, max_sel, workspace);
-  const size_t rows = (size_t)bat->batch * wbat.num_q_heads;
   uint16_t *q_grouped = (uint16_t *)((char *)workspace + workspace_bytes(*lay, wbat, max_sel));
-  float *out_grouped = (float *)((char *)q_grouped + align256(rows * lay->head_dim_k * sizeof(uint16_t)));
   int32_t *sel_out = sel ? sel : ws.sel;
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
-  const int G = bat->num_q_heads / lay->num_kv_heads;
-  hipError_t e = hipSuccess;
-  if (k_new) e = launch_append_drafts(*lay, *bat, nq, k_new, v_new, k_pool, v_pool, summ, s);
-  // q [B][nq][Hkv][G*Dk] -> [B][Hkv][nq][G*Dk]
-  if (e == hipSuccess)
-    e = launch_swap_rows(q, q_grouped, bat->batch, nq, lay->num_kv_heads,
-                         (size_t)G * lay->head_dim_k * sizeof(uint16_t), s);
+  // q [B][nq][Hkv][G][Dk] -> [B][Hkv][nq][G][Dk], and the drafts appended
+  hipError_t e = launch_prepare_drafts(*lay, *bat, nq, q, q_grouped, k_new, v_new, k_pool, v_pool, summ, s);
+  // many units: score, select and attend in one kernel per (sequence, KV head)
+  const long units = (long)bat->batch * lay->num_kv_heads;
+  if (e == hipSuccess && units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages &&
+      fused_lds_bytes(*lay, wbat, max_sel) <= 160 * 1024)
+    return status_of(launch_fused_step_gqa(*lay, wbat, wpol, q_grouped, nullptr, nullptr, k_pool, v_pool, summ,
+                                           scale, out, sel, sel_count, max_sel, s, nq, pol->window_tokens));
   if (e == hipSuccess && scored)
     e = launch_score_pages(*lay, wbat, wpol, q_grouped, summ, ws.scores, s,
                            token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr));
   if (e == hipSuccess)
     e = launch_select_topk(*lay, wbat, wpol, q_grouped, summ, ws.scores, sel_out, cnt_out, max_sel, s);
-  if (e == hipSuccess)
-    e = launch_decode_gqa(*lay, wbat, wpol, q_grouped, k_pool, v_pool, sel_out, cnt_out, max_sel, scale,
-                          out_grouped, ws, s, nq, pol->window_tokens);
-  // out [B][Hkv][nq][G*Dv] -> [B][nq][Hkv][G*Dv]
-  if (e == hipSuccess)
-    e = launch_swap_rows(out_grouped, out, bat->batch, lay->num_kv_heads, nq,
-                         (size_t)G * lay->head_dim_v * sizeof(float), s);
+  if (e == hipSuccess)  // writes out in the caller's [B][nq][Hq][Dv] order
+    e = launch_decode_gqa(*lay, wbat, wpol, q_grouped, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s,
+                          nq, pol->window_tokens);
   return status_of(e);
 }
 

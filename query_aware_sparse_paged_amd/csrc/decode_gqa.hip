@@ -66,7 +66,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
   attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
   attend::merge_waves<WAVES, DV>(lds, st, G, [&](int h, int dv, float a, float lsum, float M) {
     if (splits == 1) {
-      out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
+      size_t row = head0 + h;
+      if constexpr (CAUSAL) {  // the caller's [B][nq][Hq / nq] order
+        const int per_query = G / nq;
+        row = ((size_t)b * nq + h / per_query) * (Hq / nq) + (size_t)g * per_query + h % per_query;
+      }
+      out[row * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
     } else {
       const size_t ps_idx = (head0 + h) * splits + split;
       partial[ps_idx * DV + dv] = a;
@@ -78,13 +83,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
 // Combines the split partials of every (sequence, query head):
 // out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.  One block per
 // (sequence, head); a thread owns 4 consecutive channels and reads four
-// splits' partials per step (16-byte loads, several in flight).
+// splits' partials per step (16-byte loads, several in flight).  Head h of
+// the partials is column h % Gp of KV head h / Gp's group; with nq draft
+// queries that column is head (h % Gp) % (Gp / nq) of draft (h % Gp) / (Gp / nq),
+// written to out [B][nq][Hq / nq][Dv] (nq = 1: out [B][Hq][Dv]).
 __global__ __launch_bounds__(128) void merge_splits_kernel(const float *__restrict__ partial,
                                                            const float2 *__restrict__ partial_ml,
                                                            float *__restrict__ out, int Hq, int splits,
-                                                           int dv_dim) {
+                                                           int dv_dim, int nq, int Gp) {
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t base = ((size_t)b * Hq + h) * splits;
+  const int per_query = Gp / nq, col = h % Gp;
+  const size_t out_row = ((size_t)b * nq + col / per_query) * (Hq / nq) + (size_t)(h / Gp) * per_query +
+                         col % per_query;
   float M = -INFINITY;
   for (int s = 0; s < splits; s++) M = fmaxf(M, partial_ml[base + s].x);
   for (int c = 4 * threadIdx.x; c < dv_dim; c += 4 * blockDim.x) {
@@ -125,14 +136,14 @@ __global__ __launch_bounds__(128) void merge_splits_kernel(const float *__restri
       }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    *(float4 *)(out + ((size_t)b * Hq + h) * dv_dim + c) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    *(float4 *)(out + out_row * dv_dim + c) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
   }
 }
 
 hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,
-                               hipStream_t stream) {
+                               hipStream_t stream, int nq, int Gp) {
   hipLaunchKernelGGL(merge_splits_kernel, dim3(Hq, batch), dim3(dv_dim >= 512 ? 128 : dv_dim / 4), 0, stream,
-                     ws.partial, ws.partial_ml, out, Hq, ws.splits, dv_dim);
+                     ws.partial, ws.partial_ml, out, Hq, ws.splits, dv_dim, nq, Gp > 0 ? Gp : Hq);
   return hipGetLastError();
 }
 
@@ -153,7 +164,7 @@ hipError_t launch_decode_gqa(const qasp_layout &lay, const qasp_batch &bat, cons
                      pol.static_head_mask, nq, window_q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ws.splits == 1) return e;
-  return launch_merge_splits(ws, bat.batch, bat.num_q_heads, lay.head_dim_v, out, stream);
+  return launch_merge_splits(ws, bat.batch, bat.num_q_heads, lay.head_dim_v, out, stream, nq, G);
 }
 
 }  // namespace qasp

@@ -46,9 +46,6 @@
 
 namespace qasp {
 
-hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,
-                               hipStream_t stream);
-
 namespace {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));

@@ -90,14 +90,20 @@ __device__ __forceinline__ int2 unit_for_block(int i, const int32_t *seq_lens, i
   return make_int2(b, g);
 }
 
-template <int D, int DV, int PS, int W>
+// CAUSAL: the multi-query form (n_draft draft queries x G / n_draft heads as
+// the group's columns, query rows already in that order, drafts already
+// appended): column n scores the tokens up to its draft's position and, for a
+// static head, its own window of window_q tokens (window_tokens is then the
+// drafts' union); the output goes to [B][n_draft][Hq / n_draft][DV].
+template <int D, int DV, int PS, int W, bool CAUSAL = false>
 __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     uint16_t *__restrict__ k_pool, uint16_t *__restrict__ v_pool, uint16_t *__restrict__ summ,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, float *__restrict__ out,
     int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
-    int window_tokens, uint64_t static_mask, float scale_log2, uint32_t bucket_mul, int lpt) {
+    int window_tokens, uint64_t static_mask, float scale_log2, uint32_t bucket_mul, int lpt, int n_draft,
+    int window_q) {
   static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
@@ -297,7 +303,15 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const int win_begin = is_static ? max(0, L - window_tokens) : 0;
   uint4 bq[D / 32];
   attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
-  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  int Lq = L, winq = 0;
+  if constexpr (CAUSAL) {
+    const int per_query = G / n_draft;
+    const int i = n_col < G ? n_col / per_query : n_draft - 1;
+    Lq = L - (n_draft - 1 - i);
+    winq = max(0, Lq - window_q);
+  }
+  const attend::PageWork<PS, D, DV, CAUSAL> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin,
+                                               is_static, scale_log2, Lq, winq};
   const bool pre = wave < n_known;  // wave-uniform
   // issued by every wave (a valid page when there is nothing to preload), so
   // the registers are always defined and the load is never waited on here
@@ -352,7 +366,12 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane, pre && npg > 0, first);
   attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
     (void)M;
-    out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
+    size_t row = head0 + h;
+    if constexpr (CAUSAL) {
+      const int per_query = G / n_draft;
+      row = ((size_t)b * n_draft + h / per_query) * (Hq / n_draft) + (size_t)g * per_query + h % per_query;
+    }
+    out[row * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
   });
 }
 
@@ -464,7 +483,8 @@ size_t fused_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_se
 hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
-                                 int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream) {
+                                 int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream, int n_draft,
+                                 int window_q) {
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = FusedLds(mp, max_sel, G).total;
@@ -474,11 +494,12 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   const int units = bat.batch * lay.num_kv_heads;
   const int lpt = units > device_cu_count() ? 1 : 0;
   dim3 grid(units);
-  hipLaunchKernelGGL((fused_step_gqa_kernel<128, 128, 16, kFusedWaves>), grid, dim3(kFusedWaves * 64), lds,
-                     stream, q, k_new, v_new, k_pool, v_pool, summ, bat.page_table, bat.seq_lens, out, sel,
-                     sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G,
-                     pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens, pol.window_tokens,
-                     pol.static_head_mask, scale_log2, bucket_mul, lpt);
+  auto kernel = n_draft > 1 ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, true>
+                            : fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kFusedWaves * 64), lds, stream, q, k_new, v_new, k_pool, v_pool, summ,
+                     bat.page_table, bat.seq_lens, out, sel, sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads,
+                     lay.num_kv_heads, G, pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens,
+                     pol.window_tokens, pol.static_head_mask, scale_log2, bucket_mul, lpt, n_draft, window_q);
   return hipGetLastError();
 }
 

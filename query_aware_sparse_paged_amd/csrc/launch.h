@@ -72,19 +72,20 @@ size_t fused_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_se
 hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
-                                 int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream);
+                                 int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream, int n_draft = 1,
+                                 int window_q = 0);
 hipError_t launch_fused_reuse_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                   const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                   uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
                                   const int32_t *sel, const int32_t *sel_count, int max_sel, hipStream_t stream);
-// Multi-query step: the nq draft tokens' append, and the middle-dimension
-// exchange dst[b][y][x][:] = src[b][x][y][:] (chunk_bytes a multiple of 16).
-hipError_t launch_append_drafts(const qasp_layout &lay, const qasp_batch &bat, int nq, const uint16_t *k_new,
-                                const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ,
-                                hipStream_t stream);
-hipError_t launch_swap_rows(const void *src, void *dst, int batch, int X, int Y, size_t chunk_bytes,
-                            hipStream_t stream);
+// Multi-query step: the query into the grouped order ([B][Hkv][nq][G][Dk])
+// and, when k_new is given, the nq draft tokens written with their summaries.
+hipError_t launch_prepare_drafts(const qasp_layout &lay, const qasp_batch &bat, int nq, const uint16_t *q,
+                                 uint16_t *q_grouped, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                                 uint16_t *v_pool, uint16_t *summ, hipStream_t stream);
+// Merge of the split partials; Gp (> 0) and nq map the partials' grouped
+// heads to out [B][nq][Hq / nq][Dv] (nq = 1: out [B][Hq][Dv]).
 hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,
-                               hipStream_t stream);
+                               hipStream_t stream, int nq = 1, int Gp = 0);
 
 }  // namespace qasp

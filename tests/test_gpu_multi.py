@@ -85,8 +85,14 @@ def test_multi_step_few_sequences(nq):
 
 
 def test_multi_step_many_units_ragged_tail():
-    # 64 sequences x 8 KV heads (512 units; the decode splits), lengths not page-aligned
+    # 64 sequences x 8 KV heads: 512 units, one kernel per unit after the draft append; lengths not page-aligned
     _run("llama8b_b32_32k", 64, 4, 1000, 300)
+
+
+@pytest.mark.parametrize("nq,window", [(3, 1024), (2, 0)])
+def test_multi_step_many_units_static_heads(nq, window):
+    # 32 sequences x 8 KV heads (one kernel per unit), A-shape heads beside query-aware heads
+    _run("ragged_b64_mixed", 32, nq, 2600, 900, window_tokens=window)
 
 
 @pytest.mark.parametrize("nq", [2, 3])
