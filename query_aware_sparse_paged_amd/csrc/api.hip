@@ -172,7 +172,7 @@ static int32_t check_multi(const qasp_layout *lay, const qasp_batch *bat, const 
   if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
   if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
   if (nq < 1) return QASP_ERR_BAD_SHAPE;
-  if (nq > kMaxDrafts || family_of(*lay) != kFamilyGqa) return QASP_ERR_UNSUPPORTED;
+  if (nq > kMaxDrafts || nq > lay->page_size || family_of(*lay) != kFamilyGqa) return QASP_ERR_UNSUPPORTED;
   if ((long)(bat->num_q_heads / lay->num_kv_heads) * nq > 16) return QASP_ERR_UNSUPPORTED;
   if (pol->window_tokens > INT32_MAX - kMaxDrafts) return QASP_ERR_BAD_SHAPE;
   return QASP_OK;

@@ -16,76 +16,104 @@
 
 namespace qasp {
 
+constexpr int kDraftsMax = 16;  // drafts per sequence (at most one page of 16 tokens)
+
 // One block per (KV head g, sequence b), 128 threads:
 //   - copies the group's query rows into the grouped order: row r = i*G + h of
 //     unit (b, g) is head g*G + h of draft i;
 //   - when k_new is given, writes draft i's key row and value column at
 //     position L - nq + i (token i of b is row b * nq + i of k_new / v_new,
 //     [B][nq][Hkv][D] and [B][nq][Hkv][Dv]) and folds the keys into the page
-//     summaries: thread w < D/2 owns summary word w and carries the page's
-//     running min / max over the drafts in registers (a draft in slot 0
-//     starts a page), writing each page's words once.
+//     summaries.  The drafts span at most two pages (nq <= page size), whose
+//     physical pages are read once; thread t loads key word t and value
+//     channel t of every draft first (needs D/2 <= 128 and Dv <= 128 threads),
+//     and thread w < D/2 carries summary word w's
+//     running min / max over the drafts of a page in registers (a draft in
+//     slot 0 starts a page), writing each page's words once.
 // Drafts at negative positions (L < nq) are skipped.
 __global__ __launch_bounds__(128) void prepare_drafts_kernel(TokenAppend ap, const uint4 *__restrict__ q,
                                                              uint4 *__restrict__ q_grouped,
                                                              const int32_t *__restrict__ page_table,
                                                              const int32_t *__restrict__ seq_lens, int nq, int G,
                                                              int pt_stride) {
-  const int g = blockIdx.x, b = blockIdx.y, Hkv = ap.num_kv_heads;
+  const int g = blockIdx.x, b = blockIdx.y, Hkv = ap.num_kv_heads, tid = threadIdx.x;
+  const int words = ap.head_dim_k / 2, DV = ap.head_dim_v;
+  // every draft's key word / value entry of this thread, loaded before the
+  // length is known (the rows exist whatever the length)
+  uint32_t kv[kDraftsMax];
+  uint16_t vv[kDraftsMax];
+  if (ap.k_new != nullptr) {
+#pragma unroll
+    for (int d = 0; d < kDraftsMax; d++) {
+      kv[d] = d < nq && tid < words ? ap.k_new[(((size_t)b * nq + d) * Hkv + g) * words + tid] : 0u;
+      vv[d] = d < nq && tid < DV && ap.v_new ? ap.v_new[(((size_t)b * nq + d) * Hkv + g) * DV + tid] : 0;
+    }
+  }
+  const int L = seq_lens[b], ps = ap.ps;
+  const bool writes = ap.k_new != nullptr && L > 0;
+  const int i0 = max(0, nq - L);  // first draft with a position
+  const int p0 = L - nq + i0;     // its position
+  const int j0 = p0 / ps, t0 = p0 % ps;
+  int phys0 = 0, phys1 = 0;
+  if (writes) {
+    phys0 = page_table[(size_t)b * pt_stride + j0];
+    phys1 = page_table[(size_t)b * pt_stride + (L - 1) / ps];
+  }
   const int row16 = ap.head_dim_k / 8;  // 16-byte words per query row
-  for (int x = threadIdx.x; x < nq * G * row16; x += blockDim.x) {
+  for (int x = tid; x < nq * G * row16; x += blockDim.x) {
     const int r = x / row16, c = x % row16, i = r / G, h = r % G;
     q_grouped[(((size_t)b * Hkv + g) * nq * G + r) * row16 + c] =
         q[(((size_t)b * nq + i) * Hkv * G + (size_t)g * G + h) * row16 + c];
   }
-  if (!ap.k_new) return;
-  const int L = seq_lens[b], ps = ap.ps, words = ap.head_dim_k / 2;
-  const int i0 = max(0, nq - L);  // first draft with a position
-  for (int w = threadIdx.x; w < words; w += blockDim.x) {
+  if (!writes) return;
+  // drafts i0 ... nq - 1 are written (loops over compile-time indices keep
+  // kv / vv in registers)
+  if (tid < words) {
+    const int w = tid;
     uint32_t lo = 0, hi = 0;
-    int cur_phys = -1;
-    for (int i = i0; i < nq; i++) {
+    if (ap.summ && t0 != 0) {  // the first page already holds tokens
+      const uint32_t *sp = ap.summ + ((size_t)phys0 * Hkv + g) * 2 * words;
+      lo = sp[w];
+      hi = sp[words + w];
+    }
+#pragma unroll
+    for (int i = 0; i < kDraftsMax; i++) {
+      if (i >= nq) break;
+      if (i < i0) continue;
       const int pos = L - nq + i, t = pos % ps;
-      const int phys = page_table[(size_t)b * pt_stride + pos / ps];
-      const size_t ph = (size_t)phys * Hkv + g;
-      const uint32_t kv = ap.k_new[(((size_t)b * nq + i) * Hkv + g) * words + w];
-      ap.k_pool[(ph * ps + t) * words + w] = kv;
+      const size_t ph = (size_t)(pos / ps == j0 ? phys0 : phys1) * Hkv + g;
+      const uint32_t k = kv[i];
+      ap.k_pool[(ph * ps + t) * words + w] = k;
       if (!ap.summ) continue;
-      if (phys != cur_phys) {
-        if (cur_phys >= 0) {
-          uint32_t *sp = ap.summ + ((size_t)cur_phys * Hkv + g) * 2 * words;
+      if (t == 0) {
+        if (i > i0) {  // the drafts cross into the second page: the first page is complete
+          uint32_t *sp = ap.summ + ((size_t)phys0 * Hkv + g) * 2 * words;
           sp[w] = lo;
           sp[words + w] = hi;
         }
-        cur_phys = phys;
-        if (t == 0) {
-          lo = hi = kv;
-          continue;
-        }
-        const uint32_t *sp = ap.summ + ph * 2 * words;
-        lo = sp[w];
-        hi = sp[words + w];
+        lo = hi = k;
+        continue;
       }
-      const int v0 = bf16_order_key(kv & 0xffffu), v1 = bf16_order_key(kv >> 16);
+      const int v0 = bf16_order_key(k & 0xffffu), v1 = bf16_order_key(k >> 16);
       lo = bf16_from_order_key(min(v0, bf16_order_key(lo & 0xffffu))) |
            (bf16_from_order_key(min(v1, bf16_order_key(lo >> 16))) << 16);
       hi = bf16_from_order_key(max(v0, bf16_order_key(hi & 0xffffu))) |
            (bf16_from_order_key(max(v1, bf16_order_key(hi >> 16))) << 16);
     }
-    if (ap.summ && cur_phys >= 0) {
-      uint32_t *sp = ap.summ + ((size_t)cur_phys * Hkv + g) * 2 * words;
+    if (ap.summ) {
+      uint32_t *sp = ap.summ + ((size_t)((L - 1) / ps == j0 ? phys0 : phys1) * Hkv + g) * 2 * words;
       sp[w] = lo;
       sp[words + w] = hi;
     }
   }
-  if (!ap.v_pool) return;
-  const int DV = ap.head_dim_v;
-  for (int x = threadIdx.x; x < (nq - i0) * DV; x += blockDim.x) {
-    const int i = i0 + x / DV, dv = x % DV;
+  if (!ap.v_pool || tid >= DV) return;
+#pragma unroll
+  for (int i = 0; i < kDraftsMax; i++) {
+    if (i >= nq) break;
+    if (i < i0) continue;
     const int pos = L - nq + i;
-    const int phys = page_table[(size_t)b * pt_stride + pos / ps];
-    ap.v_pool[(((size_t)phys * Hkv + g) * DV + dv) * ps + pos % ps] =
-        ap.v_new[(((size_t)b * nq + i) * Hkv + g) * DV + dv];
+    const size_t ph = (size_t)(pos / ps == j0 ? phys0 : phys1) * Hkv + g;
+    ap.v_pool[(ph * DV + tid) * ps + pos % ps] = vv[i];
   }
 }
 

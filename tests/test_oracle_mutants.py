@@ -1,5 +1,6 @@
 """Plants plausible mistakes in a temporary copy of the oracle (on the CPU
-only) and checks that the pins in test_oracle_pins.py catch every one."""
+only) and checks that the pins in test_oracle_pins.py and
+test_oracle_multi.py catch every one."""
 import os
 import shutil
 import subprocess
@@ -30,7 +31,19 @@ MUTANTS = {
     "window one token longer": ("if (a < sink_end || e > win_begin) flags[j] = 1;",
                                 "if (a < sink_end || e >= win_begin) flags[j] = 1;"),
     "static mask ignores the sink": ("(!st || pos < sink_end || pos >= win_begin)", "(!st || pos >= win_begin)"),
+    # multi-query step
+    "drafts scored by the last one only": ("for (int32_t r = 0; r < nq * G; r++) {",
+                                           "for (int32_t r = (nq - 1) * G; r < nq * G; r++) {"),
+    "every draft stops at the first draft": ("int64_t L = (int64_t)bat->seq_lens[b] - nq + 1 + i;",
+                                             "int64_t L = (int64_t)bat->seq_lens[b] - nq + 1;"),
+    "draft sees the next draft": ("int64_t L = (int64_t)bat->seq_lens[b] - nq + 1 + i;",
+                                  "int64_t L = (int64_t)bat->seq_lens[b] - nq + 2 + i - (i == nq - 1);"),
+    "static union not widened": ("wide.window_tokens = pol->window_tokens + nq - 1;",
+                                 "wide.window_tokens = pol->window_tokens;"),
+    "empty window widened": ("if (pol->window_tokens > 0) wide.window_tokens",
+                             "if (pol->window_tokens >= 0) wide.window_tokens"),
 }
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_multi.py"]
 
 
 def _run_mutant(item):
@@ -46,8 +59,8 @@ def _run_mutant(item):
         subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-shared",
                                "-fPIC", os.path.join(d, "oracle.c"), "-o", so, "-lm"])
         env = dict(os.environ, QASP_ORACLE_LIB=so)
-        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                           [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                            env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
         # caught = a pin test failed (not a crash, import error or collection error)
         caught = r.returncode == 1 and " failed" in r.stdout and "error" not in r.stdout.split("\n")[-2]
