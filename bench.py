@@ -19,6 +19,10 @@ the next R layers append their token and attend over its selection
 --drafts N measures the multi-query step instead (qasp_decode_step_multi):
 N draft tokens per sequence appended, one shared selection, causal attention
 per draft; value = draft tokens checked per second.
+
+--host-pool measures the host-tier pool instead: K/V pools in pinned host
+memory mapped into the GPU (qasp_host_alloc), summaries in HBM; the step's
+attention reads the selected pages over the host link.
 """
 import argparse
 import json
@@ -133,6 +137,8 @@ def main():
                     help="cross-layer reuse: per group, 1 selecting layer + this many reusing layers")
     ap.add_argument("--drafts", type=int, default=0,
                     help="multi-query step: this many draft tokens per sequence")
+    ap.add_argument("--host-pool", action="store_true",
+                    help="K/V pools in pinned host memory mapped into the GPU")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (a known-size kernel for HBM counters)")
     args = ap.parse_args()
@@ -150,6 +156,8 @@ def main():
         return run_reuse(args, torch, api, workloads, dev)
     if args.drafts > 0:
         return run_drafts(args, torch, api, workloads, dev)
+    if args.host_pool:
+        return run_host_pool(args, torch, api, workloads, dev)
     layers = []
     for i in range(args.layers):
         base = workloads.SPECS[args.workload].seed
@@ -267,6 +275,71 @@ def main():
                      "traffic": profiled_traffic(kernel, spec.name) if one_kernel else None,
                      "algorithmic_bytes": total_bytes},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def run_host_pool(args, torch, api, workloads, dev):
+    """One-token steps with the K/V pools in host-tier memory (one layer
+    cache: the link does not cache, so rotation changes nothing)."""
+    w = workloads.make(args.workload, device=dev)
+    lay, pol, spec = api.layout_of(w), api.policy_of(w), w.spec
+    bat = api.Batch(w.page_table, w.seq_lens, spec.num_q_heads)
+    msel = api.max_sel(lay, pol, bat.max_pages)
+    summ = torch.zeros((w.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16, device=dev)
+    api.build_summaries(lay, bat, w.k_pool, summ)
+    kh = api.host_pool_like(w.k_pool)
+    vh = None if w.v_pool is None else api.host_pool_like(w.v_pool)
+    w.k_pool = w.v_pool = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("host-tier pools ready: %.2f GB pinned" % ((kh.buf.nbytes + (vh.buf.nbytes if vh else 0)) / 1e9))
+    ws = api.new_workspace(lay, bat, pol, msel, dev)
+    B = spec.batch
+    sel = torch.empty((B, lay.num_kv_heads, msel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, lay.num_kv_heads), dtype=torch.int32, device=dev)
+    out = torch.empty((B, spec.num_q_heads, lay.head_dim_v), dtype=torch.float32, device=dev)
+
+    def step():
+        api.decode_step(lay, bat, pol, w.q, kh, vh, summ, w.scale, ws, msel, k_new=w.k_new, v_new=w.v_new, out=out,
+                        sel=sel, sel_count=cnt)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    b_score, b_decode = step_bytes(w, cnt.cpu().tolist())
+    qo = spec.batch * spec.num_q_heads * (spec.head_dim_k * 2 + spec.head_dim_v * 4)
+    kv_link = b_decode - qo  # the selected K/V tiles: read over the host link
+    kv_link += spec.batch * spec.num_kv_heads * (spec.head_dim_k + (0 if spec.v_from_k else spec.head_dim_v)) * 2
+    link = kv_link / (ms_per_step * 1e-3) / 1e9
+    log("host-tier step: %.1f us, %.1f GB/s over the host link" % (ms_per_step * 1e3, link))
+    line = {
+        "metric": "decode tokens/s with the K/V pools in host memory (host-tier pool), %s" % spec.name,
+        "value": round(B / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": B, "seq_len": spec.seq_len, "pools": "host-tier"},
+        "roofline": {"kernel": "decode step, selected pages over the host link", "bound": "host-link",
+                     "achieved": round(link, 2), "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(link / HOST_LINK_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes": kv_link},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

@@ -24,6 +24,9 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns and
  *     allocates every buffer; the library never allocates device memory.
+ *     k_pool / v_pool may also be the device pointer of a host-tier
+ *     allocation (qasp_host_alloc): the kernels then read the selected pages,
+ *     and write the appended tokens, over the host link.
  *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting for it.
@@ -52,7 +55,8 @@ typedef enum {
     QASP_ERR_UNSUPPORTED = -3,     /* a shape the kernels are not built for   */
     QASP_ERR_WORKSPACE = -4,       /* workspace smaller than qasp_workspace_bytes */
     QASP_ERR_MAX_SEL = -5,         /* max_sel below qasp_max_sel             */
-    QASP_ERR_LAUNCH = -6           /* a HIP launch failed                     */
+    QASP_ERR_LAUNCH = -6,          /* a HIP launch failed                     */
+    QASP_ERR_ALLOC = -7            /* a host-tier allocation failed           */
 } qasp_status;
 
 /* Pool layout (row-major, bf16):
@@ -265,6 +269,21 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat,
                                float *out, int32_t *sel, int32_t *sel_count,
                                int32_t max_sel, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* Host-tier KV pool (CPU-GPU cooperative loading: the full KV cache stays in
+ * host RAM and each decode step loads only the pages it needs; SCBench notes,
+ * the discussion of CPU-GPU cooperation for Quest / RetrievalAttention).
+ * Allocates `bytes` of pinned host memory mapped into the current device's
+ * address space, coherent (GPU accesses are not cached across kernels):
+ * *host_ptr is its host address, *device_ptr the address kernels use (pass it
+ * as k_pool / v_pool).  Summaries, page tables and workspaces stay in device
+ * memory, so scoring and selection never cross the host link; the attention
+ * reads only the selected pages.  Errors: QASP_ERR_NULL_ARG,
+ * QASP_ERR_BAD_SHAPE (bytes == 0), QASP_ERR_ALLOC (both pointers set to
+ * NULL).  Free with qasp_host_free (host_ptr); the memory must not be in use
+ * by queued work. */
+int32_t qasp_host_alloc(size_t bytes, void **host_ptr, void **device_ptr);
+int32_t qasp_host_free(void *host_ptr);
 
 #ifdef __cplusplus
 }

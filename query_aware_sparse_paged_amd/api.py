@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # QASP_LIB may point at another build of the same library (e.g. a tuning build)
 LIB_PATH = os.environ.get("QASP_LIB") or os.path.join(_HERE, "libqasp.so")
 
-OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MAX_SEL, ERR_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MAX_SEL, ERR_LAUNCH, ERR_ALLOC = \
+    0, -1, -2, -3, -4, -5, -6, -7
 
 
 class QaspError(RuntimeError):
@@ -64,6 +65,8 @@ EXPORTS = {
     "qasp_decode_step_reuse": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 2 +
                                [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p]),
+    "qasp_host_alloc": (ctypes.c_int32, [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "qasp_host_free": (ctypes.c_int32, [ctypes.c_void_p]),
     "qasp_max_sel_multi": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]),
     "qasp_workspace_bytes_multi": (ctypes.c_size_t, [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_int32]),
     "qasp_decode_step_multi": (ctypes.c_int32, [ctypes.c_void_p] * 3 + [ctypes.c_int32] + [ctypes.c_void_p] * 6 +
@@ -143,6 +146,10 @@ def _ptr(t: Optional[torch.Tensor]):
 def _dev(t: Optional[torch.Tensor], dtype, name, ndim=None):
     if t is None:
         return None
+    if isinstance(t, MappedTensor):  # a host-tier pool
+        if t.dtype != dtype or (ndim is not None and t.dim() != ndim):
+            raise ValueError("%s must be a %d-dim %s host-tier view" % (name, ndim or 0, dtype))
+        return t
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
     if t.dtype != dtype:
@@ -377,3 +384,62 @@ def decode_step_multi(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v
                                         int(max_sel_n), _ptr(workspace), workspace.numel(), _stream()),
            "qasp_decode_step_multi")
     return out
+
+
+class MappedTensor:
+    """A contiguous array in host-tier memory (qasp_host_alloc): `host` is a
+    CPU tensor over the memory (to fill or read it), data_ptr() the address
+    the kernels use.  Pass it where a pool tensor is expected."""
+
+    def __init__(self, buf: "HostBuffer", shape, dtype, offset: int = 0):
+        self.buf, self.shape, self.dtype, self.offset = buf, tuple(shape), dtype, offset
+        n = 1
+        for x in self.shape:
+            n *= x
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        if offset + nbytes > buf.nbytes:
+            raise ValueError("view past the end of the host buffer")
+        raw = (ctypes.c_uint8 * nbytes).from_address(buf.host_ptr + offset)
+        self.host = torch.frombuffer(raw, dtype=torch.uint8).view(dtype).view(self.shape)
+
+    def data_ptr(self) -> int:
+        return self.buf.device_ptr + self.offset
+
+    def dim(self) -> int:
+        return len(self.shape)
+
+    def is_contiguous(self) -> bool:
+        return True
+
+
+class HostBuffer:
+    """Pinned host memory mapped into the current GPU's address space (a
+    host-tier KV pool).  Freed by free() or when garbage-collected; no queued
+    work may still use it then."""
+
+    def __init__(self, nbytes: int):
+        h, d = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib().qasp_host_alloc(int(nbytes), ctypes.byref(h), ctypes.byref(d)), "qasp_host_alloc")
+        self.host_ptr, self.device_ptr, self.nbytes = h.value, d.value, int(nbytes)
+
+    def view(self, shape, dtype=torch.bfloat16, offset: int = 0) -> MappedTensor:
+        return MappedTensor(self, shape, dtype, offset)
+
+    def free(self):
+        if self.host_ptr:
+            _check(lib().qasp_host_free(ctypes.c_void_p(self.host_ptr)), "qasp_host_free")
+            self.host_ptr = self.device_ptr = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def host_pool_like(t: torch.Tensor) -> MappedTensor:
+    """A host-tier copy of pool tensor t (same shape and dtype, contents copied)."""
+    buf = HostBuffer(t.numel() * t.element_size())
+    m = buf.view(t.shape, t.dtype)
+    m.host.copy_(t.cpu() if t.is_cuda else t)
+    return m

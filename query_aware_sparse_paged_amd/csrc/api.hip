@@ -199,6 +199,7 @@ const char *qasp_status_string(int32_t status) {
     case QASP_ERR_WORKSPACE: return "workspace too small";
     case QASP_ERR_MAX_SEL: return "max_sel smaller than the largest possible selection";
     case QASP_ERR_LAUNCH: return "HIP kernel launch failed";
+    case QASP_ERR_ALLOC: return "host-tier allocation failed";
     default: return "unknown status";
   }
 }
@@ -333,6 +334,28 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (e == hipSuccess)
     e = launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
   return status_of(e);
+}
+
+int32_t qasp_host_alloc(size_t bytes, void **host_ptr, void **device_ptr) {
+  if (!host_ptr || !device_ptr) return QASP_ERR_NULL_ARG;
+  *host_ptr = nullptr;
+  *device_ptr = nullptr;
+  if (bytes == 0) return QASP_ERR_BAD_SHAPE;
+  void *h = nullptr, *d = nullptr;
+  if (hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess || !h)
+    return QASP_ERR_ALLOC;
+  if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess || !d) {
+    (void)hipHostFree(h);
+    return QASP_ERR_ALLOC;
+  }
+  *host_ptr = h;
+  *device_ptr = d;
+  return QASP_OK;
+}
+
+int32_t qasp_host_free(void *host_ptr) {
+  if (!host_ptr) return QASP_ERR_NULL_ARG;
+  return hipHostFree(host_ptr) == hipSuccess ? QASP_OK : QASP_ERR_ALLOC;
 }
 
 int32_t qasp_max_sel_multi(const qasp_layout *lay, const qasp_policy *pol, int32_t n_query, int32_t max_pages) {

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     assert re.match(r"^\d+\.\d+\.\d+$", api.version())
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert api.status_string(s) != "unknown status"
     assert api.status_string(-99) == "unknown status"
 
@@ -195,3 +195,20 @@ def test_multi_step_argument_checks(L):
     # no launch for an empty batch, whatever the pointers
     assert _call("qasp_decode_step_multi", b(lay), b(_batch(B=0)), b(pol), 2, None, None, None, None, None, None,
                  1.0, None, None, None, ms, None, 0, None) == api.OK
+
+
+def test_host_tier_allocation_argument_checks(L):
+    """qasp_host_alloc / qasp_host_free: argument errors come before any HIP
+    call (here, without a GPU, a valid request reports QASP_ERR_ALLOC with both
+    pointers cleared)."""
+    h, d = ctypes.c_void_p(1), ctypes.c_void_p(1)
+    assert _call("qasp_host_alloc", 1024, None, ctypes.byref(d)) == api.ERR_NULL_ARG
+    assert _call("qasp_host_alloc", 1024, ctypes.byref(h), None) == api.ERR_NULL_ARG
+    assert _call("qasp_host_alloc", 0, ctypes.byref(h), ctypes.byref(d)) == api.ERR_BAD_SHAPE
+    assert h.value is None and d.value is None
+    assert _call("qasp_host_free", None) == api.ERR_NULL_ARG
+    import torch
+    if not torch.cuda.is_available():
+        h, d = ctypes.c_void_p(1), ctypes.c_void_p(1)
+        assert _call("qasp_host_alloc", 1024, ctypes.byref(h), ctypes.byref(d)) == api.ERR_ALLOC
+        assert h.value is None and d.value is None

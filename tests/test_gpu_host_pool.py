@@ -1,0 +1,73 @@
+"""GPU parity of the host-tier KV pool: the K/V pools live in pinned host
+memory mapped into the GPU (qasp_host_alloc); summaries, page tables and
+workspaces stay in device memory (CPU-GPU cooperative loading: SCBench notes,
+the discussion of CPU-GPU cooperation for Quest / RetrievalAttention).
+
+The same kernels run on the same data as with device pools, so the bar is
+bit-equality with the device-pool run: outputs, selections and the pools
+after the step's append; and the outputs within 5e-3 of the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from query_aware_sparse_paged_amd import api, workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import oracle
+    from gpu_cases import DEV, OUT_TOL, olayout, opolicy
+
+
+def _step(w, lay, pol, kp, vp, summ, bat, msel):
+    ws = api.new_workspace(lay, bat, pol, msel, DEV)
+    sel = torch.full((w.spec.batch, lay.num_kv_heads, msel), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((w.spec.batch, lay.num_kv_heads), -7, dtype=torch.int32, device=DEV)
+    out = api.decode_step(lay, bat, pol, w.q.to(DEV), kp, vp, summ, w.scale, ws, msel, k_new=w.k_new.to(DEV),
+                          v_new=None if w.v_new is None else w.v_new.to(DEV), sel=sel, sel_count=cnt)
+    torch.cuda.synchronize()
+    return out.cpu(), sel.cpu(), cnt.cpu()
+
+
+@pytest.mark.parametrize("name,batch,seq_len", [("llama8b_b32_32k", 3, 1500),    # kernel chain
+                                                ("llama8b_b32_32k", 32, 1200),   # one kernel per unit
+                                                ("ragged_b64_mixed", 32, 3000),  # static heads, one kernel
+                                                ("mla_b16_64k", 2, 6000)])       # latent heads
+def test_host_tier_pools_match_device_pools(name, batch, seq_len):
+    print("host-tier case", name, batch, seq_len, flush=True)
+    w = workloads.make(name, device="cpu", seed=5, batch=batch, seq_len=seq_len, seq_len_min=seq_len // 2)
+    lay, pol = api.layout_of(w), api.policy_of(w)
+    bat = api.Batch(w.page_table.to(DEV), w.seq_lens.to(DEV), w.spec.num_q_heads)
+    msel = api.max_sel(lay, pol, bat.max_pages)
+    # the token at L-1 is written again by the append with a new value, so the
+    # pools after the step show the append went through
+    gen = torch.Generator().manual_seed(9)
+    w.k_new = torch.randn(w.k_new.shape, generator=gen).to(torch.bfloat16)
+    if w.v_new is not None:
+        w.v_new = torch.randn(w.v_new.shape, generator=gen).to(torch.bfloat16)
+
+    summ_d = torch.zeros((lay.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16,
+                         device=DEV)
+    kd = w.k_pool.to(DEV)
+    vd = None if w.v_pool is None else w.v_pool.to(DEV)
+    api.build_summaries(lay, bat, kd, summ_d)
+    summ_h = summ_d.clone()
+    kh = api.host_pool_like(w.k_pool)
+    vh = None if w.v_pool is None else api.host_pool_like(w.v_pool)
+
+    out_d, sel_d, cnt_d = _step(w, lay, pol, kd, vd, summ_d, bat, msel)
+    out_h, sel_h, cnt_h = _step(w, lay, pol, kh, vh, summ_h, bat, msel)
+    assert torch.equal(cnt_h, cnt_d) and torch.equal(sel_h, sel_d)
+    assert torch.equal(out_h.view(torch.int32), out_d.view(torch.int32))
+    assert torch.equal(kh.host.view(torch.int16), kd.cpu().view(torch.int16))
+    if vh is not None:
+        assert torch.equal(vh.host.view(torch.int16), vd.cpu().view(torch.int16))
+    assert torch.equal(summ_h.cpu().view(torch.int16), summ_d.cpu().view(torch.int16))
+
+    # and the oracle's attention over that selection
+    olay, opol = olayout(lay), opolicy(pol)
+    kbits = workloads.bits(kh.host)
+    vbits = None if vh is None else workloads.bits(vh.host)
+    ref = oracle.attend(olay, w.page_table.numpy(), w.seq_lens.numpy(), workloads.bits(w.q), kbits, vbits,
+                        sel_h.numpy(), cnt_h.numpy(), opol, w.scale)
+    assert np.abs(out_h.numpy().astype(np.float64) - ref).max() <= OUT_TOL
