@@ -75,6 +75,9 @@ def lib():
             "orc_attend": (I32, [P, P, P, P, P, P, P, P, I32, D, P]),
             "orc_decode": (I32, [P, P, P, P, P, P, P, D, P, P, P, I32, I32]),
             "orc_max_sel": (I32, [P, P, I32]),
+            "orc_quantize": (I32, [P, P, I32, P, P, P, P, P, P]),
+            "orc_attend_quant": (I32, [P, P, P, I32, P, P, P, P, P, P, P, P, P, I32, D, P]),
+            "orc_half_bits": (ctypes.c_uint16, [D]),
             "orc_scores_multi": (I32, [P, P, P, I32, P, P, P, I32]),
             "orc_select_multi": (I32, [P, P, P, I32, P, I32, P, P, I32]),
             "orc_attend_multi": (I32, [P, P, P, I32, P, P, P, P, P, I32, D, P]),
@@ -301,4 +304,55 @@ def attend_multi(layout: Layout, page_table, seq_lens, q, k_pool, v_pool, sel, c
     _check(lib().orc_attend_multi(ctypes.byref(layout.c()), ctypes.byref(bat), ctypes.byref(_policy(keep, pol)),
                                   nq, _ptr(qq), _ptr(k), _ptr(v), _ptr(se), _ptr(cn), se.shape[2], float(scale),
                                   _ptr(out)), "attend_multi")
+    return out
+
+
+# 2-bit quantised pages (readings stated beside orc_quantize in the oracle's
+# header): logical layouts, one byte per code, binary16 (m, s) pairs.
+
+@dataclass
+class Quant:
+    residual_pages: int
+    k_codes: np.ndarray   # uint8  [pool][Hkv][ps][Dk]
+    k_meta: np.ndarray    # uint16 [pool][Hkv][ps][Dk/32][2]
+    v_codes: np.ndarray   # uint8  [pool][Hkv][ps][Dv]
+    v_meta: np.ndarray    # uint16 [pool][Hkv][ps][Dv/32][2]
+
+
+def half_bits(x: float) -> int:
+    return int(lib().orc_half_bits(float(x)))
+
+
+def quantize(layout: Layout, page_table, seq_lens, num_q_heads, residual_pages, k_pool, v_pool) -> Quant:
+    """Quantised pool with the page-heads of logical pages j < P - residual_pages filled (others zero)."""
+    keep = _Keep()
+    k = keep.arr(k_pool, np.uint16)
+    v = keep.arr(v_pool, np.uint16)
+    L = layout
+    kc = np.zeros((L.num_pool_pages, L.num_kv_heads, L.page_size, L.head_dim_k), np.uint8)
+    km = np.zeros((L.num_pool_pages, L.num_kv_heads, L.page_size, L.head_dim_k // 32, 2), np.uint16)
+    vc = np.zeros((L.num_pool_pages, L.num_kv_heads, L.page_size, L.head_dim_v), np.uint8)
+    vm = np.zeros((L.num_pool_pages, L.num_kv_heads, L.page_size, L.head_dim_v // 32, 2), np.uint16)
+    bat = _batch(keep, page_table, seq_lens, num_q_heads)
+    _check(lib().orc_quantize(ctypes.byref(L.c()), ctypes.byref(bat), int(residual_pages), _ptr(k), _ptr(v),
+                              _ptr(kc), _ptr(km), _ptr(vc), _ptr(vm)), "quantize")
+    return Quant(int(residual_pages), kc, km, vc, vm)
+
+
+def attend_quant(layout: Layout, page_table, seq_lens, q, k_pool, v_pool, quant: Quant, sel, cnt, pol: Policy,
+                 scale):
+    keep = _Keep()
+    qq = keep.arr(q, np.uint16)
+    k = keep.arr(k_pool, np.uint16)
+    v = keep.arr(v_pool, np.uint16)
+    kc, km = keep.arr(quant.k_codes, np.uint8), keep.arr(quant.k_meta, np.uint16)
+    vc, vm = keep.arr(quant.v_codes, np.uint8), keep.arr(quant.v_meta, np.uint16)
+    se = keep.arr(sel, np.int32)
+    cn = keep.arr(cnt, np.int32)
+    bat = _batch(keep, page_table, seq_lens, qq.shape[1])
+    out = np.empty((bat.batch, qq.shape[1], layout.head_dim_v), np.float64)
+    _check(lib().orc_attend_quant(ctypes.byref(layout.c()), ctypes.byref(bat), ctypes.byref(_policy(keep, pol)),
+                                  int(quant.residual_pages), _ptr(qq), _ptr(k), _ptr(v), _ptr(kc), _ptr(km),
+                                  _ptr(vc), _ptr(vm), _ptr(se), _ptr(cn), se.shape[2], float(scale), _ptr(out)),
+           "attend_quant")
     return out

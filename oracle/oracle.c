@@ -219,6 +219,89 @@ static double value_at(const orc_layout *lay, const uint16_t *k_pool,
 }
 
 /* ------------------------------------------------------------------------ */
+/* 2-bit quantised pages                                                     */
+/*                                                                           */
+/* 2-bit codes in groups of 32 (SCBench notes, the method table: KIVI with   */
+/* 2 bits and group size 32; SparseEngine article, decode-hook paragraph:    */
+/* KIVI keeps a quantised region and a full-precision residual region).      */
+/* Readings: a group is 32 consecutive channels of one token (keys and       */
+/* values alike); zero point m = the group minimum, step s = (max - min) / 3,*/
+/* both stored as IEEE binary16; code = round-half-even((x - m) / s) clamped */
+/* to 0..3 (s = 0: code 0), every step in IEEE binary32 with m and s as      */
+/* stored; the value read back is m + code * s.  The last residual_pages     */
+/* logical pages of a sequence stay full precision.                          */
+/* ------------------------------------------------------------------------ */
+
+/* IEEE binary16 pattern nearest to x (ties to even), from the format's
+ * definition: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static uint16_t half_bits(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x)) return 0x7e00;
+    if (a >= 65520.0) return sign | 0x7c00;     /* past the largest finite (65504) by half a step or more */
+    if (a < ldexp(1.0, -14)) {                  /* subnormal: a = n * 2^-24 */
+        double n = nearbyint(a * ldexp(1.0, 24));
+        return sign | (uint16_t)n;              /* n = 1024 is the smallest normal */
+    }
+    int e;
+    frexp(a, &e);                               /* a in [2^(e-1), 2^e) */
+    int E = e - 1;
+    double n = nearbyint(ldexp(a, 10 - E));     /* significand in [1024, 2048] */
+    if (n == 2048.0) {
+        n = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return sign | 0x7c00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(n - 1024.0);
+}
+
+static double half_value(uint16_t h)
+{
+    int E = (h >> 10) & 0x1f, f = h & 0x3ff;
+    double v;
+    if (E == 0) v = ldexp((double)f, -24);
+    else if (E == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), E - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+/* One group of n values (bf16 values as binary32): its zero point, step and
+ * codes. */
+static void quant_group(const float *x, int n, uint16_t *m_out, uint16_t *s_out, uint8_t *codes)
+{
+    float mn = x[0], mx = x[0];
+    for (int i = 1; i < n; i++) {
+        if (x[i] < mn) mn = x[i];
+        if (x[i] > mx) mx = x[i];
+    }
+    float d = mx - mn;
+    float st = d / 3.0f;
+    uint16_t m16 = half_bits(mn), s16 = half_bits(st);
+    float m = (float)half_value(m16), sc = (float)half_value(s16);
+    for (int i = 0; i < n; i++) {
+        float c = 0.0f;
+        if (sc != 0.0f) {
+            float r = (x[i] - m) / sc;
+            c = nearbyintf(r);
+            if (c < 0.0f) c = 0.0f;
+            if (c > 3.0f) c = 3.0f;
+        }
+        codes[i] = (uint8_t)c;
+    }
+    *m_out = m16;
+    *s_out = s16;
+}
+
+/* Value read back from a quantised page: element i of a row of codes with
+ * its group's (zero point, step) pair in meta (one pair per 32 elements). */
+static double dequant(const uint8_t *codes, const uint16_t *meta, int32_t i)
+{
+    const uint16_t *ms = meta + 2 * (i / 32);
+    return half_value(ms[0]) + (double)codes[i] * half_value(ms[1]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Summaries and append                                                      */
 /* ------------------------------------------------------------------------ */
 
@@ -384,6 +467,7 @@ static int64_t unit_select_flags(const orc_layout *lay, const orc_batch *bat,
 static void unit_attend(const orc_layout *lay, const orc_batch *bat,
                         const orc_policy *pol, const uint16_t *q,
                         const uint16_t *k_pool, const uint16_t *v_pool,
+                        const orc_quant *qz,
                         const int32_t *sel, int32_t count, double scale,
                         int32_t b, int32_t g, int32_t nq, int32_t i,
                         double *out, double *s_buf)
@@ -394,6 +478,8 @@ static void unit_attend(const orc_layout *lay, const orc_batch *bat,
     int64_t sink_end = pol->sink_tokens < L ? pol->sink_tokens : L;
     int64_t win_begin = L - pol->window_tokens;
     int st = is_static(pol, g);
+    /* pages below q_end are read back from the quantised pool */
+    int64_t q_end = qz ? num_pages(bat->seq_lens[b], ps) - qz->residual_pages : 0;
     for (int32_t h = g * G; h < (g + 1) * G; h++) {
         const uint16_t *qh = q + (((int64_t)b * nq + i) * bat->num_q_heads + h) * D;
         double *o = out + (((int64_t)b * nq + i) * bat->num_q_heads + h) * Dv;
@@ -410,9 +496,16 @@ static void unit_attend(const orc_layout *lay, const orc_batch *bat,
                     s_buf[n++] = -INFINITY;
                     continue;
                 }
-                const uint16_t *kt = key_at(lay, k_pool, phys, g, t);
                 double dot = 0.0;
-                for (int32_t d = 0; d < D; d++) dot += bf16_value(qh[d]) * bf16_value(kt[d]);
+                if (j < q_end) {
+                    int64_t row = ((int64_t)phys * lay->num_kv_heads + g) * ps + t;
+                    const uint8_t *kc = qz->k_codes + row * D;
+                    const uint16_t *km = qz->k_meta + row * (D / 32) * 2;
+                    for (int32_t d = 0; d < D; d++) dot += bf16_value(qh[d]) * dequant(kc, km, d);
+                } else {
+                    const uint16_t *kt = key_at(lay, k_pool, phys, g, t);
+                    for (int32_t d = 0; d < D; d++) dot += bf16_value(qh[d]) * bf16_value(kt[d]);
+                }
                 s_buf[n] = scale * dot;
                 if (s_buf[n] > m) m = s_buf[n];
                 n++;
@@ -429,8 +522,15 @@ static void unit_attend(const orc_layout *lay, const orc_batch *bat,
                 if (s_buf[n] == -INFINITY) continue;
                 double w = exp(s_buf[n] - m);
                 denom += w;
-                for (int32_t dv = 0; dv < Dv; dv++)
-                    o[dv] += w * value_at(lay, k_pool, v_pool, phys, g, t, dv);
+                if (j < q_end) {
+                    int64_t row = ((int64_t)phys * lay->num_kv_heads + g) * ps + t;
+                    const uint8_t *vc = qz->v_codes + row * Dv;
+                    const uint16_t *vm = qz->v_meta + row * (Dv / 32) * 2;
+                    for (int32_t dv = 0; dv < Dv; dv++) o[dv] += w * dequant(vc, vm, dv);
+                } else {
+                    for (int32_t dv = 0; dv < Dv; dv++)
+                        o[dv] += w * value_at(lay, k_pool, v_pool, phys, g, t, dv);
+                }
             }
         }
         for (int32_t dv = 0; dv < Dv; dv++) o[dv] /= denom;
@@ -543,7 +643,7 @@ int32_t orc_select_multi(const orc_layout *lay, const orc_batch *bat,
 
 static int32_t attend_nq(const orc_layout *lay, const orc_batch *bat,
                          const orc_policy *pol, int32_t nq, const uint16_t *q,
-                         const uint16_t *k_pool, const uint16_t *v_pool,
+                         const uint16_t *k_pool, const uint16_t *v_pool, const orc_quant *qz,
                          const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
                          double scale, double *out)
 {
@@ -564,7 +664,7 @@ static int32_t attend_nq(const orc_layout *lay, const orc_batch *bat,
                 if (row[i] < 0 || row[i] >= P) rc = ORC_ERR_ARG;
             if (rc != ORC_OK) break;
             for (int32_t i = 0; i < nq; i++)
-                unit_attend(lay, bat, pol, q, k_pool, v_pool, row, count, scale, b, g, nq, i, out, s_buf);
+                unit_attend(lay, bat, pol, q, k_pool, v_pool, qz, row, count, scale, b, g, nq, i, out, s_buf);
         }
     }
     free(s_buf);
@@ -577,7 +677,7 @@ int32_t orc_attend(const orc_layout *lay, const orc_batch *bat,
                    const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
                    double scale, double *out)
 {
-    return attend_nq(lay, bat, pol, 1, q, k_pool, v_pool, sel, sel_count, max_sel, scale, out);
+    return attend_nq(lay, bat, pol, 1, q, k_pool, v_pool, NULL, sel, sel_count, max_sel, scale, out);
 }
 
 int32_t orc_attend_multi(const orc_layout *lay, const orc_batch *bat,
@@ -586,8 +686,58 @@ int32_t orc_attend_multi(const orc_layout *lay, const orc_batch *bat,
                          const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
                          double scale, double *out)
 {
-    return attend_nq(lay, bat, pol, nq, q, k_pool, v_pool, sel, sel_count, max_sel, scale, out);
+    return attend_nq(lay, bat, pol, nq, q, k_pool, v_pool, NULL, sel, sel_count, max_sel, scale, out);
 }
+
+int32_t orc_quantize(const orc_layout *lay, const orc_batch *bat, int32_t residual_pages,
+                     const uint16_t *k_pool, const uint16_t *v_pool, uint8_t *k_codes, uint16_t *k_meta,
+                     uint8_t *v_codes, uint16_t *v_meta)
+{
+    if (!check_layout(lay) || !check_batch(lay, bat) || residual_pages < 1) return ORC_ERR_ARG;
+    if (lay->v_from_k || lay->head_dim_k % 32 || lay->head_dim_v % 32) return ORC_ERR_ARG;
+    if (bat->batch == 0) return ORC_OK;
+    if (!k_pool || !v_pool || !k_codes || !k_meta || !v_codes || !v_meta) return ORC_ERR_ARG;
+    const int32_t ps = lay->page_size, D = lay->head_dim_k, Dv = lay->head_dim_v;
+    float x[32];
+    for (int32_t b = 0; b < bat->batch; b++) {
+        int64_t P = num_pages(bat->seq_lens[b], ps);
+        for (int64_t j = 0; j < P - residual_pages; j++) {   /* complete pages: j < P - 1 */
+            int32_t phys = bat->page_table[(int64_t)b * bat->pt_stride + j];
+            for (int32_t g = 0; g < lay->num_kv_heads; g++)
+                for (int32_t t = 0; t < ps; t++) {
+                    int64_t row = ((int64_t)phys * lay->num_kv_heads + g) * ps + t;
+                    const uint16_t *kt = key_at(lay, k_pool, phys, g, t);
+                    for (int32_t c = 0; c < D; c += 32) {
+                        for (int32_t i = 0; i < 32; i++) x[i] = (float)bf16_value(kt[c + i]);
+                        uint16_t *ms = k_meta + (row * (D / 32) + c / 32) * 2;
+                        quant_group(x, 32, &ms[0], &ms[1], k_codes + row * D + c);
+                    }
+                    for (int32_t c = 0; c < Dv; c += 32) {
+                        for (int32_t i = 0; i < 32; i++)
+                            x[i] = (float)value_at(lay, k_pool, v_pool, phys, g, t, c + i);
+                        uint16_t *ms = v_meta + (row * (Dv / 32) + c / 32) * 2;
+                        quant_group(x, 32, &ms[0], &ms[1], v_codes + row * Dv + c);
+                    }
+                }
+        }
+    }
+    return ORC_OK;
+}
+
+int32_t orc_attend_quant(const orc_layout *lay, const orc_batch *bat, const orc_policy *pol,
+                         int32_t residual_pages, const uint16_t *q, const uint16_t *k_pool,
+                         const uint16_t *v_pool, const uint8_t *k_codes, const uint16_t *k_meta,
+                         const uint8_t *v_codes, const uint16_t *v_meta, const int32_t *sel,
+                         const int32_t *sel_count, int32_t max_sel, double scale, double *out)
+{
+    if (residual_pages < 1 || lay == NULL || lay->v_from_k || lay->head_dim_k % 32 || lay->head_dim_v % 32)
+        return ORC_ERR_ARG;
+    if (!k_codes || !k_meta || !v_codes || !v_meta) return ORC_ERR_ARG;
+    orc_quant qz = {residual_pages, k_codes, k_meta, v_codes, v_meta};
+    return attend_nq(lay, bat, pol, 1, q, k_pool, v_pool, &qz, sel, sel_count, max_sel, scale, out);
+}
+
+uint16_t orc_half_bits(double x) { return half_bits(x); }
 
 int32_t orc_decode(const orc_layout *lay, const orc_batch *bat,
                    const orc_policy *pol, const uint16_t *q,
@@ -645,7 +795,7 @@ int32_t orc_decode(const orc_layout *lay, const orc_batch *bat,
                 for (int64_t i = 0; i < max_sel; i++) sel[u * max_sel + i] = i < n ? list[i] : -1;
                 sel_count[u] = (int32_t)count;
             }
-            unit_attend(lay, bat, pol, q, k_pool, v_pool, list, (int32_t)count, scale, b, g, 1, 0, out, s_buf);
+            unit_attend(lay, bat, pol, q, k_pool, v_pool, NULL, list, (int32_t)count, scale, b, g, 1, 0, out, s_buf);
         }
         if (!ok) {
 #pragma omp critical

@@ -157,6 +157,37 @@ int32_t orc_attend_multi(const orc_layout *lay, const orc_batch *bat,
                          const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
                          double scale, double *out);
 
+/* 2-bit quantised pages (KIVI-style: 2 bits, groups of 32; a full-precision
+ * residual region of the last residual_pages logical pages).  Readings, as
+ * in oracle.c: a group is 32 consecutive channels of one token; zero point =
+ * group min, step = (max - min) / 3, both stored as binary16; code =
+ * round-half-even((x - m) / s) clamped to 0..3 in binary32 (s = 0: 0); read
+ * back as m + code * s.  Layouts (logical, one byte per code):
+ *   k_codes [num_pool_pages][num_kv_heads][page_size][head_dim_k]  uint8
+ *   k_meta  [num_pool_pages][num_kv_heads][page_size][head_dim_k/32][2] binary16 (m, s)
+ *   v_codes / v_meta likewise with head_dim_v (token-major, groups along dv).
+ * orc_quantize fills the page-heads of logical pages j < P - residual_pages
+ * of every sequence (complete pages; residual_pages >= 1). */
+typedef struct {
+    int32_t residual_pages;
+    const uint8_t *k_codes;
+    const uint16_t *k_meta;
+    const uint8_t *v_codes;
+    const uint16_t *v_meta;
+} orc_quant;
+int32_t orc_quantize(const orc_layout *lay, const orc_batch *bat, int32_t residual_pages,
+                     const uint16_t *k_pool, const uint16_t *v_pool, uint8_t *k_codes, uint16_t *k_meta,
+                     uint8_t *v_codes, uint16_t *v_meta);
+/* orc_attend with the pages j < P - residual_pages read back from the
+ * quantised pool (exact m + code * s in fp64), the others from the bf16 pools. */
+int32_t orc_attend_quant(const orc_layout *lay, const orc_batch *bat, const orc_policy *pol,
+                         int32_t residual_pages, const uint16_t *q, const uint16_t *k_pool,
+                         const uint16_t *v_pool, const uint8_t *k_codes, const uint16_t *k_meta,
+                         const uint8_t *v_codes, const uint16_t *v_meta, const int32_t *sel,
+                         const int32_t *sel_count, int32_t max_sel, double scale, double *out);
+/* binary16 pattern nearest to x (ties to even). */
+uint16_t orc_half_bits(double x);
+
 /* Largest selection any head can need under this policy. */
 int32_t orc_max_sel(const orc_layout *lay, const orc_policy *pol, int32_t max_pages);
 

@@ -1,6 +1,6 @@
 """Plants plausible mistakes in a temporary copy of the oracle (on the CPU
-only) and checks that the pins in test_oracle_pins.py and
-test_oracle_multi.py catch every one."""
+only) and checks that the pins in test_oracle_pins.py, test_oracle_multi.py
+and test_oracle_quant.py catch every one."""
 import os
 import shutil
 import subprocess
@@ -42,8 +42,16 @@ MUTANTS = {
                                  "wide.window_tokens = pol->window_tokens;"),
     "empty window widened": ("if (pol->window_tokens > 0) wide.window_tokens",
                              "if (pol->window_tokens >= 0) wide.window_tokens"),
+    # quantised pages
+    "step over four levels": ("float st = d / 3.0f;", "float st = d / 4.0f;"),
+    "codes truncated": ("c = nearbyintf(r);", "c = truncf(r);"),
+    "quantised region one page too long": ("num_pages(bat->seq_lens[b], ps) - qz->residual_pages : 0;",
+                                           "num_pages(bat->seq_lens[b], ps) - qz->residual_pages + 1 : 0;"),
+    "binary16 rounds toward zero": ("double n = nearbyint(ldexp(a, 10 - E));", "double n = trunc(ldexp(a, 10 - E));"),
+    "zero point at the maximum": ("uint16_t m16 = half_bits(mn), s16 = half_bits(st);",
+                                  "uint16_t m16 = half_bits(mx), s16 = half_bits(st);"),
 }
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_multi.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_multi.py", "test_oracle_quant.py"]
 
 
 def _run_mutant(item):
