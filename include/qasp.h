@@ -270,6 +270,47 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat,
                                int32_t max_sel, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* 2-bit quantised KV pages (KIVI-style: 2 bits, groups of 32, SCBench notes'
+ * method table; a quantised region kept with a full-precision residual region,
+ * SparseEngine article, decode-hook paragraph).  Grouped-query layouts only
+ * (page 16, head_dim 128; otherwise QASP_ERR_UNSUPPORTED).  The last
+ * residual_pages (>= 1) logical pages of a sequence stay in the bf16 pools;
+ * every earlier page is read from the quantised pool by the attention.
+ * Scoring and selection are unchanged (summaries come from the bf16 keys).
+ * Per token, each group of 32 consecutive channels of the key, and of the
+ * value, has zero point m = its minimum and step s = (max - min) / 3, stored
+ * as binary16; code = round-half-even((x - m) / s) clamped to 0..3 in binary32
+ * (s = 0: 0); read back as m + code * s.  Keys and values must lie within the
+ * binary16 range.
+ *   qpool [num_pool_pages][num_kv_heads][1536] bytes, per page-head:
+ *     [   0, 512) key codes: token t, channel 32i + 8kg + e (i, kg < 4, e < 8)
+ *                 at byte 32t + 8kg + 2i + e/4, bits 2(e%4);
+ *     [ 512, 768) key (m, s) binary16 pairs: token t, group i at 16t + 4i;
+ *     [ 768,1280) value codes: channel 16i + n (i < 8, n < 16), token 4kg + r
+ *                 at byte 8(4n + kg) + i, bits 2r;
+ *     [1280,1536) value pairs: token t, group g (channels 32g..) at 16t + 4g.
+ * qasp_quant_pool_bytes: the size of qpool (0 for an unsupported layout).
+ * qasp_quantize_pages: fills the page-heads of logical pages j < P -
+ *   residual_pages of every sequence (P = pages of seq_lens[b]) from the bf16
+ *   pools; run once to build the pool.
+ * qasp_decode_step_quant: qasp_decode_step with quantised pages: the append
+ *   (bf16, when k_new is given), then, for a sequence whose token opened a new
+ *   page, page P - 1 - residual_pages (which has just left the residual
+ *   region) is quantised; scoring, selection, attention.  Errors as
+ *   qasp_decode_step, and QASP_ERR_BAD_SHAPE for residual_pages < 1. */
+size_t qasp_quant_pool_bytes(const qasp_layout *lay);
+int32_t qasp_quantize_pages(const qasp_layout *lay, const qasp_batch *bat,
+                            int32_t residual_pages, const uint16_t *k_pool,
+                            const uint16_t *v_pool, uint8_t *qpool, void *stream);
+int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat,
+                               const qasp_policy *pol, int32_t residual_pages,
+                               const uint16_t *q, const uint16_t *k_new,
+                               const uint16_t *v_new, uint16_t *k_pool,
+                               uint16_t *v_pool, uint16_t *summ, uint8_t *qpool,
+                               float scale, float *out, int32_t *sel,
+                               int32_t *sel_count, int32_t max_sel, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Host-tier KV pool (CPU-GPU cooperative loading: the full KV cache stays in
  * host RAM and each decode step loads only the pages it needs; SCBench notes,
  * the discussion of CPU-GPU cooperation for Quest / RetrievalAttention).

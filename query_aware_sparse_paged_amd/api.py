@@ -65,6 +65,12 @@ EXPORTS = {
     "qasp_decode_step_reuse": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 2 +
                                [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p]),
+    "qasp_quant_pool_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "qasp_quantize_pages": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32] +
+                            [ctypes.c_void_p] * 4),
+    "qasp_decode_step_quant": (ctypes.c_int32, [ctypes.c_void_p] * 3 + [ctypes.c_int32] + [ctypes.c_void_p] * 7 +
+                               [ctypes.c_float] + [ctypes.c_void_p] * 3 +
+                               [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "qasp_host_alloc": (ctypes.c_int32, [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "qasp_host_free": (ctypes.c_int32, [ctypes.c_void_p]),
     "qasp_max_sel_multi": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]),
@@ -443,3 +449,46 @@ def host_pool_like(t: torch.Tensor) -> MappedTensor:
     m = buf.view(t.shape, t.dtype)
     m.host.copy_(t.cpu() if t.is_cuda else t)
     return m
+
+
+def new_quant_pool(layout: Layout, device) -> torch.Tensor:
+    """Zeroed quantised pool of qasp_quant_pool_bytes bytes ([pool][Hkv][1536] uint8)."""
+    n = int(lib().qasp_quant_pool_bytes(ctypes.byref(layout.c())))
+    if n == 0:
+        raise ValueError("quantised pages need a grouped-query layout (page 16, head_dim 128)")
+    return torch.zeros((layout.num_pool_pages, layout.num_kv_heads, n // (layout.num_pool_pages *
+                                                                         layout.num_kv_heads)),
+                       dtype=torch.uint8, device=device)
+
+
+def quantize_pages(layout: Layout, batch: Batch, residual_pages: int, k_pool, v_pool, qpool):
+    """Quantises every page below the last residual_pages of each sequence."""
+    _dev(k_pool, torch.bfloat16, "k_pool", 4)
+    _dev(v_pool, torch.bfloat16, "v_pool", 4)
+    _dev(qpool, torch.uint8, "qpool", 3)
+    _check(lib().qasp_quantize_pages(ctypes.byref(layout.c()), ctypes.byref(batch.c()), int(residual_pages),
+                                     _ptr(k_pool), _ptr(v_pool), _ptr(qpool), _stream()), "qasp_quantize_pages")
+
+
+def decode_step_quant(layout: Layout, batch: Batch, policy: Policy, residual_pages: int, q, k_pool, v_pool, summ,
+                      qpool, scale: float, workspace: torch.Tensor, max_sel_n: int, k_new=None, v_new=None, out=None,
+                      sel=None, sel_count=None) -> torch.Tensor:
+    """decode_step with the pages below the last residual_pages read from the
+    2-bit quantised pool.  Returns out fp32 [B][Hq][Dv]."""
+    for t, name, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
+                        (k_new, "k_new", 3), (v_new, "v_new", 3)):
+        _dev(t, torch.bfloat16, name, nd)
+    _dev(qpool, torch.uint8, "qpool", 3)
+    _dev(sel, torch.int32, "sel", 3)
+    _dev(sel_count, torch.int32, "sel_count", 2)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    B = batch.seq_lens.shape[0]
+    if out is None:
+        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out", 3)
+    _check(lib().qasp_decode_step_quant(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
+                                        int(residual_pages), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                        _ptr(v_pool), _ptr(summ), _ptr(qpool), float(scale), _ptr(out), _ptr(sel),
+                                        _ptr(sel_count), int(max_sel_n), _ptr(workspace), workspace.numel(),
+                                        _stream()), "qasp_decode_step_quant")
+    return out

@@ -21,7 +21,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["api.hip", "summaries.hip", "score.hip", "score_mla.hip", "select.hip", "decode_gqa.hip", "decode_mla.hip",
-           "fused_gqa.hip", "multi.hip"]
+           "fused_gqa.hip", "multi.hip", "quant.hip"]
 
 
 def _compile(src: str) -> str:

@@ -358,6 +358,61 @@ int32_t qasp_host_free(void *host_ptr) {
   return hipHostFree(host_ptr) == hipSuccess ? QASP_OK : QASP_ERR_ALLOC;
 }
 
+size_t qasp_quant_pool_bytes(const qasp_layout *lay) {
+  if (check_layout(lay) != QASP_OK || family_of(*lay) != kFamilyGqa) return 0;
+  return (size_t)lay->num_pool_pages * lay->num_kv_heads * kQuantPageHeadBytes;
+}
+
+int32_t qasp_quantize_pages(const qasp_layout *lay, const qasp_batch *bat, int32_t residual_pages,
+                            const uint16_t *k_pool, const uint16_t *v_pool, uint8_t *qpool, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if (family_of(*lay) != kFamilyGqa) return QASP_ERR_UNSUPPORTED;
+  if (residual_pages < 1) return QASP_ERR_BAD_SHAPE;
+  if (bat->batch == 0) return QASP_OK;
+  if (!k_pool || !v_pool || !qpool) return QASP_ERR_NULL_ARG;
+  return status_of(launch_quantize(*lay, *bat, residual_pages, false, k_pool, v_pool, qpool, (hipStream_t)stream));
+}
+
+int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                               int32_t residual_pages, const uint16_t *q, const uint16_t *k_new,
+                               const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ,
+                               uint8_t *qpool, float scale, float *out, int32_t *sel, int32_t *sel_count,
+                               int32_t max_sel, void *workspace, size_t workspace_bytes_given, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (family_of(*lay) != kFamilyGqa) return QASP_ERR_UNSUPPORTED;
+  if (residual_pages < 1 || max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  if (max_sel < max_sel_of(*lay, *pol, bat->max_pages)) return QASP_ERR_MAX_SEL;
+  if (bat->batch == 0) return QASP_OK;
+  if (!q || !k_pool || !v_pool || !qpool || !out || !workspace) return QASP_ERR_NULL_ARG;
+  const bool scored = !all_static(*lay, *pol);
+  if (scored && !summ) return QASP_ERR_NULL_ARG;
+  if (k_new && !v_new) return QASP_ERR_NULL_ARG;
+  if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
+  if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
+  int32_t *sel_out = sel ? sel : ws.sel;
+  int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
+  hipError_t e = hipSuccess;
+  if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
+  // a token that opened a new page pushed page P - 1 - R out of the residual region
+  if (e == hipSuccess) e = launch_quantize(*lay, *bat, residual_pages, true, k_pool, v_pool, qpool, s);
+  if (e == hipSuccess && scored)
+    e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s,
+                           token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr));
+  if (e == hipSuccess)
+    e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
+  if (e == hipSuccess)
+    e = launch_decode_quant_gqa(*lay, *bat, *pol, residual_pages, q, k_pool, v_pool, qpool, sel_out, cnt_out,
+                                max_sel, scale, out, ws, s);
+  return status_of(e);
+}
+
 int32_t qasp_max_sel_multi(const qasp_layout *lay, const qasp_policy *pol, int32_t n_query, int32_t max_pages) {
   int32_t rc = check_layout(lay);
   if (rc != QASP_OK) return rc;

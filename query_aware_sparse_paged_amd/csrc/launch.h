@@ -83,6 +83,17 @@ hipError_t launch_fused_reuse_gqa(const qasp_layout &lay, const qasp_batch &bat,
 hipError_t launch_prepare_drafts(const qasp_layout &lay, const qasp_batch &bat, int nq, const uint16_t *q,
                                  uint16_t *q_grouped, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
                                  uint16_t *v_pool, uint16_t *summ, hipStream_t stream);
+// 2-bit quantised pages (grouped-query layouts): bytes per page-head, the
+// quantiser (bulk: every page below P - residual_pages; step: the page that
+// the step's token pushed out of the residual region) and the attention.
+constexpr size_t kQuantPageHeadBytes = 1536;
+hipError_t launch_quantize(const qasp_layout &lay, const qasp_batch &bat, int residual_pages, bool step_mode,
+                           const uint16_t *k_pool, const uint16_t *v_pool, uint8_t *qpool, hipStream_t stream);
+hipError_t launch_decode_quant_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                   int residual_pages, const uint16_t *q, const uint16_t *k_pool,
+                                   const uint16_t *v_pool, const uint8_t *qpool, const int32_t *sel,
+                                   const int32_t *sel_count, int max_sel, float scale, float *out,
+                                   const Workspace &ws, hipStream_t stream);
 // Merge of the split partials; Gp (> 0) and nq map the partials' grouped
 // heads to out [B][nq][Hq / nq][Dv] (nq = 1: out [B][Hq][Dv]).
 hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,

@@ -1,0 +1,320 @@
+// 2-bit quantised KV pages for grouped-query heads (page 16, head_dim 128):
+// KIVI-style codes (2 bits, groups of 32: SCBench notes, the method table)
+// for every page outside a full-precision residual region of the last R
+// logical pages (SparseEngine article, decode-hook paragraph: a quantised
+// region managed together with a residual one).  Scoring and selection are
+// unchanged (the summaries come from the full-precision keys); only the
+// attention reads a selected page back from its codes.
+//
+// Quantiser (per token, 32 consecutive channels of the key or the value): m =
+// the group minimum and s = (max - min) / 3, both stored as binary16; code =
+// round-half-even((x - m) / s) clamped to 0..3, each step in binary32 with m
+// and s as stored (s = 0: code 0).  Read back as m + code * s.
+//
+// A quantised page-head is 1536 bytes (against 8192 in bf16), packed so that
+// each lane of the attention reads its MFMA fragment as one 8-byte load:
+//   [   0, 512) key codes:   token t, channel 32 i + 8 kg + e (i, kg < 4,
+//                            e < 8) at byte 32 t + 8 kg + 2 i + e / 4, bits
+//                            2 (e % 4)
+//   [ 512, 768) key pairs:   token t, group i: binary16 (m, s) at 16 t + 4 i
+//   [ 768,1280) value codes: channel 16 i + n (i < 8, n < 16), token 4 kg + r
+//                            at byte 8 (4 n + kg) + i, bits 2 r
+//   [1280,1536) value pairs: token t, group g (channels 32 g ...): at 16 t + 4 g
+#include <hip/hip_fp16.h>
+
+#include "attend_core.h"
+#include "launch.h"
+
+namespace qasp {
+namespace quant {
+
+constexpr int kPageHeadBytes = 1536, kKeyPairs = 512, kValCodes = 768, kValPairs = 1280;
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+  return __half2float(__ushort_as_half((unsigned short)(h & 0xffffu)));
+}
+
+// (m, s) of a group as binary16 patterns, and its m, s as binary32.
+__device__ __forceinline__ uint32_t group_pair(float mn, float mx, float &m, float &s) {
+  const float st = __fdiv_rn(mx - mn, 3.0f);
+  const __half m16 = __float2half_rn(mn), s16 = __float2half_rn(st);
+  m = __half2float(m16);
+  s = __half2float(s16);
+  return (uint32_t)__half_as_ushort(m16) | ((uint32_t)__half_as_ushort(s16) << 16);
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, float m, float s) {
+  if (s == 0.f) return 0u;
+  const float c = rintf(__fdiv_rn(x - m, s));
+  return (uint32_t)fminf(fmaxf(c, 0.f), 3.f);
+}
+
+// One block per (logical page, sequence) (bulk) or per sequence (step: the
+// page that has just left the residual region, when the step's token opened a
+// new page).  Per KV head: phase A computes the (m, s) pair of every group
+// (128 groups: 16 tokens x 4 key + 4 value groups) into LDS and memory;
+// phase B writes the code bytes (each byte is written by one thread).
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ k_pool,
+                                                       const uint16_t *__restrict__ v_pool, uint8_t *__restrict__ qpool,
+                                                       const int32_t *__restrict__ page_table,
+                                                       const int32_t *__restrict__ seq_lens, int pt_stride, int Hkv,
+                                                       int residual_pages, int step_mode) {
+  constexpr int PS = 16, D = 128, DV = 128;
+  __shared__ float sh_m[8 * PS], sh_s[8 * PS];  // [token][group: 4 key, 4 value]
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int L = seq_lens[b];
+  const int P = (L + PS - 1) / PS;
+  int j = blockIdx.x;
+  if (step_mode) {
+    if (L < 1 || (L - 1) % PS != 0) return;  // the token did not open a new page
+    j = P - 1 - residual_pages;
+  }
+  if (j < 0 || j >= P - residual_pages) return;
+  const int phys = page_table[(size_t)b * pt_stride + j];
+  for (int g = 0; g < Hkv; g++) {
+    const size_t ph = (size_t)phys * Hkv + g;
+    const uint16_t *kp = k_pool + ph * PS * D;   // [t][d]
+    const uint16_t *vp = v_pool + ph * DV * PS;  // [dv][t]
+    uint8_t *dst = qpool + ph * kPageHeadBytes;
+    if (tid < 8 * PS) {
+      const int t = tid / 8, grp = tid % 8;
+      // min / max in channel order, the first of equal values kept (so the
+      // sign of a zero minimum is that of the first zero)
+      float mn = 0.f, mx = 0.f;
+      for (int e = 0; e < 32; e++) {
+        const uint16_t bits = grp < 4 ? kp[t * D + 32 * grp + e] : vp[(32 * (grp - 4) + e) * PS + t];
+        const float x = __uint_as_float((uint32_t)bits << 16);
+        if (e == 0 || x < mn) mn = x;
+        if (e == 0 || x > mx) mx = x;
+      }
+      float m, s;
+      const uint32_t pair = group_pair(mn, mx, m, s);
+      sh_m[tid] = m;
+      sh_s[tid] = s;
+      *(uint32_t *)(dst + (grp < 4 ? kKeyPairs + 16 * t + 4 * grp : kValPairs + 16 * t + 4 * (grp - 4))) = pair;
+    }
+    __syncthreads();
+    {  // key codes: item (t, kg, i) -> 8 codes, 2 bytes
+      const int t = tid / 16, kg = (tid / 4) % 4, i = tid % 4;
+      const float m = sh_m[t * 8 + i], s = sh_s[t * 8 + i];
+      uint32_t w = 0;
+      for (int e = 0; e < 8; e++) {
+        const float x = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + e] << 16);
+        w |= code_of(x, m, s) << (2 * e);
+      }
+      *(uint16_t *)(dst + 32 * t + 8 * kg + 2 * i) = (uint16_t)w;
+    }
+    for (int item = tid; item < 16 * 4 * 8; item += 256) {  // value codes: item (n, kg, i) -> 4 codes, 1 byte
+      const int n = item / 32, kg = (item / 8) % 4, i = item % 8;
+      const int dv = 16 * i + n, grp = 4 + dv / 32;
+      uint32_t w = 0;
+      for (int r = 0; r < 4; r++) {
+        const int t = 4 * kg + r;
+        const float x = __uint_as_float((uint32_t)vp[dv * PS + t] << 16);
+        w |= code_of(x, sh_m[t * 8 + grp], sh_s[t * 8 + grp]) << (2 * r);
+      }
+      dst[kValCodes + 8 * (4 * n + kg) + i] = (uint8_t)w;
+    }
+    __syncthreads();
+  }
+}
+
+// One quantised page-head's fragments for a wave lane.
+struct QPage {
+  uint2 kc;      // key codes: token l % 16, channels 32 i + 8 (l / 16) ...
+  uint4 kp;      // key pairs of token l % 16, groups 0..3
+  uint2 vc;      // value codes: channels 16 i + l % 16, tokens 4 (l / 16) ...
+  uint4 vp[4];   // value pairs of tokens 4 (l / 16) + r, groups 0..3
+
+  __device__ __forceinline__ void load(const uint8_t *ph, int lane) {
+    const int n = lane & 15, kg = lane >> 4;
+    kc = *(const uint2 *)(ph + 32 * n + 8 * kg);
+    kp = *(const uint4 *)(ph + kKeyPairs + 16 * n);
+    vc = *(const uint2 *)(ph + kValCodes + 8 * (4 * n + kg));
+#pragma unroll
+    for (int r = 0; r < 4; r++) vp[r] = *(const uint4 *)(ph + kValPairs + 16 * (4 * kg + r));
+  }
+};
+
+__device__ __forceinline__ uint32_t dw(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// Softmax attention of the wave's head columns over one quantised page (logical
+// id j; real = false computes it fully masked).  Keys and values are read back
+// as m + code * s in binary32 and fed to the MFMAs as bf16 hi + lo parts.
+__device__ __forceinline__ void attend_qpage(attend::WaveState &st, const QPage &pg, const uint4 *bq, bool real, int j,
+                                             int L, bool is_static, int sink_end, int win_begin, float scale_log2,
+                                             int lane) {
+  constexpr int PS = 16;
+  const int kg = lane >> 4;
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t pair = dw(pg.kp, i);
+    const float m = half_bits_to_f32(pair), sc = half_bits_to_f32(pair >> 16);
+    const uint32_t codes = (i < 2 ? pg.kc.x : pg.kc.y) >> (16 * (i & 1));
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = fmaf((float)((codes >> (2 * e)) & 3u), sc, m);
+    const uint2 h0 = attend::pack_bf16x4(x[0], x[1], x[2], x[3]), h1 = attend::pack_bf16x4(x[4], x[5], x[6], x[7]);
+    const uint2 l0 = attend::pack_bf16x4(x[0] - attend::bf16_round_f32(x[0]), x[1] - attend::bf16_round_f32(x[1]),
+                                         x[2] - attend::bf16_round_f32(x[2]), x[3] - attend::bf16_round_f32(x[3]));
+    const uint2 l1 = attend::pack_bf16x4(x[4] - attend::bf16_round_f32(x[4]), x[5] - attend::bf16_round_f32(x[5]),
+                                         x[6] - attend::bf16_round_f32(x[6]), x[7] - attend::bf16_round_f32(x[7]));
+    s = mfma16x16x32(make_uint4(h0.x, h0.y, h1.x, h1.y), bq[i], s);
+    s = mfma16x16x32(make_uint4(l0.x, l0.y, l1.x, l1.y), bq[i], s);
+  }
+  float sv[4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int pos = j * PS + 4 * kg + r;
+    const bool ok = real & (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
+    sv[r] = ok ? s[r] * scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, sv[r]);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+  const float m_new = fmaxf(st.m, tmax);
+  float alpha = 1.f;
+  float p[4];
+  if (m_new == -INFINITY) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) p[r] = 0.f;
+  } else {
+    alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+#pragma unroll
+    for (int r = 0; r < 4; r++) p[r] = sv[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_new);
+  }
+  float psum = (p[0] + p[1]) + (p[2] + p[3]);
+  psum += __shfl_xor(psum, 16, kWave);
+  psum += __shfl_xor(psum, 32, kWave);
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  const uint2 ph = attend::pack_bf16x4(p[0], p[1], p[2], p[3]);
+  const uint2 pl = attend::pack_bf16x4(p[0] - attend::bf16_round_f32(p[0]), p[1] - attend::bf16_round_f32(p[1]),
+                                       p[2] - attend::bf16_round_f32(p[2]), p[3] - attend::bf16_round_f32(p[3]));
+  // value pairs of this lane's 4 tokens, groups 0..3
+  float vm[4][4], vs[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; r++)
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const uint32_t pair = dw(pg.vp[r], g);
+      vm[r][g] = half_bits_to_f32(pair);
+      vs[r][g] = half_bits_to_f32(pair >> 16);
+    }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t codes = ((i < 4 ? pg.vc.x : pg.vc.y) >> (8 * (i & 3))) & 0xffu;
+    const int g = i / 2;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) x[r] = fmaf((float)((codes >> (2 * r)) & 3u), vs[r][g], vm[r][g]);
+    const uint2 vh = attend::pack_bf16x4(x[0], x[1], x[2], x[3]);
+    const uint2 vl = attend::pack_bf16x4(x[0] - attend::bf16_round_f32(x[0]), x[1] - attend::bf16_round_f32(x[1]),
+                                         x[2] - attend::bf16_round_f32(x[2]), x[3] - attend::bf16_round_f32(x[3]));
+    st.acc[i] *= alpha;
+    st.acc[i] = mfma16x16x16(vh, ph, st.acc[i]);
+    st.acc[i] = mfma16x16x16(vh, pl, st.acc[i]);
+    st.acc[i] = mfma16x16x16(vl, ph, st.acc[i]);
+  }
+}
+
+}  // namespace quant
+
+// Sparse paged attention with quantised pages: as decode_gqa_kernel (block
+// (split, g, b), waves take every WAVES-th selected page), except that a
+// wave's pages below P - residual_pages (its first ones: the list is
+// ascending) are read from the quantised pool, the rest from the bf16 pools.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void decode_quant_gqa_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool, const uint16_t *__restrict__ v_pool,
+    const uint8_t *__restrict__ qpool, const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ sel_count, float *__restrict__ partial,
+    float2 *__restrict__ partial_ml, float *__restrict__ out, int pt_stride, int max_sel, int Hq, int Hkv, int G,
+    int splits, int pps, float scale_log2, int sink_tokens, int window_tokens, uint64_t static_mask,
+    int residual_pages) {
+  constexpr int PS = 16, D = 128, DV = 128;
+  extern __shared__ float lds[];
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int unit = b * Hkv + g;
+  const int L = seq_lens[b];
+  const int q_end = (L + PS - 1) / PS - residual_pages;  // pages below are quantised
+  const bool is_static = head_is_static(static_mask, g);
+  const int sink_end = is_static ? min(sink_tokens, L) : 0;
+  const int win_begin = is_static ? max(0, L - window_tokens) : 0;
+  const int count = sel_count[unit];
+  const int first = split * pps, last = min(first + pps, count);
+  const int npg = max(0, (last - first - wave + WAVES - 1) / WAVES);
+  int my_j = 0, my_phys = 0;
+  if (lane < npg) {
+    my_j = sel[(size_t)unit * max_sel + first + wave + WAVES * lane];
+    my_phys = page_table[(size_t)b * pt_stride + my_j];
+  }
+  const int n_q = __popcll(__ballot(lane < npg && my_j < q_end));  // the wave's first n_q pages
+  const size_t head0 = (size_t)b * Hq + (size_t)g * G;
+  uint4 bq[D / 32];
+  attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
+  attend::WaveState st;
+  attend::init_state(st);
+  if (n_q > 0) {
+    auto base = [&](int it) {
+      return qpool + ((size_t)__shfl(my_phys, min(it, n_q - 1), kWave) * Hkv + g) * quant::kPageHeadBytes;
+    };
+    quant::QPage cur, nxt;
+    cur.load(base(0), lane);
+    for (int it = 0; it < n_q; it++) {
+      nxt.load(base(it + 1), lane);  // past the end: the last page again (unused)
+      quant::attend_qpage(st, cur, bq, true, __shfl(my_j, it, kWave), L, is_static, sink_end, win_begin, scale_log2,
+                          lane);
+      cur = nxt;
+    }
+  }
+  // the remaining (residual) pages from the bf16 pools
+  const int src = min(lane + n_q, kWave - 1);
+  const int r_j = __shfl(my_j, src, kWave), r_phys = __shfl(my_phys, src, kWave);
+  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  attend::attend_pages<PS, D, DV>(st, pw, npg - n_q, r_j, r_phys, lane);
+  attend::merge_waves<WAVES, DV>(lds, st, G, [&](int h, int dv, float a, float lsum, float M) {
+    if (splits == 1) {
+      out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
+    } else {
+      const size_t ps_idx = (head0 + h) * splits + split;
+      partial[ps_idx * DV + dv] = a;
+      if (dv == 0) partial_ml[ps_idx] = make_float2(M, lsum);
+    }
+  });
+}
+
+hipError_t launch_quantize(const qasp_layout &lay, const qasp_batch &bat, int residual_pages, bool step_mode,
+                           const uint16_t *k_pool, const uint16_t *v_pool, uint8_t *qpool, hipStream_t stream) {
+  if (bat.batch == 0 || bat.max_pages == 0) return hipSuccess;
+  dim3 grid(step_mode ? 1 : bat.max_pages, bat.batch);
+  hipLaunchKernelGGL(quant::quantize_kernel, grid, dim3(256), 0, stream, k_pool, v_pool, qpool, bat.page_table,
+                     bat.seq_lens, bat.pt_stride, lay.num_kv_heads, residual_pages, step_mode ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_quant_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                   int residual_pages, const uint16_t *q, const uint16_t *k_pool,
+                                   const uint16_t *v_pool, const uint8_t *qpool, const int32_t *sel,
+                                   const int32_t *sel_count, int max_sel, float scale, float *out,
+                                   const Workspace &ws, hipStream_t stream) {
+  constexpr int W = kGqaDecodeWaves;
+  if (bat.batch == 0) return hipSuccess;
+  const int G = bat.num_q_heads / lay.num_kv_heads;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int pps = (max_sel + ws.splits - 1) / ws.splits;
+  const size_t lds = (size_t)attend::merge_lds_floats(W, G, 128) * sizeof(float);
+  dim3 grid(ws.splits, lay.num_kv_heads, bat.batch);
+  hipLaunchKernelGGL(decode_quant_gqa_kernel<W>, grid, dim3(W * 64), lds, stream, q, k_pool, v_pool, qpool,
+                     bat.page_table, bat.seq_lens, sel, sel_count, ws.partial, ws.partial_ml, out, bat.pt_stride,
+                     max_sel, bat.num_q_heads, lay.num_kv_heads, G, ws.splits, pps, scale_log2, pol.sink_tokens,
+                     pol.window_tokens, pol.static_head_mask, residual_pages);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ws.splits == 1) return e;
+  return launch_merge_splits(ws, bat.batch, bat.num_q_heads, lay.head_dim_v, out, stream);
+}
+
+}  // namespace qasp

@@ -212,3 +212,33 @@ def test_host_tier_allocation_argument_checks(L):
         h, d = ctypes.c_void_p(1), ctypes.c_void_p(1)
         assert _call("qasp_host_alloc", 1024, ctypes.byref(h), ctypes.byref(d)) == api.ERR_ALLOC
         assert h.value is None and d.value is None
+
+
+def test_quant_step_argument_checks(L):
+    """Quantised pages: grouped-query layouts only, residual_pages >= 1, the
+    pool size, null arguments."""
+    b = ctypes.byref
+    lay, pol = GQA.c(), api.Policy(1, 4, 32).c()
+    bat = _batch()
+    assert _call("qasp_quant_pool_bytes", b(lay)) == 512 * 8 * 1536
+    assert _call("qasp_quant_pool_bytes", b(MLA.c())) == 0
+    assert _call("qasp_quantize_pages", b(lay), b(bat), 0, 1, 1, 1, None) == api.ERR_BAD_SHAPE
+    assert _call("qasp_quantize_pages", b(lay), b(bat), 1, 1, None, 1, None) == api.ERR_NULL_ARG
+    assert _call("qasp_quantize_pages", b(MLA.c()), b(_batch(Hq=128)), 1, 1, 1, 1, None) == api.ERR_UNSUPPORTED
+    need = _call("qasp_workspace_bytes", b(lay), b(bat), b(pol), 37)
+    # (lay, bat, pol, R, q, k_new, v_new, k_pool, v_pool, summ, qpool, scale, out, sel, cnt, max_sel, ws, bytes, st)
+    args = lambda **kw: [kw.get(k, v) for k, v in (("R", 2), ("q", 1), ("k_new", None), ("v_new", None),
+                                                    ("k_pool", 1), ("v_pool", 1), ("summ", 1), ("qpool", 1),
+                                                    ("scale", 1.0), ("out", 1), ("sel", None), ("cnt", None),
+                                                    ("max_sel", 37), ("ws", 1), ("bytes", need), ("stream", None))]
+    call = lambda lay_=lay, bat_=bat, **kw: _call("qasp_decode_step_quant", b(lay_), b(bat_), b(pol), *args(**kw))
+    assert call(R=0) == api.ERR_BAD_SHAPE
+    assert call(qpool=None) == api.ERR_NULL_ARG
+    assert call(summ=None) == api.ERR_NULL_ARG
+    assert call(v_pool=None) == api.ERR_NULL_ARG
+    assert call(k_new=1, v_new=None) == api.ERR_NULL_ARG
+    assert call(bytes=need - 1) == api.ERR_WORKSPACE
+    assert call(max_sel=36) == api.ERR_MAX_SEL
+    assert call(lay_=MLA.c(), bat_=_batch(Hq=128)) == api.ERR_UNSUPPORTED
+    assert _call("qasp_decode_step_quant", b(lay), b(_batch(B=0)), b(pol), 1, None, None, None, None, None, None,
+                 None, 1.0, None, None, None, 37, None, 0, None) == api.OK
