@@ -20,6 +20,9 @@ the next R layers append their token and attend over its selection
 N draft tokens per sequence appended, one shared selection, causal attention
 per draft; value = draft tokens checked per second.
 
+--quant R measures 2-bit quantised pages instead (qasp_decode_step_quant):
+every page outside the last R of a sequence read from the quantised pool.
+
 --host-pool measures the host-tier pool instead: K/V pools in pinned host
 memory mapped into the GPU (qasp_host_alloc), summaries in HBM; the step's
 attention reads the selected pages over the host link.
@@ -137,6 +140,8 @@ def main():
                     help="cross-layer reuse: per group, 1 selecting layer + this many reusing layers")
     ap.add_argument("--drafts", type=int, default=0,
                     help="multi-query step: this many draft tokens per sequence")
+    ap.add_argument("--quant", type=int, default=0,
+                    help="2-bit quantised pages outside a residual region of this many pages")
     ap.add_argument("--host-pool", action="store_true",
                     help="K/V pools in pinned host memory mapped into the GPU")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -158,6 +163,8 @@ def main():
         return run_drafts(args, torch, api, workloads, dev)
     if args.host_pool:
         return run_host_pool(args, torch, api, workloads, dev)
+    if args.quant > 0:
+        return run_quant(args, torch, api, workloads, dev)
     layers = []
     for i in range(args.layers):
         base = workloads.SPECS[args.workload].seed
@@ -275,6 +282,92 @@ def main():
                      "traffic": profiled_traffic(kernel, spec.name) if one_kernel else None,
                      "algorithmic_bytes": total_bytes},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_quant(args, torch, api, workloads, dev):
+    """One-token steps with 2-bit quantised pages (residual region of R
+    pages), rotated over independent layer caches like the default mode."""
+    R = args.quant
+    layers = []
+    for i in range(args.layers):
+        base = workloads.SPECS[args.workload].seed
+        w = workloads.make(args.workload, seed=base + 100 * i, device=dev)
+        lay, pol = api.layout_of(w), api.policy_of(w)
+        bat = api.Batch(w.page_table, w.seq_lens, w.spec.num_q_heads)
+        msel = api.max_sel(lay, pol, bat.max_pages)
+        summ = torch.zeros((w.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16,
+                           device=dev)
+        api.build_summaries(lay, bat, w.k_pool, summ)
+        qpool = api.new_quant_pool(lay, dev)
+        api.quantize_pages(lay, bat, R, w.k_pool, w.v_pool, qpool)
+        B = w.spec.batch
+        layers.append(dict(w=w, lay=lay, pol=pol, bat=bat, msel=msel, summ=summ, qpool=qpool,
+                           ws=api.new_workspace(lay, bat, pol, msel, dev),
+                           sel=torch.empty((B, lay.num_kv_heads, msel), dtype=torch.int32, device=dev),
+                           cnt=torch.empty((B, lay.num_kv_heads), dtype=torch.int32, device=dev),
+                           out=torch.empty((B, w.spec.num_q_heads, lay.head_dim_v), dtype=torch.float32,
+                                           device=dev)))
+        log("layer %d ready" % i)
+    torch.cuda.synchronize()
+
+    def step(L):
+        w = L["w"]
+        api.decode_step_quant(L["lay"], L["bat"], L["pol"], R, w.q, w.k_pool, w.v_pool, L["summ"], L["qpool"],
+                              w.scale, L["ws"], L["msel"], k_new=w.k_new, v_new=w.v_new, out=L["out"], sel=L["sel"],
+                              sel_count=L["cnt"])
+
+    for i in range(args.warmup):
+        step(layers[i % len(layers)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(layers[i % len(layers)])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    w0, spec = layers[0]["w"], layers[0]["w"].spec
+    counts = layers[0]["cnt"].cpu().tolist()
+    sel = layers[0]["sel"].cpu().tolist()
+    lens = w0.seq_lens.cpu().tolist()
+    b_score, b_decode = step_bytes(w0, counts)
+    qo = spec.batch * spec.num_q_heads * (spec.head_dim_k * 2 + spec.head_dim_v * 4)
+    bf16_ph = spec.page_size * (spec.head_dim_k + spec.head_dim_v) * 2
+    n_q = n_r = 0
+    for b in range(spec.batch):
+        P = (lens[b] + spec.page_size - 1) // spec.page_size
+        for g in range(spec.num_kv_heads):
+            for j in sel[b][g][:counts[b][g]]:
+                if j < P - R:
+                    n_q += 1
+                else:
+                    n_r += 1
+    attend_bytes = n_q * 1536 + n_r * bf16_ph + qo
+    total = b_score + attend_bytes
+    gbps = total / (ms_per_step * 1e-3) / 1e9
+    log("quantised-page step (R=%d): %.1f us; %d quantised + %d residual page-heads read" %
+        (R, ms_per_step * 1e3, n_q, n_r))
+    line = {
+        "metric": "decode tokens/s with 2-bit quantised pages (residual %d pages), %s" % (R, spec.name),
+        "value": round(spec.batch / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.batch, "seq_len": spec.seq_len, "residual_pages": R,
+                   "layer_caches_rotated": args.layers},
+        "step_bytes": total,
+        "selected_bytes_quantised_vs_bf16": [attend_bytes - qo, b_decode - qo],
+        "roofline": {"kernel": "decode_step_quant (several kernels)", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes": total},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

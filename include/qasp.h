@@ -282,12 +282,16 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat,
  * as binary16; code = round-half-even((x - m) / s) clamped to 0..3 in binary32
  * (s = 0: 0); read back as m + code * s.  Keys and values must lie within the
  * binary16 range.
- *   qpool [num_pool_pages][num_kv_heads][1536] bytes, per page-head:
- *     [   0, 512) key codes: token t, channel 32i + 8kg + e (i, kg < 4, e < 8)
- *                 at byte 32t + 8kg + 2i + e/4, bits 2(e%4);
+ *   qpool [num_pool_pages][num_kv_heads][1536] bytes, per page-head.  Codes
+ *   come in 8-byte pairs of little-endian words (w0, w1) holding 16 code
+ *   pairs: pair p is in word p / 8, rotated left by 2 (p % 8) bits from the
+ *   position with its first code at bits 5-6 and its second at bits 21-22.
+ *     [   0, 512) key codes: token t, kg < 4 at byte 32t + 8kg; pair 4i + k
+ *                 (i, k < 4) = channels 32i + 8kg + 2k and 32i + 8kg + 2k + 1;
  *     [ 512, 768) key (m, s) binary16 pairs: token t, group i at 16t + 4i;
- *     [ 768,1280) value codes: channel 16i + n (i < 8, n < 16), token 4kg + r
- *                 at byte 8(4n + kg) + i, bits 2r;
+ *     [ 768,1280) value codes: n < 16, kg < 4 at byte 768 + 8(4n + kg); pair
+ *                 2i + h (i < 8, h < 2) = tokens 4kg + 2h and 4kg + 2h + 1 of
+ *                 channel 16i + n;
  *     [1280,1536) value pairs: token t, group g (channels 32g..) at 16t + 4g.
  * qasp_quant_pool_bytes: the size of qpool (0 for an unsupported layout).
  * qasp_quantize_pages: fills the page-heads of logical pages j < P -

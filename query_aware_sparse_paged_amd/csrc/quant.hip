@@ -12,14 +12,22 @@
 // and s as stored (s = 0: code 0).  Read back as m + code * s.
 //
 // A quantised page-head is 1536 bytes (against 8192 in bf16), packed so that
-// each lane of the attention reads its MFMA fragment as one 8-byte load:
-//   [   0, 512) key codes:   token t, channel 32 i + 8 kg + e (i, kg < 4,
-//                            e < 8) at byte 32 t + 8 kg + 2 i + e / 4, bits
-//                            2 (e % 4)
+// each lane of the attention reads its MFMA fragments' codes as one 8-byte
+// load (two words w0, w1) and turns each pair of codes into a pair of bf16
+// operands 4 + c with one rotate and one and-or: pair p (< 16) lives in
+// word p / 8, rotated left by a = 2 (p % 8) from the position where its first
+// code sits at bits 5-6 and its second at bits 21-22.
+//   [   0, 512) key codes:   token t, lane group kg (< 4) at byte 32 t + 8 kg;
+//                            pair p = 4 i + k holds channels 32 i + 8 kg + 2 k
+//                            and + 1 (i, k < 4)
 //   [ 512, 768) key pairs:   token t, group i: binary16 (m, s) at 16 t + 4 i
-//   [ 768,1280) value codes: channel 16 i + n (i < 8, n < 16), token 4 kg + r
-//                            at byte 8 (4 n + kg) + i, bits 2 r
+//   [ 768,1280) value codes: channel n (< 16) of each block, lane group kg at
+//                            byte 8 (4 n + kg); pair p = 2 i + h holds tokens
+//                            4 kg + 2 h and + 1 of channel 16 i + n (i < 8)
 //   [1280,1536) value pairs: token t, group g (channels 32 g ...): at 16 t + 4 g
+// The attention then needs no per-element dequantisation: with A' = 4 + c
+// as the MFMA operand, q . (m + c s) over a group = (m - 4 s) sum(q) +
+// s (q . A'), and sum_t p_t (m + c s) = sum_t p_t (m - 4 s) + (p s) . A'.
 #include <hip/hip_fp16.h>
 
 #include "attend_core.h"
@@ -41,6 +49,26 @@ __device__ __forceinline__ uint32_t group_pair(float mn, float mx, float &m, flo
   m = __half2float(m16);
   s = __half2float(s16);
   return (uint32_t)__half_as_ushort(m16) | ((uint32_t)__half_as_ushort(s16) << 16);
+}
+
+__device__ __forceinline__ uint32_t rotl(uint32_t x, int a) { return a == 0 ? x : (x << a) | (x >> (32 - a)); }
+
+// bf16 operands 4 + c of pair p (< 16) of a lane's code words (4 + c has
+// exponent 2 and the code in the two leading fraction bits).
+__device__ __forceinline__ uint32_t pair_operands(uint2 w, int p) {
+  const uint32_t x = p < 8 ? w.x : w.y;
+  const uint32_t r = __builtin_amdgcn_alignbit(x, x, 2 * (p % 8));  // rotate right
+  return (r & 0x00600060u) | 0x40804080u;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// a, b as a bf16 pair (round to nearest even) and the pair of what remains.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){ra, rb}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t code_of(float x, float m, float s) {
@@ -94,82 +122,104 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
       *(uint32_t *)(dst + (grp < 4 ? kKeyPairs + 16 * t + 4 * grp : kValPairs + 16 * t + 4 * (grp - 4))) = pair;
     }
     __syncthreads();
-    {  // key codes: item (t, kg, i) -> 8 codes, 2 bytes
-      const int t = tid / 16, kg = (tid / 4) % 4, i = tid % 4;
-      const float m = sh_m[t * 8 + i], s = sh_s[t * 8 + i];
+    if (tid < 128) {  // key codes: item (t, kg, word h) -> 16 codes (groups 2h, 2h + 1), one word
+      const int t = tid / 8, kg = (tid / 2) % 4, h = tid % 2;
       uint32_t w = 0;
-      for (int e = 0; e < 8; e++) {
-        const float x = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + e] << 16);
-        w |= code_of(x, m, s) << (2 * e);
+      for (int pp = 0; pp < 8; pp++) {  // pair 8 h + pp: group i = 2 h + pp / 4, k = pp % 4
+        const int i = 2 * h + pp / 4, k = pp % 4;
+        const float m = sh_m[t * 8 + i], s = sh_s[t * 8 + i];
+        const float x0 = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + 2 * k] << 16);
+        const float x1 = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + 2 * k + 1] << 16);
+        w |= rotl(code_of(x0, m, s) << 5 | code_of(x1, m, s) << 21, 2 * pp);
       }
-      *(uint16_t *)(dst + 32 * t + 8 * kg + 2 * i) = (uint16_t)w;
-    }
-    for (int item = tid; item < 16 * 4 * 8; item += 256) {  // value codes: item (n, kg, i) -> 4 codes, 1 byte
-      const int n = item / 32, kg = (item / 8) % 4, i = item % 8;
-      const int dv = 16 * i + n, grp = 4 + dv / 32;
+      *(uint32_t *)(dst + 32 * t + 8 * kg + 4 * h) = w;
+    } else {  // value codes: item (n, kg, word h) -> 16 codes (blocks 4h .. 4h + 3), one word
+      const int item = tid - 128, n = item / 8, kg = (item / 2) % 4, h = item % 2;
       uint32_t w = 0;
-      for (int r = 0; r < 4; r++) {
-        const int t = 4 * kg + r;
-        const float x = __uint_as_float((uint32_t)vp[dv * PS + t] << 16);
-        w |= code_of(x, sh_m[t * 8 + grp], sh_s[t * 8 + grp]) << (2 * r);
+      for (int pp = 0; pp < 8; pp++) {  // pair 8 h + pp: block i = 4 h + pp / 2, tokens 4 kg + 2 (pp % 2) + 0/1
+        const int i = 4 * h + pp / 2, dv = 16 * i + n, grp = 4 + dv / 32;
+        const int t0 = 4 * kg + 2 * (pp % 2), t1 = t0 + 1;
+        const float x0 = __uint_as_float((uint32_t)vp[dv * PS + t0] << 16);
+        const float x1 = __uint_as_float((uint32_t)vp[dv * PS + t1] << 16);
+        w |= rotl(code_of(x0, sh_m[t0 * 8 + grp], sh_s[t0 * 8 + grp]) << 5 |
+                      code_of(x1, sh_m[t1 * 8 + grp], sh_s[t1 * 8 + grp]) << 21,
+                  2 * pp);
       }
-      dst[kValCodes + 8 * (4 * n + kg) + i] = (uint8_t)w;
+      *(uint32_t *)(dst + kValCodes + 8 * (4 * n + kg) + 4 * h) = w;
     }
     __syncthreads();
   }
 }
 
 // One quantised page-head's fragments for a wave lane.
+// (the pairs are loaded separately: see the attention loop)
 struct QPage {
-  uint2 kc;      // key codes: token l % 16, channels 32 i + 8 (l / 16) ...
-  uint4 kp;      // key pairs of token l % 16, groups 0..3
-  uint2 vc;      // value codes: channels 16 i + l % 16, tokens 4 (l / 16) ...
-  uint4 vp[4];   // value pairs of tokens 4 (l / 16) + r, groups 0..3
+  uint2 kc;      // key code words: token l % 16, channels 32 i + 8 (l / 16) ...
+  uint2 vc;      // value code words: channels 16 i + l % 16, tokens 4 (l / 16) ...
 
   __device__ __forceinline__ void load(const uint8_t *ph, int lane) {
     const int n = lane & 15, kg = lane >> 4;
     kc = *(const uint2 *)(ph + 32 * n + 8 * kg);
-    kp = *(const uint4 *)(ph + kKeyPairs + 16 * n);
     vc = *(const uint2 *)(ph + kValCodes + 8 * (4 * n + kg));
-#pragma unroll
-    for (int r = 0; r < 4; r++) vp[r] = *(const uint4 *)(ph + kValPairs + 16 * (4 * kg + r));
   }
 };
 
+// Key or value pairs (at byte offset off) of tokens 4 (l / 16) + r, groups 0..3.
+__device__ __forceinline__ void load_pairs(uint4 *pr, const uint8_t *ph, int off, int lane) {
+#pragma unroll
+  for (int r = 0; r < 4; r++) pr[r] = *(const uint4 *)(ph + off + 16 * ((lane >> 4) * 4 + r));
+}
+
 __device__ __forceinline__ uint32_t dw(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
-// Softmax attention of the wave's head columns over one quantised page (logical
-// id j; real = false computes it fully masked).  Keys and values are read back
-// as m + code * s in binary32 and fed to the MFMAs as bf16 hi + lo parts.
-__device__ __forceinline__ void attend_qpage(attend::WaveState &st, const QPage &pg, const uint4 *bq, bool real, int j,
-                                             int L, bool is_static, int sink_end, int win_begin, float scale_log2,
+// Sum of head column l % 16's query over each group of 32 channels (every
+// lane of the column gets it).
+__device__ __forceinline__ void query_group_sums(const uint4 *bq, float *qs) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t w = dw(bq[i], k);
+      a += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+    }
+    a += __shfl_xor(a, 16, kWave);
+    a += __shfl_xor(a, 32, kWave);
+    qs[i] = a;
+  }
+}
+
+// Softmax attention of the wave's head columns over one quantised page
+// (logical id j; vp: its value pairs).  bacc[g] accumulates, in the scale of
+// st, this lane's tokens' share of the zero-point part of the output channels
+// of value group g (summed over the lanes of a column and added to st.acc by
+// the caller).
+__device__ __forceinline__ void attend_qpage(attend::WaveState &st, float *bacc, const QPage &pg, const uint4 *kp,
+                                             const uint4 *vp, const uint4 *bq, const float *qs, int j, int L,
+                                             bool is_static, int sink_end, int win_begin, float scale_log2,
                                              int lane) {
   constexpr int PS = 16;
   const int kg = lane >> 4;
-  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+  // S^T: per group, (m - 4 s) sum(q) + s (A' q)
+  float sv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t pair = dw(pg.kp, i);
-    const float m = half_bits_to_f32(pair), sc = half_bits_to_f32(pair >> 16);
-    const uint32_t codes = (i < 2 ? pg.kc.x : pg.kc.y) >> (16 * (i & 1));
-    float x[8];
+    const uint4 a = make_uint4(pair_operands(pg.kc, 4 * i), pair_operands(pg.kc, 4 * i + 1),
+                               pair_operands(pg.kc, 4 * i + 2), pair_operands(pg.kc, 4 * i + 3));
+    const floatx4 o = mfma16x16x32(a, bq[i], floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int e = 0; e < 8; e++) x[e] = fmaf((float)((codes >> (2 * e)) & 3u), sc, m);
-    const uint2 h0 = attend::pack_bf16x4(x[0], x[1], x[2], x[3]), h1 = attend::pack_bf16x4(x[4], x[5], x[6], x[7]);
-    const uint2 l0 = attend::pack_bf16x4(x[0] - attend::bf16_round_f32(x[0]), x[1] - attend::bf16_round_f32(x[1]),
-                                         x[2] - attend::bf16_round_f32(x[2]), x[3] - attend::bf16_round_f32(x[3]));
-    const uint2 l1 = attend::pack_bf16x4(x[4] - attend::bf16_round_f32(x[4]), x[5] - attend::bf16_round_f32(x[5]),
-                                         x[6] - attend::bf16_round_f32(x[6]), x[7] - attend::bf16_round_f32(x[7]));
-    s = mfma16x16x32(make_uint4(h0.x, h0.y, h1.x, h1.y), bq[i], s);
-    s = mfma16x16x32(make_uint4(l0.x, l0.y, l1.x, l1.y), bq[i], s);
+    for (int r = 0; r < 4; r++) {
+      const uint32_t pair = dw(kp[r], i);
+      const float m = half_bits_to_f32(pair), sc = half_bits_to_f32(pair >> 16);
+      sv[r] = fmaf(fmaf(-4.f, sc, m), qs[i], fmaf(sc, o[r], sv[r]));
+    }
   }
-  float sv[4];
   float tmax = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; r++) {
     const int pos = j * PS + 4 * kg + r;
-    const bool ok = real & (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
-    sv[r] = ok ? s[r] * scale_log2 : -INFINITY;
+    const bool ok = (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
+    sv[r] = ok ? sv[r] * scale_log2 : -INFINITY;
     tmax = fmaxf(tmax, sv[r]);
   }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
@@ -190,33 +240,28 @@ __device__ __forceinline__ void attend_qpage(attend::WaveState &st, const QPage 
   psum += __shfl_xor(psum, 32, kWave);
   st.l = st.l * alpha + psum;
   st.m = m_new;
-  const uint2 ph = attend::pack_bf16x4(p[0], p[1], p[2], p[3]);
-  const uint2 pl = attend::pack_bf16x4(p[0] - attend::bf16_round_f32(p[0]), p[1] - attend::bf16_round_f32(p[1]),
-                                       p[2] - attend::bf16_round_f32(p[2]), p[3] - attend::bf16_round_f32(p[3]));
-  // value pairs of this lane's 4 tokens, groups 0..3
-  float vm[4][4], vs[4][4];
+  // per value group g: weights p s as bf16 hi + lo, and the zero-point part
+  uint2 bh[4], bl[4];
 #pragma unroll
-  for (int r = 0; r < 4; r++)
+  for (int g = 0; g < 4; g++) {
+    float w4[4], z = 0.f;
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-      const uint32_t pair = dw(pg.vp[r], g);
-      vm[r][g] = half_bits_to_f32(pair);
-      vs[r][g] = half_bits_to_f32(pair >> 16);
+    for (int r = 0; r < 4; r++) {
+      const uint32_t pair = dw(vp[r], g);
+      const float m = half_bits_to_f32(pair), sc = half_bits_to_f32(pair >> 16);
+      w4[r] = p[r] * sc;
+      z = fmaf(p[r], fmaf(-4.f, sc, m), z);
     }
+    split2(w4[0], w4[1], bh[g].x, bl[g].x);
+    split2(w4[2], w4[3], bh[g].y, bl[g].y);
+    bacc[g] = fmaf(bacc[g], alpha, z);
+  }
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const uint32_t codes = ((i < 4 ? pg.vc.x : pg.vc.y) >> (8 * (i & 3))) & 0xffu;
-    const int g = i / 2;
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) x[r] = fmaf((float)((codes >> (2 * r)) & 3u), vs[r][g], vm[r][g]);
-    const uint2 vh = attend::pack_bf16x4(x[0], x[1], x[2], x[3]);
-    const uint2 vl = attend::pack_bf16x4(x[0] - attend::bf16_round_f32(x[0]), x[1] - attend::bf16_round_f32(x[1]),
-                                         x[2] - attend::bf16_round_f32(x[2]), x[3] - attend::bf16_round_f32(x[3]));
+    const uint2 a = make_uint2(pair_operands(pg.vc, 2 * i), pair_operands(pg.vc, 2 * i + 1));
     st.acc[i] *= alpha;
-    st.acc[i] = mfma16x16x16(vh, ph, st.acc[i]);
-    st.acc[i] = mfma16x16x16(vh, pl, st.acc[i]);
-    st.acc[i] = mfma16x16x16(vl, ph, st.acc[i]);
+    st.acc[i] = mfma16x16x16(a, bh[i / 2], st.acc[i]);
+    st.acc[i] = mfma16x16x16(a, bl[i / 2], st.acc[i]);
   }
 }
 
@@ -227,7 +272,8 @@ __device__ __forceinline__ void attend_qpage(attend::WaveState &st, const QPage 
 // wave's pages below P - residual_pages (its first ones: the list is
 // ascending) are read from the quantised pool, the rest from the bf16 pools.
 template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void decode_quant_gqa_kernel(
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4))) void
+decode_quant_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool, const uint16_t *__restrict__ v_pool,
     const uint8_t *__restrict__ qpool, const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ sel_count, float *__restrict__ partial,
@@ -262,20 +308,39 @@ __global__ __launch_bounds__(WAVES * 64) void decode_quant_gqa_kernel(
     auto base = [&](int it) {
       return qpool + ((size_t)__shfl(my_phys, min(it, n_q - 1), kWave) * Hkv + g) * quant::kPageHeadBytes;
     };
+    float qs[4], bacc[4] = {0.f, 0.f, 0.f, 0.f};
+    quant::query_group_sums(bq, qs);
+    // code words one page ahead; the pairs are loaded at the start of their
+    // page (the value pairs are waited on only after the key work)
     quant::QPage cur, nxt;
     cur.load(base(0), lane);
     for (int it = 0; it < n_q; it++) {
+      uint4 kp[4], vp[4];
+      quant::load_pairs(kp, base(it), quant::kKeyPairs, lane);
+      quant::load_pairs(vp, base(it), quant::kValPairs, lane);
       nxt.load(base(it + 1), lane);  // past the end: the last page again (unused)
-      quant::attend_qpage(st, cur, bq, true, __shfl(my_j, it, kWave), L, is_static, sink_end, win_begin, scale_log2,
-                          lane);
+      quant::attend_qpage(st, bacc, cur, kp, vp, bq, qs, __shfl(my_j, it, kWave), L, is_static, sink_end,
+                          win_begin, scale_log2, lane);
       cur = nxt;
     }
+    // output channels 16 i + 4 (l / 16) + r belong to value group i / 2; the
+    // lanes of a column hold their own tokens' shares
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      bacc[g] += __shfl_xor(bacc[g], 16, kWave);
+      bacc[g] += __shfl_xor(bacc[g], 32, kWave);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) st.acc[i] += bacc[i / 2];
   }
-  // the remaining (residual) pages from the bf16 pools
-  const int src = min(lane + n_q, kWave - 1);
-  const int r_j = __shfl(my_j, src, kWave), r_phys = __shfl(my_phys, src, kWave);
+  // the remaining (residual) pages from the bf16 pools, one at a time (a
+  // handful per wave; no prefetch stages, which keeps the kernel's registers
+  // within four waves per SIMD)
   const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
-  attend::attend_pages<PS, D, DV>(st, pw, npg - n_q, r_j, r_phys, lane);
+  for (int it = n_q; it < npg; it++) {
+    const attend::PageRegs<D, DV> pr = pw.load(__shfl(my_phys, it, kWave), lane);
+    pw.compute(st, true, __shfl(my_j, it, kWave), pr.k, pr.v, lane);
+  }
   attend::merge_waves<WAVES, DV>(lds, st, G, [&](int h, int dv, float a, float lsum, float M) {
     if (splits == 1) {
       out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
@@ -301,7 +366,7 @@ hipError_t launch_decode_quant_gqa(const qasp_layout &lay, const qasp_batch &bat
                                    const uint16_t *v_pool, const uint8_t *qpool, const int32_t *sel,
                                    const int32_t *sel_count, int max_sel, float scale, float *out,
                                    const Workspace &ws, hipStream_t stream) {
-  constexpr int W = kGqaDecodeWaves;
+  constexpr int W = 16;  // 16 waves per block, four per SIMD: a quantised page is short work, latency needs hiding
   if (bat.batch == 0) return hipSuccess;
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const float scale_log2 = scale * 1.4426950408889634f;

@@ -21,21 +21,35 @@ if torch.cuda.is_available():
     from gpu_cases import DEV, OUT_TOL, olayout, opolicy
 
 
+def _pairs(words):
+    """Code words [..., 2] (uint32) -> codes [..., 16, 2]: pair p sits in word
+    p // 8 rotated left by 2 (p % 8) from first code at bits 5-6, second at
+    bits 21-22."""
+    out = np.zeros(words.shape[:-1] + (16, 2), np.uint8)
+    for p in range(16):
+        w = words[..., p // 8].astype(np.uint64)
+        a = 2 * (p % 8)
+        r = ((w >> a) | (w << (32 - a))) & 0xffffffff if a else w
+        out[..., p, 0] = (r >> 5) & 3
+        out[..., p, 1] = (r >> 21) & 3
+    return out
+
+
 def unpack(qpool: np.ndarray):
     """Packed quantised pool [pool][Hkv][1536] -> the oracle's logical arrays
     (key codes [pool][Hkv][16][128], key pairs [pool][Hkv][16][4][2], value
-    codes, value pairs).  Layout (the library header's): key code of token t,
-    channel 32i + 8kg + e at byte 32t + 8kg + 2i + e/4, bits 2(e%4); value code
-    of channel 16i + n, token 4kg + r at byte 768 + 8(4n + kg) + i, bits 2r."""
+    codes, value pairs), per the library header's layout: key words of token
+    t, lane group kg at byte 32t + 8kg, pair 4i + k = channels 32i + 8kg + 2k
+    and + 1; value words of channel n, lane group kg at byte 768 + 8(4n + kg),
+    pair 2i + h = tokens 4kg + 2h and + 1 of channel 16i + n."""
     P, H = qpool.shape[:2]
-    shifts = np.array([0, 2, 4, 6], np.uint8)
-    kb = qpool[..., :512].reshape(P, H, 16, 4, 4, 2)                     # t, kg, i, byte
-    kc = (kb[..., None] >> shifts) & 3                                   # t, kg, i, byte, 4 -> e = 4 byte + k
-    kc = kc.reshape(P, H, 16, 4, 4, 8).transpose(0, 1, 2, 4, 3, 5).reshape(P, H, 16, 128)
+    kw = qpool[..., :512].copy().view(np.uint32).reshape(P, H, 16, 4, 2)       # t, kg, word
+    kc = _pairs(kw).reshape(P, H, 16, 4, 4, 4, 2)                              # t, kg, i, k, e
+    kc = kc.transpose(0, 1, 2, 4, 3, 5, 6).reshape(P, H, 16, 128)
     km = qpool[..., 512:768].copy().view(np.uint16).reshape(P, H, 16, 4, 2)
-    vb = qpool[..., 768:1280].reshape(P, H, 16, 4, 8)                    # n, kg, i
-    vc = (vb[..., None] >> shifts) & 3                                   # n, kg, i, r
-    vc = vc.transpose(0, 1, 3, 5, 4, 2).reshape(P, H, 16, 128)            # (kg, r) -> t, (i, n) -> dv
+    vw = qpool[..., 768:1280].copy().view(np.uint32).reshape(P, H, 16, 4, 2)   # n, kg, word
+    vc = _pairs(vw).reshape(P, H, 16, 4, 8, 2, 2)                              # n, kg, i, h, e
+    vc = vc.transpose(0, 1, 3, 5, 6, 4, 2).reshape(P, H, 16, 128)              # (kg, h, e) -> t, (i, n) -> dv
     vm = qpool[..., 1280:].copy().view(np.uint16).reshape(P, H, 16, 4, 2)
     return kc, km, vc, vm
 
