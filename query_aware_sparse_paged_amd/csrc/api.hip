@@ -399,6 +399,18 @@ int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat, co
   int32_t *sel_out = sel ? sel : ws.sel;
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   hipError_t e = hipSuccess;
+  const long units = (long)bat->batch * lay->num_kv_heads;
+  if (units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages &&
+      fused_lds_bytes(*lay, *bat, max_sel) <= 160 * 1024) {
+    // many units: append, score and select in the one-kernel step's selection-only form
+    e = launch_fused_step_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel_out, cnt_out,
+                              max_sel, s, 1, 0, true);
+    if (e == hipSuccess) e = launch_quantize(*lay, *bat, residual_pages, true, k_pool, v_pool, qpool, s);
+    if (e == hipSuccess)
+      e = launch_decode_quant_gqa(*lay, *bat, *pol, residual_pages, q, k_pool, v_pool, qpool, sel_out, cnt_out,
+                                  max_sel, scale, out, ws, s);
+    return status_of(e);
+  }
   if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
   // a token that opened a new page pushed page P - 1 - R out of the residual region
   if (e == hipSuccess) e = launch_quantize(*lay, *bat, residual_pages, true, k_pool, v_pool, qpool, s);

@@ -95,7 +95,9 @@ __device__ __forceinline__ int2 unit_for_block(int i, const int32_t *seq_lens, i
 // appended): column n scores the tokens up to its draft's position and, for a
 // static head, its own window of window_q tokens (window_tokens is then the
 // drafts' union); the output goes to [B][n_draft][Hq / n_draft][DV].
-template <int D, int DV, int PS, int W, bool CAUSAL = false>
+// SEL_ONLY: append, score and select only (the selection is written out for
+// another attention kernel; out is not touched).
+template <int D, int DV, int PS, int W, bool CAUSAL = false, bool SEL_ONLY = false>
 __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     uint16_t *__restrict__ k_pool, uint16_t *__restrict__ v_pool, uint16_t *__restrict__ summ,
@@ -347,6 +349,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const int count = fast ? sel::emit_by_threshold(sh, keys32, n, uk_fast, cand_lo, cand_hi, P, sel_row, list, max_sel)
                          : sel::emit_selection(sh, sel_bits, nwords, sel_row, list, max_sel);
   if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
+  if constexpr (SEL_ONLY) return;  // block-uniform; the unused page preload above is not emitted
   __syncthreads();
 
   // ---- attend: wave w takes attention positions w, w+W, ... (a fixed
@@ -484,7 +487,7 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
                                  int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream, int n_draft,
-                                 int window_q) {
+                                 int window_q, bool sel_only) {
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = FusedLds(mp, max_sel, G).total;
@@ -494,8 +497,9 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   const int units = bat.batch * lay.num_kv_heads;
   const int lpt = units > device_cu_count() ? 1 : 0;
   dim3 grid(units);
-  auto kernel = n_draft > 1 ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, true>
-                            : fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false>;
+  auto kernel = sel_only      ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false, true>
+                : n_draft > 1 ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, true>
+                              : fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false>;
   hipLaunchKernelGGL(kernel, grid, dim3(kFusedWaves * 64), lds, stream, q, k_new, v_new, k_pool, v_pool, summ,
                      bat.page_table, bat.seq_lens, out, sel, sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads,
                      lay.num_kv_heads, G, pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens,

@@ -56,9 +56,10 @@ def unpack(qpool: np.ndarray):
 
 @pytest.mark.parametrize("name,batch,R,kw", [
     ("llama8b_b32_32k", 3, 2, dict(seq_len=1500, seq_len_min=700)),              # kernel chain, split units
-    ("llama8b_b32_32k", 32, 8, dict(seq_len=1300, seq_len_min=500)),              # many units
+    ("llama8b_b32_32k", 32, 8, dict(seq_len=1300, seq_len_min=500)),              # many units: fused selection
     ("llama8b_b32_32k", 4, 1, dict(seq_len=900, seq_len_min=600, top_k=200)),     # every page selected
-    ("ragged_b64_mixed", 6, 3, dict(seq_len=3000, seq_len_min=1200))])            # static heads
+    ("ragged_b64_mixed", 6, 3, dict(seq_len=3000, seq_len_min=1200)),             # static heads
+    ("ragged_b64_mixed", 32, 5, dict(seq_len=2600, seq_len_min=900))])            # static heads, many units
 def test_quant_step_matches_oracle(name, batch, R, kw):
     print("quantised-page case", name, batch, R, kw, flush=True)
     w = workloads.make(name, device="cpu", seed=13, batch=batch, **kw)
