@@ -405,21 +405,19 @@ int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat, co
     // many units: append, score and select in the one-kernel step's selection-only form
     e = launch_fused_step_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel_out, cnt_out,
                               max_sel, s, 1, 0, true);
-    if (e == hipSuccess) e = launch_quantize(*lay, *bat, residual_pages, true, k_pool, v_pool, qpool, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess)  // (quantises the page leaving the residual region too)
       e = launch_decode_quant_gqa(*lay, *bat, *pol, residual_pages, q, k_pool, v_pool, qpool, sel_out, cnt_out,
                                   max_sel, scale, out, ws, s);
     return status_of(e);
   }
   if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
-  // a token that opened a new page pushed page P - 1 - R out of the residual region
-  if (e == hipSuccess) e = launch_quantize(*lay, *bat, residual_pages, true, k_pool, v_pool, qpool, s);
   if (e == hipSuccess && scored)
     e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s,
                            token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr));
   if (e == hipSuccess)
     e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
-  if (e == hipSuccess)
+  if (e == hipSuccess)  // (a token that opened a new page pushed page P - 1 - R out of the residual region:
+                        // the attention launch quantises it first)
     e = launch_decode_quant_gqa(*lay, *bat, *pol, residual_pages, q, k_pool, v_pool, qpool, sel_out, cnt_out,
                                 max_sel, scale, out, ws, s);
   return status_of(e);

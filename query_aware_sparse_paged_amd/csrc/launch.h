@@ -89,6 +89,9 @@ hipError_t launch_prepare_drafts(const qasp_layout &lay, const qasp_batch &bat, 
 constexpr size_t kQuantPageHeadBytes = 1536;
 hipError_t launch_quantize(const qasp_layout &lay, const qasp_batch &bat, int residual_pages, bool step_mode,
                            const uint16_t *k_pool, const uint16_t *v_pool, uint8_t *qpool, hipStream_t stream);
+// (the attention also quantises the page that leaves the residual region at
+// this step: inside its blocks when units are not split, else by a
+// quantiser launch before it)
 hipError_t launch_decode_quant_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                    int residual_pages, const uint16_t *q, const uint16_t *k_pool,
                                    const uint16_t *v_pool, const uint8_t *qpool, const int32_t *sel,

@@ -77,78 +77,91 @@ __device__ __forceinline__ uint32_t code_of(float x, float m, float s) {
   return (uint32_t)fminf(fmaxf(c, 0.f), 3.f);
 }
 
-// One block per (logical page, sequence) (bulk) or per sequence (step: the
-// page that has just left the residual region, when the step's token opened a
-// new page).  Per KV head: phase A computes the (m, s) pair of every group
-// (128 groups: 16 tokens x 4 key + 4 value groups) into LDS and memory;
-// phase B writes the code bytes (each byte is written by one thread).
+// Quantises page-head (phys, g) from the bf16 pools (keys [t][d], values
+// [dv][t]).  Called by every thread of a block of at least 256 threads (it
+// holds two block barriers); sm: 256 floats of LDS.  Phase A computes the
+// (m, s) pair of every group (16 tokens x 4 key + 4 value groups) into LDS and
+// memory; phase B writes the code words (each word is written by one thread).
+__device__ void quantize_page_head(const uint16_t *__restrict__ k_pool, const uint16_t *__restrict__ v_pool,
+                                   uint8_t *__restrict__ qpool, int phys, int g, int Hkv, float *sm) {
+  constexpr int PS = 16, D = 128, DV = 128;
+  float *sh_m = sm, *sh_s = sm + 8 * PS;  // [token][group: 4 key, 4 value]
+  const int tid = threadIdx.x;
+  const size_t ph = (size_t)phys * Hkv + g;
+  const uint16_t *kp = k_pool + ph * PS * D;   // [t][d]
+  const uint16_t *vp = v_pool + ph * DV * PS;  // [dv][t]
+  uint8_t *dst = qpool + ph * kPageHeadBytes;
+  if (tid < 8 * PS) {
+    const int t = tid / 8, grp = tid % 8;
+    // min / max in channel order, the first of equal values kept (so the
+    // sign of a zero minimum is that of the first zero)
+    float mn = 0.f, mx = 0.f;
+    for (int e = 0; e < 32; e++) {
+      const uint16_t bits = grp < 4 ? kp[t * D + 32 * grp + e] : vp[(32 * (grp - 4) + e) * PS + t];
+      const float x = __uint_as_float((uint32_t)bits << 16);
+      if (e == 0 || x < mn) mn = x;
+      if (e == 0 || x > mx) mx = x;
+    }
+    float m, s;
+    const uint32_t pair = group_pair(mn, mx, m, s);
+    sh_m[tid] = m;
+    sh_s[tid] = s;
+    *(uint32_t *)(dst + (grp < 4 ? kKeyPairs + 16 * t + 4 * grp : kValPairs + 16 * t + 4 * (grp - 4))) = pair;
+  }
+  __syncthreads();
+  if (tid < 128) {  // key codes: item (t, kg, word h) -> 16 codes (groups 2h, 2h + 1), one word
+    const int t = tid / 8, kg = (tid / 2) % 4, h = tid % 2;
+    uint32_t w = 0;
+    for (int pp = 0; pp < 8; pp++) {  // pair 8 h + pp: group i = 2 h + pp / 4, k = pp % 4
+      const int i = 2 * h + pp / 4, k = pp % 4;
+      const float m = sh_m[t * 8 + i], s = sh_s[t * 8 + i];
+      const float x0 = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + 2 * k] << 16);
+      const float x1 = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + 2 * k + 1] << 16);
+      w |= rotl(code_of(x0, m, s) << 5 | code_of(x1, m, s) << 21, 2 * pp);
+    }
+    *(uint32_t *)(dst + 32 * t + 8 * kg + 4 * h) = w;
+  } else if (tid < 256) {  // value codes: item (n, kg, word h) -> 16 codes (blocks 4h .. 4h + 3), one word
+    const int item = tid - 128, n = item / 8, kg = (item / 2) % 4, h = item % 2;
+    uint32_t w = 0;
+    for (int pp = 0; pp < 8; pp++) {  // pair 8 h + pp: block i = 4 h + pp / 2, tokens 4 kg + 2 (pp % 2) + 0/1
+      const int i = 4 * h + pp / 2, dv = 16 * i + n, grp = 4 + dv / 32;
+      const int t0 = 4 * kg + 2 * (pp % 2), t1 = t0 + 1;
+      const float x0 = __uint_as_float((uint32_t)vp[dv * PS + t0] << 16);
+      const float x1 = __uint_as_float((uint32_t)vp[dv * PS + t1] << 16);
+      w |= rotl(code_of(x0, sh_m[t0 * 8 + grp], sh_s[t0 * 8 + grp]) << 5 |
+                    code_of(x1, sh_m[t1 * 8 + grp], sh_s[t1 * 8 + grp]) << 21,
+                2 * pp);
+    }
+    *(uint32_t *)(dst + kValCodes + 8 * (4 * n + kg) + 4 * h) = w;
+  }
+  __syncthreads();
+}
+
+// The page of sequence b that leaves the residual region at this step: when
+// the step's token opened a new page, page P - 1 - residual_pages; else -1.
+__device__ __forceinline__ int leaving_page(int L, int residual_pages) {
+  constexpr int PS = 16;
+  if (L < 1 || (L - 1) % PS != 0) return -1;
+  const int j = (L + PS - 1) / PS - 1 - residual_pages;
+  return j >= 0 ? j : -1;
+}
+
+// One block per (logical page, sequence) (bulk: every page below P -
+// residual_pages) or per sequence (step: the page leaving the residual region).
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ k_pool,
                                                        const uint16_t *__restrict__ v_pool, uint8_t *__restrict__ qpool,
                                                        const int32_t *__restrict__ page_table,
                                                        const int32_t *__restrict__ seq_lens, int pt_stride, int Hkv,
                                                        int residual_pages, int step_mode) {
-  constexpr int PS = 16, D = 128, DV = 128;
-  __shared__ float sh_m[8 * PS], sh_s[8 * PS];  // [token][group: 4 key, 4 value]
-  const int b = blockIdx.y, tid = threadIdx.x;
+  constexpr int PS = 16;
+  __shared__ float sm[16 * PS];
+  const int b = blockIdx.y;
   const int L = seq_lens[b];
   const int P = (L + PS - 1) / PS;
-  int j = blockIdx.x;
-  if (step_mode) {
-    if (L < 1 || (L - 1) % PS != 0) return;  // the token did not open a new page
-    j = P - 1 - residual_pages;
-  }
-  if (j < 0 || j >= P - residual_pages) return;
+  const int j = step_mode ? leaving_page(L, residual_pages) : (int)blockIdx.x;
+  if (j < 0 || j >= P - residual_pages) return;  // block-uniform
   const int phys = page_table[(size_t)b * pt_stride + j];
-  for (int g = 0; g < Hkv; g++) {
-    const size_t ph = (size_t)phys * Hkv + g;
-    const uint16_t *kp = k_pool + ph * PS * D;   // [t][d]
-    const uint16_t *vp = v_pool + ph * DV * PS;  // [dv][t]
-    uint8_t *dst = qpool + ph * kPageHeadBytes;
-    if (tid < 8 * PS) {
-      const int t = tid / 8, grp = tid % 8;
-      // min / max in channel order, the first of equal values kept (so the
-      // sign of a zero minimum is that of the first zero)
-      float mn = 0.f, mx = 0.f;
-      for (int e = 0; e < 32; e++) {
-        const uint16_t bits = grp < 4 ? kp[t * D + 32 * grp + e] : vp[(32 * (grp - 4) + e) * PS + t];
-        const float x = __uint_as_float((uint32_t)bits << 16);
-        if (e == 0 || x < mn) mn = x;
-        if (e == 0 || x > mx) mx = x;
-      }
-      float m, s;
-      const uint32_t pair = group_pair(mn, mx, m, s);
-      sh_m[tid] = m;
-      sh_s[tid] = s;
-      *(uint32_t *)(dst + (grp < 4 ? kKeyPairs + 16 * t + 4 * grp : kValPairs + 16 * t + 4 * (grp - 4))) = pair;
-    }
-    __syncthreads();
-    if (tid < 128) {  // key codes: item (t, kg, word h) -> 16 codes (groups 2h, 2h + 1), one word
-      const int t = tid / 8, kg = (tid / 2) % 4, h = tid % 2;
-      uint32_t w = 0;
-      for (int pp = 0; pp < 8; pp++) {  // pair 8 h + pp: group i = 2 h + pp / 4, k = pp % 4
-        const int i = 2 * h + pp / 4, k = pp % 4;
-        const float m = sh_m[t * 8 + i], s = sh_s[t * 8 + i];
-        const float x0 = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + 2 * k] << 16);
-        const float x1 = __uint_as_float((uint32_t)kp[t * D + 32 * i + 8 * kg + 2 * k + 1] << 16);
-        w |= rotl(code_of(x0, m, s) << 5 | code_of(x1, m, s) << 21, 2 * pp);
-      }
-      *(uint32_t *)(dst + 32 * t + 8 * kg + 4 * h) = w;
-    } else {  // value codes: item (n, kg, word h) -> 16 codes (blocks 4h .. 4h + 3), one word
-      const int item = tid - 128, n = item / 8, kg = (item / 2) % 4, h = item % 2;
-      uint32_t w = 0;
-      for (int pp = 0; pp < 8; pp++) {  // pair 8 h + pp: block i = 4 h + pp / 2, tokens 4 kg + 2 (pp % 2) + 0/1
-        const int i = 4 * h + pp / 2, dv = 16 * i + n, grp = 4 + dv / 32;
-        const int t0 = 4 * kg + 2 * (pp % 2), t1 = t0 + 1;
-        const float x0 = __uint_as_float((uint32_t)vp[dv * PS + t0] << 16);
-        const float x1 = __uint_as_float((uint32_t)vp[dv * PS + t1] << 16);
-        w |= rotl(code_of(x0, sh_m[t0 * 8 + grp], sh_s[t0 * 8 + grp]) << 5 |
-                      code_of(x1, sh_m[t1 * 8 + grp], sh_s[t1 * 8 + grp]) << 21,
-                  2 * pp);
-      }
-      *(uint32_t *)(dst + kValCodes + 8 * (4 * n + kg) + 4 * h) = w;
-    }
-    __syncthreads();
-  }
+  for (int g = 0; g < Hkv; g++) quantize_page_head(k_pool, v_pool, qpool, phys, g, Hkv, sm);
 }
 
 // One quantised page-head's fragments for a wave lane.
@@ -279,13 +292,21 @@ decode_quant_gqa_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ sel_count, float *__restrict__ partial,
     float2 *__restrict__ partial_ml, float *__restrict__ out, int pt_stride, int max_sel, int Hq, int Hkv, int G,
     int splits, int pps, float scale_log2, int sink_tokens, int window_tokens, uint64_t static_mask,
-    int residual_pages) {
+    int residual_pages, uint8_t *__restrict__ qpool_w, const uint16_t *__restrict__ k_pool_q,
+    const uint16_t *__restrict__ v_pool_q) {
   constexpr int PS = 16, D = 128, DV = 128;
   extern __shared__ float lds[];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int unit = b * Hkv + g;
   const int L = seq_lens[b];
+  if (qpool_w != nullptr) {
+    // the unit is not split: its block alone reads page-head (leaving page, g),
+    // so it quantises it first (the barriers inside order the reads below)
+    const int jl = quant::leaving_page(L, residual_pages);
+    if (jl >= 0)  // block-uniform
+      quant::quantize_page_head(k_pool_q, v_pool_q, qpool_w, page_table[(size_t)b * pt_stride + jl], g, Hkv, lds);
+  }
   const int q_end = (L + PS - 1) / PS - residual_pages;  // pages below are quantised
   const bool is_static = head_is_static(static_mask, g);
   const int sink_end = is_static ? min(sink_tokens, L) : 0;
@@ -371,12 +392,20 @@ hipError_t launch_decode_quant_gqa(const qasp_layout &lay, const qasp_batch &bat
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const float scale_log2 = scale * 1.4426950408889634f;
   const int pps = (max_sel + ws.splits - 1) / ws.splits;
-  const size_t lds = (size_t)attend::merge_lds_floats(W, G, 128) * sizeof(float);
+  const size_t lds = (size_t)std::max(attend::merge_lds_floats(W, G, 128), 256) * sizeof(float);
   dim3 grid(ws.splits, lay.num_kv_heads, bat.batch);
+  // with one block per unit the block quantises its own leaving page-head;
+  // otherwise the in-step quantiser runs first
+  const bool fold = ws.splits == 1;
+  if (!fold) {
+    hipError_t e = launch_quantize(lay, bat, residual_pages, true, k_pool, v_pool, (uint8_t *)qpool, stream);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(decode_quant_gqa_kernel<W>, grid, dim3(W * 64), lds, stream, q, k_pool, v_pool, qpool,
                      bat.page_table, bat.seq_lens, sel, sel_count, ws.partial, ws.partial_ml, out, bat.pt_stride,
                      max_sel, bat.num_q_heads, lay.num_kv_heads, G, ws.splits, pps, scale_log2, pol.sink_tokens,
-                     pol.window_tokens, pol.static_head_mask, residual_pages);
+                     pol.window_tokens, pol.static_head_mask, residual_pages, fold ? (uint8_t *)qpool : nullptr,
+                     k_pool, v_pool);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ws.splits == 1) return e;
   return launch_merge_splits(ws, bat.batch, bat.num_q_heads, lay.head_dim_v, out, stream);
