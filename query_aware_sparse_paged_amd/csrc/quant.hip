@@ -54,12 +54,23 @@ __device__ __forceinline__ uint32_t group_pair(float mn, float mx, float &m, flo
 __device__ __forceinline__ uint32_t rotl(uint32_t x, int a) { return a == 0 ? x : (x << a) | (x >> (32 - a)); }
 
 // bf16 operands 4 + c of pair p (< 16) of a lane's code words (4 + c has
-// exponent 2 and the code in the two leading fraction bits).
-__device__ __forceinline__ uint32_t pair_operands(uint2 w, int p) {
+// exponent 2 and the code in the two leading fraction bits).  mask and base
+// are 0x00600060 and 0x40804080 held in registers (see CodeConsts), so the
+// and-or is one instruction.
+__device__ __forceinline__ uint32_t pair_operands(uint2 w, int p, uint32_t mask, uint32_t base) {
   const uint32_t x = p < 8 ? w.x : w.y;
   const uint32_t r = __builtin_amdgcn_alignbit(x, x, 2 * (p % 8));  // rotate right
-  return (r & 0x00600060u) | 0x40804080u;
+  return (r & mask) | base;
 }
+
+// The two constants of pair_operands, made opaque so that they stay in
+// registers (as literals they would split the and-or into two instructions).
+struct CodeConsts {
+  uint32_t mask, base;
+  __device__ __forceinline__ CodeConsts() : mask(0x00600060u), base(0x40804080u) {
+    asm volatile("" : "+v"(mask), "+v"(base));
+  }
+};
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -210,15 +221,17 @@ __device__ __forceinline__ void query_group_sums(const uint4 *bq, float *qs) {
 __device__ __forceinline__ void attend_qpage(attend::WaveState &st, float *bacc, const QPage &pg, const uint4 *kp,
                                              const uint4 *vp, const uint4 *bq, const float *qs, int j, int L,
                                              bool is_static, int sink_end, int win_begin, float scale_log2,
-                                             int lane) {
+                                             const CodeConsts &cc, int lane) {
   constexpr int PS = 16;
   const int kg = lane >> 4;
   // S^T: per group, (m - 4 s) sum(q) + s (A' q)
   float sv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint4 a = make_uint4(pair_operands(pg.kc, 4 * i), pair_operands(pg.kc, 4 * i + 1),
-                               pair_operands(pg.kc, 4 * i + 2), pair_operands(pg.kc, 4 * i + 3));
+    const uint4 a = make_uint4(pair_operands(pg.kc, 4 * i, cc.mask, cc.base),
+                               pair_operands(pg.kc, 4 * i + 1, cc.mask, cc.base),
+                               pair_operands(pg.kc, 4 * i + 2, cc.mask, cc.base),
+                               pair_operands(pg.kc, 4 * i + 3, cc.mask, cc.base));
     const floatx4 o = mfma16x16x32(a, bq[i], floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -271,7 +284,8 @@ __device__ __forceinline__ void attend_qpage(attend::WaveState &st, float *bacc,
   }
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const uint2 a = make_uint2(pair_operands(pg.vc, 2 * i), pair_operands(pg.vc, 2 * i + 1));
+    const uint2 a =
+        make_uint2(pair_operands(pg.vc, 2 * i, cc.mask, cc.base), pair_operands(pg.vc, 2 * i + 1, cc.mask, cc.base));
     st.acc[i] *= alpha;
     st.acc[i] = mfma16x16x16(a, bh[i / 2], st.acc[i]);
     st.acc[i] = mfma16x16x16(a, bl[i / 2], st.acc[i]);
@@ -333,6 +347,7 @@ decode_quant_gqa_kernel(
     quant::query_group_sums(bq, qs);
     // code words one page ahead; the pairs are loaded at the start of their
     // page (the value pairs are waited on only after the key work)
+    const quant::CodeConsts cc;
     quant::QPage cur, nxt;
     cur.load(base(0), lane);
     for (int it = 0; it < n_q; it++) {
@@ -341,7 +356,7 @@ decode_quant_gqa_kernel(
       quant::load_pairs(vp, base(it), quant::kValPairs, lane);
       nxt.load(base(it + 1), lane);  // past the end: the last page again (unused)
       quant::attend_qpage(st, bacc, cur, kp, vp, bq, qs, __shfl(my_j, it, kWave), L, is_static, sink_end,
-                          win_begin, scale_log2, lane);
+                          win_begin, scale_log2, cc, lane);
       cur = nxt;
     }
     // output channels 16 i + 4 (l / 16) + r belong to value group i / 2; the
