@@ -462,14 +462,14 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat, co
   uint16_t *q_grouped = (uint16_t *)((char *)workspace + workspace_bytes(*lay, wbat, max_sel));
   int32_t *sel_out = sel ? sel : ws.sel;
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
+  // many units: one kernel per (sequence, KV head) appends the drafts, stages
+  // the query rows in the grouped order, scores, selects and attends
+  const long units = (long)bat->batch * lay->num_kv_heads;
+  if (units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages && fused_lds_bytes(*lay, wbat, max_sel) <= 160 * 1024)
+    return status_of(launch_fused_step_gqa(*lay, wbat, wpol, q, nullptr, nullptr, k_pool, v_pool, summ, scale, out,
+                                           sel, sel_count, max_sel, s, nq, pol->window_tokens, false, k_new, v_new));
   // q [B][nq][Hkv][G][Dk] -> [B][Hkv][nq][G][Dk], and the drafts appended
   hipError_t e = launch_prepare_drafts(*lay, *bat, nq, q, q_grouped, k_new, v_new, k_pool, v_pool, summ, s);
-  // many units: score, select and attend in one kernel per (sequence, KV head)
-  const long units = (long)bat->batch * lay->num_kv_heads;
-  if (e == hipSuccess && units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages &&
-      fused_lds_bytes(*lay, wbat, max_sel) <= 160 * 1024)
-    return status_of(launch_fused_step_gqa(*lay, wbat, wpol, q_grouped, nullptr, nullptr, k_pool, v_pool, summ,
-                                           scale, out, sel, sel_count, max_sel, s, nq, pol->window_tokens));
   if (e == hipSuccess && scored)
     e = launch_score_pages(*lay, wbat, wpol, q_grouped, summ, ws.scores, s,
                            token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr));

@@ -97,6 +97,143 @@ __device__ __forceinline__ int2 unit_for_block(int i, const int32_t *seq_lens, i
 // drafts' union); the output goes to [B][n_draft][Hq / n_draft][DV].
 // SEL_ONLY: append, score and select only (the selection is written out for
 // another attention kernel; out is not touched).
+// The n_draft draft tokens of sequence b, KV head g, appended by one wave
+// (lane = key word; values two per lane) at positions L - n_draft ...: key
+// rows, value columns and the page summaries (the running min / max of a
+// page's drafts in registers; a draft in slot 0 starts a page).  Drafts go in
+// chunks of four, each chunk's loads issued together.  draft_k
+// [B][n_draft][Hkv][128], draft_v [B][n_draft][Hkv][128]; summ may be null.
+__device__ __forceinline__ void append_drafts_wave(const uint16_t *__restrict__ draft_k,
+                                                   const uint16_t *__restrict__ draft_v, uint16_t *__restrict__ k_pool,
+                                                   uint16_t *__restrict__ v_pool, uint16_t *__restrict__ summ,
+                                                   const int32_t *__restrict__ pt_row, int L, int n_draft, int b,
+                                                   int g, int Hkv, int lane) {
+  constexpr int PS = 16, D = 128, DV = 128;
+  const int i0 = max(0, n_draft - L);  // drafts at negative positions are not written
+  uint32_t lo = 0, hi = 0;
+  int cur_page = -1;
+  size_t cur_ph = 0;
+  for (int c0 = i0; c0 < n_draft; c0 += 4) {
+    uint32_t kv[4];
+    uint16_t va[4], vb[4];
+    int phys[4];
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      const int i = min(c0 + d, n_draft - 1);
+      const size_t row = ((size_t)b * n_draft + i) * Hkv + g;
+      kv[d] = ((const uint32_t *)draft_k)[row * (D / 2) + lane];
+      va[d] = draft_v[row * DV + lane];
+      vb[d] = draft_v[row * DV + lane + kWave];
+      phys[d] = pt_row[(L - n_draft + i) / PS];
+    }
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      const int i = c0 + d;
+      if (i >= n_draft) break;
+      const int pos = L - n_draft + i, t = pos % PS, page = pos / PS;
+      const size_t ph = (size_t)phys[d] * Hkv + g;
+      ((uint32_t *)k_pool)[(ph * PS + t) * (D / 2) + lane] = kv[d];
+      v_pool[(ph * DV + lane) * PS + t] = va[d];
+      v_pool[(ph * DV + lane + kWave) * PS + t] = vb[d];
+      if (summ == nullptr) continue;
+      if (page != cur_page) {
+        if (cur_page >= 0) {
+          uint32_t *sp = (uint32_t *)summ + cur_ph * D;
+          sp[lane] = lo;
+          sp[D / 2 + lane] = hi;
+        }
+        cur_page = page;
+        cur_ph = ph;
+        if (t == 0) {
+          lo = hi = kv[d];
+          continue;
+        }
+        const uint32_t *sp = (const uint32_t *)summ + ph * D;
+        lo = sp[lane];
+        hi = sp[D / 2 + lane];
+      }
+      const int v0 = bf16_order_key(kv[d] & 0xffffu), v1 = bf16_order_key(kv[d] >> 16);
+      lo = bf16_from_order_key(min(v0, bf16_order_key(lo & 0xffffu))) |
+           (bf16_from_order_key(min(v1, bf16_order_key(lo >> 16))) << 16);
+      hi = bf16_from_order_key(max(v0, bf16_order_key(hi & 0xffffu))) |
+           (bf16_from_order_key(max(v1, bf16_order_key(hi >> 16))) << 16);
+    }
+  }
+  if (summ != nullptr && cur_page >= 0) {
+    uint32_t *sp = (uint32_t *)summ + cur_ph * D;
+    sp[lane] = lo;
+    sp[D / 2 + lane] = hi;
+  }
+  __threadfence_block();
+}
+
+// Up to four draft tokens of one (sequence, KV head), appended by one wave in
+// three parts so that their latency hides under the scoring: the rows are
+// loaded in the prologue, the first page's summary once the page list is in
+// LDS, and the stores (with the summaries' min / max carried across the
+// drafts of a page) go after the scoring.  Needs L >= n_draft.
+struct DeferredDrafts {
+  static constexpr int PS = 16, D = 128, DV = 128;
+  uint32_t kv[4], lo = 0, hi = 0;
+  uint16_t va[4], vb[4];
+
+  __device__ __forceinline__ void load_rows(const uint16_t *draft_k, const uint16_t *draft_v, int b, int g, int Hkv,
+                                            int n_draft, int lane) {
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      const size_t row = ((size_t)b * n_draft + min(d, n_draft - 1)) * Hkv + g;
+      kv[d] = ((const uint32_t *)draft_k)[row * (D / 2) + lane];
+      va[d] = draft_v[row * DV + lane];
+      vb[d] = draft_v[row * DV + lane + kWave];
+    }
+  }
+  __device__ __forceinline__ void load_summary(const uint16_t *summ, const int32_t *page_phys, int L, int n_draft,
+                                               int g, int Hkv, int lane) {
+    const int p0 = L - n_draft;
+    if (summ == nullptr || p0 % PS == 0) return;
+    const uint32_t *sp = (const uint32_t *)summ + ((size_t)page_phys[p0 / PS] * Hkv + g) * D;
+    lo = sp[lane];
+    hi = sp[D / 2 + lane];
+  }
+  __device__ __forceinline__ void store(uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, const int32_t *page_phys,
+                                        int L, int n_draft, int g, int Hkv, int lane) {
+    int cur_page = (L - n_draft) / PS;
+    bool started = (L - n_draft) % PS != 0;  // lo / hi hold the first page's summary
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      if (d >= n_draft) break;
+      const int pos = L - n_draft + d, t = pos % PS, page = pos / PS;
+      const size_t ph = (size_t)page_phys[page] * Hkv + g;
+      ((uint32_t *)k_pool)[(ph * PS + t) * (D / 2) + lane] = kv[d];
+      v_pool[(ph * DV + lane) * PS + t] = va[d];
+      v_pool[(ph * DV + lane + kWave) * PS + t] = vb[d];
+      if (summ == nullptr) continue;
+      if (t == 0) {
+        if (started) {  // the first page is complete
+          uint32_t *sp = (uint32_t *)summ + ((size_t)page_phys[cur_page] * Hkv + g) * D;
+          sp[lane] = lo;
+          sp[D / 2 + lane] = hi;
+        }
+        cur_page = page;
+        started = true;
+        lo = hi = kv[d];
+        continue;
+      }
+      const int v0 = bf16_order_key(kv[d] & 0xffffu), v1 = bf16_order_key(kv[d] >> 16);
+      lo = bf16_from_order_key(min(v0, bf16_order_key(lo & 0xffffu))) |
+           (bf16_from_order_key(min(v1, bf16_order_key(lo >> 16))) << 16);
+      hi = bf16_from_order_key(max(v0, bf16_order_key(hi & 0xffffu))) |
+           (bf16_from_order_key(max(v1, bf16_order_key(hi >> 16))) << 16);
+    }
+    if (summ != nullptr) {
+      uint32_t *sp = (uint32_t *)summ + ((size_t)page_phys[cur_page] * Hkv + g) * D;
+      sp[lane] = lo;
+      sp[D / 2 + lane] = hi;
+    }
+    __threadfence_block();
+  }
+};
+
 template <int D, int DV, int PS, int W, bool CAUSAL = false, bool SEL_ONLY = false>
 __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
@@ -105,7 +242,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
     int window_tokens, uint64_t static_mask, float scale_log2, uint32_t bucket_mul, int lpt, int n_draft,
-    int window_q) {
+    int window_q, const uint16_t *__restrict__ draft_k, const uint16_t *__restrict__ draft_v) {
   static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
@@ -155,9 +292,38 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   // scoring, the exact re-scoring and the attention read them there); every
   // load of a round is issued before its results are stored
   const bool q_in_lds = (size_t)G * D * 2 <= sel::kQStageBytes;
+  // (CAUSAL) deferred draft append: block-uniform
+  const bool defer_drafts = CAUSAL && draft_k != nullptr && n_draft <= 4 && L >= n_draft &&
+                            (L - n_draft) / PS >= cand_hi;
+  DeferredDrafts drafts;
   {
     const int nq = q_in_lds ? G * D / 2 : 0;  // q words
     const uint32_t *qsrc = (const uint32_t *)(q + head0 * D);
+    // CAUSAL: q is the caller's [B][n_draft][Hq / n_draft][D]; group row r is
+    // head r % (G / n_draft) of draft r / (G / n_draft)
+    auto q_word = [&](int wq) {
+      if constexpr (CAUSAL) {
+        const int per_query = G / n_draft, r = wq / (D / 2);
+        const size_t row = ((size_t)b * n_draft + r / per_query) * (Hq / n_draft) + (size_t)g * per_query +
+                           r % per_query;
+        return ((const uint32_t *)q)[row * (D / 2) + wq % (D / 2)];
+      } else {
+        return qsrc[wq];
+      }
+    };
+    // CAUSAL: the drafts' append by the last wave.  Up to four drafts whose
+    // pages are no candidates: deferred (rows loaded now, stores after the
+    // scoring, before the barrier that precedes any read of those pages).
+    // Otherwise: written here, before the barrier below, so the scoring sees
+    // their summaries.
+    if constexpr (CAUSAL) {
+      if (draft_k != nullptr && wave == W - 1) {
+        if (defer_drafts)
+          drafts.load_rows(draft_k, draft_v, b, g, Hkv, n_draft, lane);
+        else
+          append_drafts_wave(draft_k, draft_v, k_pool, v_pool, summ, pt_row, L, n_draft, b, g, Hkv, lane);
+      }
+    }
     for (int r0 = 0; r0 < P || r0 < 4 * nq; r0 += 4 * T) {  // 4 page-table entries and 1 q word per thread a round
       int v[4];
 #pragma unroll
@@ -166,7 +332,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
         v[r] = j < P ? pt_row[j] : 0;
       }
       const int wq = r0 / 4 + tid;
-      const uint32_t qv = wq < nq ? qsrc[wq] : 0u;
+      const uint32_t qv = wq < nq ? q_word(wq) : 0u;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int j = r0 + r * T + tid;
@@ -250,6 +416,9 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   score::QOperands<D> op;
   uint4 bs[2][KSTEPS];
   int c_cur = -1, phys_cur = -1;
+  if constexpr (CAUSAL) {
+    if (defer_drafts && wave == W - 1) drafts.load_summary(summ, page_phys, L, n_draft, g, Hkv, lane);
+  }
   if (ranked) {
     c_cur = cand_of(0);
     phys_cur = page_of(c_cur);
@@ -293,6 +462,9 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     }
   }
   if (!early_append && my_append) append_stores();
+  if constexpr (CAUSAL) {
+    if (defer_drafts && wave == W - 1) drafts.store(k_pool, v_pool, summ, page_phys, L, n_draft, g, Hkv, lane);
+  }
   // the append is complete and the key range / error bound are final
   __syncthreads();
 
@@ -304,7 +476,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const int sink_end = is_static ? min(sink_tokens, L) : 0;
   const int win_begin = is_static ? max(0, L - window_tokens) : 0;
   uint4 bq[D / 32];
-  attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
+  attend::load_q_columns<D>(bq, CAUSAL ? (const uint16_t *)sh.qstage : q + head0 * D, G, lane);
   int Lq = L, winq = 0;
   if constexpr (CAUSAL) {
     const int per_query = G / n_draft;
@@ -487,7 +659,7 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
                                  int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream, int n_draft,
-                                 int window_q, bool sel_only) {
+                                 int window_q, bool sel_only, const uint16_t *draft_k, const uint16_t *draft_v) {
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = FusedLds(mp, max_sel, G).total;
@@ -503,7 +675,8 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   hipLaunchKernelGGL(kernel, grid, dim3(kFusedWaves * 64), lds, stream, q, k_new, v_new, k_pool, v_pool, summ,
                      bat.page_table, bat.seq_lens, out, sel, sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads,
                      lay.num_kv_heads, G, pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens,
-                     pol.window_tokens, pol.static_head_mask, scale_log2, bucket_mul, lpt, n_draft, window_q);
+                     pol.window_tokens, pol.static_head_mask, scale_log2, bucket_mul, lpt, n_draft, window_q, draft_k,
+                     draft_v);
   return hipGetLastError();
 }
 

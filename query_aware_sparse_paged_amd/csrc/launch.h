@@ -73,7 +73,8 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
                                  int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream, int n_draft = 1,
-                                 int window_q = 0, bool sel_only = false);
+                                 int window_q = 0, bool sel_only = false, const uint16_t *draft_k = nullptr,
+                                 const uint16_t *draft_v = nullptr);
 hipError_t launch_fused_reuse_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                   const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                   uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
