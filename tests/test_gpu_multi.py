@@ -106,6 +106,14 @@ def test_multi_step_zero_window_and_two_heads_per_group():
     _run("ragged_b64_mixed", 4, 8, 2500, 700, window_tokens=0, num_q_heads=16)
 
 
+@pytest.mark.parametrize("nq,kw", [
+    (8, dict(num_q_heads=16)),        # 8 drafts x 2 heads: the drafts are written in the kernel's prologue
+    (3, dict(n_local_pages=0)),       # no local pages: the drafts' pages are candidates, scored with them
+])
+def test_multi_step_many_units_prologue_append(nq, kw):
+    _run("llama8b_b32_32k", 32, nq, 1100, 400, **kw)
+
+
 def test_multi_step_drafts_differ():
     gout, ref = _run("llama8b_b32_32k", 2, 3, 700, 500, seed=37)
     assert np.abs(gout[:, 0] - gout[:, 2]).max() > 1e-3
