@@ -384,12 +384,20 @@ def run_host_pool(args, torch, api, workloads, dev):
     msel = api.max_sel(lay, pol, bat.max_pages)
     summ = torch.zeros((w.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16, device=dev)
     api.build_summaries(lay, bat, w.k_pool, summ)
+    R = args.quant
+    qh = None
+    if R > 0:  # 2-bit pages too: the quantised pool built on the device, then moved to host memory
+        qpool = api.new_quant_pool(lay, dev)
+        api.quantize_pages(lay, bat, R, w.k_pool, w.v_pool, qpool)
+        qh = api.host_pool_like(qpool)
+        del qpool
     kh = api.host_pool_like(w.k_pool)
     vh = None if w.v_pool is None else api.host_pool_like(w.v_pool)
     w.k_pool = w.v_pool = None
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    log("host-tier pools ready: %.2f GB pinned" % ((kh.buf.nbytes + (vh.buf.nbytes if vh else 0)) / 1e9))
+    log("host-tier pools ready: %.2f GB pinned" % ((kh.buf.nbytes + (vh.buf.nbytes if vh else 0) +
+                                                    (qh.buf.nbytes if qh else 0)) / 1e9))
     ws = api.new_workspace(lay, bat, pol, msel, dev)
     B = spec.batch
     sel = torch.empty((B, lay.num_kv_heads, msel), dtype=torch.int32, device=dev)
@@ -397,8 +405,12 @@ def run_host_pool(args, torch, api, workloads, dev):
     out = torch.empty((B, spec.num_q_heads, lay.head_dim_v), dtype=torch.float32, device=dev)
 
     def step():
-        api.decode_step(lay, bat, pol, w.q, kh, vh, summ, w.scale, ws, msel, k_new=w.k_new, v_new=w.v_new, out=out,
-                        sel=sel, sel_count=cnt)
+        if qh is None:
+            api.decode_step(lay, bat, pol, w.q, kh, vh, summ, w.scale, ws, msel, k_new=w.k_new, v_new=w.v_new,
+                            out=out, sel=sel, sel_count=cnt)
+        else:
+            api.decode_step_quant(lay, bat, pol, R, w.q, kh, vh, summ, qh, w.scale, ws, msel, k_new=w.k_new,
+                                  v_new=w.v_new, out=out, sel=sel, sel_count=cnt)
 
     for _ in range(args.warmup):
         step()
@@ -411,11 +423,21 @@ def run_host_pool(args, torch, api, workloads, dev):
     b_score, b_decode = step_bytes(w, cnt.cpu().tolist())
     qo = spec.batch * spec.num_q_heads * (spec.head_dim_k * 2 + spec.head_dim_v * 4)
     kv_link = b_decode - qo  # the selected K/V tiles: read over the host link
+    if qh is not None:  # quantised pages: 1536 B per page-head below the residual region
+        sl_, cn_ = sel.cpu().tolist(), cnt.cpu().tolist()
+        lens = w.seq_lens.cpu().tolist()
+        bf16_ph = spec.page_size * (spec.head_dim_k + spec.head_dim_v) * 2
+        kv_link = 0
+        for b_ in range(B):
+            P = (lens[b_] + spec.page_size - 1) // spec.page_size
+            for g_ in range(lay.num_kv_heads):
+                kv_link += sum(1536 if j < P - R else bf16_ph for j in sl_[b_][g_][:cn_[b_][g_]])
     kv_link += spec.batch * spec.num_kv_heads * (spec.head_dim_k + (0 if spec.v_from_k else spec.head_dim_v)) * 2
     link = kv_link / (ms_per_step * 1e-3) / 1e9
     log("host-tier step: %.1f us, %.1f GB/s over the host link" % (ms_per_step * 1e3, link))
     line = {
-        "metric": "decode tokens/s with the K/V pools in host memory (host-tier pool), %s" % spec.name,
+        "metric": "decode tokens/s with the K/V pools in host memory (host-tier pool)%s, %s" % (
+            ", 2-bit pages outside the last %d" % R if R > 0 else "", spec.name),
         "value": round(B / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -427,7 +449,8 @@ def run_host_pool(args, torch, api, workloads, dev):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name, "batch": B, "seq_len": spec.seq_len, "pools": "host-tier"},
+        "config": {"workload": spec.name, "batch": B, "seq_len": spec.seq_len, "pools": "host-tier",
+                   "residual_pages": R if R > 0 else None},
         "roofline": {"kernel": "decode step, selected pages over the host link", "bound": "host-link",
                      "achieved": round(link, 2), "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(link / HOST_LINK_PEAK_GBPS, 4), "traffic": None,

@@ -71,3 +71,35 @@ def test_host_tier_pools_match_device_pools(name, batch, seq_len):
     ref = oracle.attend(olay, w.page_table.numpy(), w.seq_lens.numpy(), workloads.bits(w.q), kbits, vbits,
                         sel_h.numpy(), cnt_h.numpy(), opol, w.scale)
     assert np.abs(out_h.numpy().astype(np.float64) - ref).max() <= OUT_TOL
+
+
+def test_host_tier_quantised_pages_match_device_pools():
+    """2-bit pages in the host tier as well: the quantised pool and the bf16
+    pools in host memory give the device-pool results bit for bit."""
+    print("host-tier quantised case", flush=True)
+    R = 4
+    w = workloads.make("llama8b_b32_32k", device="cpu", seed=6, batch=32, seq_len=1500, seq_len_min=700)
+    lay, pol = api.layout_of(w), api.policy_of(w)
+    bat = api.Batch(w.page_table.to(DEV), w.seq_lens.to(DEV), w.spec.num_q_heads)
+    msel = api.max_sel(lay, pol, bat.max_pages)
+    kd, vd = w.k_pool.to(DEV), w.v_pool.to(DEV)
+    summ_d = torch.zeros((lay.num_pool_pages, lay.num_kv_heads, 2, lay.head_dim_k), dtype=torch.bfloat16,
+                         device=DEV)
+    api.build_summaries(lay, bat, kd, summ_d)
+    summ_h = summ_d.clone()
+    qd = api.new_quant_pool(lay, DEV)
+    api.quantize_pages(lay, bat, R, kd, vd, qd)
+    kh, vh, qh = api.host_pool_like(w.k_pool), api.host_pool_like(w.v_pool), api.host_pool_like(qd)
+    runs = []
+    for kp, vp, qp, summ in ((kd, vd, qd, summ_d), (kh, vh, qh, summ_h)):
+        ws = api.new_workspace(lay, bat, pol, msel, DEV)
+        sel = torch.empty((32, lay.num_kv_heads, msel), dtype=torch.int32, device=DEV)
+        cnt = torch.empty((32, lay.num_kv_heads), dtype=torch.int32, device=DEV)
+        out = api.decode_step_quant(lay, bat, pol, R, w.q.to(DEV), kp, vp, summ, qp, w.scale, ws, msel,
+                                    k_new=w.k_new.to(DEV), v_new=w.v_new.to(DEV), sel=sel, sel_count=cnt)
+        torch.cuda.synchronize()
+        runs.append((out.cpu(), sel.cpu(), cnt.cpu()))
+    assert torch.equal(runs[0][1], runs[1][1]) and torch.equal(runs[0][2], runs[1][2])
+    assert torch.equal(runs[0][0].view(torch.int32), runs[1][0].view(torch.int32))
+    assert torch.equal(qh.host, qd.cpu())
+    assert torch.equal(kh.host.view(torch.int16), kd.cpu().view(torch.int16))
