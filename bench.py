@@ -148,7 +148,7 @@ def main():
                     help="run one plain device copy of this size first (a known-size kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the per-(sequence, KV head) work would shard by batch or KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
