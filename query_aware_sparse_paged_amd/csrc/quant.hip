@@ -282,11 +282,16 @@ __device__ __forceinline__ void attend_qpage(attend::WaveState &st, float *bacc,
     split2(w4[2], w4[3], bh[g].y, bl[g].y);
     bacc[g] = fmaf(bacc[g], alpha, z);
   }
+  // once the running maxima stop moving, alpha is exactly 1 in every lane:
+  // then the accumulators need no rescaling (a wave-uniform test)
+  if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) st.acc[i] *= alpha;
+  }
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const uint2 a =
         make_uint2(pair_operands(pg.vc, 2 * i, cc.mask, cc.base), pair_operands(pg.vc, 2 * i + 1, cc.mask, cc.base));
-    st.acc[i] *= alpha;
     st.acc[i] = mfma16x16x16(a, bh[i / 2], st.acc[i]);
     st.acc[i] = mfma16x16x16(a, bl[i / 2], st.acc[i]);
   }
