@@ -33,9 +33,17 @@
  *   - Return value: QASP_OK (0) or a negative qasp_status.  Argument checks run
  *     on the host before anything is enqueued, so an error return means no
  *     work was queued.  QASP_ERR_LAUNCH reports hipGetLastError after a launch.
- *   - Device-side data (page table entries, sequence lengths) is trusted:
- *     page ids outside [0, num_pool_pages) or lengths above
- *     max_pages * page_size are undefined behaviour.  Inputs must be finite.
+ *   - Device-side data (page-table entries, sequence lengths, a selection
+ *     passed in) is read by the kernels as given.  Outside validate mode, page
+ *     ids outside [0, num_pool_pages), lengths above max_pages * page_size and
+ *     selected ids outside [0, ceil(seq_lens[b] / page_size)) are undefined
+ *     behaviour.  Validate mode: with the environment variable QASP_VALIDATE
+ *     set (and not "0"), every call that reads the pools through the page
+ *     table first runs qasp_check_batch on its stream (a kernel that reads
+ *     only seq_lens, the page-table rows and the selection, then a stream
+ *     synchronisation) and returns QASP_ERR_BAD_PAGE_TABLE, with nothing
+ *     else enqueued, when it finds an entry out of range.  Inputs must be
+ *     finite.
  *   - Calls that share a workspace must not overlap in time.
  */
 #ifndef QASP_H
@@ -56,7 +64,10 @@ typedef enum {
     QASP_ERR_WORKSPACE = -4,       /* workspace smaller than qasp_workspace_bytes */
     QASP_ERR_MAX_SEL = -5,         /* max_sel below qasp_max_sel             */
     QASP_ERR_LAUNCH = -6,          /* a HIP launch failed                     */
-    QASP_ERR_ALLOC = -7            /* a host-tier allocation failed           */
+    QASP_ERR_ALLOC = -7,           /* a host-tier allocation failed           */
+    QASP_ERR_BAD_PAGE_TABLE = -8   /* validate mode / qasp_check_batch: a length,
+                                      page-table entry or selected id is out
+                                      of range                                */
 } qasp_status;
 
 /* Pool layout (row-major, bf16):
@@ -151,7 +162,11 @@ size_t qasp_workspace_bytes(const qasp_layout *lay, const qasp_batch *bat,
 /* Summaries of every page of every sequence (logical pages
  * [0, ceil(seq_lens[b] / page_size))), computed from k_pool and written into
  * summ at the physical pages.  Use after a prefill or to rebuild.  Only the
- * valid tokens of a partial last page enter its summary. */
+ * valid tokens of a partial last page enter its summary.
+ * Defined by: the per-page key metadata a decode-time query-aware page
+ * selector reads (SparseEngine article, blog.ontle.kr/blog/332, decode-hook
+ * paragraph naming Quest); the summary as elementwise min / max of the keys is
+ * the reading this library takes (the pages print no formula). */
 int32_t qasp_build_summaries(const qasp_layout *lay, const qasp_batch *bat,
                              const uint16_t *k_pool, uint16_t *summ, void *stream);
 
@@ -162,14 +177,23 @@ int32_t qasp_build_summaries(const qasp_layout *lay, const qasp_batch *bat,
  *   [head_dim_v] (ignored and may be NULL when v_from_k).
  * The caller has already mapped page_table[b][seq_lens[b] / page_size].
  * summ may be NULL only if every KV head is static (then no summary is kept).
- * A page being appended to must not be shared by two sequences. */
+ * A page being appended to must not be shared by two sequences.
+ * Defined by: as qasp_build_summaries, kept current as tokens arrive
+ * (SparseEngine article, decode-hook paragraph: selection happens at every
+ * decode step, over a cache that grows by one token a step). */
 int32_t qasp_append_kv(const qasp_layout *lay, const qasp_batch *bat_before,
                        const qasp_policy *pol, const uint16_t *k_new,
                        const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool,
                        uint16_t *summ, void *stream);
 
 /* Scores every candidate page of every query-aware head:
- * scores [batch][num_kv_heads][max_pages] qasp_score. */
+ * scores [batch][num_kv_heads][max_pages] qasp_score.
+ * Defined by: Quest's query-aware page selection at decode (SparseEngine
+ * article, decode-hook paragraph), page-granular (the same article's list of
+ * compared systems: Vortex routes by page), the query deciding what is read
+ * (its "dynamic sparse attention" paragraph: keep everything, read what the
+ * query needs).  Score = the group maximum of sum_d max(q_d lo_d, q_d hi_d),
+ * an upper bound on q.k over the page. */
 int32_t qasp_score_pages(const qasp_layout *lay, const qasp_batch *bat,
                          const qasp_policy *pol, const uint16_t *q,
                          const uint16_t *summ, qasp_score *scores, void *stream);
@@ -180,7 +204,12 @@ int32_t qasp_score_pages(const qasp_layout *lay, const qasp_batch *bat,
  * the exact sum) from q and summ, so the selection equals the one the exact
  * scores give.  Output: sel [batch][num_kv_heads][max_sel] logical page ids in
  * ascending order, sel_count [batch][num_kv_heads]; entries past the count
- * are -1.  q and summ may be NULL only if every KV head is static. */
+ * are -1.  q and summ may be NULL only if every KV head is static.
+ * Defined by: asking for "the top boxes" and finding them through the map
+ * (Vortex explainer, gist.science paper 2606.06453, section 1); a logical
+ * choice that evicts nothing (SparseEngine article, the paragraph separating
+ * "not looking" from "discarding"); sink + local window as the static
+ * pattern (SCBench notes, notes.yuuk.io, "Tri-shape" paragraph: A-shape). */
 int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat,
                          const qasp_policy *pol, const uint16_t *q,
                          const uint16_t *summ, const qasp_score *scores,
@@ -191,7 +220,12 @@ int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat,
  * head's selected pages (static heads: only the sink and window tokens),
  * split across pages and merged: out [batch][num_q_heads][head_dim_v] fp32.
  * scale multiplies q.k before the softmax.  A head with no token gets 0.
- * workspace: >= qasp_workspace_bytes. */
+ * workspace: >= qasp_workspace_bytes.
+ * Defined by: attention computed exactly on the selected positions (SubQ/SSA
+ * article, news.neo-ai.one/ja/article/2719, section "How SSA works"), the
+ * pages reached through the page table (Vortex explainer, section 1); a
+ * static head's tokens need nothing of the scored heads (llama.cpp
+ * draft-head article, aikeizai.jp, "facts from primary sources"). */
 int32_t qasp_sparse_paged_decode(const qasp_layout *lay, const qasp_batch *bat,
                                  const qasp_policy *pol, const uint16_t *q,
                                  const uint16_t *k_pool, const uint16_t *v_pool,
@@ -204,7 +238,11 @@ int32_t qasp_sparse_paged_decode(const qasp_layout *lay, const qasp_batch *bat,
  * NULL; bat->seq_lens is then the length AFTER the append, the token goes to
  * position seq_lens[b] - 1), scoring, selection, sparse attention and merge.
  * Scores and selections live in the workspace; sel / sel_count, when not
- * NULL, receive a copy of the selection ([batch][num_kv_heads][max_sel]). */
+ * NULL, receive a copy of the selection ([batch][num_kv_heads][max_sel]).
+ * Defined by: the decode hook as a whole (SparseEngine article, decode-hook
+ * paragraph: the engine keeps the storage, the method decides per step which
+ * pages are read; SCBench notes, complexity table: the loading class reads
+ * only part of the KV per decode step). */
 int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat,
                          const qasp_policy *pol, const uint16_t *q,
                          const uint16_t *k_new, const uint16_t *v_new,
@@ -314,6 +352,28 @@ int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat,
                                float scale, float *out, int32_t *sel,
                                int32_t *sel_count, int32_t max_sel, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* Validation of the device-side batch description, on demand (validate mode
+ * runs it inside every pool-reading call).  A kernel on `stream` reads only
+ * seq_lens, the page-table rows and, when sel is given, sel / sel_count
+ * ([batch][num_kv_heads][max_sel]); then the stream is synchronised.
+ * Checks, per sequence b with L = seq_lens[b]:
+ *   0 <= L <= max_pages * page_size and L + extra_tokens <= pt_stride *
+ *   page_size (extra_tokens = 1 for an append at position L);
+ *   0 <= page_table[b][j] < num_pool_pages for every j <
+ *   ceil((L + extra_tokens) / page_size);
+ *   with sel: 0 <= sel_count[b][g] <= max_sel and every listed id in
+ *   [0, ceil(L / page_size)).
+ * Returns QASP_OK, QASP_ERR_BAD_PAGE_TABLE, or a host-side argument error
+ * (extra_tokens outside [0, 16]: QASP_ERR_BAD_SHAPE; sel without sel_count:
+ * QASP_ERR_NULL_ARG).  Reads stay inside the stated array shapes, so a bad
+ * table cannot make the check itself read out of bounds.
+ * Defined by: the page table as the map from logical pages to scattered pool
+ * pages (Vortex explainer, section 1); a guard per buffer at the interface
+ * (llama.cpp draft-head article, "facts from primary sources"). */
+int32_t qasp_check_batch(const qasp_layout *lay, const qasp_batch *bat, int32_t extra_tokens,
+                         const int32_t *sel, const int32_t *sel_count, int32_t max_sel,
+                         void *stream);
 
 /* Host-tier KV pool (CPU-GPU cooperative loading: the full KV cache stays in
  * host RAM and each decode step loads only the pages it needs; SCBench notes,

@@ -1,7 +1,8 @@
 """Thin ctypes binding of ``include/qasp.h`` (argument marshalling only).
 
 Every function takes torch tensors that already live on the GPU, checks
-their dtype/shape/contiguity, and passes raw device pointers plus the current
+their dtype, shape (against the layout, the batch and the selection
+capacity) and contiguity, and passes raw device pointers plus the current
 HIP stream to ``libqasp.so``.  All computation happens in the HIP kernels;
 there is no CPU path, and a missing library raises ``RuntimeError``.
 bf16 tensors are passed as their 16-bit patterns.
@@ -21,6 +22,7 @@ LIB_PATH = os.environ.get("QASP_LIB") or os.path.join(_HERE, "libqasp.so")
 
 OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MAX_SEL, ERR_LAUNCH, ERR_ALLOC = \
     0, -1, -2, -3, -4, -5, -6, -7
+ERR_BAD_PAGE_TABLE = -8
 
 
 class QaspError(RuntimeError):
@@ -71,6 +73,8 @@ EXPORTS = {
     "qasp_decode_step_quant": (ctypes.c_int32, [ctypes.c_void_p] * 3 + [ctypes.c_int32] + [ctypes.c_void_p] * 7 +
                                [ctypes.c_float] + [ctypes.c_void_p] * 3 +
                                [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qasp_check_batch": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 2 +
+                         [ctypes.c_int32, ctypes.c_void_p]),
     "qasp_host_alloc": (ctypes.c_int32, [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "qasp_host_free": (ctypes.c_int32, [ctypes.c_void_p]),
     "qasp_max_sel_multi": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]),
@@ -149,22 +153,49 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t: Optional[torch.Tensor], dtype, name, ndim=None):
-    if t is None:
-        return None
-    if isinstance(t, MappedTensor):  # a host-tier pool
-        if t.dtype != dtype or (ndim is not None and t.dim() != ndim):
-            raise ValueError("%s must be a %d-dim %s host-tier view" % (name, ndim or 0, dtype))
-        return t
-    if not t.is_cuda:
-        raise ValueError("%s must be a GPU tensor" % name)
-    if t.dtype != dtype:
-        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError("%s must have %d dims" % (name, ndim))
-    return t
+class AtLeast(int):
+    """A dimension that may be larger than the given size (a pool's pages)."""
+
+
+def _check_args(*specs, devices=True):
+    """Each spec is (tensor or None, dtype, name, shape); a shape entry is an
+    int (exact), AtLeast(n) or None (any).  First every dtype, shape and
+    contiguity is checked, then (devices) that every tensor lives on the GPU
+    (or is a host-tier view), so a wrong shape is reported before the device."""
+    for t, dtype, name, shape in specs:
+        if t is None:
+            continue
+        if t.dtype != dtype:
+            raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+        have = tuple(t.shape)
+        if len(have) != len(shape):
+            raise ValueError("%s must have %d dims, got shape %s" % (name, len(shape), have))
+        for d, (h, want) in enumerate(zip(have, shape)):
+            if want is None:
+                continue
+            if isinstance(want, AtLeast):
+                if h < int(want):
+                    raise ValueError("%s: dim %d is %d, needs at least %d" % (name, d, h, int(want)))
+            elif h != want:
+                raise ValueError("%s must have shape %s, got %s" % (
+                    name, tuple("*" if w is None else (">=%d" % int(w) if isinstance(w, AtLeast) else w)
+                                for w in shape), have))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if not devices:
+        return
+    for t, _, name, _ in specs:
+        if t is None or isinstance(t, MappedTensor):  # a host-tier pool
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _pool_specs(layout: "Layout", k_pool, v_pool, summ):
+    P, H, ps = AtLeast(layout.num_pool_pages), layout.num_kv_heads, layout.page_size
+    return [(k_pool, torch.bfloat16, "k_pool", (P, H, ps, layout.head_dim_k)),
+            (v_pool, torch.bfloat16, "v_pool", (P, H, layout.head_dim_v, ps)),
+            (summ, torch.bfloat16, "summ", (P, H, 2, layout.head_dim_k))]
 
 
 def _check(status, what):
@@ -177,12 +208,23 @@ class Batch:
 
     def __init__(self, page_table: torch.Tensor, seq_lens: torch.Tensor, num_q_heads: int,
                  max_pages: Optional[int] = None):
-        self.page_table = _dev(page_table, torch.int32, "page_table", 2)
-        self.seq_lens = _dev(seq_lens, torch.int32, "seq_lens", 1)
-        if page_table.shape[0] != seq_lens.shape[0]:
-            raise ValueError("page_table and seq_lens disagree on the batch size")
+        if page_table is None or seq_lens is None:
+            raise ValueError("page_table and seq_lens are required")
+        _check_args((page_table, torch.int32, "page_table", (None, None)),
+                    (seq_lens, torch.int32, "seq_lens", (page_table.shape[0],)), devices=False)
+        self.page_table, self.seq_lens = page_table, seq_lens
         self.num_q_heads = int(num_q_heads)
         self.max_pages = int(page_table.shape[1] if max_pages is None else max_pages)
+        if not 0 <= self.max_pages <= page_table.shape[1]:
+            raise ValueError("max_pages must lie in [0, page_table.shape[1]]")
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    def specs(self):
+        return [(self.page_table, torch.int32, "page_table", (self.batch, None)),
+                (self.seq_lens, torch.int32, "seq_lens", (self.batch,))]
 
     def c(self) -> CBatch:
         return CBatch(int(self.seq_lens.shape[0]), self.num_q_heads, int(self.page_table.shape[1]),
@@ -213,36 +255,55 @@ def _u16(t):
 
 
 def build_summaries(layout: Layout, batch: Batch, k_pool: torch.Tensor, summ: torch.Tensor):
-    _dev(k_pool, torch.bfloat16, "k_pool", 4)
-    _dev(summ, torch.bfloat16, "summ", 4)
+    _check_args(*batch.specs(), *_pool_specs(layout, k_pool, None, summ))
     _check(lib().qasp_build_summaries(ctypes.byref(layout.c()), ctypes.byref(batch.c()), _ptr(k_pool),
                                       _ptr(summ), _stream()), "qasp_build_summaries")
 
 
+def _token_specs(layout: Layout, B: int, k_new, v_new, n_query=None):
+    lead = (B,) if n_query is None else (B, n_query)
+    return [(k_new, torch.bfloat16, "k_new", lead + (layout.num_kv_heads, layout.head_dim_k)),
+            (v_new, torch.bfloat16, "v_new", lead + (layout.num_kv_heads, layout.head_dim_v))]
+
+
+def _query_specs(layout: Layout, batch: Batch, q, out, n_query=None):
+    lead = (batch.batch,) if n_query is None else (batch.batch, n_query)
+    return [(q, torch.bfloat16, "q", lead + (batch.num_q_heads, layout.head_dim_k)),
+            (out, torch.float32, "out", lead + (batch.num_q_heads, layout.head_dim_v))]
+
+
+def _sel_specs(layout: Layout, batch: Batch, sel, sel_count, max_sel_n=None):
+    return [(sel, torch.int32, "sel", (batch.batch, layout.num_kv_heads, max_sel_n)),
+            (sel_count, torch.int32, "sel_count", (batch.batch, layout.num_kv_heads))]
+
+
+def _ws_spec(workspace):
+    if workspace is None:
+        raise ValueError("workspace is required")
+    return (workspace, torch.uint8, "workspace", (None,))
+
+
 def append_kv(layout: Layout, batch_before: Batch, policy: Policy, k_new, v_new, k_pool, v_pool, summ):
-    _dev(k_new, torch.bfloat16, "k_new", 3)
-    _dev(v_new, torch.bfloat16, "v_new", 3)
-    _dev(k_pool, torch.bfloat16, "k_pool", 4)
-    _dev(v_pool, torch.bfloat16, "v_pool", 4)
-    _dev(summ, torch.bfloat16, "summ", 4)
+    _check_args(*batch_before.specs(), *_token_specs(layout, batch_before.batch, k_new, v_new),
+                *_pool_specs(layout, k_pool, v_pool, summ))
     _check(lib().qasp_append_kv(ctypes.byref(layout.c()), ctypes.byref(batch_before.c()),
                                 ctypes.byref(policy.c()), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                 _ptr(v_pool), _ptr(summ), _stream()), "qasp_append_kv")
+
+
+def _score_spec(layout: Layout, batch: Batch, scores):
+    return (scores, torch.float32, "scores", (batch.batch, layout.num_kv_heads, batch.max_pages, 4))
 
 
 def score_pages(layout: Layout, batch: Batch, policy: Policy, q, summ, scores=None) -> torch.Tensor:
     """Returns float32 [B][Hkv][max_pages][4], one qasp_score per page: (fp32
     score, error bound, certified leading head, 0); the last two are int32 bit
     patterns (view the tensor as int32 to read them)."""
-    _dev(q, torch.bfloat16, "q", 3)
-    _dev(summ, torch.bfloat16, "summ", 4)
-    B = batch.seq_lens.shape[0]
     if scores is None:
-        scores = torch.empty((B, layout.num_kv_heads, batch.max_pages, 4), dtype=torch.float32,
+        scores = torch.empty((batch.batch, layout.num_kv_heads, batch.max_pages, 4), dtype=torch.float32,
                              device=batch.seq_lens.device)
-    _dev(scores, torch.float32, "scores", 4)
-    if scores.shape[-1] != 4:
-        raise ValueError("scores: last dimension must be 4 (one qasp_score per page)")
+    _check_args(*batch.specs(), *_query_specs(layout, batch, q, None), *_pool_specs(layout, None, None, summ),
+                _score_spec(layout, batch, scores))
     _check(lib().qasp_score_pages(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
                                   _ptr(q), _ptr(summ), _ptr(scores), _stream()), "qasp_score_pages")
     return scores
@@ -251,41 +312,40 @@ def score_pages(layout: Layout, batch: Batch, policy: Policy, q, summ, scores=No
 def select_topk(layout: Layout, batch: Batch, policy: Policy, q, summ, scores, max_sel_n=None, sel=None,
                 sel_count=None):
     """Returns (sel int32 [B][Hkv][max_sel], sel_count int32 [B][Hkv])."""
-    B = batch.seq_lens.shape[0]
     dev = batch.seq_lens.device
     if sel is not None:
-        max_sel_n = int(sel.shape[2])
+        if max_sel_n is not None and int(max_sel_n) != sel.shape[-1]:
+            raise ValueError("max_sel_n disagrees with sel's last dimension")
+        max_sel_n = int(sel.shape[-1])
     if max_sel_n is None:
         max_sel_n = max_sel(layout, policy, batch.max_pages)
     if sel is None:
-        sel = torch.empty((B, layout.num_kv_heads, max_sel_n), dtype=torch.int32, device=dev)
+        sel = torch.empty((batch.batch, layout.num_kv_heads, max_sel_n), dtype=torch.int32, device=dev)
     if sel_count is None:
-        sel_count = torch.empty((B, layout.num_kv_heads), dtype=torch.int32, device=dev)
-    cnt = sel_count
-    _dev(sel, torch.int32, "sel", 3)
-    _dev(cnt, torch.int32, "sel_count", 2)
-    _dev(q, torch.bfloat16, "q", 3)
-    _dev(summ, torch.bfloat16, "summ", 4)
-    _dev(scores, torch.float32, "scores", 4)
+        sel_count = torch.empty((batch.batch, layout.num_kv_heads), dtype=torch.int32, device=dev)
+    _check_args(*batch.specs(), *_sel_specs(layout, batch, sel, sel_count, max_sel_n),
+                *_query_specs(layout, batch, q, None), *_pool_specs(layout, None, None, summ),
+                _score_spec(layout, batch, scores))
     _check(lib().qasp_select_topk(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
-                                  _ptr(q), _ptr(summ), _ptr(scores), _ptr(sel), _ptr(cnt), int(max_sel_n),
+                                  _ptr(q), _ptr(summ), _ptr(scores), _ptr(sel), _ptr(sel_count), int(max_sel_n),
                                   _stream()), "qasp_select_topk")
-    return sel, cnt
+    return sel, sel_count
+
+
+def _new_out(layout: Layout, batch: Batch, q, n_query=None):
+    lead = (batch.batch,) if n_query is None else (batch.batch, n_query)
+    return torch.empty(lead + (batch.num_q_heads, layout.head_dim_v), dtype=torch.float32,
+                       device=q.device if q is not None else batch.seq_lens.device)
 
 
 def sparse_paged_decode(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, sel, sel_count,
                         scale: float, workspace: torch.Tensor, out=None) -> torch.Tensor:
     """Returns float32 [B][Hq][Dv]."""
-    _dev(q, torch.bfloat16, "q", 3)
-    _dev(k_pool, torch.bfloat16, "k_pool", 4)
-    _dev(v_pool, torch.bfloat16, "v_pool", 4)
-    _dev(sel, torch.int32, "sel", 3)
-    _dev(sel_count, torch.int32, "sel_count", 2)
-    _dev(workspace, torch.uint8, "workspace", 1)
-    B = batch.seq_lens.shape[0]
-    if out is None:
-        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
-    _dev(out, torch.float32, "out", 3)
+    if sel is None or sel_count is None:
+        raise ValueError("sel and sel_count are required")
+    out = _new_out(layout, batch, q) if out is None else out
+    _check_args(*batch.specs(), *_query_specs(layout, batch, q, out), *_pool_specs(layout, k_pool, v_pool, None),
+                *_sel_specs(layout, batch, sel, sel_count), _ws_spec(workspace))
     _check(lib().qasp_sparse_paged_decode(ctypes.byref(layout.c()), ctypes.byref(batch.c()),
                                           ctypes.byref(policy.c()), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                           _ptr(sel), _ptr(sel_count), int(sel.shape[2]), float(scale),
@@ -294,21 +354,23 @@ def sparse_paged_decode(layout: Layout, batch: Batch, policy: Policy, q, k_pool,
     return out
 
 
+def _step_specs(layout: Layout, batch: Batch, q, out, k_pool, v_pool, summ, k_new, v_new, sel, sel_count,
+                max_sel_n, workspace, n_query=None):
+    if sel is not None and int(max_sel_n) != sel.shape[-1]:
+        raise ValueError("max_sel_n (%d) disagrees with sel's last dimension (%d)" % (max_sel_n, sel.shape[-1]))
+    return [*batch.specs(), *_query_specs(layout, batch, q, out, n_query), *_pool_specs(layout, k_pool, v_pool, summ),
+            *_token_specs(layout, batch.batch, k_new, v_new, n_query),
+            *_sel_specs(layout, batch, sel, sel_count, int(max_sel_n)), _ws_spec(workspace)]
+
+
 def decode_step(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, summ, scale: float,
                 workspace: torch.Tensor, max_sel_n: int, k_new=None, v_new=None, out=None, sel=None,
                 sel_count=None) -> torch.Tensor:
     """Append (if k_new is given; batch.seq_lens then counts the new token),
     score, select, attend and merge in one call.  Returns out fp32 [B][Hq][Dv]."""
-    for t, name, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
-                        (k_new, "k_new", 3), (v_new, "v_new", 3)):
-        _dev(t, torch.bfloat16, name, nd)
-    _dev(sel, torch.int32, "sel", 3)
-    _dev(sel_count, torch.int32, "sel_count", 2)
-    _dev(workspace, torch.uint8, "workspace", 1)
-    B = batch.seq_lens.shape[0]
-    if out is None:
-        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
-    _dev(out, torch.float32, "out", 3)
+    out = _new_out(layout, batch, q) if out is None else out
+    _check_args(*_step_specs(layout, batch, q, out, k_pool, v_pool, summ, k_new, v_new, sel, sel_count, max_sel_n,
+                             workspace))
     _check(lib().qasp_decode_step(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
                                   _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(summ),
                                   float(scale), _ptr(out), _ptr(sel), _ptr(sel_count), int(max_sel_n),
@@ -323,21 +385,29 @@ def decode_step_reuse(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v
     batch.seq_lens then counts the new token) and attention over the given
     pages, no scoring or selection.  summ may be None.  Returns out fp32
     [B][Hq][Dv]."""
-    for t, name, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
-                        (k_new, "k_new", 3), (v_new, "v_new", 3)):
-        _dev(t, torch.bfloat16, name, nd)
-    _dev(sel, torch.int32, "sel", 3)
-    _dev(sel_count, torch.int32, "sel_count", 2)
-    _dev(workspace, torch.uint8, "workspace", 1)
-    B = batch.seq_lens.shape[0]
-    if out is None:
-        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
-    _dev(out, torch.float32, "out", 3)
+    if sel is None or sel_count is None:
+        raise ValueError("sel and sel_count are required")
+    out = _new_out(layout, batch, q) if out is None else out
+    _check_args(*_step_specs(layout, batch, q, out, k_pool, v_pool, summ, k_new, v_new, sel, sel_count,
+                             sel.shape[-1], workspace))
     _check(lib().qasp_decode_step_reuse(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
                                         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(summ),
                                         float(scale), _ptr(sel), _ptr(sel_count), int(sel.shape[2]), _ptr(out),
                                         _ptr(workspace), workspace.numel(), _stream()), "qasp_decode_step_reuse")
     return out
+
+
+def check_batch(layout: Layout, batch: Batch, extra_tokens: int = 0, sel=None, sel_count=None):
+    """Runs qasp_check_batch (and waits for it): raises QaspError with status
+    ERR_BAD_PAGE_TABLE when a length, page-table entry or selected id is out
+    of range.  Validate mode (environment variable QASP_VALIDATE=1) runs the
+    same check inside every call that reads the pools."""
+    max_sel_n = 0 if sel is None else int(sel.shape[-1])
+    if (sel is None) != (sel_count is None):
+        raise ValueError("sel and sel_count come together")
+    _check_args(*batch.specs(), *([] if sel is None else _sel_specs(layout, batch, sel, sel_count, max_sel_n)))
+    _check(lib().qasp_check_batch(ctypes.byref(layout.c()), ctypes.byref(batch.c()), int(extra_tokens), _ptr(sel),
+                                  _ptr(sel_count), max_sel_n, _stream()), "qasp_check_batch")
 
 
 def layout_of(w) -> Layout:
@@ -374,16 +444,12 @@ def decode_step_multi(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v
     them): append them (if k_new is given, [B][n][Hkv][Dk]), select once per
     (sequence, KV head) for all drafts, attend causally.  q [B][n][Hq][Dk];
     returns out fp32 [B][n][Hq][Dv]."""
-    for t, name, nd in ((q, "q", 4), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
-                        (k_new, "k_new", 4), (v_new, "v_new", 4)):
-        _dev(t, torch.bfloat16, name, nd)
-    _dev(sel, torch.int32, "sel", 3)
-    _dev(sel_count, torch.int32, "sel_count", 2)
-    _dev(workspace, torch.uint8, "workspace", 1)
-    B, n = batch.seq_lens.shape[0], q.shape[1]
-    if out is None:
-        out = torch.empty((B, n, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
-    _dev(out, torch.float32, "out", 4)
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be [B][n_query][Hq][Dk]")
+    n = int(q.shape[1])
+    out = _new_out(layout, batch, q, n) if out is None else out
+    _check_args(*_step_specs(layout, batch, q, out, k_pool, v_pool, summ, k_new, v_new, sel, sel_count, max_sel_n,
+                             workspace, n))
     _check(lib().qasp_decode_step_multi(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
                                         int(n), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                         _ptr(summ), float(scale), _ptr(out), _ptr(sel), _ptr(sel_count),
@@ -461,11 +527,15 @@ def new_quant_pool(layout: Layout, device) -> torch.Tensor:
                        dtype=torch.uint8, device=device)
 
 
+def _qpool_spec(layout: Layout, qpool):
+    per = int(lib().qasp_quant_pool_bytes(ctypes.byref(layout.c()))) // max(1, layout.num_pool_pages *
+                                                                            layout.num_kv_heads)
+    return (qpool, torch.uint8, "qpool", (AtLeast(layout.num_pool_pages), layout.num_kv_heads, per or None))
+
+
 def quantize_pages(layout: Layout, batch: Batch, residual_pages: int, k_pool, v_pool, qpool):
     """Quantises every page below the last residual_pages of each sequence."""
-    _dev(k_pool, torch.bfloat16, "k_pool", 4)
-    _dev(v_pool, torch.bfloat16, "v_pool", 4)
-    _dev(qpool, torch.uint8, "qpool", 3)
+    _check_args(*batch.specs(), *_pool_specs(layout, k_pool, v_pool, None), _qpool_spec(layout, qpool))
     _check(lib().qasp_quantize_pages(ctypes.byref(layout.c()), ctypes.byref(batch.c()), int(residual_pages),
                                      _ptr(k_pool), _ptr(v_pool), _ptr(qpool), _stream()), "qasp_quantize_pages")
 
@@ -475,17 +545,9 @@ def decode_step_quant(layout: Layout, batch: Batch, policy: Policy, residual_pag
                       sel=None, sel_count=None) -> torch.Tensor:
     """decode_step with the pages below the last residual_pages read from the
     2-bit quantised pool.  Returns out fp32 [B][Hq][Dv]."""
-    for t, name, nd in ((q, "q", 3), (k_pool, "k_pool", 4), (v_pool, "v_pool", 4), (summ, "summ", 4),
-                        (k_new, "k_new", 3), (v_new, "v_new", 3)):
-        _dev(t, torch.bfloat16, name, nd)
-    _dev(qpool, torch.uint8, "qpool", 3)
-    _dev(sel, torch.int32, "sel", 3)
-    _dev(sel_count, torch.int32, "sel_count", 2)
-    _dev(workspace, torch.uint8, "workspace", 1)
-    B = batch.seq_lens.shape[0]
-    if out is None:
-        out = torch.empty((B, batch.num_q_heads, layout.head_dim_v), dtype=torch.float32, device=q.device)
-    _dev(out, torch.float32, "out", 3)
+    out = _new_out(layout, batch, q) if out is None else out
+    _check_args(*_step_specs(layout, batch, q, out, k_pool, v_pool, summ, k_new, v_new, sel, sel_count, max_sel_n,
+                             workspace), _qpool_spec(layout, qpool))
     _check(lib().qasp_decode_step_quant(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
                                         int(residual_pages), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                         _ptr(v_pool), _ptr(summ), _ptr(qpool), float(scale), _ptr(out), _ptr(sel),

@@ -151,6 +151,15 @@ hipError_t launch_sparse_decode(const qasp_layout &lay, const qasp_batch &bat, c
 
 static int32_t status_of(hipError_t e) { return e == hipSuccess ? QASP_OK : QASP_ERR_LAUNCH; }
 
+// Validate mode (QASP_VALIDATE set and not "0"): the device-side lengths,
+// page-table entries and selection are checked before any kernel that reads
+// the pools through them; the check synchronises the stream.
+static int32_t maybe_validate(const qasp_layout &lay, const qasp_batch &bat, void *stream, int extra_tokens = 0,
+                              const int32_t *sel = nullptr, const int32_t *sel_count = nullptr, int max_sel = 0) {
+  if (!validate_mode()) return QASP_OK;
+  return check_batch_on_device(lay, bat, extra_tokens, sel, sel_count, max_sel, (hipStream_t)stream);
+}
+
 // Multi-query step: nq draft queries regrouped so that KV head g's group holds
 // G heads per draft query (num_q_heads * nq columns in all); a static head's
 // selection covers the union of the queries' windows (window + nq - 1 tokens
@@ -200,6 +209,7 @@ const char *qasp_status_string(int32_t status) {
     case QASP_ERR_MAX_SEL: return "max_sel smaller than the largest possible selection";
     case QASP_ERR_LAUNCH: return "HIP kernel launch failed";
     case QASP_ERR_ALLOC: return "host-tier allocation failed";
+    case QASP_ERR_BAD_PAGE_TABLE: return "a sequence length, page-table entry or selected page is out of range";
     default: return "unknown status";
   }
 }
@@ -227,6 +237,7 @@ int32_t qasp_build_summaries(const qasp_layout *lay, const qasp_batch *bat, cons
   if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
   if (bat->batch == 0) return QASP_OK;
   if (!k_pool || !summ) return QASP_ERR_NULL_ARG;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
   return status_of(launch_build_summaries(*lay, *bat, k_pool, summ, (hipStream_t)stream));
 }
 
@@ -241,6 +252,7 @@ int32_t qasp_append_kv(const qasp_layout *lay, const qasp_batch *bat_before, con
   if (!k_new || !k_pool) return QASP_ERR_NULL_ARG;
   if (!lay->v_from_k && (!v_new || !v_pool)) return QASP_ERR_NULL_ARG;
   if (!summ && !all_static(*lay, *pol)) return QASP_ERR_NULL_ARG;
+  if ((rc = maybe_validate(*lay, *bat_before, stream, 1)) != QASP_OK) return rc;
   return status_of(launch_append_kv(*lay, *bat_before, 0, k_new, v_new, k_pool, v_pool, summ,
                                     (hipStream_t)stream));
 }
@@ -254,6 +266,7 @@ int32_t qasp_score_pages(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (bat->batch == 0 || bat->max_pages == 0) return QASP_OK;
   if (!scores) return QASP_ERR_NULL_ARG;
   if (!all_static(*lay, *pol) && (!q || !summ)) return QASP_ERR_NULL_ARG;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
   return status_of(launch_score_pages(*lay, *bat, *pol, q, summ, scores, (hipStream_t)stream,
                                       token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr)));
 }
@@ -270,6 +283,7 @@ int32_t qasp_select_topk(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (bat->batch == 0) return QASP_OK;
   if (!sel || !sel_count) return QASP_ERR_NULL_ARG;
   if (!all_static(*lay, *pol) && (!q || !summ || !scores)) return QASP_ERR_NULL_ARG;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
   return status_of(launch_select_topk(*lay, *bat, *pol, q, summ, scores, sel, sel_count, max_sel,
                                       (hipStream_t)stream));
 }
@@ -287,6 +301,7 @@ int32_t qasp_sparse_paged_decode(const qasp_layout *lay, const qasp_batch *bat, 
   if (!q || !k_pool || !sel || !sel_count || !out || !workspace) return QASP_ERR_NULL_ARG;
   if (!lay->v_from_k && !v_pool) return QASP_ERR_NULL_ARG;
   if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  if ((rc = maybe_validate(*lay, *bat, stream, 0, sel, sel_count, max_sel)) != QASP_OK) return rc;
   const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
   return status_of(launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel, sel_count, max_sel, scale,
                                         out, ws, (hipStream_t)stream));
@@ -311,6 +326,7 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (k_new && !lay->v_from_k && !v_new) return QASP_ERR_NULL_ARG;
   if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
   if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   // many units: the whole step as one kernel per (sequence, KV head) block
   const long units = (long)bat->batch * lay->num_kv_heads;
@@ -334,6 +350,16 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (e == hipSuccess)
     e = launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
   return status_of(e);
+}
+
+int32_t qasp_check_batch(const qasp_layout *lay, const qasp_batch *bat, int32_t extra_tokens, const int32_t *sel,
+                         const int32_t *sel_count, int32_t max_sel, void *stream) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if (extra_tokens < 0 || extra_tokens > kMaxDrafts || max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
+  return check_batch_on_device(*lay, *bat, extra_tokens, sel, sel_count, max_sel, (hipStream_t)stream);
 }
 
 int32_t qasp_host_alloc(size_t bytes, void **host_ptr, void **device_ptr) {
@@ -372,6 +398,7 @@ int32_t qasp_quantize_pages(const qasp_layout *lay, const qasp_batch *bat, int32
   if (residual_pages < 1) return QASP_ERR_BAD_SHAPE;
   if (bat->batch == 0) return QASP_OK;
   if (!k_pool || !v_pool || !qpool) return QASP_ERR_NULL_ARG;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
   return status_of(launch_quantize(*lay, *bat, residual_pages, false, k_pool, v_pool, qpool, (hipStream_t)stream));
 }
 
@@ -394,6 +421,7 @@ int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat, co
   if (k_new && !v_new) return QASP_ERR_NULL_ARG;
   if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
   if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
   int32_t *sel_out = sel ? sel : ws.sel;
@@ -456,6 +484,7 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat, co
   if (k_new && !v_new) return QASP_ERR_NULL_ARG;
   if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
   if (workspace_bytes_given < multi_workspace_bytes(*lay, *bat, nq, max_sel)) return QASP_ERR_WORKSPACE;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   const qasp_batch wbat = multi_batch(*bat, nq);
   const Workspace ws = carve_workspace(*lay, wbat, max_sel, workspace);
@@ -496,6 +525,7 @@ int32_t qasp_decode_step_reuse(const qasp_layout *lay, const qasp_batch *bat, co
   if (!lay->v_from_k && !v_pool) return QASP_ERR_NULL_ARG;
   if (k_new && !lay->v_from_k && !v_new) return QASP_ERR_NULL_ARG;
   if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  if ((rc = maybe_validate(*lay, *bat, stream, 0, sel, sel_count, max_sel)) != QASP_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   const long units = (long)bat->batch * lay->num_kv_heads;
   if (family_of(*lay) == kFamilyGqa && units >= kFusedMinUnits)

@@ -187,6 +187,28 @@ __device__ __forceinline__ void attend_pages(WaveState &st, const PageWork<PS, D
   }
 }
 
+// Attends a wave's npg page-heads of any number: one page per lane in chunks
+// of 64 (attend_pages holds a chunk's ids in the lanes).  page_at(i) returns
+// (logical id, physical page) of the wave's i-th page; pre / first as in
+// attend_pages, for the first chunk.
+template <int PS, int D, int DV, bool CAUSAL, typename PageAt>
+__device__ __forceinline__ void attend_list(WaveState &st, const PageWork<PS, D, DV, CAUSAL> &pw, int npg, int lane,
+                                            PageAt page_at, bool pre = false,
+                                            PageRegs<D, DV> first = PageRegs<D, DV>()) {
+  const int n0 = min(npg, kWave);
+  int2 jp = make_int2(0, 0);
+  if (lane < n0) jp = page_at(lane);
+  attend_pages<PS, D, DV>(st, pw, n0, jp.x, jp.y, lane, pre, first);
+  // more than 64 pages for this wave (a selection of more than 64 pages per
+  // wave of the block): the following chunks, without the preloaded page
+  for (int c0 = kWave; c0 < npg; c0 += kWave) {
+    const int nc = min(npg - c0, kWave);
+    int2 jc = make_int2(0, 0);
+    if (lane < nc) jc = page_at(c0 + lane);
+    attend_pages<PS, D, DV>(st, pw, nc, jc.x, jc.y, lane);
+  }
+}
+
 // LDS footprint of merge_waves for W waves and G heads (floats).
 __host__ __device__ constexpr int merge_lds_floats(int W, int G, int DV) { return 2 * W * G + W * G * (DV + 4); }
 

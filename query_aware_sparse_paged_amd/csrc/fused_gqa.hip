@@ -531,14 +531,15 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     return p < cand_lo ? p : count - (P - cand_hi) + (p - cand_lo);  // sink, then local
   };
   const int npg = count > wave ? (count - wave + W - 1) / W : 0;
-  int my_j = 0, my_phys = 0;
-  if (lane < npg) {
-    my_j = list[n_known > 0 ? map_pos(wave + W * lane) : wave + W * lane];
-    my_phys = page_phys[my_j];
-  }
   attend::WaveState st;
   attend::init_state(st);
-  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane, pre && npg > 0, first);
+  attend::attend_list(
+      st, pw, npg, lane,
+      [&](int i) {
+        const int j = list[n_known > 0 ? map_pos(wave + W * i) : wave + W * i];
+        return make_int2(j, page_phys[j]);
+      },
+      pre && npg > 0, first);
   attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
     (void)M;
     size_t row = head0 + h;
@@ -580,10 +581,11 @@ __global__ __launch_bounds__(W * 64) void fused_reuse_gqa_kernel(
   const size_t head0 = (size_t)b * Hq + (size_t)g * G;
   const int count = min(sel_count[unit], max_sel);
   const int npg = count > wave ? (count - wave + W - 1) / W : 0;  // positions wave, wave + W, ...
-  // the wave's pages, lane i holding its i-th (issued before the append)
+  // the wave's first 64 pages, lane i holding its i-th (issued before the append)
+  const int n0 = min(npg, kWave);
   int my_j = 0, my_phys = 0;
-  if (lane < npg) my_j = sel[(size_t)unit * max_sel + wave + W * lane];
-  if (lane < npg) my_phys = pt_row[my_j];
+  if (lane < n0) my_j = sel[(size_t)unit * max_sel + wave + W * lane];
+  if (lane < n0) my_phys = pt_row[my_j];
 
   // append of the token at position L-1 by the last wave
   if (k_new != nullptr && L > 0 && wave == W - 1) {
@@ -626,7 +628,18 @@ __global__ __launch_bounds__(W * 64) void fused_reuse_gqa_kernel(
   const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
   attend::WaveState st;
   attend::init_state(st);
-  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
+  attend::attend_pages<PS, D, DV>(st, pw, n0, my_j, my_phys, lane);
+  // pages past the 64th of this wave (selections of more than 64 W pages)
+  const int32_t *sel_row = sel + (size_t)unit * max_sel;
+  for (int c0 = kWave; c0 < npg; c0 += kWave) {
+    const int nc = min(npg - c0, kWave);
+    int j = 0, ph = 0;
+    if (lane < nc) {
+      j = sel_row[wave + W * (c0 + lane)];
+      ph = pt_row[j];
+    }
+    attend::attend_pages<PS, D, DV>(st, pw, nc, j, ph, lane);
+  }
   attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
     (void)M;
     out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;

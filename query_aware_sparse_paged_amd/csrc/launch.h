@@ -34,6 +34,12 @@ struct Workspace {
 };
 
 int decode_splits(const qasp_layout &lay, const qasp_batch &bat, int max_sel);
+// Validate mode (the QASP_VALIDATE environment variable) and its check: a
+// kernel reads the lengths, page-table rows and selection, then the stream is
+// synchronised; QASP_OK or QASP_ERR_BAD_PAGE_TABLE.
+bool validate_mode();
+int32_t check_batch_on_device(const qasp_layout &lay, const qasp_batch &bat, int extra_tokens, const int32_t *sel,
+                              const int32_t *sel_count, int max_sel, hipStream_t stream);
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 size_t workspace_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel);

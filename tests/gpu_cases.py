@@ -2,6 +2,8 @@
 and run the oracle on the same inputs (or on a sampled sequence of them)."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
 from dataclasses import dataclass
 
 import numpy as np
@@ -71,46 +73,112 @@ class OracleRun:
     page_table: np.ndarray
 
 
+@dataclass
+class OracleInputs:
+    """Host copies (bit patterns) of a workload, or of a sub-batch of its
+    sequences re-packed into a small pool (logical page ids unchanged)."""
+    olay: "oracle.Layout"
+    pt: np.ndarray
+    sl: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: object            # np.ndarray or None (values are key channels)
+    num_q_heads: int
+    scale: float
+    phys: object = None  # device physical pages of the sub-pool rows (None: whole pool)
+
+
+def oracle_inputs(w, seqs=None, k_pool=None, v_pool=None, q=None) -> OracleInputs:
+    """Gathers the oracle's inputs: the whole workload (seqs None) or the
+    pages of sequences seqs, re-packed; the pools and query default to w's."""
+    lay = api.layout_of(w)
+    k_pool = w.k_pool if k_pool is None else k_pool
+    v_pool = w.v_pool if v_pool is None else v_pool
+    q = w.q if q is None else q
+    if seqs is None:
+        return OracleInputs(olayout(lay), w.page_table.cpu().numpy(), w.seq_lens.cpu().numpy(), workloads.bits(q),
+                            workloads.bits(k_pool), None if v_pool is None else workloads.bits(v_pool),
+                            w.spec.num_q_heads, w.scale)
+    seqs = list(seqs)
+    pt_full = w.page_table[seqs]                                   # [n][stride]
+    valid = pt_full >= 0
+    phys = pt_full[valid].long()
+    k = workloads.bits(k_pool[phys.to(k_pool.device)])
+    v = None if v_pool is None else workloads.bits(v_pool[phys.to(v_pool.device)])
+    pt = np.full(tuple(pt_full.shape), -1, np.int32)
+    pt[valid.cpu().numpy()] = np.arange(phys.numel(), dtype=np.int32)
+    olay = oracle.Layout(int(phys.numel()), lay.page_size, lay.num_kv_heads, lay.head_dim_k, lay.head_dim_v,
+                         lay.v_from_k)
+    return OracleInputs(olay, pt, w.seq_lens[seqs].cpu().numpy(), workloads.bits(q[seqs]), k, v,
+                        w.spec.num_q_heads, w.scale, phys)
+
+
+def oracle_run(inp: OracleInputs, pol: api.Policy, max_sel_n: int, num_threads=8) -> OracleRun:
+    """Summaries from the keys, scores, selection and attention, all by the oracle."""
+    opol = opolicy(pol)
+    summ = oracle.summaries(inp.olay, inp.pt, inp.sl, inp.num_q_heads, inp.k)
+    scores = oracle.scores(inp.olay, inp.pt, inp.sl, inp.q, summ, opol)
+    out, sel, cnt = oracle.decode(inp.olay, inp.pt, inp.sl, inp.q, inp.k, inp.v, summ, opol, inp.scale,
+                                  num_threads=num_threads, max_sel_n=max_sel_n)
+    return OracleRun(out, sel, cnt, scores, summ, inp.pt)
+
+
 def run_oracle(w, pol: api.Policy, max_sel_n: int, seqs=None) -> OracleRun:
     """Oracle on the whole workload (seqs None) or on a sub-batch of sequences
     re-packed into a small pool (logical page ids are unchanged)."""
-    spec = w.spec
-    lay = api.layout_of(w)
-    if seqs is None:
-        pt = w.page_table.cpu().numpy()
-        sl = w.seq_lens.cpu().numpy()
-        q = workloads.bits(w.q)
-        k = workloads.bits(w.k_pool)
-        v = None if w.v_pool is None else workloads.bits(w.v_pool)
-        olay = olayout(lay)
-    else:
-        seqs = list(seqs)
-        pt_full = w.page_table[seqs]                                   # [n][stride]
-        stride = pt_full.shape[1]
-        valid = pt_full >= 0
-        phys = pt_full[valid].long()
-        k = workloads.bits(w.k_pool[phys])
-        v = None if w.v_pool is None else workloads.bits(w.v_pool[phys])
-        pt = np.full((len(seqs), stride), -1, np.int32)
-        pt[valid.cpu().numpy()] = np.arange(phys.numel(), dtype=np.int32)
-        sl = w.seq_lens[seqs].cpu().numpy()
-        q = workloads.bits(w.q[seqs])
-        olay = oracle.Layout(int(phys.numel()), lay.page_size, lay.num_kv_heads, lay.head_dim_k,
-                             lay.head_dim_v, lay.v_from_k)
-    opol = opolicy(pol)
-    summ = oracle.summaries(olay, pt, sl, spec.num_q_heads, k)
-    scores = oracle.scores(olay, pt, sl, q, summ, opol)
-    out, sel, cnt = oracle.decode(olay, pt, sl, q, k, v, summ, opol, w.scale, num_threads=8,
-                                  max_sel_n=max_sel_n)
-    return OracleRun(out, sel, cnt, scores, summ, pt)
+    return oracle_run(oracle_inputs(w, seqs), pol, max_sel_n)
 
 
-def gpu_summaries_of(g: GpuRun, w, seqs, ref: OracleRun):
-    """GPU summaries of the sampled sequences' pages, in the sub-pool order."""
-    pt_full = w.page_table[list(seqs)]
-    phys = pt_full[pt_full >= 0].long().to(DEV)
-    s = workloads.bits(g.summ[phys])
-    return s
+def workers() -> int:
+    """Threads for oracle chunks (ctypes releases the GIL); at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def chunked(n: int, size: int):
+    return [list(range(s, min(n, s + size))) for s in range(0, n, size)]
+
+
+def map_chunks(chunks, gather, job, max_inflight=None):
+    """For each chunk of sequences: gather(chunk) on this thread (device to
+    host copies), then job(chunk, gathered) on a worker thread; at most
+    max_inflight gathered chunks are held at once.  Returns the jobs' results
+    in chunk order; the first failure is raised."""
+    nw = workers()
+    max_inflight = max_inflight or 2 * nw
+    results = [None] * len(chunks)
+    with ThreadPoolExecutor(nw) as ex:
+        pending = {}
+        for i, c in enumerate(chunks):
+            while len(pending) >= max_inflight:
+                done, _ = wait(list(pending), return_when=FIRST_COMPLETED)
+                for f in done:
+                    results[pending.pop(f)] = f.result()
+            pending[ex.submit(job, c, gather(c))] = i
+        for f in list(pending):
+            results[pending.pop(f)] = f.result()
+    return results
+
+
+def check_every_sequence(w, g: "GpuRun", pol=None, chunk=2, check_scores=True, what=""):
+    """The oracle on every sequence of w (chunks of `chunk` sequences re-packed
+    into small pools, run on worker threads): summaries and selections
+    bit-exact, outputs within OUT_TOL, every stored score inside its bound.
+    Returns the largest output error."""
+    pol = pol or api.policy_of(w)
+    B = int(w.seq_lens.shape[0])
+
+    def gather(seqs):
+        inp = oracle_inputs(w, seqs)
+        return inp, workloads.bits(g.summ[inp.phys.to(g.summ.device)])
+
+    def job(seqs, gathered):
+        inp, gsumm = gathered
+        r = oracle_run(inp, pol, g.max_sel, num_threads=1)
+        assert np.array_equal(gsumm, r.summ), "%s: summaries differ (sequences %s)" % (what, seqs)
+        return compare(g, r, seqs=seqs, check_scores=check_scores, what="%s seqs %s" % (what, seqs))
+
+    errs = map_chunks(chunked(B, chunk), gather, job)
+    return max(errs) if errs else 0.0
 
 
 def compare(g: GpuRun, r: OracleRun, seqs=None, check_scores=True, what=""):

@@ -35,8 +35,9 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     assert re.match(r"^\d+\.\d+\.\d+$", api.version())
-    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert api.status_string(s) != "unknown status"
+    assert "page-table" in api.status_string(api.ERR_BAD_PAGE_TABLE)
     assert api.status_string(-99) == "unknown status"
 
 
@@ -242,3 +243,134 @@ def test_quant_step_argument_checks(L):
     assert call(lay_=MLA.c(), bat_=_batch(Hq=128)) == api.ERR_UNSUPPORTED
     assert _call("qasp_decode_step_quant", b(lay), b(_batch(B=0)), b(pol), 1, None, None, None, None, None, None,
                  None, 1.0, None, None, None, 37, None, 0, None) == api.OK
+
+
+# ----------------------------------------------------------------------------
+# the Python binding's shape checks (run before any device check, so CPU
+# tensors of the wrong shape are reported by name)
+# ----------------------------------------------------------------------------
+
+def _cpu_args(B=2, Hq=32, max_sel_n=37, nq=None):
+    import torch
+    lay = api.Layout(64, 16, 8, 128, 128)
+    pt = torch.zeros((B, 10), dtype=torch.int32)
+    bat = api.Batch(pt, torch.full((B,), 100, dtype=torch.int32), Hq, max_pages=9)
+    lead = (B,) if nq is None else (B, nq)
+    bf = torch.bfloat16
+    a = dict(
+        q=torch.zeros(lead + (Hq, 128), dtype=bf),
+        out=torch.zeros(lead + (Hq, 128), dtype=torch.float32),
+        k_pool=torch.zeros((64, 8, 16, 128), dtype=bf),
+        v_pool=torch.zeros((64, 8, 128, 16), dtype=bf),
+        summ=torch.zeros((64, 8, 2, 128), dtype=bf),
+        k_new=torch.zeros(lead + (8, 128), dtype=bf),
+        v_new=torch.zeros(lead + (8, 128), dtype=bf),
+        sel=torch.zeros((B, 8, max_sel_n), dtype=torch.int32),
+        sel_count=torch.zeros((B, 8), dtype=torch.int32),
+        workspace=torch.zeros(16, dtype=torch.uint8),
+    )
+    return lay, bat, api.Policy(1, 4, 32), a
+
+
+def _raises(fn, match):
+    with pytest.raises((ValueError, TypeError), match=match):
+        fn()
+
+
+def test_binding_rejects_wrong_shapes(L):
+    import torch
+    lay, bat, pol, a = _cpu_args()
+
+    def step(**kw):
+        x = dict(a, **kw)
+        return lambda: api.decode_step(lay, bat, pol, x["q"], x["k_pool"], x["v_pool"], x["summ"], 0.1,
+                                       x["workspace"], 37, k_new=x["k_new"], v_new=x["v_new"], out=x["out"],
+                                       sel=x["sel"], sel_count=x["sel_count"])
+
+    # every argument right: the first complaint is the device
+    _raises(step(), "GPU tensor")
+    bf = torch.bfloat16
+    wrong = dict(
+        q=torch.zeros((2, 31, 128), dtype=bf),                  # heads
+        out=torch.zeros((3, 32, 128), dtype=torch.float32),      # batch
+        k_pool=torch.zeros((63, 8, 16, 128), dtype=bf),          # fewer pages than the layout
+        v_pool=torch.zeros((64, 8, 16, 128), dtype=bf),          # untransposed value tile
+        summ=torch.zeros((64, 8, 1, 128), dtype=bf),
+        k_new=torch.zeros((2, 4, 128), dtype=bf),
+        v_new=torch.zeros((2, 8, 64), dtype=bf),
+        sel=torch.zeros((2, 8, 36), dtype=torch.int32),          # capacity disagrees with max_sel_n
+        sel_count=torch.zeros((2, 7), dtype=torch.int32),
+    )
+    for name, t in wrong.items():
+        _raises(step(**{name: t}), name if name != "sel" else "max_sel_n|sel")
+    _raises(step(q=a["q"].float()), "q must be")
+    _raises(step(out=torch.zeros((2, 128, 32), dtype=torch.float32).transpose(1, 2)), "out must be contiguous")
+    # larger pools than the layout declares are fine (the device check comes next)
+    _raises(step(k_pool=torch.zeros((65, 8, 16, 128), dtype=bf)), "GPU tensor")
+
+
+def test_binding_shape_checks_of_the_other_calls(L):
+    import torch
+    lay, bat, pol, a = _cpu_args()
+    bf = torch.bfloat16
+    bad_scores = torch.zeros((2, 8, 8, 4), dtype=torch.float32)   # max_pages is 9
+    _raises(lambda: api.score_pages(lay, bat, pol, a["q"], a["summ"], scores=bad_scores), "scores")
+    _raises(lambda: api.select_topk(lay, bat, pol, a["q"], a["summ"], bad_scores), "scores")
+    good_scores = torch.zeros((2, 8, 9, 4), dtype=torch.float32)
+    _raises(lambda: api.select_topk(lay, bat, pol, a["q"], a["summ"], good_scores, max_sel_n=40, sel=a["sel"]),
+            "max_sel_n")
+    _raises(lambda: api.sparse_paged_decode(lay, bat, pol, a["q"], a["k_pool"], a["v_pool"], a["sel"],
+                                            torch.zeros((2,), dtype=torch.int32), 0.1, a["workspace"]), "sel_count")
+    _raises(lambda: api.decode_step_reuse(lay, bat, pol, a["q"], a["k_pool"], a["v_pool"], None, 0.1,
+                                          a["sel"][:1], a["sel_count"], a["workspace"]), "sel")
+    _raises(lambda: api.build_summaries(lay, bat, a["k_pool"], torch.zeros((64, 8, 2, 64), dtype=bf)), "summ")
+    _raises(lambda: api.append_kv(lay, bat, pol, a["k_new"][:1], a["v_new"], a["k_pool"], a["v_pool"],
+                                  a["summ"]), "k_new")
+    q4 = torch.zeros((64, 8, 1000), dtype=torch.uint8)
+    _raises(lambda: api.quantize_pages(lay, bat, 2, a["k_pool"], a["v_pool"], q4), "qpool")
+    _raises(lambda: api.decode_step_quant(lay, bat, pol, 2, a["q"], a["k_pool"], a["v_pool"], a["summ"],
+                                          torch.zeros((63, 8, 1536), dtype=torch.uint8), 0.1, a["workspace"], 37),
+            "qpool")
+    # multi-query: [B][n] leading dimensions
+    lay, bat, pol, m = _cpu_args(nq=3, max_sel_n=40)
+    _raises(lambda: api.decode_step_multi(lay, bat, pol, m["q"], m["k_pool"], m["v_pool"], m["summ"], 0.1,
+                                          m["workspace"], 40, k_new=m["k_new"][:, :2], v_new=m["v_new"]), "k_new")
+    _raises(lambda: api.decode_step_multi(lay, bat, pol, m["q"], m["k_pool"], m["v_pool"], m["summ"], 0.1,
+                                          m["workspace"], 40, out=torch.zeros((2, 32, 128))), "out")
+    _raises(lambda: api.decode_step_multi(lay, bat, pol, m["q"], m["k_pool"], m["v_pool"], m["summ"], 0.1,
+                                          m["workspace"], 40, k_new=m["k_new"], v_new=m["v_new"]), "GPU tensor")
+    # the batch itself
+    _raises(lambda: api.Batch(torch.zeros((2, 10), dtype=torch.int32), torch.zeros((3,), dtype=torch.int32), 32),
+            "seq_lens")
+    _raises(lambda: api.Batch(torch.zeros((2, 10), dtype=torch.int64), torch.zeros((2,), dtype=torch.int32), 32),
+            "page_table")
+    _raises(lambda: api.Batch(torch.zeros((2, 10), dtype=torch.int32), torch.zeros((2,), dtype=torch.int32), 32,
+                              max_pages=11), "max_pages")
+
+
+def test_check_batch_host_errors(L):
+    """qasp_check_batch's host-side argument errors come before any HIP call."""
+    b = ctypes.byref
+    lay, bat = GQA.c(), _batch()
+    assert _call("qasp_check_batch", None, b(bat), 0, None, None, 0, None) == api.ERR_NULL_ARG
+    assert _call("qasp_check_batch", b(lay), None, 0, None, None, 0, None) == api.ERR_NULL_ARG
+    assert _call("qasp_check_batch", b(lay), b(bat), -1, None, None, 0, None) == api.ERR_BAD_SHAPE
+    assert _call("qasp_check_batch", b(lay), b(bat), 17, None, None, 0, None) == api.ERR_BAD_SHAPE
+    assert _call("qasp_check_batch", b(lay), b(bat), 0, None, None, -1, None) == api.ERR_BAD_SHAPE
+    assert _call("qasp_check_batch", b(lay), b(bat), 0, 0x10, None, 4, None) == api.ERR_NULL_ARG
+    assert _call("qasp_check_batch", b(lay), b(_batch(stride=100)), 0, None, None, 0, None) == api.ERR_BAD_SHAPE
+    # an empty batch has nothing to check
+    assert _call("qasp_check_batch", b(lay), b(_batch(B=0)), 0, None, None, 0, None) == api.OK
+
+
+def test_validate_mode_keeps_host_checks_first(L, monkeypatch):
+    """In validate mode the host-side argument errors are still returned
+    before the device check would run."""
+    monkeypatch.setenv("QASP_VALIDATE", "1")
+    b = ctypes.byref
+    lay, pol, bat = GQA.c(), api.Policy(1, 4, 32).c(), _batch()
+    assert _call("qasp_decode_step", b(lay), b(bat), b(pol), 1, None, None, 1, 1, 1, 1.0, 1, None, None,
+                 36, 1, 1 << 30, None) == api.ERR_MAX_SEL
+    assert _call("qasp_sparse_paged_decode", b(lay), b(bat), b(pol), 1, 1, 1, 1, 1, 37, 1.0, 1, 1,
+                 1, None) == api.ERR_WORKSPACE
+    assert _call("qasp_build_summaries", b(lay), b(bat), None, 1, None) == api.ERR_NULL_ARG

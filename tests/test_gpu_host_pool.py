@@ -5,7 +5,8 @@ the discussion of CPU-GPU cooperation for Quest / RetrievalAttention).
 
 The same kernels run on the same data as with device pools, so the bar is
 bit-equality with the device-pool run: outputs, selections and the pools
-after the step's append; and the outputs within 5e-3 of the oracle."""
+after the step's append; and against the oracle: summaries and selections
+bit-exact, outputs within 5e-3."""
 import numpy as np
 import pytest
 import torch
@@ -15,8 +16,7 @@ from query_aware_sparse_paged_amd import api, workloads
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    import oracle
-    from gpu_cases import DEV, OUT_TOL, olayout, opolicy
+    from gpu_cases import DEV, OUT_TOL, run_oracle
 
 
 def _step(w, lay, pol, kp, vp, summ, bat, msel):
@@ -50,7 +50,9 @@ def test_host_tier_pools_match_device_pools(name, batch, seq_len):
                          device=DEV)
     kd = w.k_pool.to(DEV)
     vd = None if w.v_pool is None else w.v_pool.to(DEV)
-    api.build_summaries(lay, bat, kd, summ_d)
+    # summaries of the cache before the step's token (lengths L - 1)
+    api.build_summaries(lay, api.Batch(bat.page_table, (bat.seq_lens - 1).contiguous(), w.spec.num_q_heads), kd,
+                        summ_d)
     summ_h = summ_d.clone()
     kh = api.host_pool_like(w.k_pool)
     vh = None if w.v_pool is None else api.host_pool_like(w.v_pool)
@@ -64,13 +66,21 @@ def test_host_tier_pools_match_device_pools(name, batch, seq_len):
         assert torch.equal(vh.host.view(torch.int16), vd.cpu().view(torch.int16))
     assert torch.equal(summ_h.cpu().view(torch.int16), summ_d.cpu().view(torch.int16))
 
-    # and the oracle's attention over that selection
-    olay, opol = olayout(lay), opolicy(pol)
-    kbits = workloads.bits(kh.host)
-    vbits = None if vh is None else workloads.bits(vh.host)
-    ref = oracle.attend(olay, w.page_table.numpy(), w.seq_lens.numpy(), workloads.bits(w.q), kbits, vbits,
-                        sel_h.numpy(), cnt_h.numpy(), opol, w.scale)
-    assert np.abs(out_h.numpy().astype(np.float64) - ref).max() <= OUT_TOL
+    # and the oracle: the token written into a host copy of the pools,
+    # summaries from scratch, scores, selection and attention
+    ps = lay.page_size
+    for b in range(batch):
+        L = int(w.seq_lens[b])
+        phys = int(w.page_table[b, (L - 1) // ps])
+        w.k_pool[phys, :, (L - 1) % ps, :] = w.k_new[b]
+        if w.v_pool is not None:
+            w.v_pool[phys, :, :, (L - 1) % ps] = w.v_new[b]
+    assert torch.equal(kh.host.view(torch.int16), w.k_pool.view(torch.int16))
+    r = run_oracle(w, pol, msel)
+    used = w.page_table[w.page_table >= 0].long()
+    assert np.array_equal(workloads.bits(summ_h.cpu()[used]), r.summ[used.numpy()])
+    assert np.array_equal(cnt_h.numpy(), r.cnt) and np.array_equal(sel_h.numpy(), r.sel)
+    assert np.abs(out_h.numpy().astype(np.float64) - r.out).max() <= OUT_TOL
 
 
 def test_host_tier_quantised_pages_match_device_pools():

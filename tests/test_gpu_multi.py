@@ -117,3 +117,8 @@ def test_multi_step_many_units_prologue_append(nq, kw):
 def test_multi_step_drafts_differ():
     gout, ref = _run("llama8b_b32_32k", 2, 3, 700, 500, seed=37)
     assert np.abs(gout[:, 0] - gout[:, 2]).max() > 1e-3
+
+
+def test_multi_step_large_selection():
+    # 32 x 8 units (one kernel per unit), 2 drafts, about 530 pages selected per unit: more than 64 per wave
+    _run("llama8b_b32_32k", 32, 2, 9000, 8700, top_k=520)

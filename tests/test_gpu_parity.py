@@ -2,8 +2,8 @@
 
 Bar: summaries and selected page ids bit-exact, every fp32 score within its
 own error bound of the exact score, attention outputs within 5e-3 max-abs.
-Small cases run the oracle on everything; full-size workloads run the oracle
-on sampled sequences and check size-independent properties on the rest.
+Small cases and the full-size workloads alike run the oracle on every
+sequence (the full sizes in chunks of sequences re-packed into small pools).
 """
 import numpy as np
 import pytest
@@ -14,17 +14,11 @@ from query_aware_sparse_paged_amd import api, workloads
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from gpu_cases import DEV, compare, gpu_summaries_of, run_gpu, run_oracle
+    from gpu_cases import DEV, check_every_sequence, compare, run_gpu, run_oracle
 
 
 def _small(name, **kw):
     return workloads.make(name, device="cpu", **kw)
-
-
-def _check_full(w, g, seqs):
-    r = run_oracle(w, api.policy_of(w), g.max_sel, seqs=seqs)
-    assert np.array_equal(gpu_summaries_of(g, w, seqs, r), r.summ), "summaries differ"
-    return compare(g, r, seqs=seqs, what=w.spec.name)
 
 
 # ----------------------------------------------------------------------------
@@ -218,6 +212,26 @@ def test_single_kernel_step_matches_oracle_and_kernel_chain(name, kw):
     assert np.abs(out.cpu().numpy() - g.out).max() <= 1e-5
 
 
+@pytest.mark.parametrize("batch,seq_len,top_k", [
+    (32, 9000, 520),      # 529 pages per unit: more than 64 per wave of the one-kernel step
+    (32, 8500, 100000),   # every page of every unit selected (about 530)
+    (3, 9000, 520),       # the kernel chain
+])
+def test_large_selections(batch, seq_len, top_k):
+    """Selections of more than 512 pages (64 per wave of an 8-wave block): each
+    wave walks its list in chunks of 64 pages."""
+    print("large selections", batch, seq_len, top_k, flush=True)
+    w = workloads.make("llama8b_b32_32k", device=DEV, batch=batch, seq_len=seq_len, seq_len_min=seq_len - 300)
+    pol = api.Policy(1, 8, top_k)
+    g = run_gpu(w, pol=pol)
+    P = (w.seq_lens.cpu().numpy() + 15) // 16
+    assert (g.cnt == np.minimum(P, 1 + 8 + top_k)[:, None]).all() and g.cnt.min() > 512
+    check_every_sequence(w, g, pol=pol, what="large selections")
+    del w, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("batch", [32, 3])   # one-kernel step; kernel chain
 @pytest.mark.parametrize("local,boost", [(None, 1.0), (0, 6.0)])
 def test_step_appends(batch, local, boost):
@@ -292,7 +306,8 @@ def test_repeated_calls_are_deterministic(batch):
 
 
 # ----------------------------------------------------------------------------
-# full-size workloads: sampled sequences against the oracle
+# full-size workloads: the oracle on every sequence (chunks re-packed into
+# small pools), in the launch configuration the benchmark times
 # ----------------------------------------------------------------------------
 
 def _free():
@@ -301,34 +316,36 @@ def _free():
 
 
 def test_full_llama8b_b32_32k():
+    print("full llama8b_b32_32k", flush=True)
     w = workloads.make("llama8b_b32_32k", device=DEV)
     g = run_gpu(w)
     assert (g.cnt == 128).all()
     assert (np.diff(g.sel, axis=2) > 0).all()
-    _check_full(w, g, [0, 17, 31])
+    check_every_sequence(w, g, what="llama8b_b32_32k")
     del w, g
     _free()
 
 
 def test_full_needle_b8_128k():
+    print("full needle_b8_128k", flush=True)
     w = workloads.make("needle_b8_128k", device=DEV)
-    g = run_gpu(w, with_scores=False)
+    g = run_gpu(w)
     assert (g.cnt == 256).all()
     for b in range(8):
         pages = set((w.needle_pos[b] // 16).tolist())
         for h in range(8):
             assert pages <= set(g.sel[b, h].tolist())
-    _check_full(w, g, [5])
+    check_every_sequence(w, g, chunk=1, what="needle_b8_128k")
     del w, g
     _free()
 
 
 def test_full_ragged_b64_mixed():
+    print("full ragged_b64_mixed", flush=True)
     w = workloads.make("ragged_b64_mixed", device=DEV)
-    g = run_gpu(w, with_scores=False)
+    g = run_gpu(w)
     assert (g.cnt[:, 4:] == 64).all()
     assert ((g.cnt[:, :4] >= 65) & (g.cnt[:, :4] <= 66)).all()
-    lens = w.seq_lens.cpu().numpy()
-    _check_full(w, g, [int(np.argmin(lens)), int(np.argmax(lens)), 7])
+    check_every_sequence(w, g, what="ragged_b64_mixed")
     del w, g
     _free()

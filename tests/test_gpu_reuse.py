@@ -3,8 +3,9 @@ appends its token and attends over the pages that an earlier layer selected
 at the same step, with no scoring or selection of its own (the OmniKV /
 DeltaKV family named in the SparseEngine article's decode-hook paragraph).
 
-Oracle: this layer's pools with the token written, attention over the given
-selection (oracle.attend), summaries from scratch (oracle.summaries).  Bar:
+Oracle: the selecting layer's selection (oracle.scores / select, compared
+with the GPU's), this layer's pools with the token written, attention over
+that selection (oracle.attend), summaries from scratch (oracle.summaries).  Bar:
 pools and summaries bit-exact, outputs within 5e-3 max-abs, the selection
 left untouched."""
 import numpy as np
@@ -17,16 +18,18 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import oracle
-    from gpu_cases import DEV, OUT_TOL, olayout, opolicy
+    from gpu_cases import DEV, OUT_TOL, olayout, opolicy, run_oracle
 
 
-def _case(name, batch):
+def _case(name, batch, big=False):
     """Layer A and layer B share the page table, the lengths and the pool
     size (a pool's size follows the lengths it was drawn for, so B's pools are
     built from A's shape); B's contents differ: keys with their channels
     reversed, values negated (exact in bf16), its own queries."""
     if name.startswith("mla"):
         kw = dict(batch=batch, seq_len=6000, seq_len_min=4000)
+    elif big:
+        kw = dict(batch=batch, seq_len=9000, seq_len_min=8700)
     else:
         kw = dict(batch=batch, seq_len=900, seq_len_min=600)
     a = workloads.make(name, device="cpu", seed=11, **kw)   # the layer that selects
@@ -37,13 +40,17 @@ def _case(name, batch):
     return a, b
 
 
-@pytest.mark.parametrize("name,batch", [("llama8b_b32_32k", 32),   # one kernel per (sequence, KV head)
-                                        ("llama8b_b32_32k", 3),    # append + decode kernels
-                                        ("mla_b16_64k", 2)])
+@pytest.mark.parametrize("name,batch,top_k", [("llama8b_b32_32k", 32, None),   # one kernel per (sequence, KV head)
+                                              ("llama8b_b32_32k", 3, None),    # append + decode kernels
+                                              ("llama8b_b32_32k", 32, 530),    # > 512 pages per unit, one kernel
+                                              ("mla_b16_64k", 2, None)])
 @pytest.mark.parametrize("with_summ", [True, False])
-def test_reuse_step(name, batch, with_summ):
-    A, B = _case(name, batch)
+def test_reuse_step(name, batch, top_k, with_summ):
+    print("reuse case", name, batch, top_k, with_summ, flush=True)
+    A, B = _case(name, batch, big=top_k is not None)
     lay, pol = api.layout_of(A), api.policy_of(A)
+    if top_k is not None:
+        pol = api.Policy(pol.n_sink_pages, pol.n_local_pages, top_k)
     Hq = A.spec.num_q_heads
     pt, sl = A.page_table, A.seq_lens                # shared page table and lengths
     assert int(pt.max()) < B.k_pool.shape[0] == A.k_pool.shape[0]
@@ -63,6 +70,10 @@ def test_reuse_step(name, batch, with_summ):
                     v_new=t(A.v_new), sel=sel, sel_count=cnt)
     torch.cuda.synchronize()
     sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+    # the selection layer B reuses is the oracle's (the token A appends is the
+    # value already at L-1, so A's pools and summaries are unchanged)
+    ra = run_oracle(A, pol, msel)
+    assert np.array_equal(cnt_np, ra.cnt) and np.array_equal(sel_np, ra.sel)
 
     # layer B: a new token (not yet in its pools), its summaries before the token
     gen = torch.Generator().manual_seed(3)
@@ -93,7 +104,7 @@ def test_reuse_step(name, batch, with_summ):
     pt_np, sl_np = pt.numpy(), sl.numpy()
     kbits = workloads.bits(B.k_pool)
     vbits = None if B.v_pool is None else workloads.bits(B.v_pool)
-    ref = oracle.attend(olay, pt_np, sl_np, workloads.bits(B.q), kbits, vbits, sel_np, cnt_np, opol, B.scale)
+    ref = oracle.attend(olay, pt_np, sl_np, workloads.bits(B.q), kbits, vbits, ra.sel, ra.cnt, opol, B.scale)
     gout = out.cpu().numpy()
     assert np.isfinite(gout).all()
     assert np.abs(gout.astype(np.float64) - ref).max() <= OUT_TOL
@@ -102,3 +113,5 @@ def test_reuse_step(name, batch, with_summ):
         used = pt[pt >= 0].long()
         assert np.array_equal(workloads.bits(summ_b.cpu()[used]), rs[used.numpy()])
     assert (cnt_np > 0).all()
+    if top_k is not None:
+        assert cnt_np.min() > 512
