@@ -65,9 +65,11 @@ typedef enum {
     QASP_ERR_MAX_SEL = -5,         /* max_sel below qasp_max_sel             */
     QASP_ERR_LAUNCH = -6,          /* a HIP launch failed                     */
     QASP_ERR_ALLOC = -7,           /* a host-tier allocation failed           */
-    QASP_ERR_BAD_PAGE_TABLE = -8   /* validate mode / qasp_check_batch: a length,
+    QASP_ERR_BAD_PAGE_TABLE = -8,  /* validate mode / qasp_check_batch: a length,
                                       page-table entry or selected id is out
                                       of range                                */
+    QASP_ERR_SCRATCH = -9          /* qasp_decode_step_noalloc: the call needs
+                                      more than qasp_scratch_bytes()          */
 } qasp_status;
 
 /* Pool layout (row-major, bf16):
@@ -250,6 +252,25 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat,
                          float scale, float *out, int32_t *sel, int32_t *sel_count,
                          int32_t max_sel, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/* qasp_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is a static array of
+ * qasp_scratch_bytes() bytes (32 MiB) that the library holds on each GPU it
+ * runs on until the process ends; the call allocates nothing.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap in time on one GPU
+ * (other streams, other host threads) race and must not be issued; the array
+ * keeps the last call's contents (nothing in it needs to start at zero).
+ * Arguments, results and errors as qasp_decode_step, plus QASP_ERR_SCRATCH
+ * (with nothing enqueued) when qasp_workspace_bytes for these arguments
+ * exceeds qasp_scratch_bytes(). */
+size_t qasp_scratch_bytes(void);
+int32_t qasp_decode_step_noalloc(const qasp_layout *lay, const qasp_batch *bat,
+                                 const qasp_policy *pol, const uint16_t *q,
+                                 const uint16_t *k_new, const uint16_t *v_new,
+                                 uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ,
+                                 float scale, float *out, int32_t *sel,
+                                 int32_t *sel_count, int32_t max_sel, void *stream);
 
 /* One decode step of a layer that reuses the page selection of an earlier
  * layer at the same step (cross-layer selection reuse: the OmniKV / DeltaKV

@@ -22,7 +22,7 @@ LIB_PATH = os.environ.get("QASP_LIB") or os.path.join(_HERE, "libqasp.so")
 
 OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MAX_SEL, ERR_LAUNCH, ERR_ALLOC = \
     0, -1, -2, -3, -4, -5, -6, -7
-ERR_BAD_PAGE_TABLE = -8
+ERR_BAD_PAGE_TABLE, ERR_SCRATCH = -8, -9
 
 
 class QaspError(RuntimeError):
@@ -64,6 +64,9 @@ EXPORTS = {
                                                                            ctypes.c_size_t, ctypes.c_void_p]),
     "qasp_decode_step": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 3 +
                          [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qasp_scratch_bytes": (ctypes.c_size_t, []),
+    "qasp_decode_step_noalloc": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 3 +
+                                 [ctypes.c_int32, ctypes.c_void_p]),
     "qasp_decode_step_reuse": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 2 +
                                [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p]),
@@ -355,12 +358,13 @@ def sparse_paged_decode(layout: Layout, batch: Batch, policy: Policy, q, k_pool,
 
 
 def _step_specs(layout: Layout, batch: Batch, q, out, k_pool, v_pool, summ, k_new, v_new, sel, sel_count,
-                max_sel_n, workspace, n_query=None):
+                max_sel_n, workspace, n_query=None, with_workspace=True):
     if sel is not None and int(max_sel_n) != sel.shape[-1]:
         raise ValueError("max_sel_n (%d) disagrees with sel's last dimension (%d)" % (max_sel_n, sel.shape[-1]))
-    return [*batch.specs(), *_query_specs(layout, batch, q, out, n_query), *_pool_specs(layout, k_pool, v_pool, summ),
-            *_token_specs(layout, batch.batch, k_new, v_new, n_query),
-            *_sel_specs(layout, batch, sel, sel_count, int(max_sel_n)), _ws_spec(workspace)]
+    specs = [*batch.specs(), *_query_specs(layout, batch, q, out, n_query), *_pool_specs(layout, k_pool, v_pool, summ),
+             *_token_specs(layout, batch.batch, k_new, v_new, n_query),
+             *_sel_specs(layout, batch, sel, sel_count, int(max_sel_n))]
+    return specs + [_ws_spec(workspace)] if with_workspace else specs
 
 
 def decode_step(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, summ, scale: float,
@@ -375,6 +379,26 @@ def decode_step(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool,
                                   _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(summ),
                                   float(scale), _ptr(out), _ptr(sel), _ptr(sel_count), int(max_sel_n),
                                   _ptr(workspace), workspace.numel(), _stream()), "qasp_decode_step")
+    return out
+
+
+def scratch_bytes() -> int:
+    """Size of the library's static per-device workspace (decode_step_noalloc)."""
+    return int(lib().qasp_scratch_bytes())
+
+
+def decode_step_noalloc(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool, summ, scale: float,
+                        max_sel_n: int, k_new=None, v_new=None, out=None, sel=None, sel_count=None) -> torch.Tensor:
+    """decode_step with the library's static per-device workspace instead of a
+    caller's: the library call allocates nothing (out is allocated here when
+    not given).  Calls that overlap in time on one GPU race."""
+    out = _new_out(layout, batch, q) if out is None else out
+    _check_args(*_step_specs(layout, batch, q, out, k_pool, v_pool, summ, k_new, v_new, sel, sel_count, max_sel_n,
+                             None, with_workspace=False))
+    _check(lib().qasp_decode_step_noalloc(ctypes.byref(layout.c()), ctypes.byref(batch.c()),
+                                          ctypes.byref(policy.c()), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                          _ptr(v_pool), _ptr(summ), float(scale), _ptr(out), _ptr(sel),
+                                          _ptr(sel_count), int(max_sel_n), _stream()), "qasp_decode_step_noalloc")
     return out
 
 

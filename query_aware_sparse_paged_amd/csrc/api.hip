@@ -2,6 +2,8 @@
 // call), workspace layout and launch order.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -210,6 +212,7 @@ const char *qasp_status_string(int32_t status) {
     case QASP_ERR_LAUNCH: return "HIP kernel launch failed";
     case QASP_ERR_ALLOC: return "host-tier allocation failed";
     case QASP_ERR_BAD_PAGE_TABLE: return "a sequence length, page-table entry or selected page is out of range";
+    case QASP_ERR_SCRATCH: return "the call needs more workspace than the library's static scratch buffer holds";
     default: return "unknown status";
   }
 }
@@ -307,11 +310,16 @@ int32_t qasp_sparse_paged_decode(const qasp_layout *lay, const qasp_batch *bat, 
                                         out, ws, (hipStream_t)stream));
 }
 
-int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
-                         const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
-                         uint16_t *v_pool, uint16_t *summ, float scale, float *out, int32_t *sel,
-                         int32_t *sel_count, int32_t max_sel, void *workspace, size_t workspace_bytes_given,
-                         void *stream) {
+}  // extern "C"
+
+namespace qasp {
+
+// Checks of qasp_decode_step's arguments other than the workspace (shared
+// with its no-allocation form).
+static int32_t check_step_args(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                               const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                               const uint16_t *k_pool, const uint16_t *v_pool, const uint16_t *summ, const float *out,
+                               const int32_t *sel, const int32_t *sel_count, int32_t max_sel) {
   int32_t rc = check_layout(lay);
   if (rc != QASP_OK) return rc;
   if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
@@ -319,37 +327,98 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
   if (max_sel < 0) return QASP_ERR_BAD_SHAPE;
   if (max_sel < max_sel_of(*lay, *pol, bat->max_pages)) return QASP_ERR_MAX_SEL;
   if (bat->batch == 0) return QASP_OK;
-  if (!q || !k_pool || !out || !workspace) return QASP_ERR_NULL_ARG;
+  if (!q || !k_pool || !out) return QASP_ERR_NULL_ARG;
   if (!lay->v_from_k && !v_pool) return QASP_ERR_NULL_ARG;
-  const bool scored = !all_static(*lay, *pol);
-  if (scored && !summ) return QASP_ERR_NULL_ARG;
+  if (!all_static(*lay, *pol) && !summ) return QASP_ERR_NULL_ARG;
   if (k_new && !lay->v_from_k && !v_new) return QASP_ERR_NULL_ARG;
   if ((sel == nullptr) != (sel_count == nullptr)) return QASP_ERR_NULL_ARG;
-  if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
-  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
-  hipStream_t s = (hipStream_t)stream;
+  return QASP_OK;
+}
+
+// The step's launches once every argument has been checked; workspace holds
+// workspace_bytes(lay, bat, max_sel) bytes.
+static int32_t run_step(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol, const uint16_t *q,
+                        const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool,
+                        uint16_t *summ, float scale, float *out, int32_t *sel, int32_t *sel_count, int32_t max_sel,
+                        void *workspace, hipStream_t s) {
+  const bool scored = !all_static(lay, pol);
   // many units: the whole step as one kernel per (sequence, KV head) block
-  const long units = (long)bat->batch * lay->num_kv_heads;
-  if (family_of(*lay) == kFamilyGqa && units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages &&
-      fused_lds_bytes(*lay, *bat, max_sel) <= 160 * 1024)
-    return status_of(launch_fused_step_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out,
-                                           sel, sel_count, max_sel, s));
-  const Workspace ws = carve_workspace(*lay, *bat, max_sel, workspace);
+  const long units = (long)bat.batch * lay.num_kv_heads;
+  if (family_of(lay) == kFamilyGqa && units >= kFusedMinUnits && bat.max_pages <= kFusedMaxPages &&
+      fused_lds_bytes(lay, bat, max_sel) <= 160 * 1024)
+    return status_of(launch_fused_step_gqa(lay, bat, pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel,
+                                           sel_count, max_sel, s));
+  const Workspace ws = carve_workspace(lay, bat, max_sel, workspace);
   int32_t *sel_out = sel ? sel : ws.sel;
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   hipError_t e = hipSuccess;
   // the scoring kernel appends the token when its page is no candidate (a local
   // page); otherwise the append runs first, so the page is scored with it
-  const bool fold_append = k_new && scored && pol->n_local_pages >= 1;
-  if (k_new && !fold_append) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
+  const bool fold_append = k_new && scored && pol.n_local_pages >= 1;
+  if (k_new && !fold_append) e = launch_append_kv(lay, bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
   if (e == hipSuccess && scored)
-    e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s,
-                           token_append(*lay, fold_append ? k_new : nullptr, v_new, k_pool, v_pool, summ));
+    e = launch_score_pages(lay, bat, pol, q, summ, ws.scores, s,
+                           token_append(lay, fold_append ? k_new : nullptr, v_new, k_pool, v_pool, summ));
+  if (e == hipSuccess) e = launch_select_topk(lay, bat, pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
   if (e == hipSuccess)
-    e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
-  if (e == hipSuccess)
-    e = launch_sparse_decode(*lay, *bat, *pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
+    e = launch_sparse_decode(lay, bat, pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
   return status_of(e);
+}
+
+// The no-allocation form's workspace: one static array per device (each GPU
+// the library runs on holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: the device address of each
+// GPU's copy is looked up once, with that device current, and kept.
+constexpr size_t kScratchBytes = (size_t)QASP_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static void *scratch_on_current_device() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *ptrs[kMaxDevices] = {nullptr};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+}  // namespace qasp
+
+extern "C" {
+
+int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                         const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                         uint16_t *v_pool, uint16_t *summ, float scale, float *out, int32_t *sel,
+                         int32_t *sel_count, int32_t max_sel, void *workspace, size_t workspace_bytes_given,
+                         void *stream) {
+  int32_t rc = check_step_args(lay, bat, pol, q, k_new, v_new, k_pool, v_pool, summ, out, sel, sel_count, max_sel);
+  if (rc != QASP_OK || bat->batch == 0) return rc;
+  if (!workspace) return QASP_ERR_NULL_ARG;
+  if (workspace_bytes_given < workspace_bytes(*lay, *bat, max_sel)) return QASP_ERR_WORKSPACE;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
+  return run_step(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel, sel_count, max_sel,
+                  workspace, (hipStream_t)stream);
+}
+
+size_t qasp_scratch_bytes(void) { return kScratchBytes; }
+
+int32_t qasp_decode_step_noalloc(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                                 const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                                 uint16_t *v_pool, uint16_t *summ, float scale, float *out, int32_t *sel,
+                                 int32_t *sel_count, int32_t max_sel, void *stream) {
+  int32_t rc = check_step_args(lay, bat, pol, q, k_new, v_new, k_pool, v_pool, summ, out, sel, sel_count, max_sel);
+  if (rc != QASP_OK || bat->batch == 0) return rc;
+  if (workspace_bytes(*lay, *bat, max_sel) > kScratchBytes) return QASP_ERR_SCRATCH;
+  void *ws = scratch_on_current_device();
+  if (ws == nullptr) return QASP_ERR_LAUNCH;
+  if ((rc = maybe_validate(*lay, *bat, stream)) != QASP_OK) return rc;
+  return run_step(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel, sel_count, max_sel, ws,
+                  (hipStream_t)stream);
 }
 
 int32_t qasp_check_batch(const qasp_layout *lay, const qasp_batch *bat, int32_t extra_tokens, const int32_t *sel,

@@ -23,6 +23,10 @@ constexpr int kGqaTargetBlocks = QASP_GQA_TARGET_BLOCKS; // split units until th
 #define QASP_MLA_PAGES_PER_SPLIT 8
 #endif
 constexpr int kMlaPagesPerSplit = QASP_MLA_PAGES_PER_SPLIT;  // selected pages per latent-head decode block
+// Size of the static per-device workspace of qasp_decode_step_noalloc.
+#ifndef QASP_SCRATCH_BYTES
+#define QASP_SCRATCH_BYTES (32u << 20)
+#endif
 
 struct Workspace {
   qasp_score *scores;   // [B][Hkv][max_pages]

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     assert re.match(r"^\d+\.\d+\.\d+$", api.version())
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert api.status_string(s) != "unknown status"
     assert "page-table" in api.status_string(api.ERR_BAD_PAGE_TABLE)
     assert api.status_string(-99) == "unknown status"
@@ -374,3 +374,25 @@ def test_validate_mode_keeps_host_checks_first(L, monkeypatch):
     assert _call("qasp_sparse_paged_decode", b(lay), b(bat), b(pol), 1, 1, 1, 1, 1, 37, 1.0, 1, 1,
                  1, None) == api.ERR_WORKSPACE
     assert _call("qasp_build_summaries", b(lay), b(bat), None, 1, None) == api.ERR_NULL_ARG
+
+
+def test_noalloc_step_rejects_sizes_beyond_its_scratch(L):
+    """qasp_decode_step_noalloc refuses, before any HIP call, a call whose
+    workspace would not fit the static scratch buffer."""
+    b = ctypes.byref
+    lay, pol = GQA.c(), api.Policy(1, 4, 32).c()
+    limit = api.scratch_bytes()
+    assert limit == 32 << 20
+    small = _batch()
+    assert _call("qasp_workspace_bytes", b(lay), b(small), b(pol), 37) <= limit
+    # 4000 sequences x 8 KV heads x 4097 pages of 16-byte score records: far beyond the scratch
+    big = _batch(B=4000, stride=4097, max_pages=4097)
+    assert _call("qasp_workspace_bytes", b(lay), b(big), b(pol), 37) > limit
+    assert _call("qasp_decode_step_noalloc", b(lay), b(big), b(pol), 1, None, None, 1, 1, 1, 1.0, 1, None, None,
+                 37, None) == api.ERR_SCRATCH
+    assert "scratch" in api.status_string(api.ERR_SCRATCH)
+    # the other argument errors as qasp_decode_step
+    assert _call("qasp_decode_step_noalloc", b(lay), b(small), b(pol), 1, None, None, 1, 1, 1, 1.0, 1, None, None,
+                 36, None) == api.ERR_MAX_SEL
+    assert _call("qasp_decode_step_noalloc", b(lay), b(small), b(pol), None, None, None, 1, 1, 1, 1.0, 1, None,
+                 None, 37, None) == api.ERR_NULL_ARG
