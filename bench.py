@@ -92,21 +92,47 @@ def step_bytes(w, msel_counts):
     return score, decode
 
 
-def cpu_baseline(w, msel, n_seqs, threads):
-    """The CPU oracle (test infrastructure) timed on a bounded sample of the
-    workload: the first n_seqs sequences, all KV heads, over precomputed
-    summaries (scores + selection + attention)."""
+def cpu_info():
+    """(CPU model, nproc, CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    nproc = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = nproc
+    return model, nproc, usable
+
+
+def oracle_threads(usable):
+    """All usable CPUs, capped by OMP_NUM_THREADS when it is set."""
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return max(1, min(usable, cap) if cap > 0 else usable)
+
+
+def _oracle_inputs(w, seqs):
+    """The sequences' pages re-packed into a small host pool (bit patterns),
+    their summaries computed by the oracle (not timed)."""
     import numpy as np
     import oracle
     from query_aware_sparse_paged_amd import workloads
 
     s = w.spec
-    seqs = list(range(min(n_seqs, s.batch)))
     pt_full = w.page_table[seqs]
     valid = pt_full >= 0
     phys = pt_full[valid].long()
-    k = workloads.bits(w.k_pool[phys])
-    v = None if w.v_pool is None else workloads.bits(w.v_pool[phys])
+    k = workloads.bits(w.k_pool[phys.to(w.k_pool.device)])
+    v = None if w.v_pool is None else workloads.bits(w.v_pool[phys.to(w.v_pool.device)])
     pt = np.full(tuple(pt_full.shape), -1, np.int32)
     pt[valid.cpu().numpy()] = np.arange(phys.numel(), dtype=np.int32)
     sl = w.seq_lens[seqs].cpu().numpy()
@@ -114,17 +140,76 @@ def cpu_baseline(w, msel, n_seqs, threads):
     lay = oracle.Layout(int(phys.numel()), s.page_size, s.num_kv_heads, s.head_dim_k, s.head_dim_v, s.v_from_k)
     pol = oracle.Policy(s.n_sink_pages, s.n_local_pages, s.top_k, s.sink_tokens, s.window_tokens, s.static_heads)
     summ = oracle.summaries(lay, pt, sl, s.num_q_heads, k)
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - t_start < 1.0 and len(times) < 50):
+    return lay, pol, pt, sl, q, k, v, summ
+
+
+def _time_oracle(w, inputs, msel, threads, runs=3):
+    """Median wall time of the oracle's decode step (scores + selection +
+    attention over the precomputed summaries) and its selection counts."""
+    import oracle
+    lay, pol, pt, sl, q, k, v, summ = inputs
+    times, cnt = [], None
+    for _ in range(runs):
         t0 = time.perf_counter()
-        oracle.decode(lay, pt, sl, q, k, v, summ, pol, w.scale, num_threads=threads, max_sel_n=msel)
+        _, _, cnt = oracle.decode(lay, pt, sl, q, k, v, summ, pol, w.scale, num_threads=threads, max_sel_n=msel)
         times.append(time.perf_counter() - t0)
-    dt = statistics.median(times)
-    return {"value": len(seqs) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d sequences (all %d KV heads), one decode step over precomputed summaries; "
-                      "median of %d runs, %.3f s wall each, %.1f s total" % (
-                          len(seqs), s.batch, s.num_kv_heads, len(times), dt, sum(times))}
+    return statistics.median(times), cnt
+
+
+def cpu_baseline(w, msel, one_thread_seqs=4):
+    """The CPU oracle (test infrastructure), timed on this machine's host CPUs
+    over the whole workload (every sequence and KV head, one decode step over
+    precomputed summaries), with all usable CPUs and with one thread on a
+    bounded sample; and the tiny one-sequence workload at both thread counts.
+    Rates are tokens/s and GB/s over the same algorithmic bytes as the GPU
+    figure."""
+    from query_aware_sparse_paged_amd import workloads
+
+    model, nproc, usable = cpu_info()
+    threads = oracle_threads(usable)
+    s = w.spec
+    t_all = time.perf_counter()
+    seqs = list(range(s.batch))
+    inp = _oracle_inputs(w, seqs)
+    msel_all = msel
+    dt, cnt = _time_oracle(w, inp, msel_all, threads)
+    b_sc, b_dec = step_bytes(w, cnt.tolist())
+    one = {}
+    sub = list(range(min(one_thread_seqs, s.batch)))
+    inp1 = _oracle_inputs(w, sub)
+    dt1, cnt1 = _time_oracle(w, inp1, msel_all, 1)
+    b1 = sum(step_bytes_of(w, sub, cnt1.tolist()))
+    one[s.name] = {"tokens_per_s": round(len(sub) / dt1, 2), "gbps": round(b1 / dt1 / 1e9, 3),
+                   "sample": "%d of %d sequences" % (len(sub), s.batch)}
+    tiny = workloads.make("tiny_b1_4k", device="cpu")
+    from query_aware_sparse_paged_amd import api
+    tmsel = api.max_sel(api.layout_of(tiny), api.policy_of(tiny), tiny.max_pages)
+    tin = _oracle_inputs(tiny, [0])
+    tiny_rates = {}
+    for n in (1, threads):
+        tdt, tcnt = _time_oracle(tiny, tin, tmsel, n, runs=5)
+        tb = sum(step_bytes(tiny, tcnt.tolist()))
+        tiny_rates[n] = (round(1 / tdt, 2), round(tb / tdt / 1e9, 3))
+    one["tiny_b1_4k"] = {"tokens_per_s": tiny_rates[1][0], "gbps": tiny_rates[1][1], "sample": "the whole workload"}
+    total_s = time.perf_counter() - t_all
+    return {"value": round(s.batch / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole workload (%d sequences, all %d KV heads): one decode step over precomputed "
+                      "summaries, median of 3 runs, %.3f s each; %d threads" % (s.batch, s.num_kv_heads, dt, threads),
+            "gbps": round((b_sc + b_dec) / dt / 1e9, 3),
+            "nproc": nproc, "usable_cpus": usable, "cpu_model": model,
+            "one_thread": one,
+            "tiny_b1_4k_all_threads": {"tokens_per_s": tiny_rates[threads][0], "gbps": tiny_rates[threads][1]},
+            "wall_s": round(total_s, 1)}
+
+
+def step_bytes_of(w, seqs, counts):
+    """step_bytes restricted to the sequences seqs (counts: their rows)."""
+    import copy
+    sub = copy.copy(w)
+    sub.spec = copy.copy(w.spec)
+    sub.spec.batch = len(seqs)
+    sub.seq_lens = w.seq_lens[seqs]
+    return step_bytes(sub, counts)
 
 
 def main():
@@ -134,7 +219,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=3, help="independent layer caches rotated over")
-    ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reuse", type=int, default=0,
                     help="cross-layer reuse: per group, 1 selecting layer + this many reusing layers")
@@ -236,8 +320,8 @@ def main():
     counts = layers[0]["cnt"].cpu().tolist()
     b_score, b_decode = step_bytes(w0, counts)
     total_bytes = b_score + b_decode
-    units = spec.batch * spec.num_kv_heads
-    one_kernel = units >= 200 and w0.max_pages <= 4096 and not spec.v_from_k
+    L0 = layers[0]
+    one_kernel = api.decode_step_path(L0["lay"], L0["bat"], L0["pol"], L0["msel"]) == api.PATH_ONE_KERNEL
     kernel = "fused_step_gqa_kernel" if one_kernel else "decode_step (several kernels)"
     dom_ms = med(step_ms)
     achieved = total_bytes / (dom_ms * 1e-3) / 1e9
@@ -249,9 +333,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(w0, layers[0]["msel"], args.cpu_seqs, threads)
-        log("cpu oracle: %s" % cpu["sample"])
+        cpu = cpu_baseline(w0, layers[0]["msel"])
+        log("cpu oracle: %s; %.1f s in all" % (cpu["sample"], cpu["wall_s"]))
 
     line = {
         "metric": METRIC if spec.name == DEFAULT_WORKLOAD else
@@ -272,15 +355,17 @@ def main():
                    "page_size": spec.page_size,
                    "pages_read": "%d sink + %d local + top-%d" % (spec.n_sink_pages, spec.n_local_pages, spec.top_k),
                    "layer_caches_rotated": args.layers},
-        "kv_gbps": round(gbps, 1),
-        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "kv_gbps_wall": round(gbps, 1),
         "step_bytes": total_bytes,
-        "step_us_events": {"median": round(dom_ms * 1e3, 2), "p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
+        "step_us_events": {"median": round(dom_ms * 1e3, 2), "mean": round(statistics.mean(step_ms) * 1e3, 2),
+                           "p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
                            "p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2)},
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(kernel, spec.name) if one_kernel else None,
-                     "algorithmic_bytes": total_bytes},
+                     "algorithmic_bytes": total_bytes,
+                     "timing": "median of %d HIP-event-bracketed launches on the launch stream (the kernel's "
+                               "duration, as a rocprofv3 kernel trace records it)" % len(step_ms)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

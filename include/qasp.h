@@ -253,6 +253,19 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat,
                          int32_t max_sel, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* Which kernels qasp_decode_step (and the multi-query and quantised steps,
+ * for their own batch shapes) launch for these arguments:
+ * QASP_PATH_ONE_KERNEL, the whole step as one kernel with a block per
+ * (sequence, KV head) (grouped-query layouts with at least 200 such units
+ * and a page list that fits the kernel's on-chip arrays), or
+ * QASP_PATH_CHAIN, the append / score / select / attend / merge kernels.
+ * Negative status for invalid arguments.  (For timing tools: which kernel a
+ * profile should show.) */
+#define QASP_PATH_ONE_KERNEL 1
+#define QASP_PATH_CHAIN 2
+int32_t qasp_decode_step_path(const qasp_layout *lay, const qasp_batch *bat,
+                              const qasp_policy *pol, int32_t max_sel);
+
 /* qasp_decode_step without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  The workspace is a static array of

@@ -65,6 +65,7 @@ EXPORTS = {
     "qasp_decode_step": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 3 +
                          [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "qasp_scratch_bytes": (ctypes.c_size_t, []),
+    "qasp_decode_step_path": (ctypes.c_int32, [ctypes.c_void_p] * 3 + [ctypes.c_int32]),
     "qasp_decode_step_noalloc": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 3 +
                                  [ctypes.c_int32, ctypes.c_void_p]),
     "qasp_decode_step_reuse": (ctypes.c_int32, [ctypes.c_void_p] * 9 + [ctypes.c_float] + [ctypes.c_void_p] * 2 +
@@ -380,6 +381,17 @@ def decode_step(layout: Layout, batch: Batch, policy: Policy, q, k_pool, v_pool,
                                   float(scale), _ptr(out), _ptr(sel), _ptr(sel_count), int(max_sel_n),
                                   _ptr(workspace), workspace.numel(), _stream()), "qasp_decode_step")
     return out
+
+
+PATH_ONE_KERNEL, PATH_CHAIN = 1, 2
+
+
+def decode_step_path(layout: Layout, batch: Batch, policy: Policy, max_sel_n: int) -> int:
+    """PATH_ONE_KERNEL or PATH_CHAIN: the kernels decode_step launches here."""
+    r = lib().qasp_decode_step_path(ctypes.byref(layout.c()), ctypes.byref(batch.c()), ctypes.byref(policy.c()),
+                                    int(max_sel_n))
+    _check(0 if r >= 0 else r, "qasp_decode_step_path")
+    return r
 
 
 def scratch_bytes() -> int:

@@ -162,6 +162,16 @@ static int32_t maybe_validate(const qasp_layout &lay, const qasp_batch &bat, voi
   return check_batch_on_device(lay, bat, extra_tokens, sel, sel_count, max_sel, (hipStream_t)stream);
 }
 
+// Whether a step runs as one kernel per (sequence, KV head) unit: grouped-query
+// layouts with enough units to give every CU a block, a page list that fits
+// the kernel's LDS arrays (bat: the batch as the kernel sees it, i.e. the
+// multi-query step's widened group).
+static bool one_kernel_step(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
+  const long units = (long)bat.batch * lay.num_kv_heads;
+  return family_of(lay) == kFamilyGqa && units >= kFusedMinUnits && bat.max_pages <= kFusedMaxPages &&
+         fused_lds_bytes(lay, bat, max_sel) <= 160 * 1024;
+}
+
 // Multi-query step: nq draft queries regrouped so that KV head g's group holds
 // G heads per draft query (num_q_heads * nq columns in all); a static head's
 // selection covers the union of the queries' windows (window + nq - 1 tokens
@@ -343,9 +353,7 @@ static int32_t run_step(const qasp_layout &lay, const qasp_batch &bat, const qas
                         void *workspace, hipStream_t s) {
   const bool scored = !all_static(lay, pol);
   // many units: the whole step as one kernel per (sequence, KV head) block
-  const long units = (long)bat.batch * lay.num_kv_heads;
-  if (family_of(lay) == kFamilyGqa && units >= kFusedMinUnits && bat.max_pages <= kFusedMaxPages &&
-      fused_lds_bytes(lay, bat, max_sel) <= 160 * 1024)
+  if (one_kernel_step(lay, bat, max_sel))
     return status_of(launch_fused_step_gqa(lay, bat, pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel,
                                            sel_count, max_sel, s));
   const Workspace ws = carve_workspace(lay, bat, max_sel, workspace);
@@ -406,6 +414,16 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat, const qa
 }
 
 size_t qasp_scratch_bytes(void) { return kScratchBytes; }
+
+int32_t qasp_decode_step_path(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
+                              int32_t max_sel) {
+  int32_t rc = check_layout(lay);
+  if (rc != QASP_OK) return rc;
+  if ((rc = check_batch(*lay, bat)) != QASP_OK) return rc;
+  if ((rc = check_policy(*lay, pol)) != QASP_OK) return rc;
+  if (max_sel < 0) return QASP_ERR_BAD_SHAPE;
+  return one_kernel_step(*lay, *bat, max_sel) ? QASP_PATH_ONE_KERNEL : QASP_PATH_CHAIN;
+}
 
 int32_t qasp_decode_step_noalloc(const qasp_layout *lay, const qasp_batch *bat, const qasp_policy *pol,
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
@@ -496,9 +514,7 @@ int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat, co
   int32_t *sel_out = sel ? sel : ws.sel;
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   hipError_t e = hipSuccess;
-  const long units = (long)bat->batch * lay->num_kv_heads;
-  if (units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages &&
-      fused_lds_bytes(*lay, *bat, max_sel) <= 160 * 1024) {
+  if (one_kernel_step(*lay, *bat, max_sel)) {
     // many units: append, score and select in the one-kernel step's selection-only form
     e = launch_fused_step_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel_out, cnt_out,
                               max_sel, s, 1, 0, true);
@@ -562,8 +578,7 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat, co
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   // many units: one kernel per (sequence, KV head) appends the drafts, stages
   // the query rows in the grouped order, scores, selects and attends
-  const long units = (long)bat->batch * lay->num_kv_heads;
-  if (units >= kFusedMinUnits && bat->max_pages <= kFusedMaxPages && fused_lds_bytes(*lay, wbat, max_sel) <= 160 * 1024)
+  if (one_kernel_step(*lay, wbat, max_sel))
     return status_of(launch_fused_step_gqa(*lay, wbat, wpol, q, nullptr, nullptr, k_pool, v_pool, summ, scale, out,
                                            sel, sel_count, max_sel, s, nq, pol->window_tokens, false, k_new, v_new));
   // q [B][nq][Hkv][G][Dk] -> [B][Hkv][nq][G][Dk], and the drafts appended

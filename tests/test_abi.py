@@ -396,3 +396,24 @@ def test_noalloc_step_rejects_sizes_beyond_its_scratch(L):
                  36, None) == api.ERR_MAX_SEL
     assert _call("qasp_decode_step_noalloc", b(lay), b(small), b(pol), None, None, None, 1, 1, 1, 1.0, 1, None,
                  None, 37, None) == api.ERR_NULL_ARG
+
+
+def test_decode_step_path(L):
+    """The library's own dispatch rule, as the benchmark reads it."""
+    pol = api.Policy(1, 8, 119)
+    b = lambda B, mp: api.CBatch(B, 32, mp + 1, mp, 0x1000, 0x2000)
+    path = lambda lay, bat, p, msel: _call("qasp_decode_step_path", ctypes.byref(lay.c()), ctypes.byref(bat),
+                                           ctypes.byref(p.c()), msel)
+    big = api.Layout(131072, 16, 8, 128, 128)
+    assert path(big, b(32, 2048), pol, 128) == api.PATH_ONE_KERNEL      # 32K x 32: 256 units
+    assert path(big, b(25, 2048), pol, 128) == api.PATH_ONE_KERNEL      # 200 units
+    assert path(big, b(24, 2048), pol, 128) == api.PATH_CHAIN           # 192 units
+    assert path(big, b(8, 8192), pol, 256) == api.PATH_CHAIN            # needle: 64 units, 8192 pages
+    assert path(big, b(64, 4097), pol, 128) == api.PATH_CHAIN           # page list past the kernel's arrays
+    assert path(big, b(64, 4096), pol, 4096) == api.PATH_ONE_KERNEL     # 98 KB of on-chip arrays
+    # 16 heads per group: the merge area grows, and with every page selected the arrays pass 160 KB
+    assert path(big, api.CBatch(64, 128, 4097, 4096, 0x1000, 0x2000), pol, 4096) == api.PATH_CHAIN
+    assert path(big, api.CBatch(64, 128, 4097, 4096, 0x1000, 0x2000), pol, 128) == api.PATH_ONE_KERNEL
+    mla = api.Layout(32768, 64, 1, 576, 512, True)
+    assert path(mla, api.CBatch(256, 128, 1025, 1024, 0x1000, 0x2000), pol, 32) == api.PATH_CHAIN
+    assert path(big, b(32, 2048), pol, -1) == api.ERR_BAD_SHAPE
