@@ -163,13 +163,17 @@ static int32_t maybe_validate(const qasp_layout &lay, const qasp_batch &bat, voi
 }
 
 // Whether a step runs as one kernel per (sequence, KV head) unit: grouped-query
-// layouts with enough units to give every CU a block, a page list that fits
-// the kernel's LDS arrays (bat: the batch as the kernel sees it, i.e. the
-// multi-query step's widened group).
+// layouts whose page list fits the kernel's LDS arrays, with either enough
+// units to give every CU a block or so little work per unit (summaries of
+// every page plus the K/V tiles of a full selection) that one CU per unit
+// beats a chain of kernels, each with its own launch and drain (bat: the
+// batch as the kernel sees it, i.e. the multi-query step's widened group).
 static bool one_kernel_step(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
   const long units = (long)bat.batch * lay.num_kv_heads;
-  return family_of(lay) == kFamilyGqa && units >= kFusedMinUnits && bat.max_pages <= kFusedMaxPages &&
-         fused_lds_bytes(lay, bat, max_sel) <= 160 * 1024;
+  const size_t unit_bytes = (size_t)bat.max_pages * 2 * lay.head_dim_k * 2 +
+                            (size_t)max_sel * lay.page_size * (lay.head_dim_k + lay.head_dim_v) * 2;
+  return family_of(lay) == kFamilyGqa && (units >= kFusedMinUnits || unit_bytes <= kFusedSmallUnitBytes) &&
+         bat.max_pages <= kFusedMaxPages && fused_lds_bytes(lay, bat, max_sel) <= 160 * 1024;
 }
 
 // Multi-query step: nq draft queries regrouped so that KV head g's group holds
@@ -367,6 +371,10 @@ static int32_t run_step(const qasp_layout &lay, const qasp_batch &bat, const qas
   if (e == hipSuccess && scored)
     e = launch_score_pages(lay, bat, pol, q, summ, ws.scores, s,
                            token_append(lay, fold_append ? k_new : nullptr, v_new, k_pool, v_pool, summ));
+  // grouped-query heads: selection and attention in one launch when its LDS fits
+  if (e == hipSuccess && family_of(lay) == kFamilyGqa && select_decode_lds_bytes(lay, bat, max_sel) <= 160 * 1024)
+    return status_of(launch_select_decode_gqa(lay, bat, pol, q, k_pool, v_pool, summ, ws.scores, sel_out, cnt_out,
+                                              max_sel, scale, out, ws, s));
   if (e == hipSuccess) e = launch_select_topk(lay, bat, pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
   if (e == hipSuccess)
     e = launch_sparse_decode(lay, bat, pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);
@@ -578,9 +586,13 @@ int32_t qasp_decode_step_multi(const qasp_layout *lay, const qasp_batch *bat, co
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   // many units: one kernel per (sequence, KV head) appends the drafts, stages
   // the query rows in the grouped order, scores, selects and attends
-  if (one_kernel_step(*lay, wbat, max_sel))
+  if (one_kernel_step(*lay, wbat, max_sel)) {
+    if (nq == 1)  // one draft: the one-token step, its token appended at L - 1
+      return status_of(launch_fused_step_gqa(*lay, wbat, wpol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel,
+                                             sel_count, max_sel, s));
     return status_of(launch_fused_step_gqa(*lay, wbat, wpol, q, nullptr, nullptr, k_pool, v_pool, summ, scale, out,
                                            sel, sel_count, max_sel, s, nq, pol->window_tokens, false, k_new, v_new));
+  }
   // q [B][nq][Hkv][G][Dk] -> [B][Hkv][nq][G][Dk], and the drafts appended
   hipError_t e = launch_prepare_drafts(*lay, *bat, nq, q, q_grouped, k_new, v_new, k_pool, v_pool, summ, s);
   if (e == hipSuccess && scored)

@@ -19,6 +19,7 @@
 // head, its own window of window_q tokens (the selection holds the union).
 #include "attend_core.h"
 #include "launch.h"
+#include "select_core.h"
 
 namespace qasp {
 
@@ -78,6 +79,107 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gqa_kernel(
       if (dv == 0) partial_ml[ps_idx] = make_float2(M, lsum);
     }
   });
+}
+
+// LDS of select_decode_gqa_kernel (bytes): the selection's keys (8 bytes per
+// page), which the wave merge reuses at the end, two bit maps, the list.
+struct SelectDecodeLds {
+  size_t bits, list, total;
+  __host__ __device__ SelectDecodeLds(int max_pages, int max_sel, int W, int G) {
+    const size_t keys = (size_t)max_pages * 8, merge = (size_t)attend::merge_lds_floats(W, G, 128) * 4;
+    bits = ((keys > merge ? keys : merge) + 15) & ~(size_t)15;
+    list = bits + 2 * (size_t)((max_pages + 31) / 32) * 4;
+    total = list + (size_t)max_sel * 4;
+  }
+};
+
+// The selection and the attention of the kernel chain in one launch (one
+// kernel boundary fewer): block (unit, split) selects its unit's pages from
+// the stored scores exactly as select_topk_kernel does (every split of a
+// unit computes the same list; the first split also writes it out), then
+// attends its split of the list as decode_gqa_kernel does.  The splits of a
+// unit are consecutive items of the XCD-contiguous order, so their score
+// reads come through one L2.
+template <int W>
+__global__ __launch_bounds__(W * 64) void select_decode_gqa_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool, const uint16_t *__restrict__ v_pool,
+    const uint16_t *__restrict__ summ, const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
+    const qasp_score *__restrict__ scores, int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out,
+    float *__restrict__ partial, float2 *__restrict__ partial_ml, float *__restrict__ out, int pt_stride,
+    int max_pages, int max_sel, int Hq, int Hkv, int G, int splits, int pps, float scale_log2, int n_sink,
+    int n_local, int top_k, int sink_tokens, int window_tokens, uint64_t static_mask) {
+  constexpr int PS = 16, D = 128, DV = 128;
+  extern __shared__ uint64_t dyn[];
+  __shared__ sel::SelShared<W> sh;
+  const SelectDecodeLds lay(max_pages, max_sel, W, G);
+  uint32_t *bits = (uint32_t *)((char *)dyn + lay.bits);
+  int32_t *list = (int32_t *)((char *)dyn + lay.list);
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
+  const int unit = item / splits, split = item % splits;
+  const int b = unit / Hkv, g = unit % Hkv;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int L = seq_lens[b];
+  const bool is_static = head_is_static(static_mask, g);
+  const size_t head0 = (size_t)b * Hq + (size_t)g * G;
+  const int32_t *pt_row = page_table + (size_t)b * pt_stride;
+  const int count = sel::select_unit<D, W>(sh, dyn, bits, (max_pages + 31) / 32, scores + (size_t)unit * max_pages,
+                                           L, PS, is_static, n_sink, n_local, top_k, sink_tokens, window_tokens,
+                                           q + head0 * D, G, summ, pt_row, Hkv, g,
+                                           split == 0 ? sel_out + (size_t)unit * max_sel : nullptr, list, max_sel);
+  if (split == 0 && threadIdx.x == 0) sel_count_out[unit] = count;
+  __syncthreads();  // the list is complete; the keys are dead
+
+  const int sink_end = is_static ? min(sink_tokens, L) : 0;
+  const int win_begin = is_static ? max(0, L - window_tokens) : 0;
+  const int first = split * pps, last = min(first + pps, count);
+  const int npg = max(0, (last - first - wave + W - 1) / W);
+  int my_j = 0, my_phys = 0;
+  if (lane < npg) {
+    my_j = list[first + wave + W * lane];
+    my_phys = pt_row[my_j];
+  }
+  uint4 bq[D / 32];
+  attend::load_q_columns<D>(bq, q + head0 * D, G, lane);
+  attend::WaveState st;
+  attend::init_state(st);
+  const attend::PageWork<PS, D, DV> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin, is_static, scale_log2};
+  attend::attend_pages<PS, D, DV>(st, pw, npg, my_j, my_phys, lane);
+  attend::merge_waves<W, DV>((float *)dyn, st, G, [&](int h, int dv, float a, float lsum, float M) {
+    if (splits == 1) {
+      out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
+    } else {
+      const size_t ps_idx = (head0 + h) * splits + split;
+      partial[ps_idx * DV + dv] = a;
+      if (dv == 0) partial_ml[ps_idx] = make_float2(M, lsum);
+    }
+  });
+}
+
+size_t select_decode_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel) {
+  const int G = bat.num_q_heads / lay.num_kv_heads;
+  return SelectDecodeLds(bat.max_pages > 0 ? bat.max_pages : 1, max_sel, kGqaDecodeWaves, G).total +
+         sizeof(sel::SelShared<kGqaDecodeWaves>);
+}
+
+hipError_t launch_select_decode_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                    const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                    const uint16_t *summ, const qasp_score *scores, int32_t *sel, int32_t *sel_count,
+                                    int max_sel, float scale, float *out, const Workspace &ws, hipStream_t stream) {
+  constexpr int W = kGqaDecodeWaves;
+  const int G = bat.num_q_heads / lay.num_kv_heads;
+  const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int pps = (max_sel + ws.splits - 1) / ws.splits;
+  const size_t lds = SelectDecodeLds(mp, max_sel, W, G).total;
+  dim3 grid((unsigned)ws.splits * lay.num_kv_heads * bat.batch);
+  hipLaunchKernelGGL(select_decode_gqa_kernel<W>, grid, dim3(W * 64), lds, stream, q, k_pool, v_pool, summ,
+                     bat.page_table, bat.seq_lens, scores, sel, sel_count, ws.partial, ws.partial_ml, out,
+                     bat.pt_stride, mp, max_sel, bat.num_q_heads, lay.num_kv_heads, G, ws.splits, pps, scale_log2,
+                     pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens, pol.window_tokens,
+                     pol.static_head_mask);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ws.splits == 1) return e;
+  return launch_merge_splits(ws, bat.batch, bat.num_q_heads, lay.head_dim_v, out, stream, 1, G);
 }
 
 // Combines the split partials of every (sequence, query head):

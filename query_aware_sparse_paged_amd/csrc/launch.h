@@ -75,9 +75,22 @@ hipError_t launch_sparse_decode(const qasp_layout &lay, const qasp_batch &bat,
                                 const uint16_t *k_pool, const uint16_t *v_pool,
                                 const int32_t *sel, const int32_t *sel_count, int max_sel,
                                 float scale, float *out, const Workspace &ws, hipStream_t stream);
+// The kernel chain's selection and attention in one launch (grouped-query
+// family) when its LDS fits: bytes of LDS it needs, and the launch (merge
+// of the split partials included).
+size_t select_decode_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel);
+hipError_t launch_select_decode_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
+                                    const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                    const uint16_t *summ, const qasp_score *scores, int32_t *sel, int32_t *sel_count,
+                                    int max_sel, float scale, float *out, const Workspace &ws, hipStream_t stream);
 // The single-kernel decode step (grouped-query family), for many units.
 constexpr int kFusedMinUnits = 200;
 constexpr int kFusedMaxPages = 4096;
+// ... or fewer units, each with at most this much to read (summaries + K/V)
+#ifndef QASP_FUSED_SMALL_UNIT_BYTES
+#define QASP_FUSED_SMALL_UNIT_BYTES (640u << 10)
+#endif
+constexpr size_t kFusedSmallUnitBytes = QASP_FUSED_SMALL_UNIT_BYTES;
 size_t fused_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel);
 hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,

@@ -9,7 +9,10 @@ namespace qasp {
 
 namespace {
 constexpr int kScoreWaves = 4;
-constexpr int kScoreGroupsPerWave = 4;   // 16-page groups per wave
+#ifndef QASP_SCORE_GROUPS_PER_WAVE
+#define QASP_SCORE_GROUPS_PER_WAVE 4
+#endif
+constexpr int kScoreGroupsPerWave = QASP_SCORE_GROUPS_PER_WAVE;   // 16-page groups per wave
 constexpr int kScorePagesPerBlock = kScoreWaves * kScoreGroupsPerWave * 16;
 }  // namespace
 

@@ -19,82 +19,14 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
   extern __shared__ uint64_t dyn[];
   __shared__ sel::SelShared<NW> sh;
   const int g = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
   const int unit = b * Hkv + g;
   const int nwords = (max_pages + 31) / 32;
-  uint64_t *keys64 = dyn;                                  // [max_pages]
-  uint32_t *keys32 = (uint32_t *)dyn;                      // aliases keys64 until the band step
-  uint32_t *sel_bits = (uint32_t *)(dyn + max_pages);      // [nwords]
-  uint32_t *band_bits = sel_bits + nwords;                 // [nwords] (candidate index)
-
-  const int L = seq_lens[b];
-  const int P = num_pages_of(L, ps);
-  const bool is_static = head_is_static(static_mask, g);
-  const int cand_lo = min(n_sink, P), cand_hi = max(cand_lo, P - n_local);
-  const int n = cand_hi - cand_lo;
-  const int k = top_k;
-  const bool ranked = !is_static && k > 0 && k < n;
-
-  // issue the score loads first: eight per thread in flight
-  constexpr int kLoadUnroll = 8;
-  const qasp_score *row = scores + (size_t)unit * max_pages + cand_lo;
-  float e_loc = 0.f;
-  uint32_t k_min = ~0u, k_max = 0;
-  if (ranked) {
-    for (int i0 = 0; i0 < n; i0 += kLoadUnroll * THREADS) {
-      qasp_score sc[kLoadUnroll];
-#pragma unroll
-      for (int u = 0; u < kLoadUnroll; u++) {
-        const int i = i0 + u * THREADS + tid;
-        sc[u] = i < n ? row[i] : qasp_score{-INFINITY, 0.f, -1, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < kLoadUnroll; u++) {
-        const int i = i0 + u * THREADS + tid;
-        if (i < n) {
-          const uint32_t o = sel::f32_order(sc[u].value);
-          keys32[i] = o;
-          k_min = min(k_min, o);
-          k_max = max(k_max, o);
-          e_loc = fmaxf(e_loc, sc[u].err);
-        }
-      }
-    }
-  }
-  for (int w = tid; w < nwords; w += THREADS) {
-    sel_bits[w] = 0;
-    band_bits[w] = 0;
-  }
-  for (int w = tid; w < NW * 256; w += THREADS) (&sh.hist[0][0])[w] = 0;
-  if (tid == 0) sh.nlist = 0;
-  __syncthreads();
-
-  bool fast = false;
-  uint32_t uk_fast = 0;
-  if (is_static) {
-    const int sink_end = min(sink_tokens, L);
-    const int win_begin = max(0, L - window_tokens);
-    for (int j = tid; j < P; j += THREADS) {
-      const int a = j * ps, e = min(a + ps, L);
-      if (a < sink_end || e > win_begin) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-    }
-  } else {
-    if (ranked) {
-      sel::block_max_min_max(e_loc, k_min, k_max, sh);
-      fast = sel::select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min,
-                                           k_max, q + ((size_t)b * Hq + (size_t)g * G) * D, G, summ,
-                                           page_table + (size_t)b * pt_stride, Hkv, g, row, nullptr, &uk_fast);
-    }
-    if (!fast)
-      for (int j = tid; j < P; j += THREADS)
-        if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-  }
-  __syncthreads();
-  // without pages in doubt the list comes straight from the keys
-  int32_t *sel_row = sel + (size_t)unit * max_sel;
-  const int count = fast ? sel::emit_by_threshold(sh, keys32, n, uk_fast, cand_lo, cand_hi, P, sel_row, nullptr, max_sel)
-                         : sel::emit_selection(sh, sel_bits, nwords, sel_row, nullptr, max_sel);
-  if (tid == 0) sel_count[unit] = count;
+  const int count = sel::select_unit<D, NW>(
+      sh, dyn, (uint32_t *)(dyn + max_pages), nwords, scores + (size_t)unit * max_pages, seq_lens[b], ps,
+      head_is_static(static_mask, g), n_sink, n_local, top_k, sink_tokens, window_tokens,
+      q + ((size_t)b * Hq + (size_t)g * G) * D, G, summ, page_table + (size_t)b * pt_stride, Hkv, g,
+      sel + (size_t)unit * max_sel, nullptr, max_sel);
+  if (threadIdx.x == 0) sel_count[unit] = count;
 }
 
 hipError_t launch_select_topk(const qasp_layout &lay, const qasp_batch &bat,

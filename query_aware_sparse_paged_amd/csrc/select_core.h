@@ -484,14 +484,39 @@ __device__ __forceinline__ double i64_to_f64_rn(int64_t x) {
   return (double)hi * 4294967296.0 + (double)lo;
 }
 
-// Exact sum with 32-bit digits; every lane runs it (rare path: some term is
-// too small for the 64-bit window of exact_head_bound).
+// Wave-uniform 64-bit read of lane src's value (src the same on every lane).
+__device__ __forceinline__ int64_t readlane64(int64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), src);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Digits into [0, 2^32), lane by lane from the lowest, the carries moving up;
+// the top digit keeps the sign.  Lane i holds digit i.
+template <int kDigits>
+__device__ __forceinline__ int64_t carry_digits(int64_t dg, int lane) {
+  for (int i = 0; i + 1 < kDigits; i++) {
+    const int64_t x = readlane64(dg, i);
+    const int64_t low = x & 0xffffffffll;
+    if (lane == i) dg = low;
+    if (lane == i + 1) dg += (x - low) / ((int64_t)1 << 32);
+  }
+  return dg;
+}
+
+// Exact sum with 32-bit digits, one digit per lane (lane i: weight
+// 2^(-288 + 32 i), 22 digits from below 2^-266, the smallest term, to above
+// the largest sum); wave-wide: every lane walks the same terms (the lanes of
+// the two digits a term touches add its parts) and returns the result.  Call
+// with every lane of the wave and wave-uniform arguments.  Rare path: some
+// term is too small for the 64-bit window of exact_head_bound.
 template <int D>
-__device__ double exact_head_bound_digits(const uint16_t *qh, const uint16_t *lo, const uint16_t *hi) {
+__device__ __forceinline__ double exact_head_bound_digits(const uint16_t *qh, const uint16_t *lo, const uint16_t *hi) {
   constexpr int kDigits = 22;
   constexpr int kLow = -288;   // weight of bit 0 of digit 0: below 2^-266, the smallest term
-  int64_t dg[kDigits];
-  for (int i = 0; i < kDigits; i++) dg[i] = 0;
+  static_assert(kDigits <= kWave, "one digit per lane");
+  const int lane = threadIdx.x % kWave;
+  int64_t dg = 0;
   for (int d = 0; d < D; d++) {
     int M, E;
     bound_term(qh, lo, hi, d, M, E);
@@ -500,41 +525,30 @@ __device__ double exact_head_bound_digits(const uint16_t *qh, const uint16_t *lo
     const int di = off >> 5, sh = off & 31;
     const int64_t v = (int64_t)M * ((int64_t)1 << sh);
     const int64_t low = v & 0xffffffffll;
-    dg[di] += low;
-    dg[di + 1] += (v - low) / ((int64_t)1 << 32);
+    if (lane == di) dg += low;
+    if (lane == di + 1) dg += (v - low) / ((int64_t)1 << 32);
   }
-  // carries: digits into [0, 2^32), the top one keeps the sign
-  for (int i = 0; i + 1 < kDigits; i++) {
-    const int64_t low = dg[i] & 0xffffffffll;
-    dg[i + 1] += (dg[i] - low) / ((int64_t)1 << 32);
-    dg[i] = low;
-  }
-  bool neg = dg[kDigits - 1] < 0;
-  if (neg) {
-    for (int i = 0; i < kDigits; i++) dg[i] = -dg[i];
-    for (int i = 0; i + 1 < kDigits; i++) {
-      const int64_t low = dg[i] & 0xffffffffll;
-      dg[i + 1] += (dg[i] - low) / ((int64_t)1 << 32);
-      dg[i] = low;
-    }
-  }
-  int top = kDigits - 1;
-  while (top >= 0 && dg[top] == 0) top--;
-  if (top < 0) return 0.0;
+  dg = carry_digits<kDigits>(dg, lane);
+  const bool neg = readlane64(dg, kDigits - 1) < 0;
+  if (neg) dg = carry_digits<kDigits>(-dg, lane);
+  const uint64_t nz = __ballot(lane < kDigits && dg != 0);
+  if (nz == 0) return 0.0;
+  const int top = 63 - __builtin_clzll(nz);
   // 64-bit window ending at the leading one; lower bits fold into a sticky bit
-  const int lead = 32 * top + 31 - __builtin_clz((uint32_t)dg[top]);
+  const int lead = 32 * top + 31 - __builtin_clz((uint32_t)readlane64(dg, top));
   double r;
   if (lead < 64) {
-    const uint64_t x = (uint64_t)dg[0] | ((uint64_t)dg[1] << 32);
+    const uint64_t x = (uint64_t)readlane64(dg, 0) | ((uint64_t)readlane64(dg, 1) << 32);
     r = ldexp((double)(uint32_t)(x >> 32) * 4294967296.0 + (double)(uint32_t)x, kLow);
   } else {
     const int lo_bit = lead - 63;
     const int di = lo_bit >> 5, sh = lo_bit & 31;
-    const uint64_t w0 = (uint64_t)dg[di] | ((uint64_t)dg[di + 1] << 32);
-    const uint64_t w2 = di + 2 < kDigits ? (uint64_t)dg[di + 2] : 0;
+    const uint64_t d0 = (uint64_t)readlane64(dg, di);
+    const uint64_t w0 = d0 | ((uint64_t)readlane64(dg, di + 1) << 32);
+    const uint64_t w2 = di + 2 < kDigits ? (uint64_t)readlane64(dg, di + 2) : 0;
     uint64_t x = sh == 0 ? w0 : ((w0 >> sh) | (w2 << (64 - sh)));
-    bool sticky = sh != 0 && (dg[di] & ((1ll << sh) - 1)) != 0;
-    for (int i = 0; i < di; i++) sticky |= dg[i] != 0;
+    bool sticky = sh != 0 && (d0 & ((1ull << sh) - 1)) != 0;
+    sticky |= __ballot(lane < di && dg != 0) != 0;
     if (sticky) x |= 1;  // 11 bits below the rounding point: the sticky bit keeps RNE exact
     r = ldexp((double)(uint32_t)(x >> 32) * 4294967296.0 + (double)(uint32_t)x, lo_bit + kLow);
   }
@@ -546,7 +560,7 @@ __device__ double exact_head_bound_digits(const uint16_t *qh, const uint16_t *lo
 // patterns); the terms are placed on one 64-bit integer grid just below the
 // largest term and summed exactly across the wave.  qh may point to LDS.
 template <int D>
-__device__ double exact_head_bound(const uint16_t *qh, const uint32_t *xl, const uint32_t *xh,
+__device__ __forceinline__ double exact_head_bound(const uint16_t *qh, const uint32_t *xl, const uint32_t *xh,
                                    const uint16_t *lo, const uint16_t *hi, int lane) {
   constexpr int PER = (D + kWave - 1) / kWave;
   constexpr int LOGD = D <= 128 ? 7 : (D <= 1024 ? 10 : 16);
@@ -585,7 +599,7 @@ __device__ double exact_head_bound(const uint16_t *qh, const uint32_t *xl, const
 
 // Exact group score of one page: max over the G heads (wave-wide).
 template <int D>
-__device__ double exact_page_key(const uint16_t *qg, int G, const uint16_t *lo, const uint16_t *hi, int lane) {
+__device__ __forceinline__ double exact_page_key(const uint16_t *qg, int G, const uint16_t *lo, const uint16_t *hi, int lane) {
   constexpr int PER = (D + kWave - 1) / kWave;
   uint32_t xl[PER], xh[PER];
 #pragma unroll
@@ -605,7 +619,7 @@ __device__ double exact_page_key(const uint16_t *qg, int G, const uint16_t *lo, 
 // common 64-bit grid, then the wave takes the max over heads.  Falls back to
 // the per-head digit sum when some term lies below the grid.
 template <int D, int NP>
-__device__ double exact_page_key_heads(const uint16_t *qg, int G, const uint16_t *rows,
+__device__ __forceinline__ double exact_page_key_heads(const uint16_t *qg, int G, const uint16_t *rows,
                                        const uint16_t *lo_g, const uint16_t *hi_g, int lane) {
   constexpr int PER = D / NP;
   constexpr int LOGD = D <= 128 ? 7 : (D <= 1024 ? 10 : 16);
@@ -897,6 +911,92 @@ __device__ int emit_selection(SelShared<NW> &sh, const uint32_t *sel_bits, int n
   if (out_global)
     for (int i = count + tid; i < max_sel; i += T) out_global[i] = -1;
   return count;
+}
+
+// The whole selection of one (sequence, KV head) unit by one block of NW
+// waves, from the unit's stored scores: candidate keys into LDS, the
+// certified top-k (pages in doubt re-scored exactly), sink and local pages,
+// or a static head's sink + window pages.  The list goes, ascending, to
+// out_global (followed by -1 up to max_sel; may be null) and/or out_lds.
+// Returns the count on every thread.  Every thread of the block calls it.
+//   keys64  LDS, 8 bytes per page of max_pages (keys32 aliases it);
+//   bits    LDS, 2 * nwords words (nwords = ceil(max_pages / 32));
+//   row     the unit's scores, indexed by logical page;
+//   qg      the group's first q row (global; may be null for static heads);
+//   pt_row  the sequence's page-table row.
+template <int D, int NW>
+__device__ int select_unit(SelShared<NW> &sh, uint64_t *keys64, uint32_t *bits, int nwords, const qasp_score *row,
+                           int L, int ps, bool is_static, int n_sink, int n_local, int top_k, int sink_tokens,
+                           int window_tokens, const uint16_t *qg, int G, const uint16_t *summ, const int32_t *pt_row,
+                           int Hkv, int g, int32_t *out_global, int32_t *out_lds, int max_sel) {
+  constexpr int THREADS = NW * kWave;
+  const int tid = threadIdx.x;
+  uint32_t *keys32 = (uint32_t *)keys64;  // aliases keys64 until the band step
+  uint32_t *sel_bits = bits;
+  uint32_t *band_bits = bits + nwords;    // candidate index
+  const int P = num_pages_of(L, ps);
+  const int cand_lo = min(n_sink, P), cand_hi = max(cand_lo, P - n_local);
+  const int n = cand_hi - cand_lo;
+  const int k = top_k;
+  const bool ranked = !is_static && k > 0 && k < n;
+
+  // issue the score loads first: eight per thread in flight
+  constexpr int kLoadUnroll = 8;
+  const qasp_score *crow = row + cand_lo;
+  float e_loc = 0.f;
+  uint32_t k_min = ~0u, k_max = 0;
+  if (ranked) {
+    for (int i0 = 0; i0 < n; i0 += kLoadUnroll * THREADS) {
+      qasp_score sc[kLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int i = i0 + u * THREADS + tid;
+        sc[u] = i < n ? crow[i] : qasp_score{-INFINITY, 0.f, -1, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int i = i0 + u * THREADS + tid;
+        if (i < n) {
+          const uint32_t o = f32_order(sc[u].value);
+          keys32[i] = o;
+          k_min = min(k_min, o);
+          k_max = max(k_max, o);
+          e_loc = fmaxf(e_loc, sc[u].err);
+        }
+      }
+    }
+  }
+  for (int w = tid; w < nwords; w += THREADS) {
+    sel_bits[w] = 0;
+    band_bits[w] = 0;
+  }
+  for (int w = tid; w < NW * 256; w += THREADS) (&sh.hist[0][0])[w] = 0;
+  if (tid == 0) sh.nlist = 0;
+  __syncthreads();
+
+  bool fast = false;
+  uint32_t uk_fast = 0;
+  if (is_static) {
+    const int sink_end = min(sink_tokens, L);
+    const int win_begin = max(0, L - window_tokens);
+    for (int j = tid; j < P; j += THREADS) {
+      const int a = j * ps, e = min(a + ps, L);
+      if (a < sink_end || e > win_begin) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+    }
+  } else {
+    if (ranked) {
+      block_max_min_max(e_loc, k_min, k_max, sh);
+      fast = select_candidates<D, NW>(sh, keys32, keys64, sel_bits, band_bits, n, k, cand_lo, e_loc, k_min, k_max,
+                                      qg, G, summ, pt_row, Hkv, g, crow, nullptr, &uk_fast);
+    }
+    if (!fast)
+      for (int j = tid; j < P; j += THREADS)
+        if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  // without pages in doubt the list comes straight from the keys
+  return fast ? emit_by_threshold(sh, keys32, n, uk_fast, cand_lo, cand_hi, P, out_global, out_lds, max_sel)
+              : emit_selection(sh, sel_bits, nwords, out_global, out_lds, max_sel);
 }
 
 }  // namespace sel

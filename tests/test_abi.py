@@ -409,6 +409,9 @@ def test_decode_step_path(L):
     assert path(big, b(25, 2048), pol, 128) == api.PATH_ONE_KERNEL      # 200 units
     assert path(big, b(24, 2048), pol, 128) == api.PATH_CHAIN           # 192 units
     assert path(big, b(8, 8192), pol, 256) == api.PATH_CHAIN            # needle: 64 units, 8192 pages
+    tiny = api.Layout(512, 16, 8, 128, 128)
+    assert path(tiny, b(1, 256), api.Policy(1, 4, 32), 37) == api.PATH_ONE_KERNEL   # 8 small units
+    assert path(big, b(3, 190), pol, 128) == api.PATH_CHAIN             # 24 units of 1.1 MB each
     assert path(big, b(64, 4097), pol, 128) == api.PATH_CHAIN           # page list past the kernel's arrays
     assert path(big, b(64, 4096), pol, 4096) == api.PATH_ONE_KERNEL     # 98 KB of on-chip arrays
     # 16 heads per group: the merge area grows, and with every page selected the arrays pass 160 KB

@@ -84,6 +84,11 @@ def test_multi_step_few_sequences(nq):
     _run("llama8b_b32_32k", 3, nq, 900, 600)
 
 
+def test_multi_step_one_draft_many_units():
+    # one draft on the one-kernel path: the draft is the step's token, appended at L - 1
+    _run("llama8b_b32_32k", 32, 1, 1100, 400)
+
+
 def test_multi_step_many_units_ragged_tail():
     # 64 sequences x 8 KV heads: 512 units, one kernel per unit after the draft append; lengths not page-aligned
     _run("llama8b_b32_32k", 64, 4, 1000, 300)
