@@ -523,7 +523,12 @@ int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat, co
   int32_t *cnt_out = sel_count ? sel_count : ws.sel_count;
   hipError_t e = hipSuccess;
   if (one_kernel_step(*lay, *bat, max_sel)) {
-    // many units: append, score and select in the one-kernel step's selection-only form
+    // the whole step in one kernel (at most 64 selected pages per wave of it)
+    if (max_sel <= 64 * kFusedWaves)
+      return status_of(launch_fused_step_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out,
+                                             sel, sel_count, max_sel, s, 1, 0, false, nullptr, nullptr, qpool,
+                                             residual_pages));
+    // else: append, score and select in the one-kernel step's selection-only form
     e = launch_fused_step_gqa(*lay, *bat, *pol, q, k_new, v_new, k_pool, v_pool, summ, scale, out, sel_out, cnt_out,
                               max_sel, s, 1, 0, true);
     if (e == hipSuccess)  // (quantises the page leaving the residual region too)

@@ -9,12 +9,11 @@
 // block only, so no inter-block synchronisation is needed.
 #include "attend_core.h"
 #include "launch.h"
+#include "quant_core.h"
 #include "score_core.h"
 #include "select_core.h"
 
 namespace qasp {
-
-constexpr int kFusedWaves = 8;
 
 // Dynamic LDS layout of the fused kernel (bytes).
 struct FusedLds {
@@ -97,6 +96,10 @@ __device__ __forceinline__ int2 unit_for_block(int i, const int32_t *seq_lens, i
 // drafts' union); the output goes to [B][n_draft][Hq / n_draft][DV].
 // SEL_ONLY: append, score and select only (the selection is written out for
 // another attention kernel; out is not touched).
+// QUANT: 2-bit quantised pages (qpool) below the last residual_pages of the
+// sequence: the block quantises the page-head that leaves the residual region
+// at this step (no other block reads it), then each wave attends its pages,
+// the quantised ones from their codes (at most 64 pages per wave).
 // The n_draft draft tokens of sequence b, KV head g, appended by one wave
 // (lane = key word; values two per lane) at positions L - n_draft ...: key
 // rows, value columns and the page summaries (the running min / max of a
@@ -234,7 +237,7 @@ struct DeferredDrafts {
   }
 };
 
-template <int D, int DV, int PS, int W, bool CAUSAL = false, bool SEL_ONLY = false>
+template <int D, int DV, int PS, int W, bool CAUSAL = false, bool SEL_ONLY = false, bool QUANT = false>
 __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     uint16_t *__restrict__ k_pool, uint16_t *__restrict__ v_pool, uint16_t *__restrict__ summ,
@@ -242,8 +245,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     int32_t *__restrict__ sel_out, int32_t *__restrict__ sel_count_out, int pt_stride, int max_pages,
     int max_sel, int Hq, int Hkv, int G, int n_sink, int n_local, int top_k, int sink_tokens,
     int window_tokens, uint64_t static_mask, float scale_log2, uint32_t bucket_mul, int lpt, int n_draft,
-    int window_q, const uint16_t *__restrict__ draft_k, const uint16_t *__restrict__ draft_v) {
+    int window_q, const uint16_t *__restrict__ draft_k, const uint16_t *__restrict__ draft_v,
+    uint8_t *__restrict__ qpool, int residual_pages) {
   static_assert(D == 128 && DV == 128, "append and staging assume 128 channels");
+  static_assert(!(QUANT && (CAUSAL || SEL_ONLY)), "quantised pages: one-token attention");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
   extern __shared__ uint64_t dyn[];
@@ -486,11 +491,13 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   }
   const attend::PageWork<PS, D, DV, CAUSAL> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin,
                                                is_static, scale_log2, Lq, winq};
-  const bool pre = wave < n_known;  // wave-uniform
+  const bool pre = !QUANT && wave < n_known;  // wave-uniform
   // issued by every wave (a valid page when there is nothing to preload), so
   // the registers are always defined and the load is never waited on here
-  const attend::PageRegs<D, DV> first =
-      pw.load(pre ? page_phys[wave < cand_lo ? wave : cand_hi + (wave - cand_lo)] : (P > 0 ? page_phys[0] : 0), lane);
+  attend::PageRegs<D, DV> first;
+  if constexpr (!QUANT)
+    first = pw.load(pre ? page_phys[wave < cand_lo ? wave : cand_hi + (wave - cand_lo)] : (P > 0 ? page_phys[0] : 0),
+                    lane);
 
   // ---- select (usually no page is in doubt: then the selection is the k
   // largest keys and the list is written straight from them)
@@ -523,6 +530,27 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
   if constexpr (SEL_ONLY) return;  // block-uniform; the unused page preload above is not emitted
   __syncthreads();
+  if constexpr (QUANT) {
+    // the page leaving the residual region: quantised here (the merge area is
+    // free until the end); the barriers inside order it before every read
+    const int jl = quant::leaving_page(L, residual_pages);
+    if (jl >= 0) quant::quantize_page_head(k_pool, v_pool, qpool, page_phys[jl], g, Hkv, merge_area);
+    const int npg = count > wave ? (count - wave + W - 1) / W : 0;  // positions wave, wave + W, ... (<= 64)
+    int my_j = 0, my_phys = 0;
+    if (lane < npg) {
+      my_j = list[wave + W * lane];
+      my_phys = page_phys[my_j];
+    }
+    attend::WaveState st;
+    attend::init_state(st);
+    quant::attend_wave_quant(st, bq, npg, my_j, my_phys, P - residual_pages, qpool, k_pool, v_pool, Hkv, g, L,
+                             is_static, sink_end, win_begin, scale_log2, lane);
+    attend::merge_waves<W, DV>(merge_area, st, G, [&](int h, int dv, float a, float lsum, float M) {
+      (void)M;
+      out[(head0 + h) * DV + dv] = lsum > 0.f ? a / lsum : 0.f;
+    });
+    return;
+  }
 
   // ---- attend: wave w takes attention positions w, w+W, ... (a fixed
   // assignment, so the result does not depend on timing)
@@ -672,7 +700,8 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
                                  const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
                                  int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream, int n_draft,
-                                 int window_q, bool sel_only, const uint16_t *draft_k, const uint16_t *draft_v) {
+                                 int window_q, bool sel_only, const uint16_t *draft_k, const uint16_t *draft_v,
+                                 uint8_t *qpool, int residual_pages) {
   const int G = bat.num_q_heads / lay.num_kv_heads;
   const int mp = bat.max_pages > 0 ? bat.max_pages : 1;
   const size_t lds = FusedLds(mp, max_sel, G).total;
@@ -682,14 +711,15 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
   const int units = bat.batch * lay.num_kv_heads;
   const int lpt = units > device_cu_count() ? 1 : 0;
   dim3 grid(units);
-  auto kernel = sel_only      ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false, true>
-                : n_draft > 1 ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, true>
-                              : fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false>;
+  auto kernel = sel_only           ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false, true>
+                : n_draft > 1      ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, true>
+                : qpool != nullptr ? fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false, false, true>
+                                   : fused_step_gqa_kernel<128, 128, 16, kFusedWaves, false>;
   hipLaunchKernelGGL(kernel, grid, dim3(kFusedWaves * 64), lds, stream, q, k_new, v_new, k_pool, v_pool, summ,
                      bat.page_table, bat.seq_lens, out, sel, sel_count, bat.pt_stride, mp, max_sel, bat.num_q_heads,
                      lay.num_kv_heads, G, pol.n_sink_pages, pol.n_local_pages, pol.top_k, pol.sink_tokens,
                      pol.window_tokens, pol.static_head_mask, scale_log2, bucket_mul, lpt, n_draft, window_q, draft_k,
-                     draft_v);
+                     draft_v, qpool, residual_pages);
   return hipGetLastError();
 }
 

@@ -84,6 +84,7 @@ hipError_t launch_select_decode_gqa(const qasp_layout &lay, const qasp_batch &ba
                                     const uint16_t *summ, const qasp_score *scores, int32_t *sel, int32_t *sel_count,
                                     int max_sel, float scale, float *out, const Workspace &ws, hipStream_t stream);
 // The single-kernel decode step (grouped-query family), for many units.
+constexpr int kFusedWaves = 8;  // waves per block of the one-kernel step
 constexpr int kFusedMinUnits = 200;
 constexpr int kFusedMaxPages = 4096;
 // ... or fewer units, each with at most this much to read (summaries + K/V)
@@ -97,7 +98,8 @@ hipError_t launch_fused_step_gqa(const qasp_layout &lay, const qasp_batch &bat, 
                                  uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
                                  int32_t *sel, int32_t *sel_count, int max_sel, hipStream_t stream, int n_draft = 1,
                                  int window_q = 0, bool sel_only = false, const uint16_t *draft_k = nullptr,
-                                 const uint16_t *draft_v = nullptr);
+                                 const uint16_t *draft_v = nullptr, uint8_t *qpool = nullptr,
+                                 int residual_pages = 0);
 hipError_t launch_fused_reuse_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                   const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                                   uint16_t *k_pool, uint16_t *v_pool, uint16_t *summ, float scale, float *out,
