@@ -92,6 +92,19 @@ def step_bytes(w, msel_counts):
     return score, decode
 
 
+def auto_layers(spec):
+    """Layer caches to rotate so that at least 512 MB (twice the 256 MB
+    last-level cache) is touched between two steps on one cache: the bytes a
+    step touches are estimated from the full budget (summaries of every page,
+    K/V of the selected pages)."""
+    ps = spec.page_size
+    P = (spec.seq_len + ps - 1) // ps
+    sel = min(P, spec.n_sink_pages + spec.n_local_pages + spec.top_k)
+    kv = ps * (spec.head_dim_k + (0 if spec.v_from_k else spec.head_dim_v)) * 2
+    per_step = spec.batch * spec.num_kv_heads * (P * 4 * spec.head_dim_k + sel * kv)
+    return max(3, min(16, -(-2 * 256 * 2 ** 20 // max(1, per_step)) + 1))
+
+
 def cpu_info():
     """(CPU model, nproc, CPUs this process may run on)."""
     model = "unknown"
@@ -218,7 +231,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--layers", type=int, default=3, help="independent layer caches rotated over")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="independent layer caches rotated over (0: enough that at least 512 MB, twice the "
+                         "last-level cache, is touched between two visits of a cache; at least 3, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reuse", type=int, default=0,
                     help="cross-layer reuse: per group, 1 selecting layer + this many reusing layers")
@@ -240,6 +255,8 @@ def main():
     import torch
     from query_aware_sparse_paged_amd import api, workloads
 
+    if args.layers <= 0:
+        args.layers = auto_layers(workloads.SPECS[args.workload])
     dev = torch.device("cuda:0")
     if args.reuse > 0:
         return run_reuse(args, torch, api, workloads, dev)
@@ -294,20 +311,26 @@ def main():
         step(layers[i % len(layers)])
     torch.cuda.synchronize()
 
-    # the timed region: K steps back to back, a synchronize on both sides
+    # the timed region: K steps back to back, a synchronize on both sides;
+    # HIP events on the launch stream bracket the same K launches, so their
+    # span / K is the average launch duration as the GPU saw it (a kernel
+    # trace of back-to-back launches records the same: each one's start is the
+    # previous one's end)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
         step(layers[i % len(layers)])
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
 
     # a second pass of K steps with HIP events on the launch stream around
-    # every step (event records add a few microseconds between launches, so
-    # they stay out of the timed region); with many units the step is one
-    # kernel (append + score + select + attend), so these bracket exactly that
-    # kernel's launches
+    # every step, for the spread of single launches (event records add a few
+    # microseconds between launches, so they stay out of the timed region)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -324,13 +347,16 @@ def main():
     one_kernel = api.decode_step_path(L0["lay"], L0["bat"], L0["pol"], L0["msel"]) == api.PATH_ONE_KERNEL
     kernel = "fused_step_gqa_kernel" if one_kernel else "decode_step (several kernels)"
     dom_ms = med(step_ms)
-    achieved = total_bytes / (dom_ms * 1e-3) / 1e9
+    achieved = total_bytes / (launch_ms * 1e-3) / 1e9
     tokens_per_s = spec.batch / (ms_per_step * 1e-3)
     gbps = total_bytes / (ms_per_step * 1e-3) / 1e9
-    log("step events: median %.1f us (p10 %.1f, p90 %.1f), wall %.1f us/step"
-        % (dom_ms * 1e3, step_ms[len(step_ms) // 10] * 1e3, step_ms[(9 * len(step_ms)) // 10] * 1e3,
-           ms_per_step * 1e3))
+    log("timed region: %.1f us per launch by events, %.1f us per step by wall clock; single launches: median "
+        "%.1f us (p10 %.1f, p90 %.1f)" % (launch_ms * 1e3, ms_per_step * 1e3, dom_ms * 1e3,
+                                         step_ms[len(step_ms) // 10] * 1e3, step_ms[(9 * len(step_ms)) // 10] * 1e3))
 
+    stream_ref = stream_read_reference(torch, dev, total_bytes)
+    log("streaming-read reference: %.1f us for the step's %d bytes (%.0f GB/s)" % (
+        stream_ref["us"], total_bytes, stream_ref["gbps"]))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w0, layers[0]["msel"])
@@ -357,6 +383,7 @@ def main():
                    "layer_caches_rotated": args.layers},
         "kv_gbps_wall": round(gbps, 1),
         "step_bytes": total_bytes,
+        "launch_us_timed_region": round(launch_ms * 1e3, 2),
         "step_us_events": {"median": round(dom_ms * 1e3, 2), "mean": round(statistics.mean(step_ms) * 1e3, 2),
                            "p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
                            "p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2)},
@@ -364,11 +391,41 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(kernel, spec.name) if one_kernel else None,
                      "algorithmic_bytes": total_bytes,
-                     "timing": "median of %d HIP-event-bracketed launches on the launch stream (the kernel's "
-                               "duration, as a rocprofv3 kernel trace records it)" % len(step_ms)},
+                     "timing": "HIP events on the launch stream around the %d timed launches, span / %d (a "
+                               "rocprofv3 kernel trace of back-to-back launches records the same average)"
+                               % (args.steps, args.steps)},
+        "stream_read_reference": stream_ref,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def stream_read_reference(torch, dev, nbytes, reps=20):
+    """What a plain streaming read of the same number of bytes takes on this
+    GPU: torch's row sums over fp32 buffers of nbytes (rows of 1024, so the
+    written sums are 0.1% of the bytes), three buffers rotated, HIP events
+    around each launch, median.  Context for the roofline fraction (what this
+    memory delivers to a sequential read), not a result."""
+    rows = max(1, -(-nbytes // 4096))
+    bufs = [torch.ones((rows, 1024), dtype=torch.float32, device=dev) for _ in range(3)]
+    out = torch.empty(rows, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for i in range(3):
+        torch.sum(bufs[i], dim=1, out=out)
+    ts = []
+    for i in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.sum(bufs[i % 3], dim=1, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    us = statistics.median(ts)
+    del bufs
+    read = rows * 4096
+    return {"bytes": read, "us": round(us, 2), "gbps": round(read / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(read / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "kernel": "torch.sum over rows of 1024 fp32, three buffers rotated"}
 
 
 def run_quant(args, torch, api, workloads, dev):
