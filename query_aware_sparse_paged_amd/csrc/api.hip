@@ -17,7 +17,9 @@ hipError_t launch_decode_gqa(const qasp_layout &lay, const qasp_batch &bat, cons
 hipError_t launch_decode_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                              const uint16_t *q, const uint16_t *k_pool, const int32_t *sel,
                              const int32_t *sel_count, int max_sel, float scale, float *out,
-                             const Workspace &ws, hipStream_t stream);
+                             const Workspace &ws, hipStream_t stream, const qasp_score *scores = nullptr,
+                             const uint16_t *summ = nullptr);
+bool mla_select_fits(const qasp_batch &bat, int max_sel);
 
 constexpr int kMaxPagesLimit = 16384;  // select keeps 8 bytes per page in LDS
 
@@ -371,10 +373,13 @@ static int32_t run_step(const qasp_layout &lay, const qasp_batch &bat, const qas
   if (e == hipSuccess && scored)
     e = launch_score_pages(lay, bat, pol, q, summ, ws.scores, s,
                            token_append(lay, fold_append ? k_new : nullptr, v_new, k_pool, v_pool, summ));
-  // grouped-query heads: selection and attention in one launch when its LDS fits
+  // selection and attention in one launch when its LDS fits
   if (e == hipSuccess && family_of(lay) == kFamilyGqa && select_decode_lds_bytes(lay, bat, max_sel) <= 160 * 1024)
     return status_of(launch_select_decode_gqa(lay, bat, pol, q, k_pool, v_pool, summ, ws.scores, sel_out, cnt_out,
                                               max_sel, scale, out, ws, s));
+  if (e == hipSuccess && family_of(lay) == kFamilyMla && mla_select_fits(bat, max_sel))
+    return status_of(launch_decode_mla(lay, bat, pol, q, k_pool, sel_out, cnt_out, max_sel, scale, out, ws, s,
+                                       ws.scores, summ));
   if (e == hipSuccess) e = launch_select_topk(lay, bat, pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
   if (e == hipSuccess)
     e = launch_sparse_decode(lay, bat, pol, q, k_pool, v_pool, sel_out, cnt_out, max_sel, scale, out, ws, s);

@@ -43,6 +43,7 @@
 // partials at 16 sequences, against 67 MB with 128 heads x 2 pages per block).
 #include "launch.h"
 #include "common.h"
+#include "select_core.h"
 
 namespace qasp {
 
@@ -87,12 +88,19 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *p) {
 
 }  // namespace
 
+// SELECT: the block first selects its unit's pages from the stored scores
+// (select_unit, as select_topk_kernel does: every block of a unit computes
+// the same list, the first one also writes it to sel / sel_count), with the
+// selection's LDS laid over the page buffers, which are not in use yet.
+// Otherwise sel / sel_count are read.
+template <bool SELECT>
 __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool, const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel, const int32_t *__restrict__ sel_count,
+    const int32_t *__restrict__ seq_lens, int32_t *__restrict__ sel, int32_t *__restrict__ sel_count,
     float *__restrict__ partial, float2 *__restrict__ partial_ml, float *__restrict__ out, int pt_stride,
     int max_sel, int Hq, int Hkv, int splits, float scale_log2, int sink_tokens, int window_tokens,
-    uint64_t static_mask) {
+    uint64_t static_mask, const qasp_score *__restrict__ scores, const uint16_t *__restrict__ summ, int max_pages,
+    int n_sink, int n_local, int top_k) {
   extern __shared__ uint4 lds_u4[];
   char *kvbuf = (char *)lds_u4;                 // 2 page buffers
   char *pbuf = kvbuf + 2 * (size_t)kBufBytes;  // P^T hi, then lo
@@ -115,12 +123,31 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   };
 
   // the block's pages that hold an attended position
+  const int32_t *list = sel + (size_t)unit * max_sel;
+  int count = 0;
+  if constexpr (SELECT) {
+    // the selection's LDS over the page buffers: shared state, keys, bit maps, list
+    using Shared = sel::SelShared<kWaves>;
+    Shared &ssh = *(Shared *)kvbuf;
+    uint64_t *keys = (uint64_t *)(kvbuf + ((sizeof(Shared) + 15) & ~(size_t)15));
+    uint32_t *bits = (uint32_t *)(keys + max_pages);
+    int32_t *lds_list = (int32_t *)(bits + 2 * ((max_pages + 31) / 32));
+    const bool first_block = hg == 0 && split == 0;
+    count = sel::select_unit<kD, kWaves>(ssh, keys, bits, (max_pages + 31) / 32, scores + (size_t)unit * max_pages, L,
+                                         kPS, is_static, n_sink, n_local, top_k, sink_tokens, window_tokens,
+                                         q + ((size_t)b * Hq + (size_t)g * kG) * kD, kG, summ,
+                                         page_table + (size_t)b * pt_stride, Hkv, g,
+                                         first_block ? sel + (size_t)unit * max_sel : nullptr, lds_list, max_sel);
+    if (first_block && tid == 0) sel_count[unit] = count;
+    __syncthreads();  // the list is complete
+    list = lds_list;
+  }
   if (tid == 0) {
-    const int count = sel_count[unit];
+    if constexpr (!SELECT) count = sel_count[unit];
     const int first = split * kMlaPagesPerSplit, last = min(first + kMlaPagesPerSplit, count);
     int np = 0;
     for (int p = first; p < last; p++) {
-      const int j = sel[(size_t)unit * max_sel + p];
+      const int j = list[p];
       const int pos0 = j * kPS, pos1 = min(pos0 + kPS, L);
       if (pos0 < pos1 && (!is_static || pos0 < sink_end || pos1 > win_begin))
         sh.pages[np++] = make_int2(page_table[(size_t)b * pt_stride + j], pos0);
@@ -296,18 +323,38 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   }
 }
 
+// LDS the selection inside decode_mla_kernel<true> needs (laid over its page buffers).
+size_t mla_select_lds_bytes(int max_pages, int max_sel) {
+  return ((sizeof(sel::SelShared<kWaves>) + 15) & ~(size_t)15) + (size_t)max_pages * 8 +
+         2 * (size_t)((max_pages + 31) / 32) * 4 + (size_t)max_sel * 4;
+}
+bool mla_select_fits(const qasp_batch &bat, int max_sel) {
+  return mla_select_lds_bytes(bat.max_pages > 0 ? bat.max_pages : 1, max_sel) <= 2 * (size_t)kBufBytes;
+}
+
+// scores != nullptr: the blocks select first (sel / sel_count, then written,
+// receive the selection); else sel / sel_count are the given selection.
 hipError_t launch_decode_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                              const uint16_t *q, const uint16_t *k_pool, const int32_t *sel,
                              const int32_t *sel_count, int max_sel, float scale, float *out,
-                             const Workspace &ws, hipStream_t stream) {
+                             const Workspace &ws, hipStream_t stream, const qasp_score *scores,
+                             const uint16_t *summ) {
   const float scale_log2 = scale * 1.4426950408889634f;
   if (bat.num_q_heads != kG * lay.num_kv_heads) return hipErrorInvalidValue;
   const size_t lds = 2 * (size_t)kBufBytes + 2 * (size_t)kPBytes;
   dim3 grid((unsigned)(kG / kHeads) * ws.splits * lay.num_kv_heads * bat.batch);
-  hipLaunchKernelGGL(decode_mla_kernel, grid, dim3(kThreads), lds, stream, q, k_pool, bat.page_table,
-                     bat.seq_lens, sel, sel_count, ws.partial, ws.partial_ml, out, bat.pt_stride, max_sel,
-                     bat.num_q_heads, lay.num_kv_heads, ws.splits, scale_log2, pol.sink_tokens,
-                     pol.window_tokens, pol.static_head_mask);
+  if (scores != nullptr)
+    hipLaunchKernelGGL(decode_mla_kernel<true>, grid, dim3(kThreads), lds, stream, q, k_pool, bat.page_table,
+                       bat.seq_lens, (int32_t *)sel, (int32_t *)sel_count, ws.partial, ws.partial_ml, out,
+                       bat.pt_stride, max_sel,
+                       bat.num_q_heads, lay.num_kv_heads, ws.splits, scale_log2, pol.sink_tokens,
+                       pol.window_tokens, pol.static_head_mask, scores, summ, bat.max_pages > 0 ? bat.max_pages : 1,
+                       pol.n_sink_pages, pol.n_local_pages, pol.top_k);
+  else
+    hipLaunchKernelGGL(decode_mla_kernel<false>, grid, dim3(kThreads), lds, stream, q, k_pool, bat.page_table,
+                       bat.seq_lens, (int32_t *)sel, (int32_t *)sel_count, ws.partial, ws.partial_ml, out,
+                       bat.pt_stride, max_sel, bat.num_q_heads, lay.num_kv_heads, ws.splits, scale_log2,
+                       pol.sink_tokens, pol.window_tokens, pol.static_head_mask, nullptr, nullptr, 0, 0, 0, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ws.splits == 1) return e;
   return launch_merge_splits(ws, bat.batch, bat.num_q_heads, kDV, out, stream);
