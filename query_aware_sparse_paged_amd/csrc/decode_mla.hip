@@ -122,6 +122,14 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
     return (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
   };
 
+  // q^T of the wave's S heads: column n = head 32 hg + 16 ht + n, channels
+  // 32i + 8kg ..; loaded first, so they arrive while the pages are selected
+  const size_t head_base = (size_t)b * Hq + (size_t)g * kG + kHeads * hg;
+  uint4 qB[kD / 32];
+#pragma unroll
+  for (int i = 0; i < kD / 32; i++)
+    qB[i] = *(const uint4 *)(q + (head_base + 16 * ht + n) * kD + 32 * i + 8 * kg);
+
   // the block's pages that hold an attended position
   const int32_t *list = sel + (size_t)unit * max_sel;
   int count = 0;
@@ -142,26 +150,31 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
     __syncthreads();  // the list is complete
     list = lds_list;
   }
-  if (tid == 0) {
+  // wave 0: lane i takes the block's i-th page of the list
+  if (wave == 0) {
     if constexpr (!SELECT) count = sel_count[unit];
     const int first = split * kMlaPagesPerSplit, last = min(first + kMlaPagesPerSplit, count);
-    int np = 0;
-    for (int p = first; p < last; p++) {
+    const int p = first + lane;
+    bool keep = false;
+    int2 pg = make_int2(0, 0);
+    if (lane < kMlaPagesPerSplit && p < last) {
       const int j = list[p];
       const int pos0 = j * kPS, pos1 = min(pos0 + kPS, L);
-      if (pos0 < pos1 && (!is_static || pos0 < sink_end || pos1 > win_begin))
-        sh.pages[np++] = make_int2(page_table[(size_t)b * pt_stride + j], pos0);
+      keep = pos0 < pos1 && (!is_static || pos0 < sink_end || pos1 > win_begin);
+      if (keep) pg = make_int2(page_table[(size_t)b * pt_stride + j], pos0);
     }
-    sh.npages = np;
-    sh.overflow = 0;
+    const uint64_t kept = __ballot(keep);
+    if (keep) sh.pages[__popcll(kept & ((1ull << lane) - 1))] = pg;
+    if (lane == 0) {
+      sh.npages = __popcll(kept);
+      sh.overflow = 0;
+    }
   }
 
-  // q^T of the wave's S heads: column n = head 32 hg + 16 ht + n, channels 32i + 8kg ..
-  const size_t head_base = (size_t)b * Hq + (size_t)g * kG + kHeads * hg;
-  uint4 qB[kD / 32];
-#pragma unroll
-  for (int i = 0; i < kD / 32; i++)
-    qB[i] = *(const uint4 *)(q + (head_base + 16 * ht + n) * kD + 32 * i + 8 * kg);
+  // q has landed before the page loop: otherwise the loop's first products
+  // carry waits for q's loads, which the in-order load counter turns into
+  // waits for the page loads issued in the previous iteration
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int npages = sh.npages;
 
@@ -225,14 +238,16 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
         sv[r] = ok ? s[r] * scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, sv[r]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));  // this quarter's max of head column n
       if (m == -INFINITY) {  // first page (block-uniform): the reference is its max over all 64 tokens
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));  // this quarter's max of head column n
         if (kg == 0) sh.red[tq][16 * ht + n] = tmax;
         __syncthreads();
         m = fmaxf(fmaxf(sh.red[0][16 * ht + n], sh.red[1][16 * ht + n]),
                   fmaxf(sh.red[2][16 * ht + n], sh.red[3][16 * ht + n]));
       }
+      // the largest score seen and the weight sum stay per lane (this lane's
+      // tokens) until the loop ends
       seen = fmaxf(seen, tmax);
       if (__any(tmax > m + kHeadroom) && lane == 0) sh.overflow = 1;
       float p[4], pl[4];
@@ -243,8 +258,6 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
         psum += p[r];
         pl[r] = p[r] - bf16_round(p[r]);
       }
-      psum += __shfl_xor(psum, 16, kWave);
-      psum += __shfl_xor(psum, 32, kWave);
       l += psum;
       *(uint2 *)(pbuf + p_off) = pack_bf16x4(p);
       *(uint2 *)(pbuf + kPBytes + p_off) = pack_bf16x4(pl);
@@ -283,6 +296,8 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   run_pass();
   __syncthreads();
   if (sh.overflow) {  // some weight could exceed 2^kHeadroom: again, from the largest score seen
+    seen = fmaxf(seen, __shfl_xor(seen, 16, kWave));
+    seen = fmaxf(seen, __shfl_xor(seen, 32, kWave));
     if (kg == 0) sh.red[tq][16 * ht + n] = seen;
     __syncthreads();
     m = fmaxf(fmaxf(sh.red[0][16 * ht + n], sh.red[1][16 * ht + n]),
@@ -292,6 +307,8 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
     __syncthreads();
   }
   // the heads' sums over the four token quarters
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
   if (kg == 0) sh.red[tq][16 * ht + n] = l;
   __syncthreads();
 

@@ -5,13 +5,14 @@
 // hi_j, here a real contraction: 128 heads x 1152 channels against every
 // page.  A block of 8 waves stages the summary records of 16 pages in LDS and
 // each wave contracts its 16 heads ([q^-, q^+] formed from q on the fly as
-// the MFMA A operand, 36 steps of 16x16x32) against them.  The 32-product
-// MFMA results are summed in fp32 six at a time and the six partial sums in
-// fp64: per MFMA at most 32 roundings of unit 2^-23 (its bf16 products are
-// exact) on partial sums bounded by its S, five fp32 additions per partial
-// sum, exact fp64 conversions and negligible fp64 additions, then the final
-// rounding to fp32, so
-//     |U_fp32 - U| <= 39 * 2^-23 * 1.01 * S + 2^-50.
+// the MFMA A operand, 36 steps of 16x16x32) against them, all in fp32.  The
+// two MFMAs of a channel block are chained (the q^+ . hi product accumulates
+// onto the q^- . lo result), three such pairs are summed per chunk and the
+// six chunk sums in order.  Every bf16 product is exact, and each one passes
+// through at most 63 roundings inside its pair (any order of its 64
+// additions), 2 in its chunk and 5 across the chunks, each of unit 2^-23 on
+// a partial sum bounded by S, so
+//     |U_fp32 - U| <= 70 * 2^-23 * 1.01 * S + 2^-50.
 // S comes from Cauchy-Schwarz instead of a second contraction on absolute
 // values:
 //     S_h(j) = sum_d |q_hd| |x_hd| <= |q_h|_2 * N_j,  N_j^2 = sum_d max(lo_d^2, hi_d^2)
@@ -40,12 +41,12 @@ constexpr int kMlaWaves = 8;                  // 8 x 16 = 128 heads
 constexpr int kRecBytes = kMlaK2 * 2;         // LDS row of one page record (chunks swizzled)
 constexpr int kGroupBytes = 16 * kRecBytes;
 constexpr int kMlaGroups = 4;                 // 16-page groups per block (4 slabs: 144 KiB of LDS)
-constexpr int kMlaChunk = 6;                  // MFMA results summed in fp32 before the fp64 sum
-constexpr float kErrRelMla = 39.0f * 1.1920928955078125e-07f * 1.01f;  // see the file comment
+constexpr int kMlaChunk = 6;                  // MFMA results per chunk (three chained pairs)
+constexpr float kErrRelMla = 70.0f * 1.1920928955078125e-07f * 1.01f;  // see the file comment
 
 struct MlaScoreShared {
-  double best[kMlaGroups][kMlaWaves][16];    // per group, wave and page: largest head value,
-  double second[kMlaGroups][kMlaWaves][16];  // the runner-up,
+  float best[kMlaGroups][kMlaWaves][16];    // per group, wave and page: largest head value,
+  float second[kMlaGroups][kMlaWaves][16];  // the runner-up,
   int arg[kMlaGroups][kMlaWaves][16];        // and the leading head
   float norm2[kMlaGroups][kMlaWaves][16];    // partial page norms per wave
   float qnorm[kMlaWaves];
@@ -92,13 +93,13 @@ __device__ __forceinline__ void split_signs(const uint4 &x, uint4 &neg, uint4 &p
 __device__ __forceinline__ int slab_off(int n, int c) { return n * kRecBytes + 16 * (c ^ (n & 15)); }
 
 // Merges the top two (b1 >= b2, leader a1) with another top two.
-__device__ __forceinline__ void top2_merge(double &b1, double &b2, int &a1, double ob1, double ob2, int oa) {
+__device__ __forceinline__ void top2_merge(float &b1, float &b2, int &a1, float ob1, float ob2, int oa) {
   if (ob1 > b1) {
-    b2 = fmax(b1, ob2);
+    b2 = fmaxf(b1, ob2);
     b1 = ob1;
     a1 = oa;
   } else {
-    b2 = fmax(b2, ob1);
+    b2 = fmaxf(b2, ob1);
   }
 }
 
@@ -168,13 +169,24 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   auto slab_of = [&](int x) -> char * {
     return (char *)(x == 0 ? slab0 : x == 1 ? slab1 : x == 2 ? slab2 : slab3);
   };
+  // (the page ids of a wave's transfers are read from LDS before any is issued)
+  constexpr int kDmaPerWave = (kDmaPerGroup + kMlaWaves - 1) / kMlaWaves;
   auto issue_group = [&](int x) {
     char *slab = slab_of(x);
-    for (int t = wave; t < kDmaPerGroup; t += kMlaWaves) {
-      const int slot = 64 * t + lane, r = slot / kRecU4, sl = slot % kRecU4;
-      const int ph = max(sh.phys[x][r], 0);
-      const uint16_t *src = summ + ((size_t)ph * Hkv + g) * kMlaK2 + 8 * (sl ^ (r & 15));
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(slab + 1024 * t), 16, 0, 0);
+    int ph[kDmaPerWave];
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; k++) {
+      const int t = wave + kMlaWaves * k;
+      ph[k] = t < kDmaPerGroup ? max(sh.phys[x][(64 * t + lane) / kRecU4], 0) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; k++) {
+      const int t = wave + kMlaWaves * k;  // wave-uniform
+      if (t < kDmaPerGroup) {
+        const int slot = 64 * t + lane, r = slot / kRecU4, sl = slot % kRecU4;
+        const uint16_t *src = summ + ((size_t)ph[k] * Hkv + g) * kMlaK2 + 8 * (sl ^ (r & 15));
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(slab + 1024 * t), 16, 0, 0);
+      }
     }
   };
   if (ng > 0) issue_group(0);
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     // LDS together, one chunk ahead of the MFMAs that use them.
     static_assert(kMlaChunk == 6 && (kMlaD / 32) % 3 == 0, "three channel blocks per fp32 chunk");
     constexpr int kChunks = kMlaD / 32 / 3;
-    double u64[4] = {0.0, 0.0, 0.0, 0.0};
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
     uint4 fl[2][3], fh[2][3];  // [buffer][block in chunk]: lo and hi fragments
     // chunk 4i + kg of row n is at frag_base[i % 4] + 256 (i / 4), hi chunk
     // 72 + 4i + kg at frag_base[(i + 2) % 4] + 256 (4 + (i + 2) / 4): four
@@ -255,37 +267,40 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     for (int c = 0; c < kChunks; c++) {
       if (c + 1 < kChunks) read_chunk(c + 1, fl[(c + 1) & 1], fh[(c + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this chunk's MFMAs
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      floatx4 part;
 #pragma unroll
       for (int j = 0; j < 3; j++) {
         const int i = 3 * c + j;
         uint4 qn, qp;  // q^- and q^+ (the rest of q's bits) of channel block i
         split_signs(qraw[i], qn, qp);
-        const floatx4 un = mfma16x16x32(qn, fl[c & 1][j], floatx4{0.f, 0.f, 0.f, 0.f});
-        const floatx4 up = mfma16x16x32(qp, fh[c & 1][j], floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 t = mfma16x16x32(qp, fh[c & 1][j], mfma16x16x32(qn, fl[c & 1][j], floatx4{0.f, 0.f, 0.f, 0.f}));
+        if (j == 0) {
+          part = t;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; r++) part[r] = (part[r] + un[r]) + up[r];
+          for (int r = 0; r < 4; r++) part[r] += t[r];
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; r++) u64[r] += (double)part[r];
+      for (int r = 0; r < 4; r++) u[r] = c == 0 ? part[r] : u[r] + part[r];
     }
     // lane (n, kg) holds heads 16 wave + 4kg + r of page n: top two of the
     // wave's heads for page n (value, runner-up, leading head)
-    double b1 = -INFINITY, b2 = -INFINITY;
+    float b1 = -INFINITY, b2 = -INFINITY;
     int a1 = -1;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      if (u64[r] > b1) {
+      if (u[r] > b1) {
         b2 = b1;
-        b1 = u64[r];
+        b1 = u[r];
         a1 = 16 * wave + 4 * kg + r;
       } else {
-        b2 = fmax(b2, u64[r]);
+        b2 = fmaxf(b2, u[r]);
       }
     }
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
-      const double ob1 = __shfl_xor(b1, o, kWave), ob2 = __shfl_xor(b2, o, kWave);
+      const float ob1 = __shfl_xor(b1, o, kWave), ob2 = __shfl_xor(b2, o, kWave);
       const int oa = __shfl_xor(a1, o, kWave);
       top2_merge(b1, b2, a1, ob1, ob2, oa);
     }
@@ -295,10 +310,10 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       sh.arg[x][wave][n] = a1;
     }
   };
-  // combines the waves' results of group x into its 16 scores (wave 0)
-  auto finish = [&](int x) {
-    if (wave == 0 && lane < 16 && j0 + 16 * x + lane < cand_hi) {
-      double m = sh.best[x][0][lane], m2 = sh.second[x][0][lane];
+  // combines the waves' results of group x into its 16 scores (wave fw)
+  auto finish = [&](int x, int fw) {
+    if (wave == fw && lane < 16 && j0 + 16 * x + lane < cand_hi) {
+      float m = sh.best[x][0][lane], m2 = sh.second[x][0][lane];
       int arg = sh.arg[x][0][lane];
       float qn = sh.qnorm[0], n2 = sh.norm2[x][0][lane];
 #pragma unroll
@@ -314,13 +329,15 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   if (ng > 0) contract(0);
   if (ng > 1) contract(1);
   lds_barrier(true);  // groups 2 and 3 have landed; the results of 0 and 1 are in LDS
-  finish(0);
-  finish(1);
+  // two waves combine groups 0 and 1 before contracting 2 and 3, two others
+  // combine 2 and 3 at the end
+  finish(0, kMlaWaves - 2);
+  finish(1, kMlaWaves - 1);
   if (ng > 2) contract(2);
   if (ng > 3) contract(3);
   lds_barrier(false);
-  finish(2);
-  finish(3);
+  finish(2, 0);
+  finish(3, 1);
   lds_barrier(false);
   for (int t = tid; t < 16 * ng; t += kMlaWaves * 64) {
     const int j = j0 + t;
