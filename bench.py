@@ -489,6 +489,9 @@ def run_quant(args, torch, api, workloads, dev):
     gbps = total / (ms_per_step * 1e-3) / 1e9
     log("quantised-page step (R=%d): %.1f us; %d quantised + %d residual page-heads read" %
         (R, ms_per_step * 1e3, n_q, n_r))
+    L0 = layers[0]
+    one_kernel = api.decode_step_path(L0["lay"], L0["bat"], L0["pol"], L0["msel"]) == api.PATH_ONE_KERNEL
+    kernel = "fused_step_gqa_kernel (quantised form)" if one_kernel else "decode_step_quant (several kernels)"
     line = {
         "metric": "decode tokens/s with 2-bit quantised pages (residual %d pages), %s" % (R, spec.name),
         "value": round(spec.batch / (ms_per_step * 1e-3), 1),
@@ -506,7 +509,7 @@ def run_quant(args, torch, api, workloads, dev):
                    "layer_caches_rotated": args.layers},
         "step_bytes": total,
         "selected_bytes_quantised_vs_bf16": [attend_bytes - qo, b_decode - qo],
-        "roofline": {"kernel": "decode_step_quant (several kernels)", "bound": "hbm", "achieved": round(gbps, 1),
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes": total},
         "cpu_baseline": None,
@@ -661,6 +664,8 @@ def run_drafts(args, torch, api, workloads, dev):
     achieved = total / (step_ms * 1e-3) / 1e9
     log("multi-query step (%d drafts): events median %.1f us, wall %.1f us/step" % (n, step_ms * 1e3,
                                                                                    ms_per_step * 1e3))
+    one_kernel = api.decode_step_path(L0["lay"], L0["bat"], L0["pol"], L0["msel"]) == api.PATH_ONE_KERNEL
+    kernel = "fused_step_gqa_kernel (multi-query form)" if one_kernel else "decode_step_multi (several kernels)"
     line = {
         "metric": "draft tokens checked per second, multi-query step with %d drafts per sequence, %s" % (n, spec.name),
         "value": round(spec.batch * n / (ms_per_step * 1e-3), 1),
@@ -677,7 +682,7 @@ def run_drafts(args, torch, api, workloads, dev):
         "config": {"workload": spec.name, "batch": spec.batch, "seq_len": spec.seq_len, "drafts": n,
                    "layer_caches_rotated": args.layers},
         "step_us_events": round(step_ms * 1e3, 2),
-        "roofline": {"kernel": "decode_step_multi (several kernels)", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None, "algorithmic_bytes": total},
         "cpu_baseline": None,

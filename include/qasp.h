@@ -256,8 +256,9 @@ int32_t qasp_decode_step(const qasp_layout *lay, const qasp_batch *bat,
 /* Which kernels qasp_decode_step (and the multi-query and quantised steps,
  * for their own batch shapes) launch for these arguments:
  * QASP_PATH_ONE_KERNEL, the whole step as one kernel with a block per
- * (sequence, KV head) (grouped-query layouts with at least 200 such units
- * and a page list that fits the kernel's on-chip arrays), or
+ * (sequence, KV head) (grouped-query layouts with at least 200 such units, or
+ * with units of at most 640 KiB of summaries and selected pages each, whose
+ * page list fits the kernel's on-chip arrays), or
  * QASP_PATH_CHAIN, the append / score / select / attend / merge kernels.
  * Negative status for invalid arguments.  (For timing tools: which kernel a
  * profile should show.) */
