@@ -541,16 +541,26 @@ int32_t qasp_decode_step_quant(const qasp_layout *lay, const qasp_batch *bat, co
                                   max_sel, scale, out, ws, s);
     return status_of(e);
   }
-  if (k_new) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
+  // as in the bf16 chain: the scoring kernel appends the token when its page
+  // is no candidate, and the selection runs inside the attention launch when
+  // its LDS fits (a token that opened a new page pushed page P - 1 - R out of
+  // the residual region: the attention launch quantises it first)
+  // (the scoring kernel, when there is one, also quantises the page-head that
+  // leaves the residual region)
+  const bool fold_append = k_new && scored && pol->n_local_pages >= 1;
+  if (k_new && !fold_append) e = launch_append_kv(*lay, *bat, -1, k_new, v_new, k_pool, v_pool, summ, s);
   if (e == hipSuccess && scored)
     e = launch_score_pages(*lay, *bat, *pol, q, summ, ws.scores, s,
-                           token_append(*lay, nullptr, nullptr, nullptr, nullptr, nullptr));
+                           token_append(*lay, fold_append ? k_new : nullptr, v_new, k_pool, v_pool, summ), qpool,
+                           residual_pages, k_pool, v_pool);
+  if (e == hipSuccess && select_quant_lds_bytes(*lay, *bat, max_sel) <= 160 * 1024)
+    return status_of(launch_decode_quant_gqa(*lay, *bat, *pol, residual_pages, q, k_pool, v_pool, qpool, sel_out,
+                                             cnt_out, max_sel, scale, out, ws, s, ws.scores, summ, scored));
   if (e == hipSuccess)
     e = launch_select_topk(*lay, *bat, *pol, q, summ, ws.scores, sel_out, cnt_out, max_sel, s);
-  if (e == hipSuccess)  // (a token that opened a new page pushed page P - 1 - R out of the residual region:
-                        // the attention launch quantises it first)
+  if (e == hipSuccess)
     e = launch_decode_quant_gqa(*lay, *bat, *pol, residual_pages, q, k_pool, v_pool, qpool, sel_out, cnt_out,
-                                max_sel, scale, out, ws, s);
+                                max_sel, scale, out, ws, s, nullptr, nullptr, scored);
   return status_of(e);
 }
 

@@ -60,9 +60,13 @@ TokenAppend token_append(const qasp_layout &lay, const uint16_t *k_new, const ui
 // Scoring; with ap.k_new set, the first block of every (sequence, KV head)
 // row also appends the step's token at position L-1 (only valid when that
 // page is not a candidate, i.e. n_local_pages >= 1).
+// qpool (grouped-query layouts): also quantise the page-head that leaves the
+// residual region of residual_pages at this step (from k_pool / v_pool)
 hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
-                              qasp_score *scores, hipStream_t stream, const TokenAppend &ap);
+                              qasp_score *scores, hipStream_t stream, const TokenAppend &ap,
+                              uint8_t *qpool = nullptr, int residual_pages = 0, const uint16_t *k_pool = nullptr,
+                              const uint16_t *v_pool = nullptr);
 hipError_t launch_score_mla(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                             const uint16_t *q, const uint16_t *summ, qasp_score *scores, hipStream_t stream,
                             const TokenAppend &ap);
@@ -118,11 +122,14 @@ hipError_t launch_quantize(const qasp_layout &lay, const qasp_batch &bat, int re
 // (the attention also quantises the page that leaves the residual region at
 // this step: inside its blocks when units are not split, else by a
 // quantiser launch before it)
+// scores != nullptr: the selection inside the same launch (sel / sel_count then receive it)
 hipError_t launch_decode_quant_gqa(const qasp_layout &lay, const qasp_batch &bat, const qasp_policy &pol,
                                    int residual_pages, const uint16_t *q, const uint16_t *k_pool,
                                    const uint16_t *v_pool, const uint8_t *qpool, const int32_t *sel,
                                    const int32_t *sel_count, int max_sel, float scale, float *out,
-                                   const Workspace &ws, hipStream_t stream);
+                                   const Workspace &ws, hipStream_t stream, const qasp_score *scores = nullptr,
+                                   const uint16_t *summ = nullptr, bool quantised_before = false);
+size_t select_quant_lds_bytes(const qasp_layout &lay, const qasp_batch &bat, int max_sel);
 // Merge of the split partials; Gp (> 0) and nq map the partials' grouped
 // heads to out [B][nq][Hq / nq][Dv] (nq = 1: out [B][Hq][Dv]).
 hipError_t launch_merge_splits(const Workspace &ws, int batch, int Hq, int dv_dim, float *out,

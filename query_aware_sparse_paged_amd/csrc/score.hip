@@ -3,6 +3,7 @@
 // Candidates are the pages between the sink and the local window; every
 // other slot of a row gets value -inf, err 0.
 #include "launch.h"
+#include "quant_core.h"
 #include "score_core.h"
 
 namespace qasp {
@@ -18,13 +19,17 @@ constexpr int kScorePagesPerBlock = kScoreWaves * kScoreGroupsPerWave * 16;
 
 // Grid: (page blocks, Hkv, B); block = 4 waves; wave w scores
 // kScoreGroupsPerWave groups of 16 consecutive logical pages, loading group
-// i+1 while it computes group i.
+// i+1 while it computes group i.  With qpool, the row's first block also
+// quantises page-head (leaving page, g) of a step whose token opened a new
+// page (2-bit pages: the page that leaves the residual region; no block of
+// this kernel reads it, the attention launch after it does).
 template <int D>
 __global__ __launch_bounds__(256) void score_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ summ,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     qasp_score *__restrict__ scores, int pt_stride, int max_pages, int Hq, int Hkv, int G,
-    int ps, int n_sink, int n_local, uint64_t static_mask, TokenAppend ap) {
+    int ps, int n_sink, int n_local, uint64_t static_mask, TokenAppend ap, uint8_t *__restrict__ qpool,
+    int residual_pages, const uint16_t *__restrict__ qk_pool, const uint16_t *__restrict__ qv_pool) {
   constexpr int KSTEPS = 2 * D / 32;
   constexpr int GPW = kScoreGroupsPerWave;
   constexpr int PTR = (GPW * 16 + kWave - 1) / kWave;  // page-table registers per lane
@@ -39,6 +44,11 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
   // the step's token (page L-1 is not a candidate here), by the row's first block
   if (ap.k_new != nullptr && blockIdx.x == 0 && L > 0)
     ap.run(b, g, g + 1, page_table[(size_t)b * pt_stride + (L - 1) / ps], (L - 1) % ps, threadIdx.x, blockDim.x);
+  if (qpool != nullptr && blockIdx.x == 0) {  // block-uniform; every thread takes part (barriers inside)
+    __shared__ float qsm[256];
+    const int jl = quant::leaving_page(L, residual_pages);
+    if (jl >= 0) quant::quantize_page_head(qk_pool, qv_pool, qpool, page_table[(size_t)b * pt_stride + jl], g, Hkv, qsm);
+  }
   const int wave_first = (blockIdx.x * kScoreWaves + wave) * GPW * 16;
   if (wave_first >= max_pages) return;
 
@@ -80,7 +90,8 @@ __global__ __launch_bounds__(256) void score_gqa_kernel(
 
 hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
                               const qasp_policy &pol, const uint16_t *q, const uint16_t *summ,
-                              qasp_score *scores, hipStream_t stream, const TokenAppend &ap) {
+                              qasp_score *scores, hipStream_t stream, const TokenAppend &ap, uint8_t *qpool,
+                              int residual_pages, const uint16_t *k_pool, const uint16_t *v_pool) {
   if (bat.batch == 0 || bat.max_pages == 0) return hipSuccess;
   const int G = bat.num_q_heads / lay.num_kv_heads;
   dim3 grid((bat.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, lay.num_kv_heads,
@@ -89,7 +100,7 @@ hipError_t launch_score_pages(const qasp_layout &lay, const qasp_batch &bat,
     hipLaunchKernelGGL(score_gqa_kernel<128>, grid, dim3(256), 0, stream, q, summ, bat.page_table,
                        bat.seq_lens, scores, bat.pt_stride, bat.max_pages, bat.num_q_heads,
                        lay.num_kv_heads, G, lay.page_size, pol.n_sink_pages, pol.n_local_pages,
-                       pol.static_head_mask, ap);
+                       pol.static_head_mask, ap, qpool, residual_pages, k_pool, v_pool);
   } else if (lay.head_dim_k == 576) {
     return launch_score_mla(lay, bat, pol, q, summ, scores, stream, ap);
   } else {
