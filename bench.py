@@ -42,13 +42,21 @@ DEFAULT_WORKLOAD = "llama8b_b32_32k"
 METRIC = "decode tokens/s and achieved KV GB/s (% of MI355X HBM peak), 32K ctx, batch 32"
 
 
-def kernel_source_hash():
-    import glob
+# the sources the one-kernel step is compiled from (its file and every header it includes)
+FUSED_STEP_SOURCES = ("query_aware_sparse_paged_amd/csrc/fused_gqa.hip", "query_aware_sparse_paged_amd/csrc/attend_core.h",
+                      "query_aware_sparse_paged_amd/csrc/common.h", "query_aware_sparse_paged_amd/csrc/launch.h",
+                      "query_aware_sparse_paged_amd/csrc/quant_core.h", "query_aware_sparse_paged_amd/csrc/score_core.h",
+                      "query_aware_sparse_paged_amd/csrc/select_core.h", "include/qasp.h")
+
+
+def kernel_source_hash(files=FUSED_STEP_SOURCES):
+    """First 16 hex digits of the sha256 over the named sources (path and
+    contents): a counter record taken on other sources is stale."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "query_aware_sparse_paged_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for rel in sorted(files):
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
