@@ -56,12 +56,21 @@ __device__ __forceinline__ int2 unit_for_block(int i, const int32_t *seq_lens, i
   const int nq = B * n_qa, ns = B * (Hkv - n_qa);
   if (!lpt || B > T || nq % kEngines != 0 || ns % kEngines != 0)
     return make_int2(i % B, head_in_dispatch_order(static_mask, Hkv, i / B));
+  auto nth_head = [](uint64_t mask, int h) {
+    for (; h > 0; h--) mask &= mask - 1;  // drop the h lowest set bits
+    return __ffsll((long long)mask) - 1;
+  };
+  if (i >= nq) {  // block-uniform: a static unit, in sequence order (no ranking)
+    const int item = i - nq;
+    return make_int2(item % B, nth_head(st, item / B));
+  }
   const int tid = threadIdx.x;
   const int len = tid < B ? seq_lens[tid] : 0;
   if (tid < B) sm[tid] = len;
   __syncthreads();
   if (tid < B) {
     int rank = 0;
+#pragma unroll 8
     for (int u = 0; u < B; u++) {
       const int lu = sm[u];
       rank += lu > len || (lu == len && u < tid);
@@ -70,21 +79,9 @@ __device__ __forceinline__ int2 unit_for_block(int i, const int32_t *seq_lens, i
   }
   __syncthreads();
   const int row = i / kEngines, j = i % kEngines;
-  int b, h;
-  uint64_t mask;
-  if (i < nq) {
-    const int item = row * kEngines + (row & 1 ? kEngines - 1 - j : j);  // rank among the query-aware units
-    b = sm[T + item / n_qa];
-    h = item % n_qa;
-    mask = qa;
-  } else {
-    const int item = i - nq;
-    b = item % B;
-    h = item / B;
-    mask = st;
-  }
-  for (; h > 0; h--) mask &= mask - 1;  // drop the h lowest set bits
-  const int g = __ffsll((long long)mask) - 1;
+  const int item = row * kEngines + (row & 1 ? kEngines - 1 - j : j);  // rank among the query-aware units
+  const int b = sm[T + item / n_qa];
+  const int g = nth_head(qa, item % n_qa);
   __syncthreads();  // sm is free again
   return make_int2(b, g);
 }
@@ -281,6 +278,18 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const int k = top_k;
   const bool ranked = !is_static && k > 0 && k < n;
   const size_t head0 = (size_t)b * Hq + (size_t)g * G;
+  // a static head's selection is known without scores: the pages holding sink
+  // tokens, [0, st_sink), and those holding window tokens, [st_win, P)
+  // (st_win >= st_sink, so the two ranges do not overlap); list position i
+  // is page static_page(i)
+  int st_sink = 0, st_win = 0, st_count = 0;
+  if (is_static) {
+    const int sink_end = min(sink_tokens, L), win_begin = max(0, L - window_tokens);
+    st_sink = (sink_end + PS - 1) / PS;
+    st_win = max(st_sink, win_begin < L ? win_begin / PS : P);
+    st_count = min(st_sink + (P - st_win), max_sel);
+  }
+  auto static_page = [&](int i) { return i < st_sink ? i : st_win + (i - st_sink); };
 
   for (int w = tid; w < nwords; w += T) {
     sel_bits[w] = 0;
@@ -329,17 +338,18 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
           append_drafts_wave(draft_k, draft_v, k_pool, v_pool, summ, pt_row, L, n_draft, b, g, Hkv, lane);
       }
     }
-    for (int r0 = 0; r0 < P || r0 < 4 * nq; r0 += 4 * T) {  // 4 page-table entries and 1 q word per thread a round
-      int v[4];
+    constexpr int kPtPerRound = 8;  // page-table entries per thread a round (one round up to 4096 pages)
+    for (int r0 = 0; r0 < P || r0 < kPtPerRound * nq; r0 += kPtPerRound * T) {  // and 1 q word per thread
+      int v[kPtPerRound];
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
+      for (int r = 0; r < kPtPerRound; r++) {
         const int j = r0 + r * T + tid;
         v[r] = j < P ? pt_row[j] : 0;
       }
-      const int wq = r0 / 4 + tid;
+      const int wq = r0 / kPtPerRound + tid;
       const uint32_t qv = wq < nq ? q_word(wq) : 0u;
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
+      for (int r = 0; r < kPtPerRound; r++) {
         const int j = r0 + r * T + tid;
         if (j < P) page_phys[j] = v[r];
       }
@@ -491,24 +501,27 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   }
   const attend::PageWork<PS, D, DV, CAUSAL> pw{k_pool, v_pool, bq, Hkv, g, L, sink_end, win_begin,
                                                is_static, scale_log2, Lq, winq};
-  const bool pre = !QUANT && wave < n_known;  // wave-uniform
-  // issued by every wave (a valid page when there is nothing to preload), so
-  // the registers are always defined and the load is never waited on here
+  const bool pre = !QUANT && wave < (is_static ? st_count : n_known);  // wave-uniform
+  // issued by every wave (a valid page when there is nothing to preload:
+  // physical page 0), so the registers are always defined and the load is
+  // never waited on here
   attend::PageRegs<D, DV> first;
   if constexpr (!QUANT)
-    first = pw.load(pre ? page_phys[wave < cand_lo ? wave : cand_hi + (wave - cand_lo)] : (P > 0 ? page_phys[0] : 0),
+    first = pw.load(pre ? page_phys[is_static ? static_page(wave) : (wave < cand_lo ? wave : cand_hi + (wave - cand_lo))]
+                        : 0,
                     lane);
 
   // ---- select (usually no page is in doubt: then the selection is the k
   // largest keys and the list is written straight from them)
   bool fast = false;
   uint32_t uk_fast = 0;
-  if (is_static) {
-    const int sink_end = min(sink_tokens, L);
-    const int win_begin = max(0, L - window_tokens);
-    for (int j = tid; j < P; j += T) {
-      const int a = j * PS, e = min(a + PS, L);
-      if (a < sink_end || e > win_begin) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+  int32_t *sel_row = sel_out ? sel_out + (size_t)unit * max_sel : nullptr;
+  int count = st_count;
+  if (is_static) {  // block-uniform: the list straight from the page ranges
+    for (int i = tid; i < max_sel; i += T) {
+      const int j = i < st_count ? static_page(i) : -1;
+      if (i < st_count) list[i] = j;
+      if (sel_row) sel_row[i] = j;
     }
   } else {
     if (ranked) {
@@ -522,11 +535,10 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
     if (!fast)
       for (int j = tid; j < P; j += T)
         if (j < cand_lo || j >= cand_hi || (!ranked && k > 0)) atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+    __syncthreads();
+    count = fast ? sel::emit_by_threshold(sh, keys32, n, uk_fast, cand_lo, cand_hi, P, sel_row, list, max_sel)
+                 : sel::emit_selection(sh, sel_bits, nwords, sel_row, list, max_sel);
   }
-  __syncthreads();
-  int32_t *sel_row = sel_out ? sel_out + (size_t)unit * max_sel : nullptr;
-  const int count = fast ? sel::emit_by_threshold(sh, keys32, n, uk_fast, cand_lo, cand_hi, P, sel_row, list, max_sel)
-                         : sel::emit_selection(sh, sel_bits, nwords, sel_row, list, max_sel);
   if (tid == 0 && sel_count_out) sel_count_out[unit] = count;
   if constexpr (SEL_ONLY) return;  // block-uniform; the unused page preload above is not emitted
   __syncthreads();
