@@ -182,6 +182,8 @@ hipError_t launch_select_decode_gqa(const qasp_layout &lay, const qasp_batch &ba
   return launch_merge_splits(ws, bat.batch, bat.num_q_heads, lay.head_dim_v, out, stream, 1, G);
 }
 
+constexpr int kMergeFew = 4;  // up to this many splits: all of a thread's loads in one round
+
 // Combines the split partials of every (sequence, query head):
 // out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.  One block per
 // (sequence, head); a thread owns 4 consecutive channels and reads four
@@ -198,6 +200,37 @@ __global__ __launch_bounds__(128) void merge_splits_kernel(const float *__restri
   const int per_query = Gp / nq, col = h % Gp;
   const size_t out_row = ((size_t)b * nq + col / per_query) * (Hq / nq) + (size_t)(h / Gp) * per_query +
                          col % per_query;
+  if (splits <= kMergeFew) {  // block-uniform: every load of the thread in one round
+    float2 ml[kMergeFew];
+#pragma unroll
+    for (int s = 0; s < kMergeFew; s++) ml[s] = s < splits ? partial_ml[base + s] : make_float2(-INFINITY, 0.f);
+    for (int c = 4 * threadIdx.x; c < dv_dim; c += 4 * blockDim.x) {
+      float4 v[kMergeFew];
+#pragma unroll
+      for (int s = 0; s < kMergeFew; s++)
+        v[s] = s < splits ? *(const float4 *)(partial + (base + s) * dv_dim + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      float M = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < kMergeFew; s++) M = fmaxf(M, ml[s].x);
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      float lsum = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int s = 0; s < kMergeFew; s++) {
+          if (ml[s].x == -INFINITY) continue;  // empty split (or none): no weight
+          const float f = __builtin_amdgcn_exp2f(ml[s].x - M);
+          lsum += f * ml[s].y;
+          a.x += f * v[s].x;
+          a.y += f * v[s].y;
+          a.z += f * v[s].z;
+          a.w += f * v[s].w;
+        }
+      }
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      *(float4 *)(out + out_row * dv_dim + c) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    }
+    return;
+  }
   float M = -INFINITY;
   for (int s = 0; s < splits; s++) M = fmaxf(M, partial_ml[base + s].x);
   for (int c = 4 * threadIdx.x; c < dv_dim; c += 4 * blockDim.x) {
