@@ -109,7 +109,7 @@ __global__ __launch_bounds__(W * 64) void select_decode_gqa_kernel(
     int max_pages, int max_sel, int Hq, int Hkv, int G, int splits, int pps, float scale_log2, int n_sink,
     int n_local, int top_k, int sink_tokens, int window_tokens, uint64_t static_mask) {
   constexpr int PS = 16, D = 128, DV = 128;
-  extern __shared__ uint64_t dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t dyn[];  // 16-byte aligned: the list is written from 16-byte key loads
   __shared__ sel::SelShared<W> sh;
   const SelectDecodeLds lay(max_pages, max_sel, W, G);
   uint32_t *bits = (uint32_t *)((char *)dyn + lay.bits);

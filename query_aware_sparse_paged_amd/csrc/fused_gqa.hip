@@ -248,7 +248,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   static_assert(!(QUANT && (CAUSAL || SEL_ONLY)), "quantised pages: one-token attention");
   constexpr int NW = W, T = W * kWave;
   constexpr int KSTEPS = 2 * D / 32;
-  extern __shared__ uint64_t dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t dyn[];  // 16-byte aligned: the list is written from 16-byte key loads
   __shared__ sel::SelShared<NW> sh;
   __shared__ uint32_t sh_kmin, sh_kmax;
   __shared__ int sh_emax;

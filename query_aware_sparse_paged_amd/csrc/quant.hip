@@ -64,7 +64,7 @@ decode_quant_gqa_kernel(
     const uint16_t *__restrict__ v_pool_q, const qasp_score *__restrict__ scores, const uint16_t *__restrict__ summ,
     int max_pages, int n_sink, int n_local, int top_k) {
   constexpr int PS = 16, D = 128, DV = 128;
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte aligned: the list is written from 16-byte key loads
   int split, g, b;
   if constexpr (SELECT) {
     const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);

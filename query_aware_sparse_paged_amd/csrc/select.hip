@@ -16,7 +16,7 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(
     int max_sel, int Hq, int Hkv, int G, int ps, int n_sink, int n_local, int top_k,
     int sink_tokens, int window_tokens, uint64_t static_mask) {
   constexpr int NW = THREADS / kWave;
-  extern __shared__ uint64_t dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t dyn[];  // 16-byte aligned: the list is written from 16-byte key loads
   __shared__ sel::SelShared<NW> sh;
   const int g = blockIdx.x, b = blockIdx.y;
   const int unit = b * Hkv + g;

@@ -48,6 +48,7 @@ struct SelShared {
   int red[NW][4];             // per-wave partials of block reductions
   int digit, rem, nlist, bincnt;
   int n_in, n_band, nsel;
+  uint32_t kin, kib;          // smallest key above the band / of the band and above
   int kbin[2], krem[2], kcnt[2], nk[2];
   uint32_t uk, uk1;
   int list[kSmallBand];
@@ -665,11 +666,14 @@ __device__ __forceinline__ double exact_page_key_heads(const uint16_t *qg, int G
   return v;
 }
 
-// Marks the top-k candidates in sel_bits, or returns true without marking
-// anything when no candidate is in doubt (the k-th value beats the (k+1)-th
-// by more than twice the largest error bound): then the top k are exactly the
-// candidates whose key is >= *uk_fast (see emit_by_threshold).  Called by
-// every thread of the block.  Preconditions: keys32[0..n) hold the candidates' order keys (LDS,
+// Returns true when the top k are exactly the candidates whose key is >=
+// *uk_fast (see emit_by_threshold): always when no candidate is in doubt
+// (the k-th value beats the (k+1)-th by more than twice the largest error
+// bound), and when the pages in doubt are few (at most kSmallBand) or all
+// selected — the keys of re-scored band pages are then rewritten, winners to
+// the largest key and losers to 0.  Otherwise (a larger band, re-scored
+// through keys64) marks the top-k candidates in sel_bits and returns false.
+// Called by every thread of the block.  Preconditions: keys32[0..n) hold the candidates' order keys (LDS,
 // visible to all threads); band_bits and sh.hist are zero; emax, k_min and k_max are the
 // block-wide max error bound and the smallest and largest key;
 // 0 < k < n.  Candidate i is logical page cand_lo + i; pt_row is the
@@ -687,7 +691,10 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
                                   const int32_t *cand_phys, uint32_t *uk_fast) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   uint32_t uk, uk1;
-  if (tid == 0) sh.n_in = sh.n_band = 0;  // ordered before use by the barriers inside kth_pair
+  if (tid == 0) {  // ordered before use by the barriers inside kth_pair
+    sh.n_in = sh.n_band = 0;
+    sh.kin = sh.kib = ~0u;
+  }
   kth_pair<NW>(keys32, n, k, k_min, k_max, sh, uk, uk1);
   const float vk = f32_from_order(uk), vk1 = f32_from_order(uk1);
   const double t_in = (double)vk1 + 2.0 * (double)emax;
@@ -698,45 +705,56 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
     *uk_fast = uk;
     return true;
   }
-  int c_in = 0, c_band = 0;
+  // one pass: count the pages certainly in, the smallest key among them and
+  // among the pages not certainly out, and list the band (sh.nlist counts it;
+  // the first kSmallBand indices land in sh.list, every one in band_bits)
+  int c_in = 0;
+  uint32_t kin = ~0u, kib = ~0u;
   for (int i = tid; i < n; i += NW * kWave) {
-    const double v = (double)f32_from_order(keys32[i]);
-    const int j = cand_lo + i;
+    const uint32_t key = keys32[i];
+    const double v = (double)f32_from_order(key);
     if (v > t_in) {
-      atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
       c_in++;
+      kin = min(kin, key);
+      kib = min(kib, key);
     } else if (!(v < t_out)) {
+      kib = min(kib, key);
       atomicOr(&band_bits[i >> 5], 1u << (i & 31));
-      c_band++;
+      const int pos = atomicAdd(&sh.nlist, 1);
+      if (pos < kSmallBand) sh.list[pos] = i;
     }
   }
   c_in = wave_sum_dpp(c_in);
-  c_band = wave_sum_dpp(c_band);
+  kin = ~(uint32_t)wave_max_dpp((int)(~kin ^ 0x80000000u)) ^ 0x80000000u;  // wave min of unsigned keys
+  kib = ~(uint32_t)wave_max_dpp((int)(~kib ^ 0x80000000u)) ^ 0x80000000u;
   if (lane == 0) {
     if (c_in) atomicAdd(&sh.n_in, c_in);
-    if (c_band) atomicAdd(&sh.n_band, c_band);
+    atomicMin(&sh.kin, kin);
+    atomicMin(&sh.kib, kib);
   }
   __syncthreads();
-  const int n_in = sh.n_in, n_band = sh.n_band;
+  const int n_in = sh.n_in, n_band = sh.nlist;
   const int need = k - n_in;
-  if (need > 0 && need >= n_band) {
-    for (int i = tid; i < n; i += NW * kWave)
-      if ((band_bits[i >> 5] >> (i & 31)) & 1u) {
-        const int j = cand_lo + i;
-        atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-      }
-  } else if (need > 0) {
-    // exact scores of the band pages
-    const uint16_t *qb = qg;
-    if (qg != sh.qstage && (size_t)G * D * 2 <= kQStageBytes) {  // stage the group's q rows in LDS
-      for (int i = tid; i < G * D / 2; i += NW * kWave) ((uint32_t *)sh.qstage)[i] = ((const uint32_t *)qb)[i];
-      qb = sh.qstage;
-    }
+  if (need <= 0) {  // (block-uniform) no band page is needed: the pages above the band
+    *uk_fast = sh.kin;
+    return true;
+  }
+  if (need >= n_band) {  // every band page is needed: the band and the pages above it
+    *uk_fast = sh.kib;
+    return true;
+  }
+  // exact scores of the band pages
+  const uint16_t *qb = qg;
+  const bool stage = qg != sh.qstage && (size_t)G * D * 2 <= kQStageBytes;  // block-uniform
+  if (stage) {  // the group's q rows to LDS
+    for (int i = tid; i < G * D / 2; i += NW * kWave) ((uint32_t *)sh.qstage)[i] = ((const uint32_t *)qb)[i];
+    qb = sh.qstage;
+  }
+  {
     if (n_band <= kSmallBand) {
-      // compact list of the band, exact keys (one page per wave), rank by one wave
-      for (int i = tid; i < n; i += NW * kWave)
-        if ((band_bits[i >> 5] >> (i & 31)) & 1u) sh.list[atomicAdd(&sh.nlist, 1)] = i;
-      __syncthreads();
+      // exact keys of the listed band (one page per wave), ranked by one wave;
+      // the winners' keys become the largest key, the losers' 0
+      if (stage) __syncthreads();  // the staged q rows
       for (int e = wave; e < n_band; e += NW) {
         const int i = sh.list[e];
         const int phys = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
@@ -765,12 +783,19 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
           const double ke = sh.lkey[e];
           rank += ke > kl || (ke == kl && sh.list[e] < il);
         }
-        if (rank < need) {
-          const int j = cand_lo + il;
+        keys32[il] = rank < need ? ~0u : 0u;
+      }
+      __syncthreads();  // the rewritten keys
+      *uk_fast = sh.kin;  // the pages above the band and the winners (all keys >= it)
+      return true;
+    } else {
+      // the pages above the band into sel_bits (their keys are >= sh.kin)
+      const uint32_t kin_all = sh.kin;
+      for (int i = tid; i < n; i += NW * kWave)
+        if (keys32[i] >= kin_all) {
+          const int j = cand_lo + i;
           atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
         }
-      }
-    } else {
       __syncthreads();  // keys32 is dead from here; keys64 reuses the space
       uint64_t b_and = ~0ull, b_or = 0;
       int seen = 0;
@@ -821,13 +846,14 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
 // The ascending selection when select_candidates returned true: the sink
 // pages [0, cand_lo), the candidates whose key is >= uk, the local pages
 // [cand_hi, P).  Written to out_global (followed by -1 up to max_sel) and/or
-// out_lds; returns the count.  Thread t takes candidates 4t .. 4t+3 of a
-// round of 4T; a wave prefix sum and the wave totals in LDS give their
-// slots.  No bit map is built.
+// out_lds; returns the count.  Thread t takes candidates 16t .. 16t+15 of a
+// round of 16T (four 16-byte LDS loads); a wave prefix sum and the wave
+// totals in LDS give their slots, so a round costs one barrier.  No bit map
+// is built.  keys32 must be 16-byte aligned.
 template <int NW>
 __device__ int emit_by_threshold(SelShared<NW> &sh, const uint32_t *keys32, int n, uint32_t uk, int cand_lo,
                                  int cand_hi, int P, int32_t *out_global, int32_t *out_lds, int max_sel) {
-  constexpr int T = NW * kWave;
+  constexpr int T = NW * kWave, PER = 16;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   auto put = [&](int pos, int j) {
     if (pos < max_sel) {
@@ -837,12 +863,22 @@ __device__ int emit_by_threshold(SelShared<NW> &sh, const uint32_t *keys32, int 
   };
   for (int j = tid; j < cand_lo; j += T) put(j, j);  // sink pages
   int base = cand_lo;
-  for (int i0 = 0; i0 < n; i0 += 4 * T) {
-    const int i = i0 + 4 * tid;
-    uint32_t m = 0;  // bit r: candidate i + r is selected
+  for (int i0 = 0; i0 < n; i0 += PER * T) {
+    const int i = i0 + PER * tid;
+    // four-key chunks that start below n (the keys area holds 8 bytes per
+    // page, so a chunk's tail past n is still inside it; those keys are masked)
+    uint4 v[PER / 4];
 #pragma unroll
-    for (int r = 0; r < 4; r++)
-      if (i + r < n && keys32[i + r] >= uk) m |= 1u << r;
+    for (int r = 0; r < PER / 4; r++)
+      v[r] = i + 4 * r < n ? *(const uint4 *)(keys32 + i + 4 * r) : make_uint4(0, 0, 0, 0);
+    uint32_t m = 0;  // bit e: candidate i + e is selected
+#pragma unroll
+    for (int r = 0; r < PER / 4; r++) {
+      const uint32_t kr[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        if (i + 4 * r + e < n && kr[e] >= uk) m |= 1u << (4 * r + e);
+    }
     const int c = __popc(m);
     const int incl = wave_incl_sum(c);
     if (lane == kWave - 1) sh.red[wave][2] = incl;
@@ -855,12 +891,12 @@ __device__ int emit_by_threshold(SelShared<NW> &sh, const uint32_t *keys32, int 
       round += t;
     }
     while (m) {
-      const int r = __builtin_ctz(m);
+      const int e = __builtin_ctz(m);
       m &= m - 1;
-      put(pos++, cand_lo + i + r);
+      put(pos++, cand_lo + i + e);
     }
     base += round;
-    if (i0 + 4 * T < n) __syncthreads();  // sh.red is rewritten next round
+    if (i0 + PER * T < n) __syncthreads();  // sh.red is rewritten next round
   }
   const int nloc = P - cand_hi;
   for (int x = tid; x < nloc; x += T) put(base + x, cand_hi + x);  // local pages
