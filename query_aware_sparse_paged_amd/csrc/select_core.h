@@ -52,6 +52,7 @@ struct SelShared {
   int kbin[2], krem[2], kcnt[2], nk[2];
   uint32_t uk, uk1;
   int list[kSmallBand];
+  int bphys[kSmallBand], blead[kSmallBand];  // physical page and certified leading head of listed band pages
   uint32_t klist[kSmallBand];   // keys of one histogram bin
   uint32_t klist1[kSmallBand];  // keys of a second bin
   double lkey[kSmallBand];
@@ -708,20 +709,35 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
   // one pass: count the pages certainly in, the smallest key among them and
   // among the pages not certainly out, and list the band (sh.nlist counts it;
   // the first kSmallBand indices land in sh.list, every one in band_bits)
+  // (thread t takes candidates 16t .. 16t+15 of a round of 16T: four 16-byte
+  // LDS loads, as in emit_by_threshold)
   int c_in = 0;
   uint32_t kin = ~0u, kib = ~0u;
-  for (int i = tid; i < n; i += NW * kWave) {
-    const uint32_t key = keys32[i];
-    const double v = (double)f32_from_order(key);
-    if (v > t_in) {
-      c_in++;
-      kin = min(kin, key);
-      kib = min(kib, key);
-    } else if (!(v < t_out)) {
-      kib = min(kib, key);
-      atomicOr(&band_bits[i >> 5], 1u << (i & 31));
-      const int pos = atomicAdd(&sh.nlist, 1);
-      if (pos < kSmallBand) sh.list[pos] = i;
+  for (int i0 = 0; i0 < n; i0 += 16 * NW * kWave) {
+    const int i = i0 + 16 * tid;
+    uint4 kv[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) kv[r] = i + 4 * r < n ? *(const uint4 *)(keys32 + i + 4 * r) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const uint32_t kr[4] = {kv[r].x, kv[r].y, kv[r].z, kv[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int ie = i + 4 * r + e;
+        if (ie >= n) continue;
+        const uint32_t key = kr[e];
+        const double v = (double)f32_from_order(key);
+        if (v > t_in) {
+          c_in++;
+          kin = min(kin, key);
+          kib = min(kib, key);
+        } else if (!(v < t_out)) {
+          kib = min(kib, key);
+          atomicOr(&band_bits[ie >> 5], 1u << (ie & 31));
+          const int pos = atomicAdd(&sh.nlist, 1);
+          if (pos < kSmallBand) sh.list[pos] = ie;
+        }
+      }
     }
   }
   c_in = wave_sum_dpp(c_in);
@@ -753,14 +769,19 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
   {
     if (n_band <= kSmallBand) {
       // exact keys of the listed band (one page per wave), ranked by one wave;
-      // the winners' keys become the largest key, the losers' 0
-      if (stage) __syncthreads();  // the staged q rows
+      // the winners' keys become the largest key, the losers' 0.  The band
+      // pages' physical pages and leading heads are fetched together first.
+      if (tid < n_band) {
+        const int i = sh.list[tid];
+        sh.bphys[tid] = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
+        sh.blead[tid] = cand_scores ? cand_scores[i].head : -1;
+      }
+      __syncthreads();  // the staged q rows, the band pages' entries
       for (int e = wave; e < n_band; e += NW) {
-        const int i = sh.list[e];
-        const int phys = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
+        const int phys = sh.bphys[e];
         const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
         double key;
-        const int lead = cand_scores ? cand_scores[i].head : -1;
+        const int lead = sh.blead[e];
         if (lead >= 0) {
           key = exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane);
         } else if (D == 128 && G <= 16) {
