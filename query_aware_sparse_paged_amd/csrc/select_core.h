@@ -667,6 +667,63 @@ __device__ __forceinline__ double exact_page_key_heads(const uint16_t *qg, int G
   return v;
 }
 
+// Keys per thread of a pass over the n candidate keys with T threads: the
+// fewest (4, 8 or 16) that cover them in one round, so that small sets
+// spread over many threads and large ones need no more barriers.
+template <int T>
+__device__ __forceinline__ int keys_per_thread(int n) {
+  return n <= 4 * T ? 4 : (n <= 8 * T ? 8 : 16);
+}
+
+// Four-key chunks [i, i + PER) of the candidate keys that start below n, as
+// 16-byte LDS loads (the keys area holds 8 bytes per page, so a chunk's tail
+// past n is still inside it; callers mask those keys).  keys32 must be
+// 16-byte aligned.
+template <int PER>
+__device__ __forceinline__ void load_key_chunks(uint32_t (&kr)[PER], const uint32_t *keys32, int i, int n) {
+#pragma unroll
+  for (int r = 0; r < PER / 4; r++) {
+    const uint4 v = i + 4 * r < n ? *(const uint4 *)(keys32 + i + 4 * r) : make_uint4(0, 0, 0, 0);
+    kr[4 * r] = v.x;
+    kr[4 * r + 1] = v.y;
+    kr[4 * r + 2] = v.z;
+    kr[4 * r + 3] = v.w;
+  }
+}
+
+// The classification pass of select_candidates over this thread's keys
+// (PER per thread a round): counts the keys certainly in (value above t_in)
+// and the smallest such key (kin) and the smallest key not certainly out
+// (value not below t_out: kib); the keys in doubt go to band_bits and, the
+// first kSmallBand of them, to sh.list (sh.nlist counts them all).
+template <int NW, int PER>
+__device__ __forceinline__ void classify_keys(SelShared<NW> &sh, const uint32_t *keys32, uint32_t *band_bits, int n,
+                                              double t_in, double t_out, int &c_in, uint32_t &kin, uint32_t &kib) {
+  constexpr int T = NW * kWave;
+  for (int i0 = 0; i0 < n; i0 += PER * T) {
+    const int i = i0 + PER * (int)threadIdx.x;
+    uint32_t kr[PER];
+    load_key_chunks<PER>(kr, keys32, i, n);
+#pragma unroll
+    for (int e = 0; e < PER; e++) {
+      const int ie = i + e;
+      if (ie >= n) continue;
+      const uint32_t key = kr[e];
+      const double v = (double)f32_from_order(key);
+      if (v > t_in) {
+        c_in++;
+        kin = min(kin, key);
+        kib = min(kib, key);
+      } else if (!(v < t_out)) {
+        kib = min(kib, key);
+        atomicOr(&band_bits[ie >> 5], 1u << (ie & 31));
+        const int pos = atomicAdd(&sh.nlist, 1);
+        if (pos < kSmallBand) sh.list[pos] = ie;
+      }
+    }
+  }
+}
+
 // Returns true when the top k are exactly the candidates whose key is >=
 // *uk_fast (see emit_by_threshold): always when no candidate is in doubt
 // (the k-th value beats the (k+1)-th by more than twice the largest error
@@ -709,37 +766,17 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
   // one pass: count the pages certainly in, the smallest key among them and
   // among the pages not certainly out, and list the band (sh.nlist counts it;
   // the first kSmallBand indices land in sh.list, every one in band_bits)
-  // (thread t takes candidates 16t .. 16t+15 of a round of 16T: four 16-byte
-  // LDS loads, as in emit_by_threshold)
+  // (keys_per_thread keys per thread, 16-byte LDS loads, as in
+  // emit_by_threshold)
   int c_in = 0;
   uint32_t kin = ~0u, kib = ~0u;
-  for (int i0 = 0; i0 < n; i0 += 16 * NW * kWave) {
-    const int i = i0 + 16 * tid;
-    uint4 kv[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) kv[r] = i + 4 * r < n ? *(const uint4 *)(keys32 + i + 4 * r) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const uint32_t kr[4] = {kv[r].x, kv[r].y, kv[r].z, kv[r].w};
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int ie = i + 4 * r + e;
-        if (ie >= n) continue;
-        const uint32_t key = kr[e];
-        const double v = (double)f32_from_order(key);
-        if (v > t_in) {
-          c_in++;
-          kin = min(kin, key);
-          kib = min(kib, key);
-        } else if (!(v < t_out)) {
-          kib = min(kib, key);
-          atomicOr(&band_bits[ie >> 5], 1u << (ie & 31));
-          const int pos = atomicAdd(&sh.nlist, 1);
-          if (pos < kSmallBand) sh.list[pos] = ie;
-        }
-      }
-    }
-  }
+  const int per = keys_per_thread<NW * kWave>(n);  // block-uniform
+  if (per == 4)
+    classify_keys<NW, 4>(sh, keys32, band_bits, n, t_in, t_out, c_in, kin, kib);
+  else if (per == 8)
+    classify_keys<NW, 8>(sh, keys32, band_bits, n, t_in, t_out, c_in, kin, kib);
+  else
+    classify_keys<NW, 16>(sh, keys32, band_bits, n, t_in, t_out, c_in, kin, kib);
   c_in = wave_sum_dpp(c_in);
   kin = ~(uint32_t)wave_max_dpp((int)(~kin ^ 0x80000000u)) ^ 0x80000000u;  // wave min of unsigned keys
   kib = ~(uint32_t)wave_max_dpp((int)(~kib ^ 0x80000000u)) ^ 0x80000000u;
@@ -864,42 +901,22 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
   return false;
 }
 
-// The ascending selection when select_candidates returned true: the sink
-// pages [0, cand_lo), the candidates whose key is >= uk, the local pages
-// [cand_hi, P).  Written to out_global (followed by -1 up to max_sel) and/or
-// out_lds; returns the count.  Thread t takes candidates 16t .. 16t+15 of a
-// round of 16T (four 16-byte LDS loads); a wave prefix sum and the wave
-// totals in LDS give their slots, so a round costs one barrier.  No bit map
-// is built.  keys32 must be 16-byte aligned.
-template <int NW>
-__device__ int emit_by_threshold(SelShared<NW> &sh, const uint32_t *keys32, int n, uint32_t uk, int cand_lo,
-                                 int cand_hi, int P, int32_t *out_global, int32_t *out_lds, int max_sel) {
-  constexpr int T = NW * kWave, PER = 16;
+// The candidates whose key is >= uk, ascending, from slot base on (see
+// emit_by_threshold); thread t takes candidates PER t .. PER t + PER-1 of a
+// round of PER T; returns the slot after the last.
+template <int NW, int PER, typename Put>
+__device__ __forceinline__ int emit_keys_at_least(SelShared<NW> &sh, const uint32_t *keys32, int n, uint32_t uk,
+                                                  int cand_lo, int base, Put put) {
+  constexpr int T = NW * kWave;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  auto put = [&](int pos, int j) {
-    if (pos < max_sel) {
-      if (out_global) out_global[pos] = j;
-      if (out_lds) out_lds[pos] = j;
-    }
-  };
-  for (int j = tid; j < cand_lo; j += T) put(j, j);  // sink pages
-  int base = cand_lo;
   for (int i0 = 0; i0 < n; i0 += PER * T) {
     const int i = i0 + PER * tid;
-    // four-key chunks that start below n (the keys area holds 8 bytes per
-    // page, so a chunk's tail past n is still inside it; those keys are masked)
-    uint4 v[PER / 4];
-#pragma unroll
-    for (int r = 0; r < PER / 4; r++)
-      v[r] = i + 4 * r < n ? *(const uint4 *)(keys32 + i + 4 * r) : make_uint4(0, 0, 0, 0);
+    uint32_t kr[PER];
+    load_key_chunks<PER>(kr, keys32, i, n);
     uint32_t m = 0;  // bit e: candidate i + e is selected
 #pragma unroll
-    for (int r = 0; r < PER / 4; r++) {
-      const uint32_t kr[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-#pragma unroll
-      for (int e = 0; e < 4; e++)
-        if (i + 4 * r + e < n && kr[e] >= uk) m |= 1u << (4 * r + e);
-    }
+    for (int e = 0; e < PER; e++)
+      if (i + e < n && kr[e] >= uk) m |= 1u << e;
     const int c = __popc(m);
     const int incl = wave_incl_sum(c);
     if (lane == kWave - 1) sh.red[wave][2] = incl;
@@ -919,6 +936,32 @@ __device__ int emit_by_threshold(SelShared<NW> &sh, const uint32_t *keys32, int 
     base += round;
     if (i0 + PER * T < n) __syncthreads();  // sh.red is rewritten next round
   }
+  return base;
+}
+
+// The ascending selection when select_candidates returned true: the sink
+// pages [0, cand_lo), the candidates whose key is >= uk, the local pages
+// [cand_hi, P).  Written to out_global (followed by -1 up to max_sel) and/or
+// out_lds; returns the count.  The candidates are counted in rounds of
+// keys_per_thread keys per thread (16-byte LDS loads); a wave prefix sum and
+// the wave totals in LDS give their slots, so a round costs one barrier.  No
+// bit map is built.  keys32 must be 16-byte aligned.
+template <int NW>
+__device__ int emit_by_threshold(SelShared<NW> &sh, const uint32_t *keys32, int n, uint32_t uk, int cand_lo,
+                                 int cand_hi, int P, int32_t *out_global, int32_t *out_lds, int max_sel) {
+  constexpr int T = NW * kWave;
+  const int tid = threadIdx.x;
+  auto put = [&](int pos, int j) {
+    if (pos < max_sel) {
+      if (out_global) out_global[pos] = j;
+      if (out_lds) out_lds[pos] = j;
+    }
+  };
+  for (int j = tid; j < cand_lo; j += T) put(j, j);  // sink pages
+  const int per = keys_per_thread<T>(n);  // block-uniform
+  const int base = per == 4    ? emit_keys_at_least<NW, 4>(sh, keys32, n, uk, cand_lo, cand_lo, put)
+                   : per == 8 ? emit_keys_at_least<NW, 8>(sh, keys32, n, uk, cand_lo, cand_lo, put)
+                              : emit_keys_at_least<NW, 16>(sh, keys32, n, uk, cand_lo, cand_lo, put);
   const int nloc = P - cand_hi;
   for (int x = tid; x < nloc; x += T) put(base + x, cand_hi + x);  // local pages
   const int count = min(base + nloc, max_sel);
