@@ -82,6 +82,28 @@ def test_edges(lens, pol):
     compare(g, r, what="edge %s" % lens)
 
 
+@pytest.mark.parametrize("sink,window", [(0, 40), (5, 0), (0, 0), (33, 31), (4000, 16), (16, 17)])
+def test_static_heads_page_ranges(sink, window):
+    """A static head's list is two page ranges computed from the length (in
+    the one-kernel step, with no selection pass): pages that hold sink tokens,
+    then pages that hold window tokens; cases at page boundaries, with an empty
+    sink or window or both, and with the two ranges meeting or overlapping."""
+    lens = [1, 15, 16, 17, 31, 32, 33, 100]
+    w = _small("tiny_b1_4k", batch=len(lens), seq_len=max(lens))
+    w.seq_lens[:] = torch.tensor(lens, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        phys = int(w.page_table[b, (L - 1) // 16])
+        w.k_new[b] = w.k_pool[phys, :, (L - 1) % 16, :]
+        w.v_new[b] = w.v_pool[phys, :, :, (L - 1) % 16]
+    pol = api.Policy(1, 2, 3, sink, window, [1, 1, 0, 1, 0, 1, 1, 0])
+    lay = api.layout_of(w)
+    bat = api.Batch(w.page_table, w.seq_lens, w.spec.num_q_heads)
+    assert api.decode_step_path(lay, bat, pol, api.max_sel(lay, pol, bat.max_pages)) == api.PATH_ONE_KERNEL
+    g = run_gpu(w, pol=pol)
+    r = run_oracle(w, pol, g.max_sel)
+    compare(g, r, what="static page ranges %d/%d" % (sink, window))
+
+
 def test_all_static_heads_without_summaries():
     w = _small("ragged_b64_mixed", batch=3, seq_len=3000, seq_len_min=10)
     pol = api.Policy(0, 0, 0, 4, 100, [1] * 8)
