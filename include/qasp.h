@@ -78,9 +78,13 @@ typedef enum {
  *            (token index fastest inside a page-head), or NULL when
  *            v_from_k = 1: the value of a token is then the first head_dim_v
  *            channels of its key (one latent vector per token, as in MLA).
- *   summ     [num_pool_pages][num_kv_heads][2][head_dim_k]
+ *   summ     [num_pool_pages][num_kv_heads][2][head_dim_k] records,
  *            row 0 = elementwise minimum, row 1 = elementwise maximum of the
- *            keys of the page's valid tokens, with -0 ordered below +0.
+ *            keys of the page's valid tokens, with -0 ordered below +0; the
+ *            record of KV head g of physical page p is in slot
+ *            (g + p) mod num_kv_heads of row p (the library writes and reads
+ *            it there; the rotation spreads every head's records over all
+ *            the offsets of a row).
  * Supported shapes:
  *   grouped-query: page_size 16, head_dim_k = head_dim_v = 128,
  *                  1 <= num_q_heads / num_kv_heads <= 16, num_kv_heads <= 64;

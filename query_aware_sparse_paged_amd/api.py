@@ -258,6 +258,19 @@ def _u16(t):
     return t.view(torch.int16) if t is not None else None
 
 
+def summary_rows(summ: torch.Tensor, phys) -> torch.Tensor:
+    """The summary records of the physical pages phys (indices, or a boolean
+    mask over the pool) in KV-head order, [n][Hkv][2][Dk]: in the pool the
+    record of KV head g of page p sits in slot (g + p) mod Hkv of row p."""
+    phys = torch.as_tensor(phys, device=summ.device)
+    if phys.dtype == torch.bool:
+        phys = phys.nonzero().flatten()
+    phys = phys.to(torch.int64)
+    hkv = summ.shape[1]
+    slot = (torch.arange(hkv, device=summ.device)[None, :] + phys[:, None]) % hkv
+    return summ[phys[:, None], slot]
+
+
 def build_summaries(layout: Layout, batch: Batch, k_pool: torch.Tensor, summ: torch.Tensor):
     _check_args(*batch.specs(), *_pool_specs(layout, k_pool, None, summ))
     _check(lib().qasp_build_summaries(ctypes.byref(layout.c()), ctypes.byref(batch.c()), _ptr(k_pool),

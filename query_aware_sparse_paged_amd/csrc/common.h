@@ -178,6 +178,19 @@ __device__ __forceinline__ int xcd_contiguous_item(int blk, int total) {
   return total % kXcds == 0 ? (blk % kXcds) * (total / kXcds) + blk / kXcds : blk;
 }
 
+// Index of the summary record of KV head g of physical page phys in the
+// summary pool, [pool][Hkv] records of [2][D] bf16 (lo row, hi row): the
+// record sits in slot (g + phys) mod Hkv of the page's row.  Rotating the slot
+// with the page spreads every head's records over all the slot offsets, so no
+// head's reads fall on a fixed part of the address bits (with fixed slots the
+// even heads' records sit at 1 KiB-aligned offsets and were read measurably
+// slower than the odd heads').
+__device__ __forceinline__ size_t summ_record(int phys, int g, int Hkv) {
+  int slot = g + phys % Hkv;
+  if (slot >= Hkv) slot -= Hkv;
+  return (size_t)phys * Hkv + slot;
+}
+
 // The new token of a decode step, appended by one block for the KV heads
 // [g0, g1) of sequence b: its key row and value column go into the page
 // `phys` at slot t, and its key is folded into the page summary (slot 0
@@ -188,7 +201,7 @@ struct TokenAppend {
   const uint16_t *v_new;  // [B][Hkv][Dv], or null (latent heads)
   uint32_t *k_pool;       // [pool][Hkv][ps][D / 2]
   uint16_t *v_pool;       // [pool][Hkv][Dv][ps], or null
-  uint32_t *summ;         // [pool][Hkv][2][D / 2], or null
+  uint32_t *summ;         // [pool][Hkv][2][D / 2] (record slots: summ_record), or null
   int num_kv_heads, head_dim_k, head_dim_v, ps;
 
   __device__ void run(int b, int g0, int g1, int phys, int t, int tid, int nthreads) const {
@@ -199,7 +212,7 @@ struct TokenAppend {
       const uint32_t kv = k_new[((size_t)b * num_kv_heads + g) * words + w];
       k_pool[(ph * ps + t) * words + w] = kv;
       if (summ) {
-        uint32_t *s = summ + ph * 2 * words;
+        uint32_t *s = summ + summ_record(phys, g, num_kv_heads) * 2 * words;
         uint32_t lo = kv, hi = kv;
         if (t != 0) {
           const int v0 = bf16_order_key(kv & 0xffffu), v1 = bf16_order_key(kv >> 16);

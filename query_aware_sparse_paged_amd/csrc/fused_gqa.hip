@@ -112,7 +112,7 @@ __device__ __forceinline__ void append_drafts_wave(const uint16_t *__restrict__ 
   const int i0 = max(0, n_draft - L);  // drafts at negative positions are not written
   uint32_t lo = 0, hi = 0;
   int cur_page = -1;
-  size_t cur_ph = 0;
+  size_t cur_sr = 0;  // summary record of the current page
   for (int c0 = i0; c0 < n_draft; c0 += 4) {
     uint32_t kv[4];
     uint16_t va[4], vb[4];
@@ -138,17 +138,17 @@ __device__ __forceinline__ void append_drafts_wave(const uint16_t *__restrict__ 
       if (summ == nullptr) continue;
       if (page != cur_page) {
         if (cur_page >= 0) {
-          uint32_t *sp = (uint32_t *)summ + cur_ph * D;
+          uint32_t *sp = (uint32_t *)summ + cur_sr * D;
           sp[lane] = lo;
           sp[D / 2 + lane] = hi;
         }
         cur_page = page;
-        cur_ph = ph;
+        cur_sr = summ_record(phys[d], g, Hkv);
         if (t == 0) {
           lo = hi = kv[d];
           continue;
         }
-        const uint32_t *sp = (const uint32_t *)summ + ph * D;
+        const uint32_t *sp = (const uint32_t *)summ + cur_sr * D;
         lo = sp[lane];
         hi = sp[D / 2 + lane];
       }
@@ -160,7 +160,7 @@ __device__ __forceinline__ void append_drafts_wave(const uint16_t *__restrict__ 
     }
   }
   if (summ != nullptr && cur_page >= 0) {
-    uint32_t *sp = (uint32_t *)summ + cur_ph * D;
+    uint32_t *sp = (uint32_t *)summ + cur_sr * D;
     sp[lane] = lo;
     sp[D / 2 + lane] = hi;
   }
@@ -191,7 +191,7 @@ struct DeferredDrafts {
                                                int g, int Hkv, int lane) {
     const int p0 = L - n_draft;
     if (summ == nullptr || p0 % PS == 0) return;
-    const uint32_t *sp = (const uint32_t *)summ + ((size_t)page_phys[p0 / PS] * Hkv + g) * D;
+    const uint32_t *sp = (const uint32_t *)summ + summ_record(page_phys[p0 / PS], g, Hkv) * D;
     lo = sp[lane];
     hi = sp[D / 2 + lane];
   }
@@ -210,7 +210,7 @@ struct DeferredDrafts {
       if (summ == nullptr) continue;
       if (t == 0) {
         if (started) {  // the first page is complete
-          uint32_t *sp = (uint32_t *)summ + ((size_t)page_phys[cur_page] * Hkv + g) * D;
+          uint32_t *sp = (uint32_t *)summ + summ_record(page_phys[cur_page], g, Hkv) * D;
           sp[lane] = lo;
           sp[D / 2 + lane] = hi;
         }
@@ -226,7 +226,7 @@ struct DeferredDrafts {
            (bf16_from_order_key(max(v1, bf16_order_key(hi >> 16))) << 16);
     }
     if (summ != nullptr) {
-      uint32_t *sp = (uint32_t *)summ + ((size_t)page_phys[cur_page] * Hkv + g) * D;
+      uint32_t *sp = (uint32_t *)summ + summ_record(page_phys[cur_page], g, Hkv) * D;
       sp[lane] = lo;
       sp[D / 2 + lane] = hi;
     }
@@ -368,18 +368,19 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
   const int a_t = appending ? (L - 1) % PS : 0;
   // set and used only under my_append (no merge with other values where the
   // branches join, so nothing waits for these loads before the stores)
-  size_t a_ph;
+  size_t a_ph, a_sr;  // page-head of the K/V pools, summary record
   uint32_t a_k, a_lo, a_hi;
   uint16_t a_v0, a_v1;
   auto append_loads = [&]() {
     a_ph = (size_t)page_phys[(L - 1) / PS] * Hkv + g;
+    a_sr = summ_record(page_phys[(L - 1) / PS], g, Hkv);
     const uint32_t *krow = (const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D);  // D / 2 = 64 words
     a_k = krow[lane];
     const uint16_t *vn = v_new + ((size_t)b * Hkv + g) * DV;
     a_v0 = vn[lane];
     a_v1 = vn[lane + kWave];
     // the summary rows (without summaries, the key row again: read, unused)
-    const uint32_t *sl = summ != nullptr ? (const uint32_t *)summ + a_ph * D : krow;
+    const uint32_t *sl = summ != nullptr ? (const uint32_t *)summ + a_sr * D : krow;
     a_lo = sl[lane];
     a_hi = sl[(summ != nullptr ? D / 2 : 0) + lane];
   };
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(W * 64) void fused_step_gqa_kernel(
         hi = bf16_from_order_key(max(v0, bf16_order_key(a_hi & 0xffffu))) |
              (bf16_from_order_key(max(v1, bf16_order_key(a_hi >> 16))) << 16);
       }
-      uint32_t *sp = (uint32_t *)summ + a_ph * D;
+      uint32_t *sp = (uint32_t *)summ + a_sr * D;
       sp[lane] = lo;
       sp[D / 2 + lane] = hi;
     }
@@ -631,13 +632,14 @@ __global__ __launch_bounds__(W * 64) void fused_reuse_gqa_kernel(
   if (k_new != nullptr && L > 0 && wave == W - 1) {
     const int a_t = (L - 1) % PS;
     const size_t a_ph = (size_t)pt_row[(L - 1) / PS] * Hkv + g;
+    const size_t a_sr = summ_record(pt_row[(L - 1) / PS], g, Hkv);
     const uint32_t *krow = (const uint32_t *)(k_new + ((size_t)b * Hkv + g) * D);  // D / 2 = 64 words
     const uint32_t a_k = krow[lane];
     const uint16_t *vn = v_new + ((size_t)b * Hkv + g) * DV;
     const uint16_t a_v0 = vn[lane], a_v1 = vn[lane + kWave];
     uint32_t a_lo = 0, a_hi = 0;
     if (summ != nullptr) {
-      const uint32_t *sl = (const uint32_t *)summ + a_ph * D;
+      const uint32_t *sl = (const uint32_t *)summ + a_sr * D;
       a_lo = sl[lane];
       a_hi = sl[D / 2 + lane];
     }
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(W * 64) void fused_reuse_gqa_kernel(
         hi = bf16_from_order_key(max(v0, bf16_order_key(a_hi & 0xffffu))) |
              (bf16_from_order_key(max(v1, bf16_order_key(a_hi >> 16))) << 16);
       }
-      uint32_t *sp = (uint32_t *)summ + a_ph * D;
+      uint32_t *sp = (uint32_t *)summ + a_sr * D;
       sp[lane] = lo;
       sp[D / 2 + lane] = hi;
     }

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(128) void prepare_drafts_kernel(TokenAppend ap, con
     const int w = tid;
     uint32_t lo = 0, hi = 0;
     if (ap.summ && t0 != 0) {  // the first page already holds tokens
-      const uint32_t *sp = ap.summ + ((size_t)phys0 * Hkv + g) * 2 * words;
+      const uint32_t *sp = ap.summ + summ_record(phys0, g, Hkv) * 2 * words;
       lo = sp[w];
       hi = sp[words + w];
     }
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(128) void prepare_drafts_kernel(TokenAppend ap, con
       if (!ap.summ) continue;
       if (t == 0) {
         if (i > i0) {  // the drafts cross into the second page: the first page is complete
-          uint32_t *sp = ap.summ + ((size_t)phys0 * Hkv + g) * 2 * words;
+          uint32_t *sp = ap.summ + summ_record(phys0, g, Hkv) * 2 * words;
           sp[w] = lo;
           sp[words + w] = hi;
         }
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(128) void prepare_drafts_kernel(TokenAppend ap, con
            (bf16_from_order_key(max(v1, bf16_order_key(hi >> 16))) << 16);
     }
     if (ap.summ) {
-      uint32_t *sp = ap.summ + ((size_t)((L - 1) / ps == j0 ? phys0 : phys1) * Hkv + g) * 2 * words;
+      uint32_t *sp = ap.summ + summ_record((L - 1) / ps == j0 ? phys0 : phys1, g, Hkv) * 2 * words;
       sp[w] = lo;
       sp[words + w] = hi;
     }

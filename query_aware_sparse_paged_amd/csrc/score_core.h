@@ -79,7 +79,7 @@ __device__ __forceinline__ void load_q_operands(QOperands<D, ABS> &op, const uin
 // layout: lane l holds page column l % 16 ... the caller passes the lane's page.
 template <int D>
 __device__ __forceinline__ void load_group(uint4 *dst, const uint16_t *summ, int phys, int Hkv, int g, int lane) {
-  const uint16_t *sp = summ + ((size_t)phys * Hkv + g) * (2 * D) + 8 * (lane >> 4);
+  const uint16_t *sp = summ + summ_record(phys, g, Hkv) * (2 * D) + 8 * (lane >> 4);
 #pragma unroll
   for (int i = 0; i < 2 * D / 32; i++) dst[i] = *(const uint4 *)(sp + 32 * i);
 }

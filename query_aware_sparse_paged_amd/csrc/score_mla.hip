@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       const int t = wave + kMlaWaves * k;  // wave-uniform
       if (t < kDmaPerGroup) {
         const int slot = 64 * t + lane, r = slot / kRecU4, sl = slot % kRecU4;
-        const uint16_t *src = summ + ((size_t)ph[k] * Hkv + g) * kMlaK2 + 8 * (sl ^ (r & 15));
+        const uint16_t *src = summ + summ_record(ph[k], g, Hkv) * kMlaK2 + 8 * (sl ^ (r & 15));
         __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(slab + 1024 * t), 16, 0, 0);
       }
     }

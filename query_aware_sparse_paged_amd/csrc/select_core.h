@@ -816,7 +816,7 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
       __syncthreads();  // the staged q rows, the band pages' entries
       for (int e = wave; e < n_band; e += NW) {
         const int phys = sh.bphys[e];
-        const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
+        const uint16_t *lo = summ + summ_record(phys, g, Hkv) * 2 * D;
         double key;
         const int lead = sh.blead[e];
         if (lead >= 0) {
@@ -864,7 +864,7 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
           bits &= bits - 1;
           if ((seen++ % NW) != wave) continue;
           const int phys = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
-          const uint16_t *lo = summ + ((size_t)phys * Hkv + g) * 2 * D;
+          const uint16_t *lo = summ + summ_record(phys, g, Hkv) * 2 * D;
           const int lead = cand_scores ? cand_scores[i].head : -1;
           const uint64_t o = f64_order(lead >= 0 ? exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane)
                                                  : exact_page_key<D>(qb, G, lo, lo + D, lane));

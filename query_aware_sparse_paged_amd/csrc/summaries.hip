@@ -38,8 +38,9 @@ __global__ __launch_bounds__(256) void build_summaries_kernel(
     const uint32_t *kp = k_pool + ph * ps * words + w;
     uint32_t lo = kp[0], hi = lo;
     for (int t = 1; t < valid; t++) minmax_bf16x2(kp[(size_t)t * words], lo, hi);
-    summ[ph * 2 * words + w] = lo;
-    summ[ph * 2 * words + words + w] = hi;
+    const size_t sr = summ_record(phys, g, num_kv_heads);
+    summ[sr * 2 * words + w] = lo;
+    summ[sr * 2 * words + words + w] = hi;
   }
 }
 

@@ -169,7 +169,7 @@ def check_every_sequence(w, g: "GpuRun", pol=None, chunk=2, check_scores=True, w
 
     def gather(seqs):
         inp = oracle_inputs(w, seqs)
-        return inp, workloads.bits(g.summ[inp.phys.to(g.summ.device)])
+        return inp, workloads.bits(api.summary_rows(g.summ, inp.phys))
 
     def job(seqs, gathered):
         inp, gsumm = gathered

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from query_aware_sparse_paged_amd import api
 
@@ -420,3 +421,24 @@ def test_decode_step_path(L):
     mla = api.Layout(32768, 64, 1, 576, 512, True)
     assert path(mla, api.CBatch(256, 128, 1025, 1024, 0x1000, 0x2000), pol, 32) == api.PATH_CHAIN
     assert path(big, b(32, 2048), pol, -1) == api.ERR_BAD_SHAPE
+
+
+def test_summary_rows_undo_the_slot_rotation():
+    """The summary pool keeps the record of KV head g of page p in slot
+    (g + p) mod Hkv of row p; summary_rows returns records in head order."""
+    pool, hkv, d = 11, 8, 4
+    summ = torch.zeros((pool, hkv, 2, d), dtype=torch.float32)
+    for p in range(pool):
+        for g in range(hkv):
+            summ[p, (g + p) % hkv] = 100 * p + g  # the record of (page p, head g)
+    phys = torch.tensor([3, 0, 10, 7])
+    rows = api.summary_rows(summ, phys)
+    assert rows.shape == (4, hkv, 2, d)
+    for i, p in enumerate(phys.tolist()):
+        for g in range(hkv):
+            assert (rows[i, g] == 100 * p + g).all()
+    mask = torch.zeros(pool, dtype=torch.bool)
+    mask[[2, 5]] = True
+    assert torch.equal(api.summary_rows(summ, mask), api.summary_rows(summ, torch.tensor([2, 5])))
+    one = torch.arange(6.0).reshape(3, 1, 2, 1)  # one KV head: no rotation
+    assert torch.equal(api.summary_rows(one, torch.tensor([2, 0])), one[[2, 0]])

@@ -52,7 +52,7 @@ def test_full_multi_query_4_drafts():
     def gather(seqs):
         after = oracle_inputs(w, seqs, q=dq)
         before = oracle_inputs(w, seqs, k_pool=k_before, v_pool=v_before, q=dq)
-        return after, before, workloads.bits(summ[after.phys])
+        return after, before, workloads.bits(api.summary_rows(summ, after.phys))
 
     def job(seqs, gathered):
         after, before, gsumm = gathered
@@ -106,7 +106,7 @@ def test_full_quantised_pages():
 
     def gather(seqs):
         inp = oracle_inputs(w, seqs)
-        return inp, workloads.bits(summ[inp.phys]), qpool[inp.phys].cpu().numpy()
+        return inp, workloads.bits(api.summary_rows(summ, inp.phys)), qpool[inp.phys].cpu().numpy()
 
     def job(seqs, gathered):
         inp, gsumm, gq = gathered
@@ -164,7 +164,7 @@ def test_full_cross_layer_reuse():
 
     def gather(seqs):
         ia = oracle_inputs(a, seqs)
-        return ia, oracle_inputs(a, seqs, k_pool=kb_pool, v_pool=vb_pool, q=qb), workloads.bits(summ[ia.phys])
+        return ia, oracle_inputs(a, seqs, k_pool=kb_pool, v_pool=vb_pool, q=qb), workloads.bits(api.summary_rows(summ, ia.phys))
 
     def job(seqs, gathered):
         ia, ib, gsumm = gathered

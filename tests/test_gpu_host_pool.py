@@ -78,7 +78,7 @@ def test_host_tier_pools_match_device_pools(name, batch, seq_len):
     assert torch.equal(kh.host.view(torch.int16), w.k_pool.view(torch.int16))
     r = run_oracle(w, pol, msel)
     used = w.page_table[w.page_table >= 0].long()
-    assert np.array_equal(workloads.bits(summ_h.cpu()[used]), r.summ[used.numpy()])
+    assert np.array_equal(workloads.bits(api.summary_rows(summ_h.cpu(), used)), r.summ[used.numpy()])
     assert np.array_equal(cnt_h.numpy(), r.cnt) and np.array_equal(sel_h.numpy(), r.sel)
     assert np.abs(out_h.numpy().astype(np.float64) - r.out).max() <= OUT_TOL
 

@@ -62,7 +62,7 @@ def _run(name, batch, nq, seq_len, seq_len_min, seed=31, **overrides):
     rs = oracle.summaries(olay, pt_np, sl_np, Hq, kbits)
     used = pt[pt >= 0].long()
     used = used[used < lay.num_pool_pages]
-    assert np.array_equal(workloads.bits(summ.cpu()[used]), rs[used.numpy()])
+    assert np.array_equal(workloads.bits(api.summary_rows(summ.cpu(), used)), rs[used.numpy()])
     qbits = workloads.bits(dq)
     sc = oracle.scores_multi(olay, pt_np, sl_np, qbits, rs, opol)
     rsel, rcnt = oracle.select_multi(olay, pt_np, sl_np, Hq, nq, sc, opol, max_sel_n=msel)

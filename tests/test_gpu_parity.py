@@ -30,7 +30,7 @@ def test_tiny_config_exact():
     g = run_gpu(w)
     r = run_oracle(w, api.policy_of(w), g.max_sel)
     k_phys = w.page_table[0, :256].long()
-    assert np.array_equal(workloads.bits(g.summ.cpu()[k_phys]), r.summ[k_phys.numpy()])
+    assert np.array_equal(workloads.bits(api.summary_rows(g.summ.cpu(), k_phys)), r.summ[k_phys.numpy()])
     compare(g, r, what="tiny_b1_4k")
     assert (g.cnt == 37).all()
 
@@ -192,7 +192,7 @@ def test_append_updates_summaries_incrementally():
     import oracle
     from gpu_cases import olayout
     osumm = oracle.summaries(olayout(lay), w.page_table.numpy(), lens.numpy(), 32, workloads.bits(kp))
-    assert np.array_equal(workloads.bits(summ[used]), osumm[used.cpu().numpy()])
+    assert np.array_equal(workloads.bits(api.summary_rows(summ, used)), osumm[used.cpu().numpy()])
 
 
 def test_split_entry_points_match_decode_step():
@@ -292,7 +292,7 @@ def test_step_appends(batch, local, boost):
     r = run_oracle(w, pol, msel)
     used = w.page_table[:, :44].reshape(-1).long()
     used = used[used >= 0]
-    assert np.array_equal(workloads.bits(summ.cpu()[used]), r.summ[used.numpy()])
+    assert np.array_equal(workloads.bits(api.summary_rows(summ.cpu(), used)), r.summ[used.numpy()])
     assert np.array_equal(cnt.cpu().numpy(), r.cnt) and np.array_equal(sel.cpu().numpy(), r.sel)
     assert np.abs(out.cpu().numpy().astype(np.float64) - r.out).max() <= 5e-3
     if local == 0:  # the test is only sensitive if the boosted last pages are chosen

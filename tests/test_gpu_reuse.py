@@ -111,7 +111,7 @@ def test_reuse_step(name, batch, top_k, with_summ):
     if with_summ:
         rs = oracle.summaries(olay, pt_np, sl_np, Hq, kbits)
         used = pt[pt >= 0].long()
-        assert np.array_equal(workloads.bits(summ_b.cpu()[used]), rs[used.numpy()])
+        assert np.array_equal(workloads.bits(api.summary_rows(summ_b.cpu(), used)), rs[used.numpy()])
     assert (cnt_np > 0).all()
     if top_k is not None:
         assert cnt_np.min() > 512
