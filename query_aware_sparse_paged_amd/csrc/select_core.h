@@ -47,7 +47,7 @@ struct SelShared {
   int hist[NW][256];          // one digit histogram per wave
   int red[NW][4];             // per-wave partials of block reductions
   int digit, rem, nlist, bincnt;
-  int n_in, n_band, nsel;
+  int n_in, nsel;
   uint32_t kin, kib;          // smallest key above the band / of the band and above
   int kbin[2], krem[2], kcnt[2], nk[2];
   uint32_t uk, uk1;
@@ -750,7 +750,7 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   uint32_t uk, uk1;
   if (tid == 0) {  // ordered before use by the barriers inside kth_pair
-    sh.n_in = sh.n_band = 0;
+    sh.n_in = 0;
     sh.kin = sh.kib = ~0u;
   }
   kth_pair<NW>(keys32, n, k, k_min, k_max, sh, uk, uk1);
@@ -803,99 +803,97 @@ __device__ bool select_candidates(SelShared<NW> &sh, uint32_t *keys32, uint64_t 
     for (int i = tid; i < G * D / 2; i += NW * kWave) ((uint32_t *)sh.qstage)[i] = ((const uint32_t *)qb)[i];
     qb = sh.qstage;
   }
-  {
-    if (n_band <= kSmallBand) {
-      // exact keys of the listed band (one page per wave), ranked by one wave;
-      // the winners' keys become the largest key, the losers' 0.  The band
-      // pages' physical pages and leading heads are fetched together first.
-      if (tid < n_band) {
-        const int i = sh.list[tid];
-        sh.bphys[tid] = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
-        sh.blead[tid] = cand_scores ? cand_scores[i].head : -1;
+  if (n_band <= kSmallBand) {
+    // exact keys of the listed band (one page per wave), ranked by one wave;
+    // the winners' keys become the largest key, the losers' 0.  The band
+    // pages' physical pages and leading heads are fetched together first.
+    if (tid < n_band) {
+      const int i = sh.list[tid];
+      sh.bphys[tid] = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
+      sh.blead[tid] = cand_scores ? cand_scores[i].head : -1;
+    }
+    __syncthreads();  // the staged q rows, the band pages' entries
+    for (int e = wave; e < n_band; e += NW) {
+      const int phys = sh.bphys[e];
+      const uint16_t *lo = summ + summ_record(phys, g, Hkv) * 2 * D;
+      double key;
+      const int lead = sh.blead[e];
+      if (lead >= 0) {
+        key = exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane);
+      } else if (D == 128 && G <= 16) {
+        for (int x = lane; x < D; x += kWave) sh.rows[wave][x] = ((const uint32_t *)lo)[x];
+        const uint16_t *rows = (const uint16_t *)sh.rows[wave];
+        key = G <= 4 ? exact_page_key_heads<D, 16>(qb, G, rows, lo, lo + D, lane)
+                     : (G <= 8 ? exact_page_key_heads<D, 8>(qb, G, rows, lo, lo + D, lane)
+                               : exact_page_key_heads<D, 4>(qb, G, rows, lo, lo + D, lane));
+      } else {
+        key = exact_page_key<D>(qb, G, lo, lo + D, lane);
       }
-      __syncthreads();  // the staged q rows, the band pages' entries
-      for (int e = wave; e < n_band; e += NW) {
-        const int phys = sh.bphys[e];
+      if (lane == 0) sh.lkey[e] = key;
+    }
+    __syncthreads();
+    if (wave == 0 && lane < n_band) {
+      const double kl = sh.lkey[lane];
+      const int il = sh.list[lane];
+      int rank = 0;  // band pages that beat this one: larger key, or equal key and lower id
+      for (int e = 0; e < n_band; e++) {
+        const double ke = sh.lkey[e];
+        rank += ke > kl || (ke == kl && sh.list[e] < il);
+      }
+      keys32[il] = rank < need ? ~0u : 0u;
+    }
+    __syncthreads();  // the rewritten keys
+    *uk_fast = sh.kin;  // the pages above the band and the winners (all keys >= it)
+    return true;
+  } else {
+    // the pages above the band into sel_bits (their keys are >= sh.kin)
+    const uint32_t kin_all = sh.kin;
+    for (int i = tid; i < n; i += NW * kWave)
+      if (keys32[i] >= kin_all) {
+        const int j = cand_lo + i;
+        atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+      }
+    __syncthreads();  // keys32 is dead from here; keys64 reuses the space
+    uint64_t b_and = ~0ull, b_or = 0;
+    int seen = 0;
+    for (int w = 0; w < (n + 31) / 32; w++) {
+      uint32_t bits = band_bits[w];
+      while (bits) {
+        const int i = w * 32 + __builtin_ctz(bits);
+        bits &= bits - 1;
+        if ((seen++ % NW) != wave) continue;
+        const int phys = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
         const uint16_t *lo = summ + summ_record(phys, g, Hkv) * 2 * D;
-        double key;
-        const int lead = sh.blead[e];
-        if (lead >= 0) {
-          key = exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane);
-        } else if (D == 128 && G <= 16) {
-          for (int x = lane; x < D; x += kWave) sh.rows[wave][x] = ((const uint32_t *)lo)[x];
-          const uint16_t *rows = (const uint16_t *)sh.rows[wave];
-          key = G <= 4 ? exact_page_key_heads<D, 16>(qb, G, rows, lo, lo + D, lane)
-                       : (G <= 8 ? exact_page_key_heads<D, 8>(qb, G, rows, lo, lo + D, lane)
-                                 : exact_page_key_heads<D, 4>(qb, G, rows, lo, lo + D, lane));
-        } else {
-          key = exact_page_key<D>(qb, G, lo, lo + D, lane);
-        }
-        if (lane == 0) sh.lkey[e] = key;
+        const int lead = cand_scores ? cand_scores[i].head : -1;
+        const uint64_t o = f64_order(lead >= 0 ? exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane)
+                                               : exact_page_key<D>(qb, G, lo, lo + D, lane));
+        if (lane == 0) keys64[i] = o;
+        b_and &= o;
+        b_or |= o;
       }
-      __syncthreads();
-      if (wave == 0 && lane < n_band) {
-        const double kl = sh.lkey[lane];
-        const int il = sh.list[lane];
-        int rank = 0;  // band pages that beat this one: larger key, or equal key and lower id
-        for (int e = 0; e < n_band; e++) {
-          const double ke = sh.lkey[e];
-          rank += ke > kl || (ke == kl && sh.list[e] < il);
-        }
-        keys32[il] = rank < need ? ~0u : 0u;
+    }
+    block_and_or64(b_and, b_or, sh);
+    const uint64_t kth = kth_largest<uint64_t, NW>(keys64, band_bits, n, need, b_and, b_or, sh);
+    // all band pages above kth, then the lowest ids among those equal to it
+    int above = 0, zero = 0;
+    for (int i = tid; i < n; i += NW * kWave)
+      if (((band_bits[i >> 5] >> (i & 31)) & 1u) && keys64[i] > kth) {
+        const int j = cand_lo + i;
+        atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+        above++;
       }
-      __syncthreads();  // the rewritten keys
-      *uk_fast = sh.kin;  // the pages above the band and the winners (all keys >= it)
-      return true;
-    } else {
-      // the pages above the band into sel_bits (their keys are >= sh.kin)
-      const uint32_t kin_all = sh.kin;
-      for (int i = tid; i < n; i += NW * kWave)
-        if (keys32[i] >= kin_all) {
-          const int j = cand_lo + i;
-          atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-        }
-      __syncthreads();  // keys32 is dead from here; keys64 reuses the space
-      uint64_t b_and = ~0ull, b_or = 0;
-      int seen = 0;
-      for (int w = 0; w < (n + 31) / 32; w++) {
-        uint32_t bits = band_bits[w];
-        while (bits) {
-          const int i = w * 32 + __builtin_ctz(bits);
-          bits &= bits - 1;
-          if ((seen++ % NW) != wave) continue;
-          const int phys = cand_phys ? cand_phys[i] : pt_row[cand_lo + i];
-          const uint16_t *lo = summ + summ_record(phys, g, Hkv) * 2 * D;
-          const int lead = cand_scores ? cand_scores[i].head : -1;
-          const uint64_t o = f64_order(lead >= 0 ? exact_page_key<D>(qb + (size_t)lead * D, 1, lo, lo + D, lane)
-                                                 : exact_page_key<D>(qb, G, lo, lo + D, lane));
-          if (lane == 0) keys64[i] = o;
-          b_and &= o;
-          b_or |= o;
-        }
+    block_sum2(above, zero, sh);
+    int take = need - above;
+    for (int i0 = 0; i0 < n && take > 0; i0 += NW * kWave) {
+      const int i = i0 + tid;
+      const int tie = i < n && ((band_bits[i >> 5] >> (i & 31)) & 1u) && keys64[i] == kth;
+      int total;
+      const int before = block_exclusive_scan(tie, &total, sh);
+      if (tie && before < take) {
+        const int j = cand_lo + i;
+        atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
       }
-      block_and_or64(b_and, b_or, sh);
-      const uint64_t kth = kth_largest<uint64_t, NW>(keys64, band_bits, n, need, b_and, b_or, sh);
-      // all band pages above kth, then the lowest ids among those equal to it
-      int above = 0, zero = 0;
-      for (int i = tid; i < n; i += NW * kWave)
-        if (((band_bits[i >> 5] >> (i & 31)) & 1u) && keys64[i] > kth) {
-          const int j = cand_lo + i;
-          atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-          above++;
-        }
-      block_sum2(above, zero, sh);
-      int take = need - above;
-      for (int i0 = 0; i0 < n && take > 0; i0 += NW * kWave) {
-        const int i = i0 + tid;
-        const int tie = i < n && ((band_bits[i >> 5] >> (i & 31)) & 1u) && keys64[i] == kth;
-        int total;
-        const int before = block_exclusive_scan(tie, &total, sh);
-        if (tie && before < take) {
-          const int j = cand_lo + i;
-          atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-        }
-        take -= min(total, take);
-      }
+      take -= min(total, take);
     }
   }
   return false;
