@@ -11,10 +11,14 @@
 // Block (split, head group, unit) takes the selected pages [8 split, 8 split
 // + 8) of unit (b, g) for 32 of the 128 heads; the four head groups of a
 // (unit, split) run on one XCD, so its L2 serves the pages to all four.  A
-// page (64 tokens x 1152 bytes) is read from HBM into registers (9 pieces of
-// 16 bytes per thread) and stored to LDS token-major (rows padded so the 16
-// rows of an A fragment fall on different banks), one page ahead of the
-// computation; two page buffers.  Per page, wave w:
+// page (64 tokens x 1152 bytes) goes from HBM straight into LDS
+// (global_load_lds, 16 bytes per lane, 73 wave-wide transfers of 1 KiB),
+// token-major with rows padded to 73 pieces of 16 bytes so the 16 rows of an
+// A fragment fall on different banks (the pad piece of a row receives a copy
+// of its last piece, never read).  Two page buffers, each an LDS object of
+// its own so the compiler sees which transfers a read depends on: page c + 1
+// loads into the buffer page c - 1 used while page c is computed.  Per page,
+// wave w:
 //   - S^T of tokens 16 (w % 4) .. +16 and heads 16 (w / 4) .. +16 (18 MFMAs,
 //     q^T of its 16 heads kept in registers), softmax weights, which go to an
 //     LDS P^T tile (bf16 hi and lo parts);
@@ -30,9 +34,9 @@
 // follows: k slot (kg, r) of a lane is token 4kg + r for r < 4 and 16 + 4kg +
 // r - 4 for r >= 4 of each 32-token half, and the P^T tile stores its tokens
 // in that order, so a B fragment is 16 contiguous bytes.
-// Tokens that are not attended (past the length, outside a static head's
-// sink and window) are zeroed while staging, so stale pool contents never
-// reach the products, and get weight 0.
+// The rows of tokens that are not attended (past the length, outside a
+// static head's sink and window) are written as zeros instead of loaded, so
+// stale pool or LDS contents never reach the products, and get weight 0.
 // P is split into bf16 hi + lo parts (two MFMAs) to keep ~16 significant bits.
 // Softmax in the exp2 domain against a fixed reference max per head (the max
 // over the first page), so the accumulators are never rescaled: weights stay
@@ -59,11 +63,14 @@ constexpr int kThreads = kWaves * kWave;         // 512
 constexpr int kKRow = kD * 2 + 16;               // bytes per LDS row (padded): 1168
 constexpr int kBufBytes = kPS * kKRow;           // 74752 per page buffer
 constexpr int kRowU4 = kD / 8;                   // 72 pieces of 16 bytes per row
-constexpr int kStage = kPS * kRowU4 / kThreads;  // 9 loads per thread per page
+constexpr int kRowSlots = kKRow / 16;            // 73 slots per LDS row (the last one padding)
+constexpr int kXfer = kBufBytes / 1024;          // 73 wave-wide transfers per page
+constexpr int kXferPerWave = (kXfer + kWaves - 1) / kWaves;  // 10 for wave 0, 9 for the others
+static_assert(kXfer == kWaves * (kXferPerWave - 1) + 1, "one more transfer for wave 0 than for the others");
 constexpr int kPRow = kPS * 2 + 16;              // bytes per P^T row (one head, padded): 144
 constexpr int kPBytes = kHeads * kPRow;          // 4608 per part (hi, lo)
 constexpr float kHeadroom = 64.f;                // weights stay below 2^64 (log2 units)
-static_assert(kStage * kThreads == kPS * kRowU4, "whole pages per staging round");
+static_assert(kXfer * 1024 == kBufBytes && kRowSlots == kRowU4 + 1, "whole transfers per page buffer");
 static_assert(kBufBytes % 16 == 0 && kKRow % 16 == 0 && kPRow % 16 == 0, "LDS alignment");
 static_assert(kMlaPagesPerSplit <= 16, "page list");
 
@@ -80,6 +87,28 @@ __device__ __forceinline__ uint2 pack_bf16x4(const float *a) {
 
 __device__ __forceinline__ float bf16_round(float a) { return __uint_as_float(f32_to_bf16_rne(a) << 16); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Waits until at most N (< 16) of this wave's vector memory operations are
+// outstanding.  The empty asm statements keep the compiler from moving
+// memory accesses across it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));  // vmcnt N, expcnt and lgkmcnt at their maximum
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after this wave's LDS operations (not its transfers into
+// LDS still in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt and expcnt at their maximum, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Transposing 8-byte LDS read (see the file comment for its lane layout).
 __device__ __forceinline__ uint2 lds_read_tr16(const char *p) {
   const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)p);
@@ -91,7 +120,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *p) {
 // SELECT: the block first selects its unit's pages from the stored scores
 // (select_unit, as select_topk_kernel does: every block of a unit computes
 // the same list, the first one also writes it to sel / sel_count), with the
-// selection's LDS laid over the page buffers, which are not in use yet.
+// selection's LDS laid over the first page buffer, which is not in use yet.
 // Otherwise sel / sel_count are read.
 template <bool SELECT>
 __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
@@ -101,10 +130,12 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
     int max_sel, int Hq, int Hkv, int splits, float scale_log2, int sink_tokens, int window_tokens,
     uint64_t static_mask, const qasp_score *__restrict__ scores, const uint16_t *__restrict__ summ, int max_pages,
     int n_sink, int n_local, int top_k) {
-  extern __shared__ uint4 lds_u4[];
-  char *kvbuf = (char *)lds_u4;                 // 2 page buffers
-  char *pbuf = kvbuf + 2 * (size_t)kBufBytes;  // P^T hi, then lo
+  // the two page buffers are LDS objects of their own (see the file comment)
+  __shared__ uint4 kbuf0[kBufBytes / 16], kbuf1[kBufBytes / 16];
+  __shared__ uint4 pbuf_u4[2 * kPBytes / 16];
   __shared__ MlaDecodeShared sh;
+  char *kvbuf = (char *)kbuf0;     // the selection's LDS, before the pages
+  char *pbuf = (char *)pbuf_u4;    // P^T hi, then lo
   constexpr int kGroups = kG / kHeads;  // 4 head groups
   // the head groups and splits of a unit run on one XCD
   const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
@@ -134,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   const int32_t *list = sel + (size_t)unit * max_sel;
   int count = 0;
   if constexpr (SELECT) {
-    // the selection's LDS over the page buffers: shared state, keys, bit maps, list
+    // the selection's LDS over the first page buffer: shared state, keys, bit maps, list
     using Shared = sel::SelShared<kWaves>;
     Shared &ssh = *(Shared *)kvbuf;
     uint64_t *keys = (uint64_t *)(kvbuf + ((sizeof(Shared) + 15) & ~(size_t)15));
@@ -178,23 +209,39 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   __syncthreads();
   const int npages = sh.npages;
 
-  // staging: thread loads the 16-byte pieces e = tid + 512 u of a page
-  // (token e / 72, channels 8 (e % 72) ..), consecutive lanes along a row
-  uint4 stg[kStage];
-  auto load_page = [&](int c) {
-    const int2 pg = sh.pages[c];
-    const uint4 *base = (const uint4 *)(k_pool + ((size_t)pg.x * Hkv + g) * kPS * kD);
+  // transfer k of this wave (t = wave + 8 k < kXfer) fills slots 64 t .. 64 t
+  // + 63 of a page buffer; lane l's slot e = 64 t + l is piece e % 73 of LDS
+  // row e / 73, which receives the same piece of token row e / 73 (the pad
+  // piece a copy of piece 71)
+  int xrow[kXferPerWave], xsrc[kXferPerWave];
 #pragma unroll
-    for (int u = 0; u < kStage; u++) stg[u] = base[tid + u * kThreads];
+  for (int k = 0; k < kXferPerWave; k++) {
+    const int e = 64 * (wave + kWaves * k) + lane, r = e / kRowSlots, cb = e % kRowSlots;
+    xrow[k] = r;
+    xsrc[k] = r * kD + 8 * min(cb, kRowU4 - 1);
+  }
+  // page c into buffer kb: every transfer is issued, so the wave's count of
+  // outstanding transfers per page is fixed
+  auto issue_page = [&](int c, char *kb) __attribute__((always_inline)) {
+    const uint16_t *base = k_pool + ((size_t)sh.pages[c].x * Hkv + g) * kPS * kD;
+#pragma unroll
+    for (int k = 0; k < kXferPerWave; k++) {
+      const int t = wave + kWaves * k;  // wave-uniform
+      if (t < kXfer)
+        __builtin_amdgcn_global_load_lds((const void *)(base + xsrc[k]), (lds_void *)(kb + 1024 * t), 16, 0, 0);
+    }
   };
-  auto store_page = [&](int c, int buf) {
+  // once this wave's transfers of page c have landed: zeros over the rows of
+  // the tokens it does not attend (slots this lane's transfers wrote)
+  auto zero_rows = [&](int c, char *kb) __attribute__((always_inline)) {
     const int pos0 = sh.pages[c].y;
-    char *kb = kvbuf + (size_t)buf * kBufBytes;
+    const bool whole = pos0 + kPS <= L && (!is_static || pos0 + kPS <= sink_end || pos0 >= win_begin);
+    if (!whole) {  // block-uniform
 #pragma unroll
-    for (int u = 0; u < kStage; u++) {
-      const int e = tid + u * kThreads, t = e / kRowU4, cb = e % kRowU4;
-      const uint32_t k = attended(pos0 + t) ? ~0u : 0u;
-      *(uint4 *)(kb + t * kKRow + 16 * cb) = make_uint4(stg[u].x & k, stg[u].y & k, stg[u].z & k, stg[u].w & k);
+      for (int k = 0; k < kXferPerWave; k++) {
+        const int t = wave + kWaves * k;
+        if (t < kXfer && !attended(pos0 + xrow[k])) *(uint4 *)(kb + 1024 * t + 16 * lane) = make_uint4(0, 0, 0, 0);
+      }
     }
   };
   // lane's transposing-read address inside a page buffer: token 4kg + n/4, channels 4 (n % 4) ..
@@ -205,105 +252,120 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
 
   floatx4 acc[4][2];  // O^T: value channel tile 4 wave + d, head tile t
   float m = -INFINITY, l = 0.f, seen = -INFINITY;  // head column n of tile ht (log2 units)
-  // one pass over the block's pages with reference m (fixed once set)
-  auto run_pass = [&]() {
+  // page c, in buffer kb (the other buffer: ob); on entry this wave has page
+  // c's transfers and, for c = 0, page 1's outstanding.  (Page 0 is peeled off
+  // the loop below, so the compiler's count of the transfers in flight at
+  // each read is exact.)
+  auto page_step = [&](int c, char *kb, char *ob) __attribute__((always_inline)) {
+    const int pos0 = sh.pages[c].y;
+    // this wave's transfers of page c have landed (for c = 0 page 1's may
+    // still be in flight)
+    if (c == 0 && npages > 1) {
+      if (wave == 0) vm_wait<kXferPerWave>();
+      else vm_wait<kXferPerWave - 1>();
+    } else {
+      vm_wait<0>();
+    }
+    zero_rows(c, kb);
+    // page c is complete; the previous page's products are done, so ob and
+    // P^T are free
+    lds_barrier();
+    if (c >= 1 && c + 1 < npages) issue_page(c + 1, ob);
+
+    // S^T: token 16 tq + 4 kg + r of head column n
+    floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      const char *kr = kb + (16 * tq + n) * kKRow + 16 * kg;
+#pragma unroll
+      for (int i = 0; i < kD / 32; i++) s = mfma16x16x32(*(const uint4 *)(kr + 64 * i), qB[i], s);
+    }
+    float sv[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const bool ok = attended(pos0 + 16 * tq + 4 * kg + r);
+      sv[r] = ok ? s[r] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[r]);
+    }
+    if (m == -INFINITY) {  // first page (block-uniform): the reference is its max over all 64 tokens
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));  // this quarter's max of head column n
+      if (kg == 0) sh.red[tq][16 * ht + n] = tmax;
+      lds_barrier();
+      m = fmaxf(fmaxf(sh.red[0][16 * ht + n], sh.red[1][16 * ht + n]),
+                fmaxf(sh.red[2][16 * ht + n], sh.red[3][16 * ht + n]));
+    }
+    // the largest score seen and the weight sum stay per lane (this lane's
+    // tokens) until the loop ends
+    seen = fmaxf(seen, tmax);
+    if (__any(tmax > m + kHeadroom) && lane == 0) sh.overflow = 1;
+    float p[4], pl[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      p[r] = sv[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m);
+      psum += p[r];
+      pl[r] = p[r] - bf16_round(p[r]);
+    }
+    l += psum;
+    *(uint2 *)(pbuf + p_off) = pack_bf16x4(p);
+    *(uint2 *)(pbuf + kPBytes + p_off) = pack_bf16x4(pl);
+    lds_barrier();  // P^T is complete (a plain __syncthreads would also wait for page c + 1)
+
+    // O^T += V^T P^T over value channels 16 (4 wave + d) + n, both head tiles
+    const char *vb = kb + tr_off;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++) {  // 32-token halves of the page
+      uint4 ph[2], plo[2];
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const int o = (16 * t + n) * kPRow + 2 * (32 * h2 + 8 * kg);
+        ph[t] = *(const uint4 *)(pbuf + o);
+        plo[t] = *(const uint4 *)(pbuf + kPBytes + o);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const int dv0 = 16 * (4 * wave + d);
+        const uint2 x0 = lds_read_tr16(vb + (32 * h2) * kKRow + 2 * dv0),
+                    x1 = lds_read_tr16(vb + (32 * h2 + 16) * kKRow + 2 * dv0);
+        const uint4 a = make_uint4(x0.x, x0.y, x1.x, x1.y);
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          acc[d][t] = mfma16x16x32(a, ph[t], acc[d][t]);
+          acc[d][t] = mfma16x16x32(a, plo[t], acc[d][t]);
+        }
+      }
+    }
+  };
+  // one pass over the block's pages with reference m (fixed once set); the
+  // loop is unrolled by two so that each step reads a known buffer
+  auto run_pass = [&]() __attribute__((always_inline)) {
     l = 0.f;
 #pragma unroll
     for (int d = 0; d < 4; d++)
 #pragma unroll
       for (int t = 0; t < 2; t++) acc[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (npages > 0) {
-      load_page(0);
-      store_page(0, 0);
-    }
-    if (npages > 1) load_page(1);
-    for (int c = 0; c < npages; c++) {
-      const int buf = c & 1;
-      const char *kb = kvbuf + (size_t)buf * kBufBytes;
-      const int pos0 = sh.pages[c].y;
-      __syncthreads();  // page c is in buf; the previous page's products are done (P^T is free)
-
-      // S^T: token 16 tq + 4 kg + r of head column n
-      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-      {
-        const char *kr = kb + (16 * tq + n) * kKRow + 16 * kg;
-#pragma unroll
-        for (int i = 0; i < kD / 32; i++) s = mfma16x16x32(*(const uint4 *)(kr + 64 * i), qB[i], s);
-      }
-      float sv[4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const bool ok = attended(pos0 + 16 * tq + 4 * kg + r);
-        sv[r] = ok ? s[r] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[r]);
-      }
-      if (m == -INFINITY) {  // first page (block-uniform): the reference is its max over all 64 tokens
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));  // this quarter's max of head column n
-        if (kg == 0) sh.red[tq][16 * ht + n] = tmax;
-        __syncthreads();
-        m = fmaxf(fmaxf(sh.red[0][16 * ht + n], sh.red[1][16 * ht + n]),
-                  fmaxf(sh.red[2][16 * ht + n], sh.red[3][16 * ht + n]));
-      }
-      // the largest score seen and the weight sum stay per lane (this lane's
-      // tokens) until the loop ends
-      seen = fmaxf(seen, tmax);
-      if (__any(tmax > m + kHeadroom) && lane == 0) sh.overflow = 1;
-      float p[4], pl[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        p[r] = sv[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m);
-        psum += p[r];
-        pl[r] = p[r] - bf16_round(p[r]);
-      }
-      l += psum;
-      *(uint2 *)(pbuf + p_off) = pack_bf16x4(p);
-      *(uint2 *)(pbuf + kPBytes + p_off) = pack_bf16x4(pl);
-      __syncthreads();  // P^T is complete; every wave is done with the other buffer
-      if (c + 1 < npages) {
-        store_page(c + 1, buf ^ 1);  // loaded while page c was computed
-        if (c + 2 < npages) load_page(c + 2);
-      }
-
-      // O^T += V^T P^T over value channels 16 (4 wave + d) + n, both head tiles
-      const char *vb = kb + tr_off;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; h2++) {  // 32-token halves of the page
-        uint4 ph[2], plo[2];
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-          const int o = (16 * t + n) * kPRow + 2 * (32 * h2 + 8 * kg);
-          ph[t] = *(const uint4 *)(pbuf + o);
-          plo[t] = *(const uint4 *)(pbuf + kPBytes + o);
-        }
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-          const int dv0 = 16 * (4 * wave + d);
-          const uint2 x0 = lds_read_tr16(vb + (32 * h2) * kKRow + 2 * dv0),
-                      x1 = lds_read_tr16(vb + (32 * h2 + 16) * kKRow + 2 * dv0);
-          const uint4 a = make_uint4(x0.x, x0.y, x1.x, x1.y);
-#pragma unroll
-          for (int t = 0; t < 2; t++) {
-            acc[d][t] = mfma16x16x32(a, ph[t], acc[d][t]);
-            acc[d][t] = mfma16x16x32(a, plo[t], acc[d][t]);
-          }
-        }
-      }
+    if (npages > 0) issue_page(0, (char *)kbuf0);
+    if (npages > 1) issue_page(1, (char *)kbuf1);
+    if (npages > 0) page_step(0, (char *)kbuf0, (char *)kbuf1);
+    for (int c = 1; c < npages; c += 2) {
+      page_step(c, (char *)kbuf1, (char *)kbuf0);
+      if (c + 1 < npages) page_step(c + 1, (char *)kbuf0, (char *)kbuf1);
     }
   };
-  run_pass();
-  __syncthreads();
-  if (sh.overflow) {  // some weight could exceed 2^kHeadroom: again, from the largest score seen
+  // a second pass only if some weight could exceed 2^kHeadroom, then from
+  // the largest score seen (one copy of the loop body in the code)
+#pragma clang loop unroll(disable)
+  for (int pass = 0; pass < 2; pass++) {
+    run_pass();
+    __syncthreads();
+    if (pass == 1 || !sh.overflow) break;
     seen = fmaxf(seen, __shfl_xor(seen, 16, kWave));
     seen = fmaxf(seen, __shfl_xor(seen, 32, kWave));
     if (kg == 0) sh.red[tq][16 * ht + n] = seen;
     __syncthreads();
     m = fmaxf(fmaxf(sh.red[0][16 * ht + n], sh.red[1][16 * ht + n]),
               fmaxf(sh.red[2][16 * ht + n], sh.red[3][16 * ht + n]));
-    __syncthreads();
-    run_pass();
     __syncthreads();
   }
   // the heads' sums over the four token quarters
@@ -340,13 +402,13 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   }
 }
 
-// LDS the selection inside decode_mla_kernel<true> needs (laid over its page buffers).
+// LDS the selection inside decode_mla_kernel<true> needs (laid over its first page buffer).
 size_t mla_select_lds_bytes(int max_pages, int max_sel) {
   return ((sizeof(sel::SelShared<kWaves>) + 15) & ~(size_t)15) + (size_t)max_pages * 8 +
          2 * (size_t)((max_pages + 31) / 32) * 4 + (size_t)max_sel * 4;
 }
 bool mla_select_fits(const qasp_batch &bat, int max_sel) {
-  return mla_select_lds_bytes(bat.max_pages > 0 ? bat.max_pages : 1, max_sel) <= 2 * (size_t)kBufBytes;
+  return mla_select_lds_bytes(bat.max_pages > 0 ? bat.max_pages : 1, max_sel) <= (size_t)kBufBytes;
 }
 
 // scores != nullptr: the blocks select first (sel / sel_count, then written,
@@ -358,17 +420,16 @@ hipError_t launch_decode_mla(const qasp_layout &lay, const qasp_batch &bat, cons
                              const uint16_t *summ) {
   const float scale_log2 = scale * 1.4426950408889634f;
   if (bat.num_q_heads != kG * lay.num_kv_heads) return hipErrorInvalidValue;
-  const size_t lds = 2 * (size_t)kBufBytes + 2 * (size_t)kPBytes;
   dim3 grid((unsigned)(kG / kHeads) * ws.splits * lay.num_kv_heads * bat.batch);
   if (scores != nullptr)
-    hipLaunchKernelGGL(decode_mla_kernel<true>, grid, dim3(kThreads), lds, stream, q, k_pool, bat.page_table,
+    hipLaunchKernelGGL(decode_mla_kernel<true>, grid, dim3(kThreads), 0, stream, q, k_pool, bat.page_table,
                        bat.seq_lens, (int32_t *)sel, (int32_t *)sel_count, ws.partial, ws.partial_ml, out,
                        bat.pt_stride, max_sel,
                        bat.num_q_heads, lay.num_kv_heads, ws.splits, scale_log2, pol.sink_tokens,
                        pol.window_tokens, pol.static_head_mask, scores, summ, bat.max_pages > 0 ? bat.max_pages : 1,
                        pol.n_sink_pages, pol.n_local_pages, pol.top_k);
   else
-    hipLaunchKernelGGL(decode_mla_kernel<false>, grid, dim3(kThreads), lds, stream, q, k_pool, bat.page_table,
+    hipLaunchKernelGGL(decode_mla_kernel<false>, grid, dim3(kThreads), 0, stream, q, k_pool, bat.page_table,
                        bat.seq_lens, (int32_t *)sel, (int32_t *)sel_count, ws.partial, ws.partial_ml, out,
                        bat.pt_stride, max_sel, bat.num_q_heads, lay.num_kv_heads, ws.splits, scale_log2,
                        pol.sink_tokens, pol.window_tokens, pol.static_head_mask, nullptr, nullptr, 0, 0, 0, 0);
