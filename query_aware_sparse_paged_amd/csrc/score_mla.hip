@@ -18,12 +18,9 @@
 //     S_h(j) = sum_d |q_hd| |x_hd| <= |q_h|_2 * N_j,  N_j^2 = sum_d max(lo_d^2, hi_d^2)
 // (times 1.01 for the fp32 evaluation of the norms).
 // A block takes up to kMlaGroups consecutive 16-page groups of one sequence
-// and loads their summary records straight into one LDS slab per group
-// (global_load_lds, 16 bytes per lane, no registers held): the first two
-// slabs, then, once those have landed, the other two, which load while the
-// first two are contracted.  Each slab is an LDS object of its own, so the
-// compiler sees which transfers a read depends on, and the barriers between
-// the steps wait for LDS and for this wave's own transfers explicitly.  Chunk
+// and stages their summary records in one LDS slab per group, through
+// registers (16 bytes per lane and load): two groups are in flight while the
+// one before them is contracted.  Chunk
 // c (16 bytes) of page row n sits at slot c ^ (n % 16) of the row, so the 16
 // rows of an MFMA B fragment fall on different banks.  The block also writes
 // the row's non-candidate slots (-inf), so the score row needs no separate
@@ -55,23 +52,9 @@ struct MlaScoreShared {
 };
 
 constexpr int kRecU4 = kMlaK2 / 8;              // 144 chunks of 16 bytes per record
-constexpr int kDmaPerGroup = 16 * kRecU4 / 64;  // 36 wave-wide 1 KB transfers per group
+constexpr int kDmaPerGroup = 16 * kRecU4 / 64;  // 36 wave-wide 1 KB loads per group
 static_assert(kRecU4 % 16 == 0 && (16 * kRecU4) % 64 == 0, "swizzle and transfer granularity");
-typedef __attribute__((address_space(3))) void lds_void;
 
-// Workgroup barrier that waits for this wave's LDS operations (and, with
-// all_vm, for all of its vector memory operations) but not for transfers
-// into LDS still in flight otherwise.  The empty asm statements keep the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier(bool all_vm) {
-  asm volatile("" ::: "memory");
-  if (all_vm)
-    __builtin_amdgcn_s_waitcnt(0);
-  else  // vmcnt and expcnt at their maximum, lgkmcnt 0
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Negative and non-negative parts of four bf16 pairs: an arithmetic shift of
 // each 16-bit half by 15 gives its sign mask (one packed instruction), so
@@ -132,6 +115,14 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const int j = n_sink + gfirst * 16 + tid;
     if (tid < 16 * kMlaGroups && j < max_pages) pv = page_table[(size_t)b * pt_stride + j];
   }
+  // q of the wave's 16 heads: column n = head 16 wave + n, channels 32i + 8kg ..
+  // (loaded with the page-table entries)
+  uint4 qraw[kMlaD / 32];
+  {
+    const uint16_t *qg = q + ((size_t)b * Hq + (size_t)wave * 16) * kMlaD;
+#pragma unroll
+    for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qg + (size_t)n * kMlaD + 32 * i + 8 * kg);
+  }
   const int L = seq_lens[b];
   const int P = num_pages_of(L, ps);
   const int cand_lo = min(n_sink, P);
@@ -153,13 +144,6 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     if (cand_lo != n_sink && j < max_pages) pv = page_table[(size_t)b * pt_stride + j];  // short sequence
     sh.phys[x][tid % 16] = x < ng && j < cand_hi ? pv : -1;
   }
-  // q of the wave's 16 heads: column n = head 16 wave + n, channels 32i + 8kg ..
-  uint4 qraw[kMlaD / 32];
-  {
-    const uint16_t *qg = q + ((size_t)b * Hq + (size_t)wave * 16) * kMlaD;
-#pragma unroll
-    for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qg + (size_t)n * kMlaD + 32 * i + 8 * kg);
-  }
   __syncthreads();  // sh.phys is complete
 
   // every record of group x, straight to its slab: transfer t fills slots
@@ -169,28 +153,43 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   auto slab_of = [&](int x) -> char * {
     return (char *)(x == 0 ? slab0 : x == 1 ? slab1 : x == 2 ? slab2 : slab3);
   };
-  // (the page ids of a wave's transfers are read from LDS before any is issued)
-  constexpr int kDmaPerWave = (kDmaPerGroup + kMlaWaves - 1) / kMlaWaves;
-  auto issue_group = [&](int x) {
-    char *slab = slab_of(x);
-    int ph[kDmaPerWave];
+  // the records of group x reach its slab through registers: load k of this
+  // wave (t = wave + 8 k < 36) fills slots 64 t .. 64 t + 63, lane l loading
+  // the chunk whose swizzled slot is 64 t + l.  (Loads straight into LDS
+  // would make the compiler wait for every one still in flight before any LDS
+  // read, so no group could be contracted while the next one loads.)
+  constexpr int kLdPerWave = (kDmaPerGroup + kMlaWaves - 1) / kMlaWaves;
+  // (every wave issues kLdPerWave loads: a load past the 36 of a group
+  // repeats the group's last one and is not stored)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // (a plain vector: the arrays stay in registers)
+  auto load_group = [&](int x, u32x4 (&st)[kLdPerWave]) __attribute__((always_inline)) {
+    int ph[kLdPerWave];  // the page ids are read from LDS before any load is issued
 #pragma unroll
-    for (int k = 0; k < kDmaPerWave; k++) {
-      const int t = wave + kMlaWaves * k;
-      ph[k] = t < kDmaPerGroup ? max(sh.phys[x][(64 * t + lane) / kRecU4], 0) : 0;
+    for (int k = 0; k < kLdPerWave; k++) {
+      const int t = min(wave + kMlaWaves * k, kDmaPerGroup - 1);
+      ph[k] = max(sh.phys[x][(64 * t + lane) / kRecU4], 0);
     }
 #pragma unroll
-    for (int k = 0; k < kDmaPerWave; k++) {
-      const int t = wave + kMlaWaves * k;  // wave-uniform
-      if (t < kDmaPerGroup) {
-        const int slot = 64 * t + lane, r = slot / kRecU4, sl = slot % kRecU4;
-        const uint16_t *src = summ + summ_record(ph[k], g, Hkv) * kMlaK2 + 8 * (sl ^ (r & 15));
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(slab + 1024 * t), 16, 0, 0);
-      }
+    for (int k = 0; k < kLdPerWave; k++) {
+      const int t = min(wave + kMlaWaves * k, kDmaPerGroup - 1);
+      const int slot = 64 * t + lane, r = slot / kRecU4, sl = slot % kRecU4;
+      st[k] = *(const u32x4 *)(summ + summ_record(ph[k], g, Hkv) * kMlaK2 + 8 * (sl ^ (r & 15)));
     }
   };
-  if (ng > 0) issue_group(0);
-  if (ng > 1) issue_group(1);
+  auto store_group = [&](int x, const u32x4 (&st)[kLdPerWave]) __attribute__((always_inline)) {
+    char *slab = slab_of(x);
+#pragma unroll
+    for (int k = 0; k < kLdPerWave; k++) {
+      const int t = wave + kMlaWaves * k;
+      if (t < kDmaPerGroup) *(u32x4 *)(slab + 1024 * t + 16 * lane) = st[k];
+    }
+  };
+  // two groups in flight: A holds groups 0 and 2, B groups 1 and 3.  Groups
+  // past the block's (sh.phys -1) load page 0's record, never used, so that
+  // the loads do not depend on ng.
+  u32x4 stA[kLdPerWave], stB[kLdPerWave];
+  load_group(0, stA);
+  load_group(1, stB);
 
   // the largest |q_h| of the wave's heads
   {
@@ -209,12 +208,6 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const float qmax = wave_max(sqrtf(s2));
     if (lane == 0) sh.qnorm[wave] = qmax;
   }
-  // groups 0 and 1 have landed (this wave's part); groups 2 and 3 load while
-  // they are contracted
-  __builtin_amdgcn_s_waitcnt(0);
-  if (ng > 2) issue_group(2);
-  if (ng > 3) issue_group(3);
-  lds_barrier(false);
 
   // contracts group x: every wave's top two heads and partial norm per page
   auto contract = [&](int x) {
@@ -326,19 +319,26 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
       sh.out[x][lane] = score::make_score(m, bound, m2, arg, kErrRelMla);
     }
   };
+  // group x goes to LDS once its loads have landed (the compiler waits for
+  // exactly those registers), then group x + 2 loads into the same registers
+  // and group x is contracted while x + 1 and x + 2 load
+  store_group(0, stA);
+  __syncthreads();
+  load_group(2, stA);
   if (ng > 0) contract(0);
+  store_group(1, stB);
+  __syncthreads();
+  load_group(3, stB);
   if (ng > 1) contract(1);
-  lds_barrier(true);  // groups 2 and 3 have landed; the results of 0 and 1 are in LDS
-  // two waves combine groups 0 and 1 before contracting 2 and 3, two others
-  // combine 2 and 3 at the end
-  finish(0, kMlaWaves - 2);
-  finish(1, kMlaWaves - 1);
+  store_group(2, stA);
+  __syncthreads();
   if (ng > 2) contract(2);
+  store_group(3, stB);
+  __syncthreads();
   if (ng > 3) contract(3);
-  lds_barrier(false);
-  finish(2, 0);
-  finish(3, 1);
-  lds_barrier(false);
+  __syncthreads();  // every wave's results of every group are in LDS
+  if (wave < ng) finish(wave, wave);
+  __syncthreads();
   for (int t = tid; t < 16 * ng; t += kMlaWaves * 64) {
     const int j = j0 + t;
     if (j < cand_hi) row[j] = sh.out[t / 16][t % 16];
