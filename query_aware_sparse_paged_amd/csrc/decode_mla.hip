@@ -153,13 +153,17 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
     return (pos < L) & (!is_static | (pos < sink_end) | (pos >= win_begin));
   };
 
-  // q^T of the wave's S heads: column n = head 32 hg + 16 ht + n, channels
-  // 32i + 8kg ..; loaded first, so they arrive while the pages are selected
   const size_t head_base = (size_t)b * Hq + (size_t)g * kG + kHeads * hg;
+  // q^T of the wave's S heads: column n = head 32 hg + 16 ht + n, channels
+  // 32i + 8kg ..; with the selection, loaded right after its score loads are
+  // issued (loads complete in order: q first would hold the scores up)
   uint4 qB[kD / 32];
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < kD / 32; i++)
-    qB[i] = *(const uint4 *)(q + (head_base + 16 * ht + n) * kD + 32 * i + 8 * kg);
+    for (int i = 0; i < kD / 32; i++)
+      qB[i] = *(const uint4 *)(q + (head_base + 16 * ht + n) * kD + 32 * i + 8 * kg);
+  };
+  if constexpr (!SELECT) load_q();
 
   // the block's pages that hold an attended position
   const int32_t *list = sel + (size_t)unit * max_sel;
@@ -176,7 +180,8 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
                                          kPS, is_static, n_sink, n_local, top_k, sink_tokens, window_tokens,
                                          q + ((size_t)b * Hq + (size_t)g * kG) * kD, kG, summ,
                                          page_table + (size_t)b * pt_stride, Hkv, g,
-                                         first_block ? sel + (size_t)unit * max_sel : nullptr, lds_list, max_sel);
+                                         first_block ? sel + (size_t)unit * max_sel : nullptr, lds_list, max_sel,
+                                         load_q);
     if (first_block && tid == 0) sel_count[unit] = count;
     __syncthreads();  // the list is complete
     list = lds_list;

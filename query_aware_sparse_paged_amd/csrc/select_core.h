@@ -1021,12 +1021,19 @@ __device__ int emit_selection(SelShared<NW> &sh, const uint32_t *sel_bits, int n
 //   bits    LDS, 2 * nwords words (nwords = ceil(max_pages / 32));
 //   row     the unit's scores, indexed by logical page;
 //   qg      the group's first q row (global; may be null for static heads);
-//   pt_row  the sequence's page-table row.
-template <int D, int NW>
+//   pt_row  the sequence's page-table row;
+//   after_issue  called once by every thread right after its score loads are
+//           issued (before any is waited for): loads the caller issues there
+//           complete behind the scores, not ahead of them.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <int D, int NW, typename AfterIssue = NoHook>
 __device__ int select_unit(SelShared<NW> &sh, uint64_t *keys64, uint32_t *bits, int nwords, const qasp_score *row,
                            int L, int ps, bool is_static, int n_sink, int n_local, int top_k, int sink_tokens,
                            int window_tokens, const uint16_t *qg, int G, const uint16_t *summ, const int32_t *pt_row,
-                           int Hkv, int g, int32_t *out_global, int32_t *out_lds, int max_sel) {
+                           int Hkv, int g, int32_t *out_global, int32_t *out_lds, int max_sel,
+                           AfterIssue after_issue = AfterIssue()) {
   constexpr int THREADS = NW * kWave;
   const int tid = threadIdx.x;
   uint32_t *keys32 = (uint32_t *)keys64;  // aliases keys64 until the band step
@@ -1043,25 +1050,39 @@ __device__ int select_unit(SelShared<NW> &sh, uint64_t *keys64, uint32_t *bits, 
   const qasp_score *crow = row + cand_lo;
   float e_loc = 0.f;
   uint32_t k_min = ~0u, k_max = 0;
+  // a round issues kLoadUnroll score loads per thread, then turns them into
+  // keys; after_issue comes between the first round's two halves, at one
+  // call site (the empty asm keeps the compiler from moving the caller's
+  // loads ahead of the scores')
+  qasp_score sc[kLoadUnroll];
+  auto issue = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kLoadUnroll; u++) {
+      const int i = i0 + u * THREADS + tid;
+      sc[u] = i < n ? crow[i] : qasp_score{-INFINITY, 0.f, -1, 0};
+    }
+  };
+  auto to_keys = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kLoadUnroll; u++) {
+      const int i = i0 + u * THREADS + tid;
+      if (i < n) {
+        const uint32_t o = f32_order(sc[u].value);
+        keys32[i] = o;
+        k_min = min(k_min, o);
+        k_max = max(k_max, o);
+        e_loc = fmaxf(e_loc, sc[u].err);
+      }
+    }
+  };
+  if (ranked) issue(0);
+  asm volatile("" ::: "memory");
+  after_issue();
   if (ranked) {
-    for (int i0 = 0; i0 < n; i0 += kLoadUnroll * THREADS) {
-      qasp_score sc[kLoadUnroll];
-#pragma unroll
-      for (int u = 0; u < kLoadUnroll; u++) {
-        const int i = i0 + u * THREADS + tid;
-        sc[u] = i < n ? crow[i] : qasp_score{-INFINITY, 0.f, -1, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < kLoadUnroll; u++) {
-        const int i = i0 + u * THREADS + tid;
-        if (i < n) {
-          const uint32_t o = f32_order(sc[u].value);
-          keys32[i] = o;
-          k_min = min(k_min, o);
-          k_max = max(k_max, o);
-          e_loc = fmaxf(e_loc, sc[u].err);
-        }
-      }
+    to_keys(0);
+    for (int i0 = kLoadUnroll * THREADS; i0 < n; i0 += kLoadUnroll * THREADS) {
+      issue(i0);
+      to_keys(i0);
     }
   }
   for (int w = tid; w < nwords; w += THREADS) {
