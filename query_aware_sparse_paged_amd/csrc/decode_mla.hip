@@ -73,6 +73,10 @@ constexpr float kHeadroom = 64.f;                // weights stay below 2^64 (log
 static_assert(kXfer * 1024 == kBufBytes && kRowSlots == kRowU4 + 1, "whole transfers per page buffer");
 static_assert(kBufBytes % 16 == 0 && kKRow % 16 == 0 && kPRow % 16 == 0, "LDS alignment");
 static_assert(kMlaPagesPerSplit <= 16, "page list");
+constexpr int kQChunks = kHeads * kD / 8;        // 16-byte chunks of the block's q rows: 2304
+constexpr int kQLoads = (kQChunks + kThreads - 1) / kThreads;  // 5 per lane (the last for half the lanes)
+constexpr int kQRow = kD * 2 + 16;               // LDS row of one head's q (padded: conflict-free reads)
+static_assert(kHeads * kQRow <= kBufBytes && kRowU4 == kD / 8, "q staging fits the second page buffer");
 
 struct MlaDecodeShared {
   int2 pages[kMlaPagesPerSplit];  // (physical page, first position) of the block's pages
@@ -154,14 +158,21 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
   };
 
   const size_t head_base = (size_t)b * Hq + (size_t)g * kG + kHeads * hg;
-  // q^T of the wave's S heads: column n = head 32 hg + 16 ht + n, channels
-  // 32i + 8kg ..; with the selection, loaded right after its score loads are
-  // issued (loads complete in order: q first would hold the scores up)
-  uint4 qB[kD / 32];
+  // q of the block's 32 heads (36 KB) is loaded coalesced, 16 bytes per lane
+  // and load (chunk c = tid + 512 k of the heads' contiguous rows), then goes
+  // through LDS (rows padded to kQRow bytes) into the MFMA layout: q^T of the
+  // wave's S heads, column n = head 32 hg + 16 ht + n, channels 32i + 8kg ..
+  // (Loading that layout straight from memory touches 16 rows per load and
+  // took ~3 us longer.)  With the selection, the loads are issued right after
+  // its score loads (loads complete in order: q first would hold them up).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // (a plain vector: the array stays in registers)
+  u32x4 qs[kQLoads];
   auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kD / 32; i++)
-      qB[i] = *(const uint4 *)(q + (head_base + 16 * ht + n) * kD + 32 * i + 8 * kg);
+    for (int k = 0; k < kQLoads; k++) {
+      const int c = tid + kThreads * k;
+      qs[k] = *(const u32x4 *)(q + head_base * kD + 8 * min(c, kQChunks - 1));
+    }
   };
   if constexpr (!SELECT) load_q();
 
@@ -207,9 +218,24 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(
     }
   }
 
-  // q has landed before the page loop: otherwise the loop's first products
-  // carry waits for q's loads, which the in-order load counter turns into
-  // waits for the page loads issued in the previous iteration
+  // q into the MFMA layout through the second page buffer (free until the
+  // page loop starts; the selection's LDS lies in the first)
+  {
+    char *qstage = (char *)kbuf1;
+#pragma unroll
+    for (int k = 0; k < kQLoads; k++) {
+      const int c = tid + kThreads * k;
+      if (c < kQChunks) *(u32x4 *)(qstage + (c / kRowU4) * kQRow + 16 * (c % kRowU4)) = qs[k];
+    }
+  }
+  __syncthreads();
+  uint4 qB[kD / 32];
+#pragma unroll
+  for (int i = 0; i < kD / 32; i++)
+    qB[i] = *(const uint4 *)((const char *)kbuf1 + (16 * ht + n) * kQRow + 64 * i + 16 * kg);
+  // q is in registers before the page loop (which then reuses kbuf1), and
+  // every load has landed: otherwise the loop's first products carry waits
+  // that the in-order load counter turns into waits for page loads
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int npages = sh.npages;
