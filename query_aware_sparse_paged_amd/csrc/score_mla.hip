@@ -20,11 +20,11 @@
 // A block takes up to kMlaGroups consecutive 16-page groups of one sequence
 // and stages their summary records in one LDS slab per group, through
 // registers (16 bytes per lane and load): two groups are in flight while the
-// one before them is contracted.  Chunk
-// c (16 bytes) of page row n sits at slot c ^ (n % 16) of the row, so the 16
-// rows of an MFMA B fragment fall on different banks.  The block also writes
-// the row's non-candidate slots (-inf), so the score row needs no separate
-// fill.
+// one before them is contracted.  Chunk c (16 bytes) of page row n sits at
+// slot c ^ (n % 16) of the row, so the 16 rows of an MFMA B fragment fall on
+// different banks.  Before the first group, the slabs carry the sequence's q
+// (loaded coalesced) into the MFMA layout.  The block also writes the row's
+// non-candidate slots (-inf), so the score row needs no separate fill.
 #include "launch.h"
 #include "score_core.h"
 
@@ -55,6 +55,18 @@ constexpr int kRecU4 = kMlaK2 / 8;              // 144 chunks of 16 bytes per re
 constexpr int kDmaPerGroup = 16 * kRecU4 / 64;  // 36 wave-wide 1 KB loads per group
 static_assert(kRecU4 % 16 == 0 && (16 * kRecU4) % 64 == 0, "swizzle and transfer granularity");
 
+
+// Workgroup barrier for LDS data: waits for this wave's LDS operations, not
+// for its global loads and stores (a __syncthreads also waits for those,
+// which here would hold the group loads up behind q's, or every load behind
+// the first block's stores).  The empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt and expcnt at their maximum, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Negative and non-negative parts of four bf16 pairs: an arithmetic shift of
 // each 16-bit half by 15 gives its sign mask (one packed instruction), so
@@ -93,9 +105,8 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
     qasp_score *__restrict__ scores, int batch, int pt_stride, int max_pages, int Hq, int Hkv, int ps,
     int n_sink, int n_local, uint64_t static_mask, int groups_per_seq, TokenAppend ap) {
-  // one LDS object per group slab (see the file comment)
-  __shared__ uint4 slab0[kGroupBytes / 16], slab1[kGroupBytes / 16], slab2[kGroupBytes / 16],
-      slab3[kGroupBytes / 16];
+  // the four group slabs, one after the other (also q's way into the MFMA layout)
+  __shared__ uint4 slabs[kMlaGroups * kGroupBytes / 16];
   static_assert(kMlaGroups == 4, "four slabs: two loading while two are contracted");
   __shared__ MlaScoreShared sh;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -115,13 +126,21 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
     const int j = n_sink + gfirst * 16 + tid;
     if (tid < 16 * kMlaGroups && j < max_pages) pv = page_table[(size_t)b * pt_stride + j];
   }
-  // q of the wave's 16 heads: column n = head 16 wave + n, channels 32i + 8kg ..
-  // (loaded with the page-table entries)
-  uint4 qraw[kMlaD / 32];
+  // q of the sequence's 128 heads (144 KB), loaded with the page-table
+  // entries, coalesced: chunk c = tid + 512 k (16 bytes) of the heads'
+  // contiguous rows.  It reaches the MFMA layout through LDS below (loading
+  // that layout straight from memory touches 16 head rows per load and is
+  // several us slower).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // (a plain vector: arrays stay in registers)
+  constexpr int kQChunks = kMlaWaves * 16 * kMlaD / 8;  // 9216
+  static_assert(kQChunks % (kMlaWaves * 64) == 0 && kQChunks * 16 == kMlaGroups * kGroupBytes,
+                "q fills the four slabs exactly");
+  constexpr int kQLoads = kQChunks / (kMlaWaves * 64);  // 18
+  u32x4 qc[kQLoads];
   {
-    const uint16_t *qg = q + ((size_t)b * Hq + (size_t)wave * 16) * kMlaD;
+    const uint16_t *qb = q + (size_t)b * Hq * kMlaD;
 #pragma unroll
-    for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qg + (size_t)n * kMlaD + 32 * i + 8 * kg);
+    for (int k = 0; k < kQLoads; k++) qc[k] = *(const u32x4 *)(qb + 8 * (tid + kMlaWaves * 64 * k));
   }
   const int L = seq_lens[b];
   const int P = num_pages_of(L, ps);
@@ -141,18 +160,21 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   const int j0 = cand_lo + gfirst * 16;
   if (tid < 16 * kMlaGroups) {
     const int x = tid / 16, j = j0 + tid;
-    if (cand_lo != n_sink && j < max_pages) pv = page_table[(size_t)b * pt_stride + j];  // short sequence
-    sh.phys[x][tid % 16] = x < ng && j < cand_hi ? pv : -1;
+    const bool cand = x < ng && j < cand_hi;
+    if (cand_lo != n_sink) {  // short sequence: re-read (block-uniform; apart, so the usual path waits only for pv)
+      const int pv2 = j < max_pages ? page_table[(size_t)b * pt_stride + j] : -1;
+      sh.phys[x][tid % 16] = cand ? pv2 : -1;
+    } else {
+      sh.phys[x][tid % 16] = cand ? pv : -1;
+    }
   }
-  __syncthreads();  // sh.phys is complete
+  lds_barrier();  // sh.phys is complete
 
   // every record of group x, straight to its slab: transfer t fills slots
   // 64 t .. 64 t + 63 (row slot / 144), lane l loading the chunk whose
   // swizzled slot is 64 t + l; rows past the candidates read page 0 (their
   // columns are never stored)
-  auto slab_of = [&](int x) -> char * {
-    return (char *)(x == 0 ? slab0 : x == 1 ? slab1 : x == 2 ? slab2 : slab3);
-  };
+  auto slab_of = [&](int x) -> char * { return (char *)slabs + x * kGroupBytes; };
   // the records of group x reach its slab through registers: load k of this
   // wave (t = wave + 8 k < 36) fills slots 64 t .. 64 t + 63, lane l loading
   // the chunk whose swizzled slot is 64 t + l.  (Loads straight into LDS
@@ -190,6 +212,27 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   u32x4 stA[kLdPerWave], stB[kLdPerWave];
   load_group(0, stA);
   load_group(1, stB);
+
+  // q into the MFMA layout: chunk c (head c / 72, piece p = c % 72) goes to
+  // row c / 72 of the slab area at position p ^ (head % 8), so that the 8
+  // rows of a wave's b128 reads fall on different banks; the wave then reads
+  // q of its 16 heads, column n = head 16 wave + n, channels 32i + 8kg ..
+  // (piece 4i + kg).  The slabs are free until group 0 is stored.
+#pragma unroll
+  for (int k = 0; k < kQLoads; k++) {
+    const int c = tid + kMlaWaves * 64 * k, h = c / (kMlaD / 8), pc = c % (kMlaD / 8);
+    *(u32x4 *)((char *)slabs + h * (2 * kMlaD) + 16 * (pc ^ (h & 7))) = qc[k];
+  }
+  lds_barrier();
+  uint4 qraw[kMlaD / 32];
+  {
+    // piece 4i + kg of row 16 wave + n sits at 4 (i ^ (s >> 2)) + (kg ^ (s & 3)), s = n % 8
+    const int sq = n & 7;
+    const char *qrow = (const char *)slabs + (16 * wave + n) * (2 * kMlaD) + 16 * (kg ^ (sq & 3));
+#pragma unroll
+    for (int i = 0; i < kMlaD / 32; i++) qraw[i] = *(const uint4 *)(qrow + 64 * (i ^ (sq >> 2)));
+  }
+  lds_barrier();  // the slabs take the groups next
 
   // the largest |q_h| of the wave's heads
   {
@@ -323,22 +366,22 @@ __global__ __launch_bounds__(kMlaWaves * 64) void score_mla_kernel(
   // exactly those registers), then group x + 2 loads into the same registers
   // and group x is contracted while x + 1 and x + 2 load
   store_group(0, stA);
-  __syncthreads();
+  lds_barrier();
   load_group(2, stA);
   if (ng > 0) contract(0);
   store_group(1, stB);
-  __syncthreads();
+  lds_barrier();
   load_group(3, stB);
   if (ng > 1) contract(1);
   store_group(2, stA);
-  __syncthreads();
+  lds_barrier();
   if (ng > 2) contract(2);
   store_group(3, stB);
-  __syncthreads();
+  lds_barrier();
   if (ng > 3) contract(3);
-  __syncthreads();  // every wave's results of every group are in LDS
+  lds_barrier();  // every wave's results of every group are in LDS
   if (wave < ng) finish(wave, wave);
-  __syncthreads();
+  lds_barrier();
   for (int t = tid; t < 16 * ng; t += kMlaWaves * 64) {
     const int j = j0 + t;
     if (j < cand_hi) row[j] = sh.out[t / 16][t % 16];
